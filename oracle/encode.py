@@ -1,0 +1,124 @@
+"""TurboQuant encode (oracle): per-vector quantisers, in the pages' order.
+
+Inputs are the exact float64 values of the fp16/bf16 K/V vectors, shape (..., d).
+Every function also returns which decisions sit within ``BAND`` (1e-6) of a
+decision threshold, measured in that quantiser's normalised input; the GPU
+comparison excludes exactly those and reports how many there were.
+
+Keys, LM + QJL (TurboQuant vLLM guide, section 2 steps 1-3; TurboQuant benchmark
+page, compression algorithm details): rotate, quantise every coordinate with the
+Lloyd-Max codebook, then keep one sign bit per dimension of a Gaussian projection
+of the quantisation residual so that the inner-product estimate is unbiased.
+
+Values, group-32 symmetric (TurboQuant vLLM guide, section 2 step 4): each group
+of 32 consecutive channels gets one scale and symmetric 2- or 4-bit levels.
+
+Keys, per-block affine 8-bit and values, rotated Lloyd-Max 3-bit (vllm-metal
+TurboQuant guide, quantisation principle table): keys keep their own scale and
+offset per block with no rotation; values are rotated, then mapped to the
+8-centroid codebook.
+
+Readings where the pages are silent (each also listed in the design notes):
+  * the vector is normalised before rotation; its norm n (and the residual norm
+    gamma) are kept as fp16, rounded to nearest-even; the rotated-LM value norm is fp32;
+  * LM decision: idx_j = #{i : t_i < y_j} with float32 thresholds t_i (ties go low);
+  * the QJL projection acts on the rotated-domain residual r = y - c[idx];
+    S is d x d i.i.d. N(0,1); stored bit = (z_j >= 0), z = S r.  The sign is decided in
+    float32, z = fl32(S) . fl32(r) accumulated in float32 -- the kernel's precision;
+  * group scale Delta = fp16(2 amax / (L-1)), idx = clamp(rne(v/Delta + (L-1)/2), 0, L-1)
+    with the stored Delta; Delta = 0 gives idx = L-1, 0, L/2 for v > 0, v < 0, v = 0;
+  * affine scale a = fp16((max-min)/255), offset m = fp16(min), q = clamp(rne((k-m)/a), 0, 255);
+    a = 0 gives q = 0.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .rotation import rotation_matrix
+
+BAND = 1e-6
+
+
+def _lm_decide(y: np.ndarray, thresholds32: np.ndarray):
+    t = thresholds32.astype(np.float64)
+    idx = np.zeros(y.shape, dtype=np.int64)
+    near = np.zeros(y.shape, dtype=bool)
+    for ti in t:
+        idx += (y > ti)
+        near |= np.abs(y - ti) < BAND
+    return idx, near
+
+
+def encode_k_lm_qjl(k: np.ndarray, signs: np.ndarray, S32: np.ndarray,
+                    centroids32: np.ndarray, thresholds32: np.ndarray) -> dict:
+    d = k.shape[-1]
+    # norm and unit vector
+    n = np.sqrt(np.sum(k * k, axis=-1))
+    safe = np.where(n > 0, n, 1.0)
+    u = np.where(n[..., None] > 0, k / safe[..., None], 0.0)
+    # step 1: random rotation
+    y = u @ rotation_matrix(signs).T
+    # step 2: Lloyd-Max indices
+    idx, near_lm = _lm_decide(y, thresholds32)
+    # step 3: residual and its sign sketch
+    r = y - centroids32.astype(np.float64)[idx]
+    gamma = np.sqrt(np.sum(r * r, axis=-1))
+    z32 = r.astype(np.float32) @ S32.T                  # float32 decision
+    z64 = r @ S32.astype(np.float64).T                  # exact reference, for the band only
+    bits = z32 >= 0
+    near_qjl = (np.abs(z64) < BAND) | (np.abs(z32) < BAND)
+    # a vector with a near-threshold LM index may legitimately differ in its residual,
+    # so all of its sign bits are excluded too
+    near_qjl |= np.any(near_lm, axis=-1, keepdims=True)
+    return {
+        "idx": idx, "qjl": bits,
+        "n16": n.astype(np.float16), "g16": gamma.astype(np.float16),
+        "near_idx": near_lm, "near_qjl": near_qjl,
+        "y": y, "z": z64,
+    }
+
+
+def encode_v_group_sym(v: np.ndarray, bits: int) -> dict:
+    d = v.shape[-1]
+    L = 1 << bits
+    vg = v.reshape(v.shape[:-1] + (d // 32, 32))
+    amax = np.max(np.abs(vg), axis=-1)
+    scale16 = (2.0 * amax / (L - 1)).astype(np.float16)
+    delta = scale16.astype(np.float64)[..., None]
+    off = (L - 1) / 2.0
+    with np.errstate(divide="ignore", invalid="ignore"):
+        x = vg / delta + off
+    idx = np.clip(np.rint(x), 0, L - 1)
+    zero = np.broadcast_to(delta == 0, vg.shape)
+    idx = np.where(zero, np.where(vg > 0, L - 1, np.where(vg < 0, 0, L // 2)), idx).astype(np.int64)
+    frac = x - np.floor(x)
+    near = (~zero) & (np.abs(frac - 0.5) < BAND)
+    return {"idx": idx.reshape(v.shape), "scale16": scale16,
+            "near_idx": near.reshape(v.shape)}
+
+
+def encode_k_affine8(k: np.ndarray) -> dict:
+    d = k.shape[-1]
+    kg = k.reshape(k.shape[:-1] + (d // 32, 32))
+    lo = np.min(kg, axis=-1)
+    hi = np.max(kg, axis=-1)
+    a16 = ((hi - lo) / 255.0).astype(np.float16)
+    m16 = lo.astype(np.float16)
+    a = a16.astype(np.float64)[..., None]
+    m = m16.astype(np.float64)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        x = (kg - m) / a
+    q = np.where(a == 0, 0, np.clip(np.rint(x), 0, 255)).astype(np.int64)
+    frac = x - np.floor(x)
+    near = (a != 0) & (np.abs(frac - 0.5) < BAND)
+    return {"q8": q.reshape(k.shape), "a16": a16, "m16": m16, "near_idx": near.reshape(k.shape)}
+
+
+def encode_v_lm_rot(v: np.ndarray, signs: np.ndarray,
+                    centroids32: np.ndarray, thresholds32: np.ndarray) -> dict:
+    n = np.sqrt(np.sum(v * v, axis=-1))
+    safe = np.where(n > 0, n, 1.0)
+    u = np.where(n[..., None] > 0, v / safe[..., None], 0.0)
+    y = u @ rotation_matrix(signs).T
+    idx, near = _lm_decide(y, thresholds32)
+    return {"idx": idx, "n32": n.astype(np.float32), "near_idx": near, "y": y}
