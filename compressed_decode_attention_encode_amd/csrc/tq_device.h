@@ -1,0 +1,75 @@
+// Device helpers for the gfx950 kernels: input conversion, exact fp64 -> fp16
+// rounding, and wavefront (64-lane) reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "../../include/tq.h"
+
+namespace tq {
+
+constexpr int kWave = 64;
+
+// fp16 / bf16 storage bits -> float (exact).
+template <int DT>
+__device__ __forceinline__ float in_to_f32(uint32_t bits16) {
+  if constexpr (DT == TQ_F16) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+  } else {
+    return __uint_as_float(bits16 << 16);
+  }
+}
+
+__device__ __forceinline__ float f16_to_f32(uint32_t bits16) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+
+// float64 -> fp16 bits, round to nearest even, computed directly from the double
+// (no intermediate float rounding).  Overflow gives +-inf.
+__device__ __forceinline__ uint32_t f64_to_f16_rne(double x) {
+  uint64_t b = (uint64_t)__double_as_longlong(x);
+  uint32_t sign = (uint32_t)(b >> 48) & 0x8000u;
+  b &= 0x7FFFFFFFFFFFFFFFull;
+  if (b >= 0x7FF0000000000000ull) return sign | 0x7C00u | (b > 0x7FF0000000000000ull ? 0x200u : 0u);
+  if (b == 0) return sign;
+  int e = (int)(b >> 52) - 1023;
+  uint64_t m = (b & 0x000FFFFFFFFFFFFFull) | 0x0010000000000000ull;  // 53-bit significand
+  if (e < -25) return sign;                                             // below half the smallest subnormal
+  int shift = (e >= -14) ? 42 : 42 + (-14 - e);                        // bits to drop
+  uint64_t keep = m >> shift;
+  uint64_t rem = m & ((1ull << shift) - 1);
+  uint64_t half = 1ull << (shift - 1);
+  if (rem > half || (rem == half && (keep & 1))) keep += 1;
+  if (e >= -14) {
+    int ee = e + 15;
+    if (keep == (1ull << 11)) { keep >>= 1; ee += 1; }
+    if (ee >= 31) return sign | 0x7C00u;
+    return sign | ((uint32_t)ee << 10) | ((uint32_t)keep & 0x3FFu);
+  }
+  return sign | (uint32_t)keep;  // subnormal (keep == 0x400 encodes the smallest normal)
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) v += __shfl_xor(v, m);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) v = fmaxf(v, __shfl_xor(v, m));
+  return v;
+}
+
+// Sum over the `n` consecutive lanes that share lane / n (n a power of two <= 64).
+template <int N, typename T>
+__device__ __forceinline__ T group_sum(T v) {
+#pragma unroll
+  for (int m = 1; m < N; m <<= 1) v += __shfl_xor(v, m);
+  return v;
+}
+
+}  // namespace tq

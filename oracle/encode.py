@@ -28,7 +28,12 @@ Readings where the pages are silent (each also listed in the design notes):
   * group scale Delta = fp16(2 amax / (L-1)), idx = clamp(rne(v/Delta + (L-1)/2), 0, L-1)
     with the stored Delta; Delta = 0 gives idx = L-1, 0, L/2 for v > 0, v < 0, v = 0;
   * affine scale a = fp16((max-min)/255), offset m = fp16(min), q = clamp(rne((k-m)/a), 0, 255);
-    a = 0 gives q = 0.
+    a = 0 gives q = 0;
+  * a quotient lying exactly on a half-integer is an exact tie, decided by round-half-
+    to-even and compared like any other element; only inexact values within BAND of a
+    boundary are marked near.  Exact ties are common with fp16 inputs (a value that is
+    an exact multiple of the stored scale), and they are detected in exact arithmetic:
+    the doubled quotient is an integer r with r * scale reproducing the doubled numerator.
 """
 from __future__ import annotations
 
@@ -37,6 +42,19 @@ import numpy as np
 from .rotation import rotation_matrix
 
 BAND = 1e-6
+
+
+def _exact_half(num: np.ndarray, den: np.ndarray, off: float) -> np.ndarray:
+    """num/den + off lies exactly on a half-integer (num, den dyadic; num exact in float64).
+
+    2 num/den + 2 off must be an odd integer r' ; with r = 2 num/den rounded to an integer,
+    r * den == 2 num is an exact float64 identity for the small integers involved.
+    """
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = np.rint(2.0 * num / den)
+        exact = (den != 0) & (r * den == 2.0 * num)
+    odd = np.mod(r + 2.0 * off, 2.0) == 1.0
+    return exact & odd
 
 
 def _lm_decide(y: np.ndarray, thresholds32: np.ndarray):
@@ -92,7 +110,7 @@ def encode_v_group_sym(v: np.ndarray, bits: int) -> dict:
     zero = np.broadcast_to(delta == 0, vg.shape)
     idx = np.where(zero, np.where(vg > 0, L - 1, np.where(vg < 0, 0, L // 2)), idx).astype(np.int64)
     frac = x - np.floor(x)
-    near = (~zero) & (np.abs(frac - 0.5) < BAND)
+    near = (~zero) & (np.abs(frac - 0.5) < BAND) & ~_exact_half(vg, delta, (L - 1) / 2.0)
     return {"idx": idx.reshape(v.shape), "scale16": scale16,
             "near_idx": near.reshape(v.shape)}
 
@@ -110,7 +128,7 @@ def encode_k_affine8(k: np.ndarray) -> dict:
         x = (kg - m) / a
     q = np.where(a == 0, 0, np.clip(np.rint(x), 0, 255)).astype(np.int64)
     frac = x - np.floor(x)
-    near = (a != 0) & (np.abs(frac - 0.5) < BAND)
+    near = (a != 0) & (np.abs(frac - 0.5) < BAND) & ~_exact_half(kg - m, a, 0.0)
     return {"q8": q.reshape(k.shape), "a16": a16, "m16": m16, "near_idx": near.reshape(k.shape)}
 
 

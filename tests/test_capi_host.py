@@ -1,0 +1,160 @@
+"""C-ABI host side, no GPU: the library loads, exports every declared symbol, its host
+math matches the oracle, and every argument check fails loudly before any HIP call."""
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import codebook as cb
+from oracle import layout as OL
+from oracle import rotation as R
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+tq = pytest.importorskip("compressed_decode_attention_encode_amd.tq",
+                         reason="libtq.so not built (run __graft_entry__.build())")
+
+
+def declared_symbols():
+    text = open(os.path.join(ROOT, "include", "tq.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(tq_\w+)\s*\(", text, re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_symbols()
+    assert set(names) == set(tq.EXPORTED)
+    for n in names:
+        assert hasattr(tq._lib, n)
+
+
+@pytest.mark.parametrize("d", [64, 128, 256, 512])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_codebook_matches_oracle(d, bits):
+    c, t, dist = tq.tq_make_codebook(d, bits)
+    c2, t2 = cb.codebook_f32(d, bits)
+    # independent solvers (quadrature vs incomplete beta) agree to the last float32 bit
+    assert np.array_equal(c, c2) and np.array_equal(t, t2)
+    c64, _ = cb.lloyd_max(d, bits)
+    assert abs(dist - cb.distortion(c64, d)) < 1e-12
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_rotation_state_matches_reference_generator(d):
+    s, q = tq.tq_make_rotation(d, 20260101 + d)
+    s2, q2 = R.reference_rotation_state(d, 20260101 + d)
+    assert np.array_equal(s, s2)
+    assert np.max(np.abs(q.astype(np.float64) - q2.astype(np.float64)) / (1 + np.abs(q2))) <= 2 ** -23
+
+
+CONFIGS = [(64, "lm_qjl", 3, "group_sym", 2), (128, "lm_qjl", 4, "group_sym", 4), (128, "affine8", 8, "lm_rot", 3),
+           (256, "lm_qjl", 4, "group_sym", 4), (128, "lm_qjl", 2, "lm_rot", 2)]
+
+
+@pytest.mark.parametrize("cfg", CONFIGS)
+def test_plane_bytes_match_layout(cfg):
+    d, kk, kb, vk, vb = cfg
+    L = tq.make_layout(d, 8, 2, kk, kb, vk, vb)
+    got = tq.tq_cache_plane_bytes(L, 3, 17)
+    per = OL.bytes_per_token_head(d, kk, kb, vk, vb)
+    rows = 3 * 2 * 17
+    assert got == [rows * per[n] for n in ("k_codes", "k_signs", "k_aux", "v_codes", "v_aux")]
+
+
+# ------------------------------------------------------------------------- argument checks
+FAKE = 0x10000      # aligned non-null address: never dereferenced, checks fail first
+
+
+def _layout(**kw):
+    base = dict(head_dim=128, n_q_heads=8, n_kv_heads=2, k_kind="lm_qjl", k_bits=3, v_kind="group_sym", v_bits=2)
+    base.update(kw)
+    return tq.make_layout(**base)
+
+
+def _state():
+    return tq.tq_state(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+
+
+def _cache(batch=1, cap=256):
+    return tq.tq_cache(FAKE, FAKE, FAKE, FAKE, FAKE, batch, cap)
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(head_dim=96), tq.TQ_ERR_UNSUPPORTED),
+    (dict(n_q_heads=7), tq.TQ_ERR_UNSUPPORTED),
+    (dict(k_bits=5), tq.TQ_ERR_UNSUPPORTED),
+    (dict(k_kind="affine8", k_bits=4), tq.TQ_ERR_UNSUPPORTED),
+    (dict(v_bits=3), tq.TQ_ERR_UNSUPPORTED),
+    (dict(v_kind="lm_rot", v_bits=5), tq.TQ_ERR_UNSUPPORTED),
+    (dict(n_kv_heads=0), tq.TQ_ERR_INVALID),
+    (dict(in_dtype=7), tq.TQ_ERR_UNSUPPORTED),
+])
+def test_encode_rejects_bad_layouts(bad, code):
+    with pytest.raises(tq.TQError) as e:
+        tq.tq_encode(_layout(**bad), _state(), FAKE, FAKE, 1, 16, 0, _cache())
+    assert e.value.status == code
+    assert tq.tq_last_error()
+
+
+def test_encode_rejects_bad_arguments():
+    L = _layout()
+    cases = [
+        (dict(k=None, v=None), tq.TQ_ERR_INVALID),
+        (dict(k=FAKE + 4), tq.TQ_ERR_INVALID),                    # misaligned input
+        (dict(batch=2), tq.TQ_ERR_INVALID),                       # != cache batch
+        (dict(n_tokens=-1), tq.TQ_ERR_INVALID),
+        (dict(dst_offset=250, n_tokens=16), tq.TQ_ERR_CAPACITY),  # 266 > 256
+        (dict(cache=tq.tq_cache(None, FAKE, FAKE, FAKE, FAKE, 1, 256)), tq.TQ_ERR_INVALID),
+        (dict(state=tq.tq_state(FAKE, FAKE, None, None, FAKE, None, None)), tq.TQ_ERR_INVALID),  # no QJL matrix
+    ]
+    for over, code in cases:
+        a = dict(k=FAKE, v=FAKE, batch=1, n_tokens=16, dst_offset=0, cache=_cache(), state=_state())
+        a.update(over)
+        with pytest.raises(tq.TQError) as e:
+            tq.tq_encode(L, a["state"], a["k"], a["v"], a["batch"], a["n_tokens"], a["dst_offset"], a["cache"])
+        assert e.value.status == code, (over, e.value)
+
+
+def test_encode_unsupported_head_dim_512_is_loud():
+    with pytest.raises(tq.TQError) as e:
+        tq.tq_encode(_layout(head_dim=512), _state(), FAKE, FAKE, 1, 16, 0, _cache())
+    assert e.value.status == tq.TQ_ERR_UNSUPPORTED
+
+
+def test_decode_rejects_bad_arguments():
+    L = _layout()
+    ws = tq.tq_decode_workspace_bytes(L, 1, 256)
+    assert ws > 0
+    base = dict(q=FAKE, n_c=100, rk=FAKE, rv=FAKE, n_r=8, rcap=128, out=FAKE, ws=FAKE, wsb=ws, cache=_cache())
+    cases = [
+        (dict(n_c=0, n_r=0), tq.TQ_ERR_INVALID),
+        (dict(n_r=129, rcap=256), tq.TQ_ERR_INVALID),
+        (dict(rk=None), tq.TQ_ERR_INVALID),
+        (dict(rcap=4), tq.TQ_ERR_INVALID),
+        (dict(wsb=16), tq.TQ_ERR_INVALID),
+        (dict(n_c=300), tq.TQ_ERR_CAPACITY),
+        (dict(out=FAKE + 8), tq.TQ_ERR_INVALID),
+        (dict(q=None), tq.TQ_ERR_INVALID),
+    ]
+    for over, code in cases:
+        a = dict(base)
+        a.update(over)
+        with pytest.raises(tq.TQError) as e:
+            tq.tq_decode_attn(L, _state(), a["q"], a["cache"], a["n_c"], a["rk"], a["rv"], a["n_r"], a["rcap"],
+                              a["out"], a["ws"], a["wsb"])
+        assert e.value.status == code, (over, e.value)
+    with pytest.raises(tq.TQError) as e:
+        tq.tq_decode_attn(_layout(n_q_heads=18, n_kv_heads=2), _state(), FAKE, _cache(), 100, None, None, 0, 0,
+                          FAKE, FAKE, 1 << 30)       # n_rep 9: no kernel compiled
+    assert e.value.status == tq.TQ_ERR_UNSUPPORTED
+
+
+def test_workspace_bound_covers_every_length():
+    L = _layout(head_dim=64, n_q_heads=32, n_kv_heads=8)
+    import ctypes
+    bound = tq.tq_decode_workspace_bytes(L, 1, 40000)
+    # the plan for any shorter cache never needs more than the bound
+    for n in list(range(1, 3000, 37)) + [32640, 32768, 40000]:
+        need = tq.tq_decode_workspace_bytes(L, 1, n)
+        assert need <= bound
+    assert tq.tq_strerror(tq.TQ_ERR_CAPACITY) == "cache capacity exceeded"

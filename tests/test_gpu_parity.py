@@ -1,0 +1,196 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Reduced sizes keep every workload's geometry and encoding but shorten the context so
+the oracle finishes in seconds while still spanning several 64-token tiles and a ragged
+tail; the full-size tests run the benchmark's launch configuration and compare sampled
+(batch, kv-head) slices and query heads.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+
+from compressed_decode_attention_encode_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu_ok():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+if not _gpu_ok():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import gpu_harness as H  # noqa: E402
+
+NAMES = list(W.WORKLOADS)
+
+
+def small(name, n_ctx=None, batch=None):
+    wl = W.WORKLOADS[name]
+    n_ctx = n_ctx or (357 + wl.n_recent)          # 5 full tiles + a ragged 37-token tile
+    return wl.scaled(n_ctx, batch=batch or min(wl.batch, 2))
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_encode_parity(name):
+    wl = small(name)
+    s = H.Setup(wl)
+    K, V = s.kv()
+    n, off, cap = wl.n_compressed, 13, wl.n_compressed + 40
+    H.log(f"[encode parity] {wl.name} n={n} dst_offset={off} cap={cap}")
+    cache = s.gpu_encode(K[:, :, :n], V[:, :, :n], n, cap, dst_offset=off)
+    gpu = H.download(cache, wl, K.shape[0], cap)
+    _, ek, ev = s.oracle_encode(K[:, :, :n], V[:, :, :n])
+    st = H.compare_encode(wl, gpu, ek, ev, rows=slice(off, off + n))
+    H.log(f"  {st}")
+    assert H.untouched(gpu, slice(off, off + n), cap), "encode wrote outside [dst_offset, dst_offset + n)"
+
+
+@pytest.mark.parametrize("name", NAMES)
+@pytest.mark.parametrize("variant", ["normal", "needle"])
+def test_decode_parity_identical_codes(name, variant):
+    wl = small(name)
+    s = H.Setup(wl)
+    K, V = s.kv()
+    n = wl.n_compressed
+    planes, _, _ = s.oracle_encode(K[:, :, :n], V[:, :, :n])
+    rk, rv, R = s.recent(K, V)
+    Q = W.q_bits(wl, variant)
+    H.log(f"[decode parity] {wl.name} {variant} n_c={n} n_recent={R}")
+    cache = s.tq.alloc_cache(s.layout, K.shape[0], n)
+    H.upload_planes(cache, planes)
+    out = s.gpu_decode(cache, Q, n, rk, rv, R)
+    ref = s.oracle_decode(planes, Q, n, rk, rv, R)
+    err = H.rel_err(out, ref)
+    H.log(f"  max rel err {err:.3e}")
+    assert err <= H.ATTN_TOL
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_end_to_end_and_exact_deviation(name):
+    """Each side encodes for itself; also reports the deviation from exact attention."""
+    from oracle import decode as OD
+    wl = small(name)
+    s = H.Setup(wl)
+    K, V = s.kv()
+    n = wl.n_compressed
+    rk, rv, R = s.recent(K, V)
+    Q = W.q_bits(wl)
+    cache = s.gpu_encode(K[:, :, :n], V[:, :, :n], n, n)
+    out = s.gpu_decode(cache, Q, n, rk, rv, R)
+    planes, _, _ = s.oracle_encode(K[:, :, :n], V[:, :, :n])
+    ref = s.oracle_decode(planes, Q, n, rk, rv, R)
+    err = H.rel_err(out, ref)
+    q = W.storage_to_f64(Q, wl.in_dtype)
+    kk = W.storage_to_f64(K, wl.in_dtype)
+    vv = W.storage_to_f64(V, wl.in_dtype)
+    if R:
+        kk[:, :, n:] = W.storage_to_f64(rk[:, :, :R], wl.recent_dtype)
+        vv[:, :, n:] = W.storage_to_f64(rv[:, :, :R], wl.recent_dtype)
+    exact = OD.exact_attention(wl, q, kk, vv)
+    dev = H.rel_err(out, exact)
+    H.log(f"[end to end] {wl.name}: rel err vs oracle {err:.3e}; deviation from exact attention {dev:.3e}")
+    assert err <= H.ATTN_TOL
+
+
+@pytest.mark.parametrize("n_c,n_recent", [(0, 128), (0, 1), (1, 0), (5, 3), (64, 0), (65, 128), (257, 0)])
+def test_decode_edge_lengths(n_c, n_recent):
+    base = W.WORKLOADS["llama1b_h32x8_d64_t32k"]
+    wl = dataclasses.replace(base.scaled(n_c + n_recent, batch=1), n_recent=n_recent)
+    s = H.Setup(wl)
+    K, V = s.kv()
+    rk, rv, R = s.recent(K, V)
+    Q = W.q_bits(wl)
+    H.log(f"[edge] n_c={n_c} n_recent={n_recent}")
+    if n_c:
+        planes, _, _ = s.oracle_encode(K[:, :, :n_c], V[:, :, :n_c])
+        cache = s.tq.alloc_cache(s.layout, 1, n_c)          # capacity == n_c: reads end at the plane end
+        H.upload_planes(cache, planes)
+    else:
+        planes = {}
+        cache = s.tq.alloc_cache(s.layout, 1, 1)
+    out = s.gpu_decode(cache, Q, n_c, rk, rv, R)
+    ref = s.oracle_decode(planes, Q, n_c, rk, rv, R)
+    assert H.rel_err(out, ref) <= H.ATTN_TOL
+
+
+def test_flush_encode_equals_single_call():
+    """128-token flushes write exactly what one whole-history call writes."""
+    wl = small("qwen7b_h28x4_d128_b16_t32k", n_ctx=128 * 3 + 128)
+    s = H.Setup(wl)
+    K, V = s.kv()
+    n = wl.n_compressed
+    a = H.download(s.gpu_encode(K[:, :, :n], V[:, :, :n], n, n), wl, K.shape[0], n)
+    wl1 = dataclasses.replace(wl, flush_tokens=0)
+    s1 = H.Setup(wl1)
+    b = H.download(s1.gpu_encode(K[:, :, :n], V[:, :, :n], n, n), wl1, K.shape[0], n)
+    for name in a:
+        assert np.array_equal(a[name], b[name]), name
+
+
+def test_deterministic_repeat():
+    wl = small("qwen32b_h40x8_d128_b4_t128k")
+    s = H.Setup(wl)
+    K, V = s.kv()
+    n = wl.n_compressed
+    Q = W.q_bits(wl)
+    c1 = s.gpu_encode(K, V, n, n)
+    c2 = s.gpu_encode(K, V, n, n)
+    a, b = H.download(c1, wl, K.shape[0], n), H.download(c2, wl, K.shape[0], n)
+    for name in a:
+        assert np.array_equal(a[name], b[name]), name
+    o1 = s.gpu_decode(c1, Q, n)
+    o2 = s.gpu_decode(c1, Q, n)
+    assert np.array_equal(o1, o2)
+
+
+# ---------------------------------------------------------------------------- full sizes
+FULL = [("llama1b_h32x8_d64_t32k", [(0, 3)]),
+        ("qwen7b_h28x4_d128_b16_t32k", [(15, 2)]),
+        ("qwen0p6b_h16x4_d128_b8_t64k", [(7, 1)]),
+        ("qwen32b_h40x8_d128_b4_t128k", [(3, 5)]),
+        ("qwen32b_h40x8_d256_b4_t128k", [(1, 6)])]
+
+
+@pytest.mark.parametrize("name,slices", FULL)
+def test_full_size_sampled(name, slices):
+    """Whole workload encoded and decoded on the GPU; sampled slices/heads checked."""
+    import torch
+    wl = W.WORKLOADS[name]
+    s = H.Setup(wl)
+    n = wl.n_compressed
+    B = wl.batch
+    H.log(f"[full size] {name}: B={B} Hkv={wl.n_kv_heads} n_c={n} n_recent={wl.n_recent}")
+    K, V = s.kv()
+    rk, rv, R = s.recent(K, V)
+    Q = W.q_bits(wl)
+    cache = s.gpu_encode(K[:, :, :n], V[:, :, :n], n, n)
+    out = s.gpu_decode(cache, Q, n, rk, rv, R)
+    assert np.all(np.isfinite(out))
+    gpu = H.download(cache, wl, B, n)
+    for (b, g) in slices:
+        gk = {nme: a[b:b + 1, g:g + 1] for nme, a in gpu.items()}
+        # the oracle sees only this slice: one kv-head and its n_rep query heads
+        planes, ek, ev = s.oracle_encode(K[b:b + 1, g:g + 1, :n], V[b:b + 1, g:g + 1, :n])
+        st = H.compare_encode(wl, gk, ek, ev)
+        H.log(f"  slice ({b},{g}) {st}")
+        sub = dataclasses.replace(wl, batch=1, n_q_heads=wl.n_rep, n_kv_heads=1)
+        s_sub = H.Setup.__new__(H.Setup)
+        s_sub.wl, s_sub.ostate = sub, s.ostate
+        hs = slice(g * wl.n_rep, (g + 1) * wl.n_rep)
+        ref = s_sub.oracle_decode(planes, Q[b:b + 1, hs], n,
+                                  rk[b:b + 1, g:g + 1] if R else None, rv[b:b + 1, g:g + 1] if R else None, R,
+                                  heads=[(0, 0), (0, wl.n_rep - 1)])
+        got = np.full_like(ref, np.nan)
+        got[0, [0, wl.n_rep - 1]] = out[b, [g * wl.n_rep, g * wl.n_rep + wl.n_rep - 1]]
+        err = H.rel_err(got, ref)
+        H.log(f"  heads of ({b},{g}): max rel err {err:.3e}")
+        assert err <= H.ATTN_TOL
+    del cache
+    torch.cuda.empty_cache()
