@@ -1,0 +1,300 @@
+#!/usr/bin/env python3
+"""Benchmark of the TurboQuant KV encode + decode-attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+tq_encode of the workload's compressed history (keys, then values) followed by one
+tq_decode_attn (query prep, split-K attention on the packed cache, combine with the
+exact recent buffer).  Codebooks and rotation state are built once before timing.
+
+Inputs and packed caches rotate over >= 1 GiB of distinct copies so that the 256 MB
+Infinity Cache cannot serve a repeat: step i encodes input copy i into cache copy i
+and decodes a cache copy written half a ring earlier.  Kernel durations come from HIP
+events recorded on the stream the library launches on; the whole-step time from a
+synchronized wall clock around exactly K steps.
+
+Prints one JSON line on stdout:
+  value       decode-attention KV GB/s (algorithmic bytes / decode kernel time)
+  roofline    the dominant kernel against its MI355X peak
+  cpu_baseline  the CPU oracle timed on a bounded sample of the same workload
+"""
+from __future__ import annotations
+
+import argparse
+import dataclasses
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from compressed_decode_attention_encode_amd import workloads as W  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_F32_PEAK_TFLOPS = 157.3   # MI355X dense FP32 matrix, published
+METRIC = "decode-attn KV GB/s (% of HBM peak) + encode tokens/s, at 32K–128K context"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "compressed_decode_attention_encode_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic(wl):
+    """Bytes / flops the method must move or compute per step, per kernel group."""
+    from oracle import layout as OL   # byte accounting of the documented layout
+    B, Hkv, Hq, d, n, R = wl.batch, wl.n_kv_heads, wl.n_q_heads, wl.head_dim, wl.n_compressed, wl.n_recent
+    per = OL.bytes_per_token_head(d, wl.k_kind, wl.k_bits, wl.v_kind, wl.v_bits)
+    rows = B * Hkv * n
+    k_out = rows * (per["k_codes"] + per["k_signs"] + per["k_aux"])
+    v_out = rows * (per["v_codes"] + per["v_aux"])
+    inb = rows * d * 2
+    dec = rows * sum(per.values()) + 2 * B * Hkv * R * d * 2 + B * Hq * d * 2 + B * Hq * d * 4
+    qjl_flops = 2.0 * d * d * rows if wl.k_kind == "lm_qjl" else 0.0
+    return {"encode_k_bytes": inb + k_out, "encode_v_bytes": inb + v_out, "decode_bytes": dec,
+            "encode_k_qjl_flops": qjl_flops, "vectors": rows}
+
+
+def read_traffic(workload: str, digest: str):
+    """HBM bytes per launch of the dominant kernel from the committed counter summary, or
+    None when it is absent or was taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_digest") != digest:
+        return None
+    try:
+        return {"kernel": kv["kernel"], "bytes": float(kv["hbm_bytes_per_launch"])}
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(wl, budget_s: float = 15.0):
+    """Time the CPU oracle (as it stands) on whole (batch, kv-head) slices of the workload
+    until about `budget_s` of CPU work: encode of the slice's keys and values, then
+    decode of its n_rep query heads.  Reported in the metric's unit (decode GB/s)."""
+    from oracle import cache as OC
+    from oracle import decode as OD
+    from oracle import layout as OL
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    sk, sv, S = W.rotation_signs(wl, "k"), W.rotation_signs(wl, "v"), W.qjl_matrix(wl)
+    st = OC.make_state(wl, sk, sv, S)
+    sub = dataclasses.replace(wl, batch=1, n_q_heads=wl.n_rep, n_kv_heads=1)
+    n, d, R = wl.n_compressed, wl.head_dim, wl.n_recent
+    per = sum(OL.bytes_per_token_head(d, wl.k_kind, wl.k_bits, wl.v_kind, wl.v_bits).values())
+    t_enc = t_dec = 0.0
+    done = 0
+    q_all = W.storage_to_f64(W.q_bits(wl), wl.in_dtype)
+    start = time.time()
+    for b in range(wl.batch):
+        for g in range(wl.n_kv_heads):
+            Kb = W.kv_slice_bits(wl, W.ROLE_K, b, g)
+            Vb = W.kv_slice_bits(wl, W.ROLE_V, b, g)
+            k = W.storage_to_f64(Kb[None, None, :n], wl.in_dtype)
+            v = W.storage_to_f64(Vb[None, None, :n], wl.in_dtype)
+            t0 = time.perf_counter()
+            ek = OC.encode_k(sub, k, st)
+            ev = OC.encode_v(sub, v, st)
+            t1 = time.perf_counter()
+            planes = {nm: a for nm, a in {**ek, **ev}.items() if nm in ("k_codes", "k_signs", "k_aux", "v_codes", "v_aux")}
+            rk = rv = None
+            if R:
+                rk = W.storage_to_f64(W.to_storage(W.storage_to_f64(Kb[None, None, n:], wl.in_dtype).astype(np.float32),
+                                                   wl.recent_dtype), wl.recent_dtype)
+                rv = W.storage_to_f64(W.to_storage(W.storage_to_f64(Vb[None, None, n:], wl.in_dtype).astype(np.float32),
+                                                   wl.recent_dtype), wl.recent_dtype)
+            q = q_all[b:b + 1, g * wl.n_rep:(g + 1) * wl.n_rep]
+            t2 = time.perf_counter()
+            OD.decode_attention(sub, q, planes, n, st, rk, rv)
+            t3 = time.perf_counter()
+            t_enc += t1 - t0
+            t_dec += t3 - t2
+            done += 1
+            if time.time() - start > budget_s:
+                break
+        else:
+            continue
+        break
+    dec_bytes = done * (n * per + 2 * R * d * 2 + wl.n_rep * d * 6)
+    return {"value": dec_bytes / t_dec / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {wl.batch * wl.n_kv_heads} (batch, kv-head) slices, {n} compressed + {R} recent "
+                      f"tokens each: oracle encode of keys+values, then decode of the slice's {wl.n_rep} query heads",
+            "encode_tokens_per_s": done * n / t_enc, "decode_s": t_dec, "encode_s": t_enc}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=W.BENCH_WORKLOAD, choices=sorted(W.WORKLOADS))
+    ap.add_argument("--ring-gib", type=float, default=1.0, help="distinct input/cache bytes to rotate over")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    a = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if a.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {a.gpus}, "
+              f"WORLD_SIZE {world}); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from compressed_decode_attention_encode_amd import tq
+
+    wl = W.WORKLOADS[a.workload]
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    B, n, R = wl.batch, wl.n_compressed, wl.n_recent
+    lay = tq.layout_of(wl)
+    state = tq.upload_state(lay, W.signs_to_mask(W.rotation_signs(wl, "k")), W.signs_to_mask(W.rotation_signs(wl, "v")),
+                            W.qjl_matrix(wl), device=dev)
+
+    t0 = time.time()
+    K = W.kv_bits(wl, W.ROLE_K)
+    V = W.kv_bits(wl, W.ROLE_V)
+    log(f"[bench] {wl.name}: inputs {K.shape} generated in {time.time() - t0:.1f}s")
+
+    def dev16(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev)
+
+    k0, v0 = dev16(K[:, :, :n]), dev16(V[:, :, :n])
+    rk = rv = None
+    if R:
+        conv = lambda X: W.to_storage(W.storage_to_f64(X[:, :, n:], wl.in_dtype).astype(np.float32), wl.recent_dtype)
+        rk, rv = dev16(conv(K)), dev16(conv(V))
+    q = dev16(W.q_bits(wl))
+    del K, V
+
+    in_bytes = 2 * k0.numel() * 2
+    cache_bytes = sum(tq.tq_cache_plane_bytes(lay, B, n))
+    ring = int(a.ring_gib * (1 << 30))
+    n_in = max(1, min(16, -(-ring // in_bytes)))
+    n_cache = max(2, min(256, -(-ring // cache_bytes)))
+    ins = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(n_in - 1)]
+    caches = [tq.alloc_cache(lay, B, n, device=dev) for _ in range(n_cache)]
+    ws_bytes = tq.tq_decode_workspace_bytes(lay, B, n)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    out = torch.empty((B, wl.n_q_heads, wl.head_dim), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    log(f"[bench] ring: {n_in} input copies ({in_bytes / 2**20:.1f} MiB each), {n_cache} caches "
+        f"({cache_bytes / 2**20:.1f} MiB each)")
+
+    def enc_k(i):
+        kk, _ = ins[i % n_in]
+        tq.tq_encode(lay, state.struct, kk, None, B, n, 0, caches[i % n_cache].struct, stream)
+
+    def enc_v(i):
+        _, vv = ins[i % n_in]
+        tq.tq_encode(lay, state.struct, None, vv, B, n, 0, caches[i % n_cache].struct, stream)
+
+    def dec(i):
+        c = caches[(i + n_cache // 2) % n_cache]
+        tq.tq_decode_attn(lay, state.struct, q, c.struct, n, rk, rv, R, R, out, ws, ws_bytes, stream)
+
+    # every cache holds a valid encoding before the timed region
+    for i in range(n_cache):
+        enc_k(i)
+        enc_v(i)
+    for i in range(a.warmup):
+        enc_k(i), enc_v(i), dec(i)
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(a.steps):
+        e = evs[i]
+        e[0].record(stream)
+        enc_k(i)
+        e[1].record(stream)
+        enc_v(i)
+        e[2].record(stream)
+        dec(i)
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    assert torch.isfinite(out).all(), "non-finite attention output"
+
+    ms = lambda j: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(a.steps)]))
+    t_ek, t_ev, t_dec = ms(0), ms(1), ms(2)
+    alg = algorithmic(wl)
+    dec_gbs = alg["decode_bytes"] / (t_dec * 1e-3) / 1e9
+    enc_tok = B * n / ((t_ek + t_ev) * 1e-3)
+
+    digest = source_digest()
+    groups = {
+        "encode_k": {"kernel": "encode_lm_kernel (keys, QJL on MFMA)" if wl.k_kind == "lm_qjl" else "encode_affine8_kernel",
+                     "ms": t_ek},
+        "encode_v": {"kernel": "encode_group_kernel" if wl.v_kind == "group_sym" else "encode_lm_kernel (values)",
+                     "ms": t_ev},
+        "decode": {"kernel": "decode_prep + decode_main + decode_combine", "ms": t_dec},
+    }
+    rl = {}
+    if wl.k_kind == "lm_qjl":
+        tf = alg["encode_k_qjl_flops"] / (t_ek * 1e-3) / 1e12
+        rl["encode_k"] = {"bound": "mfma", "achieved": tf, "peak": MFMA_F32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                          "frac": tf / MFMA_F32_PEAK_TFLOPS, "traffic": None,
+                          "algorithmic_per_launch": alg["encode_k_qjl_flops"]}
+    else:
+        gb = alg["encode_k_bytes"] / (t_ek * 1e-3) / 1e9
+        rl["encode_k"] = {"bound": "hbm", "achieved": gb, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": gb / HBM_PEAK_GBS, "traffic": None, "algorithmic_per_launch": alg["encode_k_bytes"]}
+    gb = alg["encode_v_bytes"] / (t_ev * 1e-3) / 1e9
+    rl["encode_v"] = {"bound": "hbm", "achieved": gb, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gb / HBM_PEAK_GBS,
+                      "traffic": None, "algorithmic_per_launch": alg["encode_v_bytes"]}
+    rl["decode"] = {"bound": "hbm", "achieved": dec_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": dec_gbs / HBM_PEAK_GBS, "traffic": None, "algorithmic_per_launch": alg["decode_bytes"]}
+    dom = max(groups, key=lambda g: groups[g]["ms"])
+    tr = read_traffic(wl.name, digest)
+    if tr and tr["kernel"] == dom:
+        rl[dom]["traffic"] = tr["bytes"]
+    for g in rl:
+        rl[g]["kernel"] = groups[g]["kernel"]
+        rl[g]["ms_per_launch"] = groups[g]["ms"]
+
+    line = {
+        "metric": METRIC, "value": dec_gbs, "unit": "GB/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": wall * 1e3 / a.steps, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": wl.name, "batch": B, "q_heads": wl.n_q_heads, "kv_heads": wl.n_kv_heads,
+                   "head_dim": wl.head_dim, "context": wl.n_ctx, "compressed_tokens": n, "recent_tokens": R,
+                   "keys": f"{wl.k_kind}{wl.k_bits}", "values": f"{wl.v_kind}{wl.v_bits}", "input_dtype": wl.in_dtype,
+                   "parallelism": "single-gpu"},
+        "decode_pct_hbm_peak": 100.0 * dec_gbs / HBM_PEAK_GBS,
+        "encode_tokens_per_s": enc_tok,
+        "kernel_ms": {g: groups[g]["ms"] for g in groups},
+        "roofline": {k: rl[dom][k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")} | {
+            "kernel": rl[dom]["kernel"], "group": dom},
+        "rooflines": rl,
+        "source_digest": digest,
+    }
+    if not a.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample ...")
+        line["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
