@@ -55,11 +55,18 @@ decode_prep_kernel(const uint16_t* __restrict__ q, const uint32_t* __restrict__ 
     }
     const float rs = rsqrtf((float)D);
     if (j < D) out[j] = s_x[j] * rs * scale;   // qa = Pi q
-    // q_s = S q_r; thread i takes row i of S
+    // q_s = S q_r; thread i takes row i of S with independent 16-byte loads
     if (j < D) {
-      const float* srow = S + (size_t)j * D;
+      const float4* srow = reinterpret_cast<const float4*>(S + (size_t)j * D);
       float acc = 0.f;
-      for (int k = 0; k < D; ++k) acc = fmaf(srow[k], s_x[k], acc);
+#pragma unroll 8
+      for (int k = 0; k < D / 4; ++k) {
+        const float4 sv = srow[k];
+        acc = fmaf(sv.x, s_x[4 * k], acc);
+        acc = fmaf(sv.y, s_x[4 * k + 1], acc);
+        acc = fmaf(sv.z, s_x[4 * k + 2], acc);
+        acc = fmaf(sv.w, s_x[4 * k + 3], acc);
+      }
       const float qjl = 1.2533141373155003f / (float)D;   // sqrt(pi/2)/d
       out[D + j] = acc * rs * scale * qjl;
     }
@@ -76,110 +83,26 @@ decode_prep_kernel(const uint16_t* __restrict__ q, const uint32_t* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------------
-// combine: merge splits, fold in the recent tokens, inverse rotation, normalise
+// finish: merge the splits of one (query head, batch), with the recent buffer and the
+// inverse rotation (also the whole decode when nothing is compressed: zero splits).
 // ---------------------------------------------------------------------------------
-template <int D, int VK, int RDT>
-__global__ void __launch_bounds__(256)
-decode_combine_kernel(const float* __restrict__ part, int nsplit, const float* __restrict__ qprep,
-                      const uint16_t* __restrict__ rk, const uint16_t* __restrict__ rv, int n_recent,
-                      int recent_cap, const uint32_t* __restrict__ vsign_mask, float* __restrict__ out,
-                      int Hq, int Hkv) {
-  constexpr int QF = 4 * D;
-  constexpr int PS = D + 4;
-  __shared__ float s_red[256];
-  __shared__ float s_w[256];          // split weights, then recent weights
-  __shared__ float s_qn[D];
-  __shared__ float s_acc[D];
-  __shared__ float s_pr[kMaxRecent];
-  const int h = blockIdx.x, b = blockIdx.y;
-  const int tid = threadIdx.x;
-  const int g = h / (Hq / Hkv);
-  const float* qp = qprep + (size_t)(b * Hq + h) * QF;
-  const float* pp = part + (size_t)(b * Hq + h) * nsplit * PS;
-  if (tid < D) s_qn[tid] = qp[2 * D + tid];
-
-  // max over split maxima
-  float mloc = -INFINITY;
-  for (int s = tid; s < nsplit; s += blockDim.x) mloc = fmaxf(mloc, pp[(size_t)s * PS]);
-  // recent scores
-  __syncthreads();
-  const size_t rbase = ((size_t)b * Hkv + g) * recent_cap;
-  float sr = -INFINITY;
-  if (tid < n_recent) {
-    const uint16_t* kr = rk + (rbase + tid) * D;
-    float a = 0.f;
-    for (int k = 0; k < D; ++k) a = fmaf(s_qn[k], in_to_f32<RDT>(kr[k]), a);
-    sr = a;
-    mloc = fmaxf(mloc, a);
-  }
-  s_red[tid] = mloc;
-  __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (tid < w) s_red[tid] = fmaxf(s_red[tid], s_red[tid + w]);
-    __syncthreads();
-  }
-  const float M = s_red[0];
-  __syncthreads();
-
-  // normaliser
-  float lloc = 0.f;
-  for (int s = tid; s < nsplit; s += blockDim.x) {
-    const float m = pp[(size_t)s * PS];
-    lloc += (m == -INFINITY) ? 0.f : pp[(size_t)s * PS + 1] * exp2f(m - M);
-  }
-  if (tid < n_recent) {
-    const float pr = exp2f(sr - M);
-    s_pr[tid] = pr;
-    lloc += pr;
-  }
-  s_red[tid] = lloc;
-  __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (tid < w) s_red[tid] += s_red[tid + w];
-    __syncthreads();
-  }
-  const float l = s_red[0];
-
-  // value sums: compressed part (rotated domain for LM values), recent part (natural)
-  float main_j = 0.f, rec_j = 0.f;
-  if (tid < D) {
-    for (int s = 0; s < nsplit; ++s) {
-      const float m = pp[(size_t)s * PS];
-      if (m != -INFINITY) main_j = fmaf(pp[(size_t)s * PS + 4 + tid], exp2f(m - M), main_j);
-    }
-    const uint16_t* vr = rv + rbase * D + tid;
-    for (int r = 0; r < n_recent; ++r) rec_j = fmaf(s_pr[r], in_to_f32<RDT>(vr[(size_t)r * D]), rec_j);
-  }
-  if constexpr (VK == TQ_V_LM_ROT) {
-    // Pi^T acc = diag(s) H acc / sqrt(d): one fast transform of the summed vector
-    if (tid < D) s_acc[tid] = main_j;
-    __syncthreads();
-    for (int hs = 1; hs < D; hs <<= 1) {
-      float a = 0.f, c = 0.f;
-      int lo = 0;
-      if (tid < D / 2) {
-        lo = (tid / hs) * 2 * hs + (tid % hs);
-        a = s_acc[lo];
-        c = s_acc[lo + hs];
-      }
-      __syncthreads();
-      if (tid < D / 2) {
-        s_acc[lo] = a + c;
-        s_acc[lo + hs] = a - c;
-      }
-      __syncthreads();
-    }
-    if (tid < D) {
-      const float hv = s_acc[tid] * rsqrtf((float)D);
-      main_j = ((vsign_mask[tid >> 5] >> (tid & 31)) & 1u) ? -hv : hv;
-    }
-  }
-  if (tid < D) out[(size_t)(b * Hq + h) * D + tid] = (main_j + rec_j) / l;
+template <int D, int VK>
+__global__ void __launch_bounds__(256) decode_finish_kernel(const DecodeArgs A, int nrep) {
+  __shared__ float sm[finish_floats<D, 1>()];
+  const int h = blockIdx.x;
+  finish_group<D, 1, VK>(A, blockIdx.y, h / nrep, h, sm);
 }
 
 // ---------------------------------------------------------------------------------
 // plan and launch
 // ---------------------------------------------------------------------------------
+// Workspace: prepared queries [B][Hq][4d] | split partials [B][Hq][n_splits][d+4].
+static size_t ws_layout_bytes(const tq_layout& L, int batch, int n_splits) {
+  const size_t d = L.head_dim;
+  return sizeof(float) *
+         ((size_t)batch * L.n_q_heads * 4 * d + (size_t)batch * L.n_q_heads * n_splits * (d + 4));
+}
+
 DecodePlan plan_decode(const tq_layout& L, int batch, int n_c) {
   DecodePlan p{};
   const int d = L.head_dim;
@@ -190,24 +113,24 @@ DecodePlan plan_decode(const tq_layout& L, int batch, int n_c) {
     p.chunk = 0;
   } else {
     int want = ceil_div(kTargetDecodeGroups, units);
-    want = std::max(1, std::min(want, ceil_div(tiles, 4)));   // >= 4 tiles (one per wave) per split
+    want = std::min(want, kMaxFinishSplits);   // the finishing merge stages every split in LDS
+    want = std::max(1, std::min(want, ceil_div(tiles, kMinTilesPerSplit)));
     const int tiles_per = ceil_div(tiles, want);
     p.chunk = tiles_per * kTile;
     p.n_splits = ceil_div(tiles, tiles_per);
   }
   p.q_floats = 4 * (size_t)d;
   p.part_stride = (size_t)d + 4;
-  p.ws_bytes = sizeof(float) * ((size_t)batch * L.n_q_heads * p.q_floats +
-                                (size_t)batch * L.n_q_heads * p.n_splits * p.part_stride);
+  p.ws_bytes = ws_layout_bytes(L, batch, p.n_splits);
   return p;
 }
 
 size_t decode_ws_bound(const tq_layout& L, int batch, int max_c) {
   // n_splits of any n_c <= max_c is at most min(ceil(target/units), tiles(max_c))
   const long units = (long)batch * L.n_kv_heads;
-  const int max_splits = std::max(0, std::min(ceil_div(kTargetDecodeGroups, units), ceil_div(std::max(max_c, 0), kTile)));
-  const size_t d = L.head_dim;
-  return sizeof(float) * ((size_t)batch * L.n_q_heads * 4 * d + (size_t)batch * L.n_q_heads * max_splits * (d + 4));
+  const int max_splits =
+      std::max(0, std::min(ceil_div(kTargetDecodeGroups, units), ceil_div(std::max(max_c, 0), kTile)));
+  return ws_layout_bytes(L, batch, max_splits);
 }
 
 namespace {
@@ -247,17 +170,8 @@ hipError_t run_prep(const tq_layout& L, const tq_state& S, const void* q, float*
 }
 
 template <int D, int VK>
-hipError_t run_combine(const tq_layout& L, const tq_state& S, const float* part, int nsplit, const float* qprep,
-                       const void* rk, const void* rv, int n_recent, int rcap, float* out, int batch,
-                       hipStream_t st) {
-  if (L.recent_dtype == TQ_F16)
-    hipLaunchKernelGGL((decode_combine_kernel<D, VK, TQ_F16>), dim3(L.n_q_heads, batch), dim3(256), 0, st, part,
-                       nsplit, qprep, (const uint16_t*)rk, (const uint16_t*)rv, n_recent, rcap, S.v_signs, out,
-                       L.n_q_heads, L.n_kv_heads);
-  else
-    hipLaunchKernelGGL((decode_combine_kernel<D, VK, TQ_BF16>), dim3(L.n_q_heads, batch), dim3(256), 0, st, part,
-                       nsplit, qprep, (const uint16_t*)rk, (const uint16_t*)rv, n_recent, rcap, S.v_signs, out,
-                       L.n_q_heads, L.n_kv_heads);
+hipError_t run_finish(const DecodeArgs& A, int nrep, int batch, hipStream_t st) {
+  hipLaunchKernelGGL((decode_finish_kernel<D, VK>), dim3(A.Hq, batch), dim3(256), 0, st, A, nrep);
   return hipGetLastError();
 }
 
@@ -271,16 +185,38 @@ hipError_t run_decode_d(const tq_layout& L, const tq_state& S, const void* q, co
   hipError_t e = (L.k_kind == TQ_K_LM_QJL) ? run_prep<D, TQ_K_LM_QJL>(L, S, q, qprep, batch, st)
                                            : run_prep<D, TQ_K_AFFINE8>(L, S, q, qprep, batch, st);
   if (e != hipSuccess) return e;
+  DecodeArgs A{};
+  A.kc = (const uint32_t*)C.k_codes;
+  A.ks = (const uint32_t*)C.k_signs;
+  A.ka = (const uint32_t*)C.k_aux;
+  A.vc = (const uint32_t*)C.v_codes;
+  A.va = (const uint32_t*)C.v_aux;
+  A.kcent = S.k_centroids;
+  A.vcent = S.v_centroids;
+  A.vsign = S.v_signs;
+  A.qprep = qprep;
+  A.part = part;
+  A.rk = (const uint16_t*)rk;
+  A.rv = (const uint16_t*)rv;
+  A.out = out;
+  A.Hq = L.n_q_heads;
+  A.Hkv = L.n_kv_heads;
+  A.cap = C.capacity;
+  A.n_c = n_c;
+  A.chunk = plan.chunk;
+  A.nsplit = plan.n_splits;
+  A.n_recent = n_recent;
+  A.recent_cap = rcap;
+  A.recent_bf16 = (L.recent_dtype == TQ_BF16) ? 1 : 0;
   if (n_c > 0) {
     MainLaunch fn = find_main(L);
     if (!fn) return hipErrorInvalidDeviceFunction;
-    e = fn(dim3(plan.n_splits, L.n_kv_heads, batch), st, C, S, qprep, part, L.n_kv_heads, n_c, plan.chunk,
-           plan.n_splits);
+    e = fn(dim3(plan.n_splits, L.n_kv_heads, batch), st, A);
     if (e != hipSuccess) return e;
   }
-  return (L.v_kind == TQ_V_GROUP_SYM)
-             ? run_combine<D, TQ_V_GROUP_SYM>(L, S, part, plan.n_splits, qprep, rk, rv, n_recent, rcap, out, batch, st)
-             : run_combine<D, TQ_V_LM_ROT>(L, S, part, plan.n_splits, qprep, rk, rv, n_recent, rcap, out, batch, st);
+  const int nrep = L.n_q_heads / L.n_kv_heads;
+  return (L.v_kind == TQ_V_GROUP_SYM) ? run_finish<D, TQ_V_GROUP_SYM>(A, nrep, batch, st)
+                                      : run_finish<D, TQ_V_LM_ROT>(A, nrep, batch, st);
 }
 
 }  // namespace

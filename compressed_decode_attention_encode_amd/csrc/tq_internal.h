@@ -14,8 +14,10 @@ namespace tq {
 constexpr int kTile = 64;
 // Largest recent buffer accepted by the decode (vLLM guide, section 5: 128-token buffer).
 constexpr int kMaxRecent = 128;
-// Decode work-group count the split policy aims for (8 per CU on 256 CUs).
-constexpr int kTargetDecodeGroups = 2048;
+// Decode work-group count the split policy aims for (4 per CU on 256 CUs), and the
+// fewest 64-token tiles a split gets (two per wave, so a wave's loads overlap compute).
+constexpr int kTargetDecodeGroups = 1024;
+constexpr int kMinTilesPerSplit = 8;
 
 inline int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
 

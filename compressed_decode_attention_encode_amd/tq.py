@@ -17,7 +17,28 @@ LIB_PATH = os.path.join(_HERE, "libtq.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -m compressed_decode_attention_encode_amd.build`")
+
+# Device memory and streams come from torch, so libtq must run on torch's HIP runtime.
+# torch ships its own libamdhip64 whose soname matches the one libtq links; importing
+# torch first makes the loader bind libtq to that copy instead of loading a second one.
+try:
+    import torch  # noqa: F401
+except ImportError:   # plain C-ABI use without torch: libtq loads the system runtime
+    torch = None
 _lib = ctypes.CDLL(LIB_PATH)
+
+
+def _hip_runtimes_loaded():
+    try:
+        with open(f"/proc/{os.getpid()}/maps") as fh:
+            return sorted({ln.split()[-1] for ln in fh if "libamdhip64" in ln})
+    except OSError:
+        return []
+
+
+if len(_hip_runtimes_loaded()) > 1:
+    raise ImportError(f"two HIP runtimes are loaded in this process: {_hip_runtimes_loaded()}; "
+                      "import torch before anything that loads another libamdhip64")
 
 TQ_OK, TQ_ERR_INVALID, TQ_ERR_UNSUPPORTED, TQ_ERR_CAPACITY, TQ_ERR_HIP = 0, -1, -2, -3, -4
 TQ_F16, TQ_BF16 = 0, 1

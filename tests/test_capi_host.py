@@ -158,3 +158,9 @@ def test_workspace_bound_covers_every_length():
         need = tq.tq_decode_workspace_bytes(L, 1, n)
         assert need <= bound
     assert tq.tq_strerror(tq.TQ_ERR_CAPACITY) == "cache capacity exceeded"
+
+
+def test_one_hip_runtime_in_process():
+    # libtq must share torch's HIP runtime (device pointers and streams come from torch)
+    loaded = tq._hip_runtimes_loaded()
+    assert len(loaded) == 1, loaded
