@@ -153,6 +153,8 @@ def main():
     ap.add_argument("--workload", default=W.BENCH_WORKLOAD, choices=sorted(W.WORKLOADS))
     ap.add_argument("--ring-gib", type=float, default=1.0, help="distinct input/cache bytes to rotate over")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run 10 plain device-to-device copies of MIB MiB (counter calibration) and exit")
     a = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
@@ -162,6 +164,19 @@ def main():
 
     import torch
     from compressed_decode_attention_encode_amd import tq
+
+    if a.calibrate_copy:
+        # a copy of known size: each launch reads and writes MIB MiB, for scaling the HBM
+        # byte counters of the profiled kernels
+        n = a.calibrate_copy << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "launches": 10}))
+        return
 
     wl = W.WORKLOADS[a.workload]
     torch.cuda.set_device(0)

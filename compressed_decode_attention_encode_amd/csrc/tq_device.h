@@ -51,6 +51,44 @@ __device__ __forceinline__ uint32_t f64_to_f16_rne(double x) {
   return sign | (uint32_t)keep;  // subnormal (keep == 0x400 encodes the smallest normal)
 }
 
+// Lane exchange with lane ^ M (M = 1, 2, 4, 8) through DPP moves (VALU, no LDS):
+//   xor 1 / xor 2: quad_perm [1,0,3,2] / [2,3,0,1];
+//   xor 4: row_half_mirror (i -> 7-i in 8 lanes) then quad_perm [3,2,1,0];
+//   xor 8: row_mirror (i -> 15-i in 16 lanes) then row_half_mirror.
+template <int M>
+__device__ __forceinline__ uint32_t xor_lanes_u32(uint32_t v) {
+  static_assert(M == 1 || M == 2 || M == 4 || M == 8, "DPP xor covers 1, 2, 4, 8");
+  if constexpr (M == 1) {
+    return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);
+  } else if constexpr (M == 2) {
+    return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);
+  } else if constexpr (M == 4) {
+    const uint32_t t = __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, false);
+    return __builtin_amdgcn_mov_dpp(t, 0x1B, 0xF, 0xF, false);
+  } else {
+    const uint32_t t = __builtin_amdgcn_mov_dpp(v, 0x140, 0xF, 0xF, false);
+    return __builtin_amdgcn_mov_dpp(t, 0x141, 0xF, 0xF, false);
+  }
+}
+
+template <int M>
+__device__ __forceinline__ double xor_lanes(double x) {
+  const uint64_t u = (uint64_t)__double_as_longlong(x);
+  const uint32_t lo = xor_lanes_u32<M>((uint32_t)u);
+  const uint32_t hi = xor_lanes_u32<M>((uint32_t)(u >> 32));
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// Sum over the N consecutive lanes sharing lane / N (N <= 16), by DPP exchanges.
+template <int N>
+__device__ __forceinline__ double group_sum_dpp(double v) {
+  if constexpr (N >= 2) v += xor_lanes<1>(v);
+  if constexpr (N >= 4) v += xor_lanes<2>(v);
+  if constexpr (N >= 8) v += xor_lanes<4>(v);
+  if constexpr (N >= 16) v += xor_lanes<8>(v);
+  return v;
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_sum(T v) {
 #pragma unroll

@@ -29,7 +29,7 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 // QJL = false: rotated values (codes + fp32 n).
 // ---------------------------------------------------------------------------------
 template <int D, int KB, int DT, bool QJL>
-__global__ void __launch_bounds__(2 * D)
+__global__ void __launch_bounds__(2 * D) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 2 : 1)))
 encode_lm_kernel(const uint16_t* __restrict__ x, int T, int tiles_per_slice, int n_tiles,
                  int dst_offset, int cap,
                  const float* __restrict__ cent, const float* __restrict__ thr,
@@ -43,7 +43,7 @@ encode_lm_kernel(const uint16_t* __restrict__ x, int T, int tiles_per_slice, int
   constexpr int RS = D + 4;                        // LDS row stride of the residual tile (floats)
   constexpr int SW = D / 32;                       // sign words per row
 
-  __shared__ float s_cent[16];
+  __shared__ double s_cent[16];
   __shared__ __attribute__((aligned(16))) uint32_t s_code[kTile * D / 4];   // code bytes
   __shared__ __attribute__((aligned(16))) float s_res[QJL ? kTile * RS : 4];
   __shared__ uint32_t s_sgn[QJL ? kTile * SW : 1];
@@ -55,10 +55,12 @@ encode_lm_kernel(const uint16_t* __restrict__ x, int T, int tiles_per_slice, int
   const int vec = tid / P;     // vector within the tile
   const int part = tid % P;    // which 32 coordinates
 
-  if (tid < L) s_cent[tid] = cent[tid];
-  double th[L - 1];
+  if (tid < L) s_cent[tid] = (double)cent[tid];
+  // symmetric codebook: t[L/2-1] = 0 and t[L/2-1+i] = -t[L/2-1-i]; only the positive
+  // thresholds are compared, against |y|
+  double thp[L / 2 - 1];
 #pragma unroll
-  for (int i = 0; i < L - 1; ++i) th[i] = (double)thr[i];
+  for (int i = 0; i < L / 2 - 1; ++i) thp[i] = (double)thr[L / 2 + i];
   const uint32_t smask = sign_mask[part];
 
   // Rows of S this wave keeps for the whole kernel: lane holds S[32*wave + lane%32][2kk + lane/32].
@@ -107,16 +109,21 @@ encode_lm_kernel(const uint16_t* __restrict__ x, int T, int tiles_per_slice, int
         }
       }
     }
-#pragma unroll
-    for (int m = 1; m < P; m <<= 1) {
-      const bool hi = (part & m) != 0;
-#pragma unroll
-      for (int e = 0; e < 32; ++e) {
-        const double o = __shfl_xor(xv[e], m);
-        xv[e] = hi ? (o - xv[e]) : (xv[e] + o);
-      }
+    // butterflies across the P lanes of the vector (stride 32*m <-> lane xor m)
+#define TQ_XSTAGE(M)                                              \
+    if constexpr (P > M) {                                        \
+      const bool hi = (part & M) != 0;                            \
+      _Pragma("unroll") for (int e = 0; e < 32; ++e) {            \
+        const double o = xor_lanes<M>(xv[e]);                     \
+        xv[e] = hi ? (o - xv[e]) : (xv[e] + o);                   \
+      }                                                           \
     }
-    ss = group_sum<P>(ss);
+    TQ_XSTAGE(1)
+    TQ_XSTAGE(2)
+    TQ_XSTAGE(4)
+    TQ_XSTAGE(8)
+#undef TQ_XSTAGE
+    ss = group_sum_dpp<P>(ss);
     const double n = sqrt(ss);
     const double scale = (n > 0.0) ? 1.0 / (sqrt((double)D) * n) : 0.0;
 
@@ -126,13 +133,18 @@ encode_lm_kernel(const uint16_t* __restrict__ x, int T, int tiles_per_slice, int
 #pragma unroll
     for (int e = 0; e < 32; ++e) {
       const double y = xv[e] * scale;
-      int idx = 0;
+      // idx = #{i : t_i < y}: with cnt = #{positive t_i < |y|} (sign bit of t_i - |y|) this is
+      // L/2 + cnt for y > 0 and L/2 - 1 - cnt otherwise (equal except when |y| == t_i exactly)
+      const double ay = fabs(y);
+      uint32_t cnt = 0;
 #pragma unroll
-      for (int i = 0; i < L - 1; ++i) idx += (y > th[i]) ? 1 : 0;
+      for (int i = 0; i < L / 2 - 1; ++i) cnt += (uint32_t)((uint64_t)__double_as_longlong(thp[i] - ay) >> 63);
+      const uint32_t pos = (uint32_t)((uint64_t)__double_as_longlong(0.0 - y) >> 63);   // y > 0
+      const int idx = pos ? (int)(L / 2 + cnt) : (int)(L / 2 - 1 - cnt);
       if ((e & 3) == 0) packed[e >> 2] = 0;
       packed[e >> 2] |= (uint32_t)idx << (8 * (e & 3));
       if constexpr (QJL) {
-        const double r = y - (double)s_cent[idx];
+        const double r = y - s_cent[idx];
         gg = fma(r, r, gg);
         xv[e] = r;
       }
@@ -143,7 +155,7 @@ encode_lm_kernel(const uint16_t* __restrict__ x, int T, int tiles_per_slice, int
       dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
     }
     if constexpr (QJL) {
-      gg = group_sum<P>(gg);
+      gg = group_sum_dpp<P>(gg);
       float4* dst = reinterpret_cast<float4*>(&s_res[vec * RS + 32 * part]);
 #pragma unroll
       for (int i = 0; i < 8; ++i)
@@ -202,53 +214,70 @@ encode_lm_kernel(const uint16_t* __restrict__ x, int T, int tiles_per_slice, int
 }
 
 // ---------------------------------------------------------------------------------
-// Group-32 symmetric values.  One thread per (token, 32-group).  The level boundaries
-// tau_k = Delta (k - L/2) are exact in float32 (an fp16 Delta times a small integer), so
-// the float32 estimate of rne(v/Delta + (L-1)/2) is corrected by two exact comparisons;
-// a tie at a boundary goes to the even level, as round-half-to-even does.
+// Group-32 symmetric values and per-block affine 8-bit keys: four lanes per 32-element
+// group, 8 elements (one 16-byte load) per lane, so consecutive lanes read consecutive
+// 16 bytes; the group's max / min is reduced across the lane quad with DPP moves.
 // ---------------------------------------------------------------------------------
+__device__ __forceinline__ float quad_max(float v) {
+  v = fmaxf(v, __uint_as_float(xor_lanes_u32<1>(__float_as_uint(v))));
+  return fmaxf(v, __uint_as_float(xor_lanes_u32<2>(__float_as_uint(v))));
+}
+__device__ __forceinline__ float quad_min(float v) {
+  v = fminf(v, __uint_as_float(xor_lanes_u32<1>(__float_as_uint(v))));
+  return fminf(v, __uint_as_float(xor_lanes_u32<2>(__float_as_uint(v))));
+}
+
+template <int DT>
+__device__ __forceinline__ void load8(const uint16_t* __restrict__ p, float (&v)[8]) {
+  const uint4 r = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    v[2 * k] = in_to_f32<DT>(w[k] & 0xFFFFu);
+    v[2 * k + 1] = in_to_f32<DT>(w[k] >> 16);
+  }
+}
+
+// Symmetric group quantiser.  The level boundaries tau_k = Delta (k - L/2) are exact in
+// float32 (an fp16 Delta times a small integer), so the float32 estimate of
+// rne(v/Delta + (L-1)/2) is corrected by two exact comparisons; a value exactly on a
+// boundary goes to the even level, as round-half-to-even does.
 __device__ __forceinline__ bool passes(float v, float tau, int k) {
   return (k & 1) ? (v > tau) : (v >= tau);
 }
 
 template <int D, int VB, int DT>
 __global__ void __launch_bounds__(256)
-encode_group_kernel(const uint16_t* __restrict__ x, int T, long n_groups, int dst_offset, int cap,
+encode_group_kernel(const uint16_t* __restrict__ x, int T, long n_parts, int dst_offset, int cap,
                     uint32_t* __restrict__ codes_out, uint16_t* __restrict__ scale_out) {
   constexpr int G = D / 32;
   constexpr int L = 1 << VB;
   const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= n_groups) return;
-  const int g = (int)(gid % G);
-  const long vt = gid / G;            // slice * T + t
-  const long slice = vt / T;
-  const long t = vt % T;
+  // n_parts is a multiple of 4 and the grid a multiple of 64: whole quads are in or out
+  const bool live = gid < n_parts;
+  const long gq = live ? gid : n_parts - 4 + (gid & 3);
+  const int sub = (int)(gq & 3);                 // which 8 elements of the group
+  const int g = (int)((gq >> 2) % G);
+  const long vt = (gq >> 2) / G;                 // slice * T + t
+  const long slice = vt / T, t = vt % T;
 
-  float v[32];
-  {
-    const uint4* src = reinterpret_cast<const uint4*>(x + vt * D + 32 * g);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint4 r = src[i];
-      const uint32_t w[4] = {r.x, r.y, r.z, r.w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        v[8 * i + 2 * k] = in_to_f32<DT>(w[k] & 0xFFFFu);
-        v[8 * i + 2 * k + 1] = in_to_f32<DT>(w[k] >> 16);
-      }
-    }
-  }
+  float v[8];
+  load8<DT>(x + vt * D + 32 * g + 8 * sub, v);
   float amax = 0.f;
 #pragma unroll
-  for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(v[e]));
-  const uint32_t dbits = f64_to_f16_rne(2.0 * (double)amax / (double)(L - 1));
+  for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
+  amax = quad_max(amax);
+  // Delta = fp16(2 amax / (L-1)): amax is an fp16/bf16 value, so the exact quotient has a
+  // repeating binary fraction (k/3 or k/15) that stays >= 1/30 of an fp16 ulp away from a
+  // rounding tie; the float32 product with the rounded reciprocal (error ~1e-7 relative)
+  // therefore rounds to the same fp16 value as the exact quotient.
+  const uint32_t dbits = __builtin_bit_cast(uint16_t, (_Float16)(2.0f * amax * (1.0f / (float)(L - 1))));
   const float delta = f16_to_f32(dbits);
-
-  uint32_t words[VB] = {};
   const float inv = (delta > 0.f) ? 1.0f / delta : 0.f;
   const float off = 0.5f * (float)(L - 1);
+  uint32_t code = 0;
 #pragma unroll
-  for (int e = 0; e < 32; ++e) {
+  for (int e = 0; e < 8; ++e) {
     int k;
     if (delta > 0.f) {
       k = (int)rintf(fmaf(v[e], inv, off));
@@ -261,62 +290,58 @@ encode_group_kernel(const uint16_t* __restrict__ x, int T, long n_groups, int ds
     } else {
       k = (v[e] > 0.f) ? L - 1 : ((v[e] < 0.f) ? 0 : L / 2);
     }
-    words[(e * VB) / 32] |= (uint32_t)k << ((e * VB) % 32);
+    code |= (uint32_t)k << (VB * e);
   }
+  if (!live) return;
   const size_t row = (size_t)slice * cap + dst_offset + t;
   constexpr int WV = D * VB / 32;
-#pragma unroll
-  for (int i = 0; i < VB; ++i) codes_out[row * WV + g * VB + i] = words[i];
-  scale_out[row * G + g] = (uint16_t)dbits;
+  if constexpr (VB == 4) {
+    codes_out[row * WV + g * 4 + sub] = code;                     // 8 codes = one word
+  } else {
+    reinterpret_cast<uint16_t*>(codes_out + row * WV + g * 2)[sub] = (uint16_t)code;   // half a word
+  }
+  if (sub == 0) scale_out[row * G + g] = (uint16_t)dbits;
 }
 
-// ---------------------------------------------------------------------------------
-// Per-block affine 8-bit keys.  One thread per (token, 32-block).  Level boundaries
-// m + a (q - 1/2) are exact in float64 for fp16 a and m, so a float32 estimate of
-// rne((k - m)/a) is corrected by two exact float64 comparisons (ties to even).
-// ---------------------------------------------------------------------------------
+// Per-block affine 8-bit keys.  Boundaries m + a (q -+ 1/2) are exact in float64 for fp16
+// a and m, so a float32 estimate of rne((k - m)/a) is corrected by two exact float64
+// comparisons (ties to even).
 __device__ __forceinline__ bool passes64(double v, double tau, int k) {
   return (k & 1) ? (v > tau) : (v >= tau);
 }
 
 template <int D, int DT>
 __global__ void __launch_bounds__(256)
-encode_affine8_kernel(const uint16_t* __restrict__ x, int T, long n_groups, int dst_offset, int cap,
+encode_affine8_kernel(const uint16_t* __restrict__ x, int T, long n_parts, int dst_offset, int cap,
                       uint32_t* __restrict__ codes_out, uint32_t* __restrict__ aux_out) {
   constexpr int G = D / 32;
   const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= n_groups) return;
-  const int g = (int)(gid % G);
-  const long vt = gid / G;
-  const long slice = vt / T;
-  const long t = vt % T;
+  const bool live = gid < n_parts;
+  const long gq = live ? gid : n_parts - 4 + (gid & 3);
+  const int sub = (int)(gq & 3);
+  const int g = (int)((gq >> 2) % G);
+  const long vt = (gq >> 2) / G;
+  const long slice = vt / T, t = vt % T;
 
-  float v[32];
-  {
-    const uint4* src = reinterpret_cast<const uint4*>(x + vt * D + 32 * g);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint4 r = src[i];
-      const uint32_t w[4] = {r.x, r.y, r.z, r.w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        v[8 * i + 2 * k] = in_to_f32<DT>(w[k] & 0xFFFFu);
-        v[8 * i + 2 * k + 1] = in_to_f32<DT>(w[k] >> 16);
-      }
-    }
-  }
+  float v[8];
+  load8<DT>(x + vt * D + 32 * g + 8 * sub, v);
   float lo = v[0], hi = v[0];
 #pragma unroll
-  for (int e = 1; e < 32; ++e) { lo = fminf(lo, v[e]); hi = fmaxf(hi, v[e]); }
-  const uint32_t abits = f64_to_f16_rne(((double)hi - (double)lo) / 255.0);
-  const uint32_t mbits = f64_to_f16_rne((double)lo);
+  for (int e = 1; e < 8; ++e) { lo = fminf(lo, v[e]); hi = fmaxf(hi, v[e]); }
+  lo = quad_min(lo);
+  hi = quad_max(hi);
+  // a = fp16((hi - lo)/255): the difference is exact in float64; the quotient's binary
+  // fraction repeats with period 8 (1/255), far from an fp16 rounding tie, so rounding the
+  // float64 product to float32 and then to fp16 gives the exactly rounded result.
+  const uint32_t abits =
+      __builtin_bit_cast(uint16_t, (_Float16)(float)(((double)hi - (double)lo) * (1.0 / 255.0)));
+  const uint32_t mbits = __builtin_bit_cast(uint16_t, (_Float16)lo);
   const double a = (double)f16_to_f32(abits);
   const double m = (double)f16_to_f32(mbits);
   const float inva = (a > 0.0) ? (float)(1.0 / a) : 0.f;
-
-  uint32_t words[8] = {};
+  uint32_t words[2] = {0u, 0u};
 #pragma unroll
-  for (int e = 0; e < 32; ++e) {
+  for (int e = 0; e < 8; ++e) {
     int q = 0;
     if (a > 0.0) {
       const double ve = (double)v[e];
@@ -330,11 +355,10 @@ encode_affine8_kernel(const uint16_t* __restrict__ x, int T, long n_groups, int 
     }
     words[e >> 2] |= (uint32_t)q << (8 * (e & 3));
   }
+  if (!live) return;
   const size_t row = (size_t)slice * cap + dst_offset + t;
-  uint4* dst = reinterpret_cast<uint4*>(codes_out + row * (D / 4) + 8 * g);
-  dst[0] = make_uint4(words[0], words[1], words[2], words[3]);
-  dst[1] = make_uint4(words[4], words[5], words[6], words[7]);
-  aux_out[row * G + g] = abits | (mbits << 16);
+  *reinterpret_cast<uint2*>(codes_out + row * (D / 4) + 8 * g + 2 * sub) = make_uint2(words[0], words[1]);
+  if (sub == 0) aux_out[row * G + g] = abits | (mbits << 16);
 }
 
 // ---------------------------------------------------------------------------------
@@ -378,7 +402,7 @@ hipError_t run_lm(const tq_layout& Lay, const tq_state& S, const void* x, int ba
 template <int D, int VB, int DT>
 hipError_t run_group(const tq_layout& Lay, const void* x, int batch, int T, int dst, const tq_cache& C,
                      hipStream_t st) {
-  const long n = (long)batch * Lay.n_kv_heads * T * (D / 32);
+  const long n = (long)batch * Lay.n_kv_heads * T * (D / 8);   // 4 lanes per 32-group
   hipLaunchKernelGGL((encode_group_kernel<D, VB, DT>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
                      (const uint16_t*)x, T, n, dst, C.capacity, (uint32_t*)C.v_codes, (uint16_t*)C.v_aux);
   return hipGetLastError();
@@ -387,7 +411,7 @@ hipError_t run_group(const tq_layout& Lay, const void* x, int batch, int T, int 
 template <int D, int DT>
 hipError_t run_affine(const tq_layout& Lay, const void* x, int batch, int T, int dst, const tq_cache& C,
                       hipStream_t st) {
-  const long n = (long)batch * Lay.n_kv_heads * T * (D / 32);
+  const long n = (long)batch * Lay.n_kv_heads * T * (D / 8);
   hipLaunchKernelGGL((encode_affine8_kernel<D, DT>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
                      (const uint16_t*)x, T, n, dst, C.capacity, (uint32_t*)C.k_codes, (uint32_t*)C.k_aux);
   return hipGetLastError();
