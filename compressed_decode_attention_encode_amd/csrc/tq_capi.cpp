@@ -103,7 +103,7 @@ int check_state(const tq_state* S, const tq_layout* L, bool need_k, bool need_v)
   if (need_k && L->k_kind == TQ_K_LM_QJL) {
     if (!S->k_centroids || !S->k_thresholds || !S->k_signs || !S->qjl)
       return fail(TQ_ERR_INVALID, "LM+QJL keys need k_centroids, k_thresholds, k_signs and qjl");
-    if (!aligned4(S->k_centroids) || !aligned4(S->k_thresholds) || !aligned4(S->k_signs) || !aligned4(S->qjl))
+    if (!aligned4(S->k_centroids) || !aligned4(S->k_thresholds) || !aligned4(S->k_signs) || !aligned16(S->qjl))
       return fail(TQ_ERR_INVALID, "state arrays must be 4-byte aligned");
   }
   if (need_v && L->v_kind == TQ_V_LM_ROT) {
@@ -192,6 +192,30 @@ double norm_quantile(double p) {
   return 0.5 * (lo + hi);
 }
 
+// float64 -> fp16 bits, round to nearest even (directly, no float32 step).
+uint16_t f64_to_f16_bits(double x) {
+  uint64_t b;
+  std::memcpy(&b, &x, 8);
+  const uint32_t sign = (uint32_t)(b >> 48) & 0x8000u;
+  b &= 0x7FFFFFFFFFFFFFFFull;
+  if (b >= 0x7FF0000000000000ull) return (uint16_t)(sign | 0x7C00u | (b > 0x7FF0000000000000ull ? 0x200u : 0u));
+  if (b == 0) return (uint16_t)sign;
+  const int e = (int)(b >> 52) - 1023;
+  const uint64_t m = (b & 0x000FFFFFFFFFFFFFull) | 0x0010000000000000ull;
+  if (e < -25) return (uint16_t)sign;
+  const int shift = (e >= -14) ? 42 : 42 + (-14 - e);
+  uint64_t keep = m >> shift;
+  const uint64_t rem = m & ((1ull << shift) - 1), half = 1ull << (shift - 1);
+  if (rem > half || (rem == half && (keep & 1))) keep += 1;
+  if (e >= -14) {
+    int ee = e + 15;
+    if (keep == (1ull << 11)) { keep >>= 1; ee += 1; }
+    if (ee >= 31) return (uint16_t)(sign | 0x7C00u);
+    return (uint16_t)(sign | ((uint32_t)ee << 10) | ((uint32_t)keep & 0x3FFu));
+  }
+  return (uint16_t)(sign | (uint32_t)keep);
+}
+
 }  // namespace
 
 extern "C" {
@@ -249,7 +273,7 @@ int tq_make_codebook(int head_dim, int bits, float* centroids, float* thresholds
   return TQ_OK;
 }
 
-int tq_make_rotation(int head_dim, uint64_t seed, uint32_t* signs, float* qjl) {
+int tq_make_rotation(int head_dim, uint64_t seed, uint32_t* signs, uint16_t* qjl) {
   if (!signs) return fail(TQ_ERR_INVALID, "signs output is NULL");
   if (head_dim < 32 || head_dim > 4096 || (head_dim & (head_dim - 1)))
     return fail(TQ_ERR_UNSUPPORTED, "head_dim %d must be a power of two in 32..4096", head_dim);
@@ -269,8 +293,8 @@ int tq_make_rotation(int head_dim, uint64_t seed, uint32_t* signs, float* qjl) {
       const double u1 = (double)((x1 >> 11) + 1) * 0x1.0p-53;
       const double u2 = (double)(x2 >> 11) * 0x1.0p-53;
       const double rho = std::sqrt(-2.0 * std::log(u1));
-      qjl[i] = (float)(rho * std::cos(2.0 * M_PI * u2));
-      qjl[i + 1] = (float)(rho * std::sin(2.0 * M_PI * u2));
+      qjl[i] = f64_to_f16_bits(rho * std::cos(2.0 * M_PI * u2));
+      qjl[i + 1] = f64_to_f16_bits(rho * std::sin(2.0 * M_PI * u2));
     }
   }
   return TQ_OK;
@@ -302,6 +326,8 @@ int tq_encode(const tq_layout* L, const tq_state* S, const void* k, const void* 
   if (n_tokens < 0 || dst_offset < 0) return fail(TQ_ERR_INVALID, "n_tokens %d / dst_offset %d negative", n_tokens, dst_offset);
   if ((long)dst_offset + n_tokens > C->capacity)
     return fail(TQ_ERR_CAPACITY, "dst_offset %d + n_tokens %d > capacity %d", dst_offset, n_tokens, C->capacity);
+  if ((long)n_tokens * (L->head_dim / 8) > (1L << 30))
+    return fail(TQ_ERR_UNSUPPORTED, "n_tokens %d too large for one call (split it)", n_tokens);
   if (k && !encode_k_compiled(*L)) return fail(TQ_ERR_UNSUPPORTED, "no key encoder compiled for this layout (head_dim %d)", L->head_dim);
   if (v && !encode_v_compiled(*L)) return fail(TQ_ERR_UNSUPPORTED, "no value encoder compiled for this layout (head_dim %d)", L->head_dim);
   if (n_tokens == 0) return TQ_OK;

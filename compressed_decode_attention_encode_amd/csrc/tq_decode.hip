@@ -22,7 +22,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 template <int D, int KK, int DT>
 __global__ void __launch_bounds__(256)
 decode_prep_kernel(const uint16_t* __restrict__ q, const uint32_t* __restrict__ sign_mask,
-                   const float* __restrict__ S, float* __restrict__ qprep, int Hq) {
+                   const uint16_t* __restrict__ S, float* __restrict__ qprep, int Hq) {
   constexpr int QF = 4 * D;
   __shared__ float s_x[D];
   const int h = blockIdx.x, b = blockIdx.y;
@@ -55,17 +55,19 @@ decode_prep_kernel(const uint16_t* __restrict__ q, const uint32_t* __restrict__ 
     }
     const float rs = rsqrtf((float)D);
     if (j < D) out[j] = s_x[j] * rs * scale;   // qa = Pi q
-    // q_s = S q_r; thread i takes row i of S with independent 16-byte loads
+    // q_s = S q_r; thread i takes row i of S (fp16) with independent 16-byte loads
     if (j < D) {
-      const float4* srow = reinterpret_cast<const float4*>(S + (size_t)j * D);
+      const uint4* srow = reinterpret_cast<const uint4*>(S + (size_t)j * D);
       float acc = 0.f;
-#pragma unroll 8
-      for (int k = 0; k < D / 4; ++k) {
-        const float4 sv = srow[k];
-        acc = fmaf(sv.x, s_x[4 * k], acc);
-        acc = fmaf(sv.y, s_x[4 * k + 1], acc);
-        acc = fmaf(sv.z, s_x[4 * k + 2], acc);
-        acc = fmaf(sv.w, s_x[4 * k + 3], acc);
+#pragma unroll 4
+      for (int k = 0; k < D / 8; ++k) {
+        const uint4 sv = srow[k];
+        const uint32_t w[4] = {sv.x, sv.y, sv.z, sv.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc = fmaf(f16_to_f32(w[i] & 0xFFFFu), s_x[8 * k + 2 * i], acc);
+          acc = fmaf(f16_to_f32(w[i] >> 16), s_x[8 * k + 2 * i + 1], acc);
+        }
       }
       const float qjl = 1.2533141373155003f / (float)D;   // sqrt(pi/2)/d
       out[D + j] = acc * rs * scale * qjl;

@@ -79,6 +79,16 @@ __device__ __forceinline__ double xor_lanes(double x) {
   return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 
+template <int M>
+__device__ __forceinline__ float xor_lanes(float x) {
+  return __uint_as_float(xor_lanes_u32<M>(__float_as_uint(x)));
+}
+
+// Value of lane + 1 within the lane's row of 16 (row_shl:1); the last lane of a row gets 0.
+__device__ __forceinline__ uint32_t next_lane_u32(uint32_t v) {
+  return __builtin_amdgcn_mov_dpp(v, 0x101, 0xF, 0xF, true);
+}
+
 // Sum over the N consecutive lanes sharing lane / N (N <= 16), by DPP exchanges.
 template <int N>
 __device__ __forceinline__ double group_sum_dpp(double v) {

@@ -7,16 +7,24 @@
 // Per-block affine 8-bit keys: vllm-metal TurboQuant guide (wmrh.cn), quantisation
 //   principle table (per-block scale, no rotation).
 //
-// Work decomposition (rotated-LM kernel): a work-group owns a tile of 64 consecutive
-// tokens of one (batch, kv-head) slice.  Each vector is handled by P = d/32 consecutive
-// lanes, each holding 32 coordinates in float64: the first five butterfly stages of the
-// Walsh-Hadamard transform stay inside a lane, the remaining log2(P) stages go across
-// lanes with xor shuffles.  Norm, rotation, Lloyd-Max decision and residual are float64,
-// so every decision matches a float64 evaluation up to the last bits.
+// Work decomposition (rotated-LM kernel): a persistent work-group walks 64-token tiles
+// of the (batch, kv-head) slices, prefetching the next tile's inputs into registers while
+// it computes the current one.  Each vector is handled by P = d/32 consecutive lanes,
+// each holding 32 coordinates: the first five butterfly stages of the Walsh-Hadamard
+// transform stay inside a lane, the remaining log2(P) stages go across lanes with DPP
+// exchanges.  Keys rotate in float64, so n, gamma and every decision match a float64
+// evaluation; values rotate in float32 (only their decisions depend on it, and those
+// move only within a float32 ulp of a threshold) with a float64 norm.  Codes are packed
+// in registers and stored straight from the lanes.
 // The QJL projection Z = R S^T (64 x d times d x d) is a dense contraction and runs on
-// the matrix cores with v_mfma_f32_32x32x2f32: each of the d/32 waves keeps its 32 rows
-// of S resident in VGPRs for the whole (persistent) kernel and streams the residual
-// tile from LDS; the sign bits fall out of one ballot per accumulator register.
+// the fp16 matrix cores (v_mfma_f32_32x32x16_f16): S is stored at fp16 resolution, the
+// float32 residual is split into fp16 hi + lo halves, and Z accumulates S*hi + S*lo in
+// float32 -- every product exact, the residual carried to ~21 significant bits -- at two
+// fp16 MFMAs instead of sixteen float32 ones per k-block of 16.  Each of the d/32 waves
+// keeps its 32 rows of S in VGPRs for the whole kernel and reads the residual tile from
+// LDS; each lane packs the sign bits of its accumulators.
+#include <type_traits>
+
 #include "tq_internal.h"
 #include "tq_device.h"
 
@@ -28,26 +36,57 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 // Rotated Lloyd-Max encode.  QJL = true: keys (codes + QJL signs + fp16 (n, gamma));
 // QJL = false: rotated values (codes + fp32 n).
 // ---------------------------------------------------------------------------------
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+
+// Keys work on y, thresholds and centroids scaled by 2^12 (exact): the residual then
+// enters the fp16 split as |r| 2^12 < 4096, where the low half of nearly every coordinate
+// stays a normal fp16 number; decisions are unchanged, the projection's sign needs no
+// rescaling and gamma = sqrt(sum r'^2) 2^-12 exactly.
+constexpr double kKeyScale = 4096.0;
+
+// Number of positive thresholds p_0 < p_1 < ... below |y| (binary search over the L/2
+// magnitude cells of the symmetric codebook).
+template <int KB>
+__device__ __forceinline__ uint32_t magnitude_cell(float ay, const float (&p)[(1 << KB) / 2 - 1]) {
+  if constexpr (KB == 2) {
+    return ay > p[0] ? 1u : 0u;
+  } else if constexpr (KB == 3) {
+    const uint32_t c1 = ay > p[1] ? 1u : 0u;
+    const uint32_t c2 = ay > (c1 ? p[2] : p[0]) ? 1u : 0u;
+    return 2u * c1 + c2;
+  } else {
+    const uint32_t c1 = ay > p[3] ? 1u : 0u;
+    const uint32_t c2 = ay > (c1 ? p[5] : p[1]) ? 1u : 0u;
+    const float t3 = c1 ? (c2 ? p[6] : p[4]) : (c2 ? p[2] : p[0]);
+    const uint32_t c3 = ay > t3 ? 1u : 0u;
+    return 4u * c1 + 2u * c2 + c3;
+  }
+}
+
 template <int D, int KB, int DT, bool QJL>
-__global__ void __launch_bounds__(2 * D) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 2 : 1)))
+__global__ void __launch_bounds__(2 * D) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1)))
 encode_lm_kernel(const uint16_t* __restrict__ x, int T, int tiles_per_slice, int n_tiles,
                  int dst_offset, int cap,
                  const float* __restrict__ cent, const float* __restrict__ thr,
-                 const uint32_t* __restrict__ sign_mask, const float* __restrict__ S,
+                 const uint32_t* __restrict__ sign_mask, const uint16_t* __restrict__ S,
                  uint32_t* __restrict__ codes_out, uint32_t* __restrict__ signs_out,
                  uint32_t* __restrict__ aux_out) {
+  // keys: float64 rotation and residual, so n, gamma and every decision agree with a
+  // float64 evaluation; values: float32 rotation (only the decisions depend on it) and a
+  // float64 norm
+  using W = typename std::conditional<QJL, double, float>::type;
   constexpr int P = D / 32;            // lanes per vector
   constexpr int L = 1 << KB;
   constexpr int PER = (KB == 3) ? 10 : 32 / KB;   // codes per word
   constexpr int WK = (D + PER - 1) / PER;          // words per row
-  constexpr int RS = D + 4;                        // LDS row stride of the residual tile (floats)
   constexpr int SW = D / 32;                       // sign words per row
+  constexpr int RH = D + 8;                        // LDS row stride of the residual halves
+  constexpr int NKB = D / 16;                      // MFMA k-blocks
 
   __shared__ double s_cent[16];
-  __shared__ __attribute__((aligned(16))) uint32_t s_code[kTile * D / 4];   // code bytes
-  __shared__ __attribute__((aligned(16))) float s_res[QJL ? kTile * RS : 4];
-  __shared__ uint32_t s_sgn[QJL ? kTile * SW : 1];
-  __shared__ uint32_t s_aux[kTile];
+  __shared__ __attribute__((aligned(16))) uint32_t s_xm[P * 16];
+  __shared__ __attribute__((aligned(16))) _Float16 s_rhi[QJL ? kTile * RH : 8];
+  __shared__ __attribute__((aligned(16))) _Float16 s_rlo[QJL ? kTile * RH : 8];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -55,21 +94,52 @@ encode_lm_kernel(const uint16_t* __restrict__ x, int T, int tiles_per_slice, int
   const int vec = tid / P;     // vector within the tile
   const int part = tid % P;    // which 32 coordinates
 
-  if (tid < L) s_cent[tid] = (double)cent[tid];
+  constexpr double kPre = QJL ? kKeyScale : 1.0;
+  if (tid < L) s_cent[tid] = (double)cent[tid] * kPre;
+  if (tid < P * 16) {
+    // sign flips as xor masks on pairs of packed 16-bit inputs: coordinate 32 p + 2 i at
+    // bit 15, 32 p + 2 i + 1 at bit 31
+    const uint32_t sm = sign_mask[tid / 16];
+    const int i = tid % 16;
+    s_xm[tid] = (((sm >> (2 * i)) & 1u) << 15) | (((sm >> (2 * i + 1)) & 1u) << 31);
+  }
   // symmetric codebook: t[L/2-1] = 0 and t[L/2-1+i] = -t[L/2-1-i]; only the positive
   // thresholds are compared, against |y|
-  double thp[L / 2 - 1];
+  float thp[L / 2 - 1];
 #pragma unroll
-  for (int i = 0; i < L / 2 - 1; ++i) thp[i] = (double)thr[L / 2 + i];
-  const uint32_t smask = sign_mask[part];
+  for (int i = 0; i < L / 2 - 1; ++i) thp[i] = thr[L / 2 + i] * (float)kPre;
 
-  // Rows of S this wave keeps for the whole kernel: lane holds S[32*wave + lane%32][2kk + lane/32].
-  float sb[QJL ? D / 2 : 1];
+  // QJL: the wave's 32 rows of S (projection outputs 32 wave .. 32 wave + 31), fp16, as
+  // MFMA A operands: lane l holds S[32 wave + l % 32][16 kb + 8 (l / 32) + i], i = 0..7.
+  half8 sop[QJL ? NKB : 1];
   if constexpr (QJL) {
-    const float* srow = S + (size_t)(32 * wave + (lane & 31)) * D + (lane >> 5);
+    const uint16_t* srow = S + (size_t)(32 * wave + (lane & 31)) * D + 8 * (lane >> 5);
 #pragma unroll
-    for (int kk = 0; kk < D / 2; ++kk) sb[kk] = srow[2 * kk];
+    for (int kb = 0; kb < NKB; ++kb) sop[kb] = __builtin_bit_cast(half8, *reinterpret_cast<const uint4*>(srow + 16 * kb));
   }
+
+  // 3-bit codes: word kw holds codes 10 kw .. 10 kw + 9, so words straddle the lanes'
+  // 32-code ranges.  A lane writes the words that start in its range, kw0 .. kw1, taking
+  // the first bits of the next lane's stream where a word runs past its own.
+  const int kw0 = (32 * part + PER - 1) / PER;
+  const int kw1 = min((32 * part + 31) / PER, WK - 1);
+  const int b0 = KB * (PER * kw0 - 32 * part);     // bit offset of word kw0 in the lane's stream
+
+  auto load_tile = [&](int tile, uint4 (&raw)[4]) {
+    const int slice = tile / tiles_per_slice;
+    const int t0 = (tile % tiles_per_slice) * kTile;
+    if (tile < n_tiles && vec < min(kTile, T - t0)) {
+      const uint4* src = reinterpret_cast<const uint4*>(x + ((size_t)slice * T + t0 + vec) * D + 32 * part);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) raw[i] = src[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) raw[i] = make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+
+  uint4 raw[4];
+  load_tile(blockIdx.x, raw);
   __syncthreads();
 
   for (int tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
@@ -77,139 +147,170 @@ encode_lm_kernel(const uint16_t* __restrict__ x, int T, int tiles_per_slice, int
     const int t0 = (tile % tiles_per_slice) * kTile;
     const int nv = min(kTile, T - t0);
     const bool valid = vec < nv;
+    const size_t row0 = (size_t)slice * cap + dst_offset + t0;
 
-    // ---- phase A: load 32 coordinates, sign flip, Walsh-Hadamard in float64 -------------
-    double xv[32];
+    uint32_t w[16];
     {
-      uint4 raw[4] = {};
-      if (valid) {
-        const uint4* src = reinterpret_cast<const uint4*>(x + ((size_t)slice * T + t0 + vec) * D + 32 * part);
+      const uint32_t* rw = reinterpret_cast<const uint32_t*>(raw);
+      const uint4* xm4 = reinterpret_cast<const uint4*>(&s_xm[part * 16]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) raw[i] = src[i];
-      }
-      const uint32_t* w = reinterpret_cast<const uint32_t*>(raw);
-#pragma unroll
-      for (int e = 0; e < 32; ++e) {
-        uint32_t b = (w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-        b ^= ((smask >> e) & 1u) << 15;   // s_j = -1 flips the sign bit
-        xv[e] = (double)in_to_f32<DT>(b);
+      for (int i = 0; i < 4; ++i) {
+        const uint4 m = xm4[i];
+        w[4 * i] = rw[4 * i] ^ m.x;
+        w[4 * i + 1] = rw[4 * i + 1] ^ m.y;
+        w[4 * i + 2] = rw[4 * i + 2] ^ m.z;
+        w[4 * i + 3] = rw[4 * i + 3] ^ m.w;
       }
     }
+    // the next tile's inputs stay in flight while this one is computed
+    load_tile(tile + gridDim.x, raw);
+
+    // ---- phase A: sign flip, norm (float64), Walsh-Hadamard ----------------------------
+    W xv[32];
     double ss = 0.0;
 #pragma unroll
-    for (int e = 0; e < 32; ++e) ss = fma(xv[e], xv[e], ss);
+    for (int i = 0; i < 16; ++i) {
+      const float a = in_to_f32<DT>(w[i] & 0xFFFFu);
+      const float b = in_to_f32<DT>(w[i] >> 16);
+      ss = fma((double)a, (double)a, ss);
+      ss = fma((double)b, (double)b, ss);
+      xv[2 * i] = (W)a;
+      xv[2 * i + 1] = (W)b;
+    }
 #pragma unroll
     for (int h = 1; h < 32; h <<= 1) {
 #pragma unroll
       for (int e = 0; e < 32; ++e) {
         if ((e & h) == 0) {
-          const double a = xv[e], b = xv[e + h];
+          const W a = xv[e], b = xv[e + h];
           xv[e] = a + b;
           xv[e + h] = a - b;
         }
       }
     }
-    // butterflies across the P lanes of the vector (stride 32*m <-> lane xor m)
+    // butterflies across the P lanes of the vector (stride 32 m <-> lane xor m): the upper
+    // lane of each pair keeps partner - own, the lower own + partner
 #define TQ_XSTAGE(M)                                              \
     if constexpr (P > M) {                                        \
-      const bool hi = (part & M) != 0;                            \
+      const W sg = (part & M) ? W(-1) : W(1);                     \
       _Pragma("unroll") for (int e = 0; e < 32; ++e) {            \
-        const double o = xor_lanes<M>(xv[e]);                     \
-        xv[e] = hi ? (o - xv[e]) : (xv[e] + o);                   \
+        const W o = xor_lanes<M>(xv[e]);                          \
+        xv[e] = fma(xv[e], sg, o);                                \
       }                                                           \
     }
     TQ_XSTAGE(1)
     TQ_XSTAGE(2)
     TQ_XSTAGE(4)
-    TQ_XSTAGE(8)
 #undef TQ_XSTAGE
     ss = group_sum_dpp<P>(ss);
     const double n = sqrt(ss);
-    const double scale = (n > 0.0) ? 1.0 / (sqrt((double)D) * n) : 0.0;
+    const double scale64 = (n > 0.0) ? kPre / (sqrt((double)D) * n) : 0.0;
+    const W scale = (W)scale64;
 
-    // ---- Lloyd-Max decision and residual --------------------------------------------
-    uint32_t packed[8];
+    // ---- Lloyd-Max decision, packed codes, residual -----------------------------------
+    uint32_t cw[4] = {0u, 0u, 0u, 0u};   // the lane's 32 codes as a KB-bit stream
     double gg = 0.0;
+    // eight coordinates at a time (keeps the centroid reads and residuals of one chunk
+    // in registers); keys write each chunk's residual halves to LDS:
+    // hi = fp16(r) and lo = fp16(r - hi), both rounded toward zero -- the pair carries 21+
+    // significant bits and every product of halves is exact in float32
 #pragma unroll
-    for (int e = 0; e < 32; ++e) {
-      const double y = xv[e] * scale;
-      // idx = #{i : t_i < y}: with cnt = #{positive t_i < |y|} (sign bit of t_i - |y|) this is
-      // L/2 + cnt for y > 0 and L/2 - 1 - cnt otherwise (equal except when |y| == t_i exactly)
-      const double ay = fabs(y);
-      uint32_t cnt = 0;
+    for (int c = 0; c < 4; ++c) {
+      float rf[8];
 #pragma unroll
-      for (int i = 0; i < L / 2 - 1; ++i) cnt += (uint32_t)((uint64_t)__double_as_longlong(thp[i] - ay) >> 63);
-      const uint32_t pos = (uint32_t)((uint64_t)__double_as_longlong(0.0 - y) >> 63);   // y > 0
-      const int idx = pos ? (int)(L / 2 + cnt) : (int)(L / 2 - 1 - cnt);
-      if ((e & 3) == 0) packed[e >> 2] = 0;
-      packed[e >> 2] |= (uint32_t)idx << (8 * (e & 3));
+      for (int k = 0; k < 8; ++k) {
+        const int e = 8 * c + k;
+        const W y = xv[e] * scale;
+        // idx = #{i : t_i < y} = L/2 + cnt for y > 0 and L/2 - 1 - cnt otherwise, with cnt
+        // the number of positive thresholds below |y| (L/2 + cnt = cnt ^ L/2 and
+        // L/2 - 1 - cnt = cnt ^ (L/2 - 1) for cnt < L/2); float32 |y| changes a decision
+        // only where y lies within one float32 ulp of a threshold
+        const float yf = (float)y;
+        const uint32_t cnt = magnitude_cell<KB>(fabsf(yf), thp);
+        const uint32_t idx = cnt ^ ((yf > 0.f) ? (uint32_t)(L / 2) : (uint32_t)(L / 2 - 1));
+        const int bit = KB * e;
+        cw[bit >> 5] |= idx << (bit & 31);
+        if ((bit & 31) + KB > 32) cw[(bit >> 5) + 1] |= idx >> (32 - (bit & 31));
+        if constexpr (QJL) {
+          const double r = (double)y - s_cent[idx];
+          gg = fma(r, r, gg);
+          rf[k] = (float)r;
+        }
+      }
       if constexpr (QJL) {
-        const double r = y - s_cent[idx];
-        gg = fma(r, r, gg);
-        xv[e] = r;
+        uint32_t hw[4], lw[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const auto h = __builtin_amdgcn_cvt_pkrtz(rf[2 * q], rf[2 * q + 1]);
+          const auto l = __builtin_amdgcn_cvt_pkrtz(rf[2 * q] - (float)h[0], rf[2 * q + 1] - (float)h[1]);
+          hw[q] = __builtin_bit_cast(uint32_t, h);
+          lw[q] = __builtin_bit_cast(uint32_t, l);
+        }
+        *reinterpret_cast<uint4*>(&s_rhi[vec * RH + 32 * part + 8 * c]) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        *reinterpret_cast<uint4*>(&s_rlo[vec * RH + 32 * part + 8 * c]) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (valid) {
+      uint32_t* crow = codes_out + (row0 + vec) * WK;
+      if constexpr (KB == 2) {
+        *reinterpret_cast<uint2*>(crow + 2 * part) = make_uint2(cw[0], cw[1]);
+      } else if constexpr (KB == 4) {
+        *reinterpret_cast<uint4*>(crow + 4 * part) = make_uint4(cw[0], cw[1], cw[2], cw[3]);
       }
     }
-    {
-      uint4* dst = reinterpret_cast<uint4*>(&s_code[(vec * D + 32 * part) / 4]);
-      dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-      dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+    if constexpr (KB == 3) {
+      // the lane's stream is 96 bits; word kw0 + j starts at bit b0 + 30 j (< 118)
+      const uint32_t nx = next_lane_u32(cw[0]);
+      const uint32_t s3 = (part == P - 1) ? 0u : nx;
+      const uint32_t st[4] = {cw[0], cw[1], cw[2], s3};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        // bit bb of the stream lies in stream word j (j = 0 always) or j - 1
+        const int bb = b0 + 30 * j;
+        const bool up = j == 0 || (bb >> 5) == j;
+        const uint32_t lo = up ? st[j] : st[j - 1];
+        const uint32_t hi = up ? (j < 3 ? st[j + 1] : 0u) : st[j];
+        const uint32_t word = __builtin_amdgcn_alignbit(hi, lo, (uint32_t)(bb & 31)) & 0x3FFFFFFFu;
+        if (valid && kw0 + j <= kw1) codes_out[(row0 + vec) * WK + kw0 + j] = word;
+      }
     }
     if constexpr (QJL) {
       gg = group_sum_dpp<P>(gg);
-      float4* dst = reinterpret_cast<float4*>(&s_res[vec * RS + 32 * part]);
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        dst[i] = make_float4((float)xv[4 * i], (float)xv[4 * i + 1], (float)xv[4 * i + 2], (float)xv[4 * i + 3]);
-      if (part == 0) s_aux[vec] = f64_to_f16_rne(n) | (f64_to_f16_rne(sqrt(gg)) << 16);
+      if (valid && part == 0)
+        aux_out[row0 + vec] = f64_to_f16_rne(n) | (f64_to_f16_rne(sqrt(gg) * (1.0 / kKeyScale)) << 16);
     } else {
-      if (part == 0) s_aux[vec] = __float_as_uint((float)n);
+      if (valid && part == 0) aux_out[row0 + vec] = __float_as_uint((float)n);
     }
-    __syncthreads();
 
-    // ---- phase B: QJL projection on the matrix cores, sign bits by ballot ----------------
+    // ---- phase B: QJL projection on the matrix cores, sign bits packed per lane --------
+    // Z^T = S R^T per 32-token block: A = the wave's S rows (outputs), B = residual rows.
     if constexpr (QJL) {
-      floatx16 acc0 = {}, acc1 = {};
-      const float* a0 = &s_res[(lane & 31) * RS + (lane >> 5)];
-      const float* a1 = a0 + 32 * RS;
-#pragma unroll
-      for (int kk = 0; kk < D / 2; ++kk) {
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a0[2 * kk], sb[kk], acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a1[2 * kk], sb[kk], acc1, 0, 0, 0);
-      }
-      // acc register r of lane l holds row 8(r/4) + 4(l/32) + r%4, column l%32.
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = 8 * (r >> 2) + (r & 3);
-        const uint64_t b0 = __ballot(acc0[r] >= 0.0f);
-        const uint64_t b1 = __ballot(acc1[r] >= 0.0f);
-        if (lane == 0) {
-          s_sgn[row * SW + wave] = (uint32_t)b0;
-          s_sgn[(row + 4) * SW + wave] = (uint32_t)(b0 >> 32);
-          s_sgn[(32 + row) * SW + wave] = (uint32_t)b1;
-          s_sgn[(36 + row) * SW + wave] = (uint32_t)(b1 >> 32);
-        }
-      }
       __syncthreads();
-    }
-
-    // ---- phase C: pack and store the tile's rows (contiguous in every plane) -------------
-    const size_t row0 = (size_t)slice * cap + dst_offset + t0;
-    const uint8_t* cb = reinterpret_cast<const uint8_t*>(s_code);
-    for (int q = tid; q < nv * WK; q += 2 * D) {
-      const int v = q / WK, kw = q % WK;
-      uint32_t word = 0;
 #pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        const int j = kw * PER + i;
-        if (j < D) word |= (uint32_t)cb[v * D + j] << (KB * i);
+      for (int mb = 0; mb < 2; ++mb) {
+        floatx16 acc = {};
+        const _Float16* ah = &s_rhi[(32 * mb + (lane & 31)) * RH + 8 * (lane >> 5)];
+        const _Float16* al = &s_rlo[(32 * mb + (lane & 31)) * RH + 8 * (lane >> 5)];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          const half8 r_h = *reinterpret_cast<const half8*>(ah + 16 * kb);
+          const half8 r_l = *reinterpret_cast<const half8*>(al + 16 * kb);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(sop[kb], r_h, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(sop[kb], r_l, acc, 0, 0, 0);
+        }
+        // acc register r of lane l: token 32 mb + l % 32, projection output
+        // 32 wave + 8 (r / 4) + 4 (l / 32) + r % 4.  Stored bit = (z >= 0), from the sign bit.
+        uint32_t neg = 0u;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) neg |= (__float_as_uint(acc[r]) >> 31) << (8 * (r >> 2) + (r & 3));
+        const uint32_t half_bits = (~neg & 0x0F0F0F0Fu) << (4 * (lane >> 5));
+        const uint32_t word = half_bits | (uint32_t)__shfl_xor((int)half_bits, 32);
+        const int t = 32 * mb + lane;
+        if (lane < 32 && t < nv) signs_out[(row0 + t) * SW + wave] = word;
       }
-      codes_out[row0 * WK + q] = word;
+      __syncthreads();   // the residual tile is overwritten by the next tile
     }
-    if constexpr (QJL) {
-      for (int q = tid; q < nv * SW; q += 2 * D) signs_out[row0 * SW + q] = s_sgn[q];
-    }
-    for (int q = tid; q < nv; q += 2 * D) aux_out[row0 + q] = s_aux[q];
-    __syncthreads();
   }
 }
 
@@ -246,61 +347,85 @@ __device__ __forceinline__ bool passes(float v, float tau, int k) {
   return (k & 1) ? (v > tau) : (v >= tau);
 }
 
+// Thread-to-data map of the group kernels: grid.y walks the (batch, kv-head) slices, and a
+// work-group covers kGroupItems * 256 consecutive 8-element parts of one slice; item u of
+// a thread is part  blockIdx.x * 256 * kGroupItems + 256 u + threadIdx.x, so each item's
+// loads are coalesced and all of a thread's loads are in flight before any is used.
+// A part count per slice of T * d / 8 is a multiple of 4 and every item offset is a
+// multiple of 64: a lane quad (one 32-group) is entirely inside or outside the slice.
+constexpr int kGroupItems = 4;
+
 template <int D, int VB, int DT>
 __global__ void __launch_bounds__(256)
-encode_group_kernel(const uint16_t* __restrict__ x, int T, long n_parts, int dst_offset, int cap,
+encode_group_kernel(const uint16_t* __restrict__ x, int T, int slices, int dst_offset, int cap,
                     uint32_t* __restrict__ codes_out, uint16_t* __restrict__ scale_out) {
   constexpr int G = D / 32;
   constexpr int L = 1 << VB;
-  const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  // n_parts is a multiple of 4 and the grid a multiple of 64: whole quads are in or out
-  const bool live = gid < n_parts;
-  const long gq = live ? gid : n_parts - 4 + (gid & 3);
-  const int sub = (int)(gq & 3);                 // which 8 elements of the group
-  const int g = (int)((gq >> 2) % G);
-  const long vt = (gq >> 2) / G;                 // slice * T + t
-  const long slice = vt / T, t = vt % T;
-
-  float v[8];
-  load8<DT>(x + vt * D + 32 * g + 8 * sub, v);
-  float amax = 0.f;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
-  amax = quad_max(amax);
-  // Delta = fp16(2 amax / (L-1)): amax is an fp16/bf16 value, so the exact quotient has a
-  // repeating binary fraction (k/3 or k/15) that stays >= 1/30 of an fp16 ulp away from a
-  // rounding tie; the float32 product with the rounded reciprocal (error ~1e-7 relative)
-  // therefore rounds to the same fp16 value as the exact quotient.
-  const uint32_t dbits = __builtin_bit_cast(uint16_t, (_Float16)(2.0f * amax * (1.0f / (float)(L - 1))));
-  const float delta = f16_to_f32(dbits);
-  const float inv = (delta > 0.f) ? 1.0f / delta : 0.f;
-  const float off = 0.5f * (float)(L - 1);
-  uint32_t code = 0;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    int k;
-    if (delta > 0.f) {
-      k = (int)rintf(fmaf(v[e], inv, off));
-      k = min(max(k, 0), L - 1);
-      if (k > 0 && !passes(v[e], delta * (float)(k - L / 2), k)) {
-        k -= 1;
-      } else if (k < L - 1 && passes(v[e], delta * (float)(k + 1 - L / 2), k + 1)) {
-        k += 1;
-      }
-    } else {
-      k = (v[e] > 0.f) ? L - 1 : ((v[e] < 0.f) ? 0 : L / 2);
-    }
-    code |= (uint32_t)k << (VB * e);
-  }
-  if (!live) return;
-  const size_t row = (size_t)slice * cap + dst_offset + t;
   constexpr int WV = D * VB / 32;
-  if constexpr (VB == 4) {
-    codes_out[row * WV + g * 4 + sub] = code;                     // 8 codes = one word
-  } else {
-    reinterpret_cast<uint16_t*>(codes_out + row * WV + g * 2)[sub] = (uint16_t)code;   // half a word
+  const int parts = T * (D / 8);
+  for (int slice = blockIdx.y; slice < slices; slice += gridDim.y) {
+    const uint16_t* xs = x + (size_t)slice * T * D;
+    const size_t row_s = (size_t)slice * cap + dst_offset;
+    float v[kGroupItems][8];
+#pragma unroll
+    for (int u = 0; u < kGroupItems; ++u) {
+      const int p = (blockIdx.x * kGroupItems + u) * 256 + threadIdx.x;
+      if (p < parts) {
+        load8<DT>(xs + (size_t)p * 8, v[u]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[u][e] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kGroupItems; ++u) {
+      const int p = (blockIdx.x * kGroupItems + u) * 256 + threadIdx.x;
+      const int sub = p & 3, g = (p >> 2) % G, t = p / (D / 8);
+      float amax = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[u][e]));
+      amax = quad_max(amax);
+      // Delta = fp16(2 amax / (L-1)): amax is an fp16/bf16 value, so the exact quotient has
+      // a repeating binary fraction (k/3 or k/15) that stays >= 1/30 of an fp16 ulp away
+      // from a rounding tie; the float32 product with the rounded reciprocal (error ~1e-7
+      // relative) therefore rounds to the same fp16 value as the exact quotient.
+      const uint32_t dbits = __builtin_bit_cast(uint16_t, (_Float16)(2.0f * amax * (1.0f / (float)(L - 1))));
+      const float delta = f16_to_f32(dbits);
+      const float inv = (delta > 0.f) ? 1.0f / delta : 0.f;
+      const float off = 0.5f * (float)(L - 1);
+      uint32_t code = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float ve = v[u][e];
+        // x = v/Delta + (L-1)/2 to within 2^-20; only an x within 2^-16 of a half-integer
+        // (a level boundary, exact ties included) needs the exact test
+        const float x = fmaf(ve, inv, off);
+        const float kr = rintf(x);
+        float kf = fminf(fmaxf(kr, 0.f), (float)(L - 1));
+        if (fabsf(fabsf(x - kr) - 0.5f) < 0x1p-16f || delta == 0.f) {
+          if (delta == 0.f) {
+            kf = (ve > 0.f) ? (float)(L - 1) : ((ve < 0.f) ? 0.f : (float)(L / 2));
+          } else {
+            // boundary b sits between levels b-1 and b at v = Delta (b - L/2), exact in float32
+            const float bf = rintf(x + 0.5f);
+            const int bi = (int)bf;
+            kf = passes(ve, delta * (bf - (float)(L / 2)), bi) ? bf : bf - 1.f;
+            kf = fminf(fmaxf(kf, 0.f), (float)(L - 1));
+          }
+        }
+        code |= (uint32_t)kf << (VB * e);
+      }
+      if (p < parts) {
+        const size_t row = row_s + t;
+        if constexpr (VB == 4) {
+          codes_out[row * WV + g * 4 + sub] = code;                     // 8 codes = one word
+        } else {
+          reinterpret_cast<uint16_t*>(codes_out + row * WV + g * 2)[sub] = (uint16_t)code;   // half a word
+        }
+        if (sub == 0) scale_out[row * G + g] = (uint16_t)dbits;
+      }
+    }
   }
-  if (sub == 0) scale_out[row * G + g] = (uint16_t)dbits;
 }
 
 // Per-block affine 8-bit keys.  Boundaries m + a (q -+ 1/2) are exact in float64 for fp16
@@ -312,53 +437,67 @@ __device__ __forceinline__ bool passes64(double v, double tau, int k) {
 
 template <int D, int DT>
 __global__ void __launch_bounds__(256)
-encode_affine8_kernel(const uint16_t* __restrict__ x, int T, long n_parts, int dst_offset, int cap,
+encode_affine8_kernel(const uint16_t* __restrict__ x, int T, int slices, int dst_offset, int cap,
                       uint32_t* __restrict__ codes_out, uint32_t* __restrict__ aux_out) {
   constexpr int G = D / 32;
-  const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  const bool live = gid < n_parts;
-  const long gq = live ? gid : n_parts - 4 + (gid & 3);
-  const int sub = (int)(gq & 3);
-  const int g = (int)((gq >> 2) % G);
-  const long vt = (gq >> 2) / G;
-  const long slice = vt / T, t = vt % T;
-
-  float v[8];
-  load8<DT>(x + vt * D + 32 * g + 8 * sub, v);
-  float lo = v[0], hi = v[0];
+  const int parts = T * (D / 8);
+  for (int slice = blockIdx.y; slice < slices; slice += gridDim.y) {
+    const uint16_t* xs = x + (size_t)slice * T * D;
+    const size_t row_s = (size_t)slice * cap + dst_offset;
+    float v[kGroupItems][8];
 #pragma unroll
-  for (int e = 1; e < 8; ++e) { lo = fminf(lo, v[e]); hi = fmaxf(hi, v[e]); }
-  lo = quad_min(lo);
-  hi = quad_max(hi);
-  // a = fp16((hi - lo)/255): the difference is exact in float64; the quotient's binary
-  // fraction repeats with period 8 (1/255), far from an fp16 rounding tie, so rounding the
-  // float64 product to float32 and then to fp16 gives the exactly rounded result.
-  const uint32_t abits =
-      __builtin_bit_cast(uint16_t, (_Float16)(float)(((double)hi - (double)lo) * (1.0 / 255.0)));
-  const uint32_t mbits = __builtin_bit_cast(uint16_t, (_Float16)lo);
-  const double a = (double)f16_to_f32(abits);
-  const double m = (double)f16_to_f32(mbits);
-  const float inva = (a > 0.0) ? (float)(1.0 / a) : 0.f;
-  uint32_t words[2] = {0u, 0u};
+    for (int u = 0; u < kGroupItems; ++u) {
+      const int p = (blockIdx.x * kGroupItems + u) * 256 + threadIdx.x;
+      if (p < parts) {
+        load8<DT>(xs + (size_t)p * 8, v[u]);
+      } else {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    int q = 0;
-    if (a > 0.0) {
-      const double ve = (double)v[e];
-      q = (int)rintf((float)(ve - m) * inva);
-      q = min(max(q, 0), 255);
-      if (q > 0 && !passes64(ve, fma(a, (double)q - 0.5, m), q)) {
-        q -= 1;
-      } else if (q < 255 && passes64(ve, fma(a, (double)q + 0.5, m), q + 1)) {
-        q += 1;
+        for (int e = 0; e < 8; ++e) v[u][e] = 0.f;
       }
     }
-    words[e >> 2] |= (uint32_t)q << (8 * (e & 3));
+#pragma unroll
+    for (int u = 0; u < kGroupItems; ++u) {
+      const int p = (blockIdx.x * kGroupItems + u) * 256 + threadIdx.x;
+      const int sub = p & 3, g = (p >> 2) % G, t = p / (D / 8);
+      float lo = v[u][0], hi = v[u][0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) { lo = fminf(lo, v[u][e]); hi = fmaxf(hi, v[u][e]); }
+      lo = quad_min(lo);
+      hi = quad_max(hi);
+      // a = fp16((hi - lo)/255): the difference is exact in float64; the quotient's binary
+      // fraction repeats with period 8 (1/255), far from an fp16 rounding tie, so rounding
+      // the float64 product to float32 and then to fp16 gives the exactly rounded result.
+      const uint32_t abits =
+          __builtin_bit_cast(uint16_t, (_Float16)(float)(((double)hi - (double)lo) * (1.0 / 255.0)));
+      const uint32_t mbits = __builtin_bit_cast(uint16_t, (_Float16)lo);
+      const double a = (double)f16_to_f32(abits);
+      const double m = (double)f16_to_f32(mbits);
+      const float inva = (a > 0.0) ? (float)(1.0 / a) : 0.f;
+      const float mf = (float)m;
+      uint32_t words[2] = {0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float ve = v[u][e];
+        // x = (v - m)/a to within ~2^-14 absolute (|x| <= 256); only an x within 2^-11 of
+        // a half-integer (a level boundary, exact ties included) needs the exact test
+        const float x = (ve - mf) * inva;
+        const float qr = rintf(x);
+        float qf = fminf(fmaxf(qr, 0.f), 255.f);
+        if (fabsf(fabsf(x - qr) - 0.5f) < 0x1p-11f && a > 0.0) {
+          // boundary b between levels b-1 and b at m + a (b - 1/2), exact in float64
+          const float bf = rintf(x + 0.5f);
+          qf = passes64((double)ve, fma(a, (double)bf - 0.5, m), (int)bf) ? bf : bf - 1.f;
+          qf = fminf(fmaxf(qf, 0.f), 255.f);
+        }
+        words[e >> 2] |= (uint32_t)qf << (8 * (e & 3));
+      }
+      if (p < parts) {
+        const size_t row = row_s + t;
+        *reinterpret_cast<uint2*>(codes_out + row * (D / 4) + 8 * g + 2 * sub) = make_uint2(words[0], words[1]);
+        if (sub == 0) aux_out[row * G + g] = abits | (mbits << 16);
+      }
+    }
   }
-  if (!live) return;
-  const size_t row = (size_t)slice * cap + dst_offset + t;
-  *reinterpret_cast<uint2*>(codes_out + row * (D / 4) + 8 * g + 2 * sub) = make_uint2(words[0], words[1]);
-  if (sub == 0) aux_out[row * G + g] = abits | (mbits << 16);
 }
 
 // ---------------------------------------------------------------------------------
@@ -378,18 +517,30 @@ int device_cus() {
 }
 
 template <int D, int KB, int DT, bool QJL>
+int lm_blocks_per_cu() {
+  static const int n = [] {
+    int b = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, encode_lm_kernel<D, KB, DT, QJL>, 2 * D, 0) != hipSuccess ||
+        b <= 0)
+      b = 1;
+    return b;
+  }();
+  return n;
+}
+
+template <int D, int KB, int DT, bool QJL>
 hipError_t run_lm(const tq_layout& Lay, const tq_state& S, const void* x, int batch, int T, int dst,
                   const tq_cache& C, hipStream_t st, bool values) {
   const int slices = batch * Lay.n_kv_heads;
   const int tps = ceil_div(T, kTile);
   const int n_tiles = slices * tps;
-  // persistent: enough groups for every CU, each keeps its rows of S in registers
-  const int per_cu = (D <= 64) ? 6 : (D <= 128 ? 3 : 1);
-  const int grid = std::min(n_tiles, device_cus() * per_cu);
+  // persistent: as many groups as fit on the device at once; each loads its rows of S
+  // (keys) once and walks the tiles with a stride of the grid size
+  const int grid = std::min(n_tiles, device_cus() * lm_blocks_per_cu<D, KB, DT, QJL>());
   if (values) {
     hipLaunchKernelGGL((encode_lm_kernel<D, KB, DT, QJL>), dim3(grid), dim3(2 * D), 0, st,
                        (const uint16_t*)x, T, tps, n_tiles, dst, C.capacity, S.v_centroids, S.v_thresholds,
-                       S.v_signs, (const float*)nullptr, (uint32_t*)C.v_codes, (uint32_t*)nullptr,
+                       S.v_signs, (const uint16_t*)nullptr, (uint32_t*)C.v_codes, (uint32_t*)nullptr,
                        (uint32_t*)C.v_aux);
   } else {
     hipLaunchKernelGGL((encode_lm_kernel<D, KB, DT, QJL>), dim3(grid), dim3(2 * D), 0, st,
@@ -399,21 +550,28 @@ hipError_t run_lm(const tq_layout& Lay, const tq_state& S, const void* x, int ba
   return hipGetLastError();
 }
 
+// Grid of the group kernels: x covers one slice's parts, y the slices (looped past 65535).
+inline dim3 group_grid(int slices, int T, int D) {
+  const long parts = (long)T * (D / 8);
+  const long per_block = 256L * kGroupItems;
+  return dim3((unsigned)((parts + per_block - 1) / per_block), (unsigned)std::min(slices, 65535));
+}
+
 template <int D, int VB, int DT>
 hipError_t run_group(const tq_layout& Lay, const void* x, int batch, int T, int dst, const tq_cache& C,
                      hipStream_t st) {
-  const long n = (long)batch * Lay.n_kv_heads * T * (D / 8);   // 4 lanes per 32-group
-  hipLaunchKernelGGL((encode_group_kernel<D, VB, DT>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
-                     (const uint16_t*)x, T, n, dst, C.capacity, (uint32_t*)C.v_codes, (uint16_t*)C.v_aux);
+  const int slices = batch * Lay.n_kv_heads;
+  hipLaunchKernelGGL((encode_group_kernel<D, VB, DT>), group_grid(slices, T, D), dim3(256), 0, st,
+                     (const uint16_t*)x, T, slices, dst, C.capacity, (uint32_t*)C.v_codes, (uint16_t*)C.v_aux);
   return hipGetLastError();
 }
 
 template <int D, int DT>
 hipError_t run_affine(const tq_layout& Lay, const void* x, int batch, int T, int dst, const tq_cache& C,
                       hipStream_t st) {
-  const long n = (long)batch * Lay.n_kv_heads * T * (D / 8);
-  hipLaunchKernelGGL((encode_affine8_kernel<D, DT>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
-                     (const uint16_t*)x, T, n, dst, C.capacity, (uint32_t*)C.k_codes, (uint32_t*)C.k_aux);
+  const int slices = batch * Lay.n_kv_heads;
+  hipLaunchKernelGGL((encode_affine8_kernel<D, DT>), group_grid(slices, T, D), dim3(256), 0, st,
+                     (const uint16_t*)x, T, slices, dst, C.capacity, (uint32_t*)C.k_codes, (uint32_t*)C.k_aux);
   return hipGetLastError();
 }
 

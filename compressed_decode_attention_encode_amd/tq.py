@@ -135,11 +135,11 @@ def tq_make_codebook(head_dim: int, bits: int):
 
 
 def tq_make_rotation(head_dim: int, seed: int, with_qjl: bool = True):
-    """-> (sign mask uint32[d/32], QJL matrix float32[d, d] or None)."""
+    """-> (sign mask uint32[d/32], QJL matrix float16[d, d] or None)."""
     s = np.zeros(max(head_dim // 32, 1), dtype=np.uint32)
-    q = np.zeros((head_dim, head_dim), dtype=np.float32) if with_qjl and head_dim > 0 else None
+    q = np.zeros((head_dim, head_dim), dtype=np.uint16) if with_qjl and head_dim > 0 else None
     _check(_lib.tq_make_rotation(head_dim, seed, s.ctypes.data, None if q is None else q.ctypes.data))
-    return s, q
+    return s, (None if q is None else q.view(np.float16))
 
 
 def tq_cache_plane_bytes(layout: tq_layout, batch: int, capacity: int):
@@ -200,7 +200,8 @@ def upload_state(layout: tq_layout, signs_k, signs_v, qjl, device="cuda") -> Dev
         t["k_centroids"] = torch.from_numpy(c).to(device)
         t["k_thresholds"] = torch.from_numpy(th.copy()).to(device)
         t["k_signs"] = torch.from_numpy(np.asarray(signs_k, dtype=np.uint32).view(np.int32).copy()).to(device)
-        t["qjl"] = torch.from_numpy(np.ascontiguousarray(qjl, dtype=np.float32)).to(device)
+        # fp16 S (a float16 array is passed through; other dtypes are rounded to nearest even)
+        t["qjl"] = torch.from_numpy(np.ascontiguousarray(qjl, dtype=np.float16).view(np.int16).copy()).to(device)
     if layout.v_kind == TQ_V_LM_ROT:
         c, th, _ = tq_make_codebook(d, layout.v_bits)
         t["v_centroids"] = torch.from_numpy(c).to(device)

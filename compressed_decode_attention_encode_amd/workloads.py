@@ -219,5 +219,6 @@ def signs_to_mask(s: np.ndarray) -> np.ndarray:
 
 
 def qjl_matrix(wl: Workload) -> np.ndarray:
-    """QJL projection S in R^{d x d}, i.i.d. N(0,1), stored as float32 (row-major)."""
-    return _rng(wl, ROLE_QJL, 0).standard_normal((wl.head_dim, wl.head_dim)).astype(np.float32)
+    """QJL projection S in R^{d x d}, i.i.d. N(0,1) drawn in float64 and stored as fp16
+    (rounded to nearest even), row-major."""
+    return _rng(wl, ROLE_QJL, 0).standard_normal((wl.head_dim, wl.head_dim)).astype(np.float16)

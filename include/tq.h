@@ -92,7 +92,10 @@ typedef struct {
  *   v_centroids, v_thresholds                     (TQ_V_LM_ROT; else may be NULL)
  *   k_signs      uint32[d/32]: bit j%32 of word j/32 set <=> s_j = -1  (TQ_K_LM_QJL)
  *   v_signs      uint32[d/32], same convention     (TQ_V_LM_ROT)
- *   qjl          float[d*d] row-major S, S[i*d + j] (TQ_K_LM_QJL)                   */
+ *   qjl          fp16 bits [d*d], row-major S, S[i*d + j] (TQ_K_LM_QJL), 16-byte
+ *                aligned: the Gaussian sketch is stored at fp16 resolution (its
+ *                statistics do not depend on more), which keeps it exact in the fp16
+ *                matrix-core projection                                           */
 typedef struct {
   const float* k_centroids;
   const float* k_thresholds;
@@ -100,7 +103,7 @@ typedef struct {
   const float* v_thresholds;
   const uint32_t* k_signs;
   const uint32_t* v_signs;
-  const float* qjl;
+  const uint16_t* qjl;
 } tq_state;
 
 /* The packed cache: five device planes, each laid out [batch][n_kv_heads][capacity][row]
@@ -141,11 +144,11 @@ int tq_make_codebook(int head_dim, int bits, float* centroids, float* thresholds
  *   signs word w = low 32 bits of output w, w = 0..d/32-1;
  *   S filled row-major in pairs by Box-Muller from the next two outputs x1, x2:
  *   u1 = ((x1>>11)+1)*2^-53, u2 = (x2>>11)*2^-53, rho = sqrt(-2 ln u1),
- *   (rho cos 2 pi u2, rho sin 2 pi u2), each rounded to float32.
+ *   (rho cos 2 pi u2, rho sin 2 pi u2), each rounded from float64 to fp16 (nearest even).
  *   head_dim  power of two, 32..4096;  signs host uint32[d/32] (out);
- *   qjl       host float[d*d] (out) or NULL.
+ *   qjl       host fp16 bits uint16[d*d] (out) or NULL.
  * Returns TQ_OK, TQ_ERR_INVALID or TQ_ERR_UNSUPPORTED.                             */
-int tq_make_rotation(int head_dim, uint64_t seed, uint32_t* signs, float* qjl);
+int tq_make_rotation(int head_dim, uint64_t seed, uint32_t* signs, uint16_t* qjl);
 
 /* Bytes of each plane for `batch` x n_kv_heads x `capacity` tokens:
  * out[0..4] = k_codes, k_signs, k_aux, v_codes, v_aux (k_signs is 0 for AFFINE8).
@@ -160,7 +163,8 @@ int tq_cache_plane_bytes(const tq_layout* layout, int batch, int capacity, size_
  *   batch     must equal cache->batch
  * Errors: TQ_ERR_CAPACITY if dst_offset + n_tokens > cache->capacity; TQ_ERR_INVALID
  * for null/misaligned planes of the half being encoded or negative sizes;
- * TQ_ERR_UNSUPPORTED for layouts outside the compiled set; TQ_ERR_HIP on launch failure.
+ * TQ_ERR_UNSUPPORTED for layouts outside the compiled set or n_tokens * head_dim / 8
+ * above 2^30 (split such a call); TQ_ERR_HIP on launch failure.
  * n_tokens == 0 is a no-op.                                                         */
 int tq_encode(const tq_layout* layout, const tq_state* state, const void* k, const void* v,
               int batch, int n_tokens, int dst_offset, const tq_cache* cache, void* stream);

@@ -65,10 +65,10 @@ def read_v(lay, planes: dict, state: dict) -> dict:
     return {"idx": idx, "n": np.asarray(planes["v_aux"], dtype=np.float32).astype(np.float64)}
 
 
-def make_state(lay, signs_k, signs_v, S32) -> dict:
+def make_state(lay, signs_k, signs_v, S) -> dict:
     """Oracle state: its own codebooks plus the drawn random numbers (signs, QJL matrix)."""
     from .codebook import codebook_f32
-    st = {"signs_k": np.asarray(signs_k), "signs_v": np.asarray(signs_v), "S": np.asarray(S32, dtype=np.float32)}
+    st = {"signs_k": np.asarray(signs_k), "signs_v": np.asarray(signs_v), "S": np.asarray(S)}
     if lay.k_kind == "lm_qjl":
         st["cb_k"] = codebook_f32(lay.head_dim, lay.k_bits)
     if lay.v_kind == "lm_rot":

@@ -63,11 +63,11 @@ def reference_rotation_state(d: int, seed: int):
 
     * sign words: word w = low 32 bits of the w-th SplitMix64 output
       (bit j%32 of word j/32 set <=> s_j = -1);
-    * QJL matrix (row-major, d*d float32): entries filled in pairs by Box-Muller
+    * QJL matrix (row-major, d*d fp16): entries filled in pairs by Box-Muller
       (Box and Muller, 1958) from the next two outputs x1, x2:
       u1 = ((x1 >> 11) + 1) * 2^-53 in (0, 1], u2 = (x2 >> 11) * 2^-53 in [0, 1),
       rho = sqrt(-2 ln u1), pair = (rho cos(2 pi u2), rho sin(2 pi u2)),
-      each rounded to float32.
+      each rounded from float64 to fp16 (nearest even).
     """
     g = SplitMix64(seed)
     words = np.array([g.next() & 0xFFFFFFFF for _ in range(d // 32)], dtype=np.uint32)
@@ -79,7 +79,7 @@ def reference_rotation_state(d: int, seed: int):
         rho = math.sqrt(-2.0 * math.log(u1))
         out[i] = rho * math.cos(2.0 * math.pi * u2)
         out[i + 1] = rho * math.sin(2.0 * math.pi * u2)
-    return words, out.astype(np.float32).reshape(d, d)
+    return words, out.astype(np.float16).reshape(d, d)
 
 
 def mask_to_signs(words: np.ndarray, d: int) -> np.ndarray:

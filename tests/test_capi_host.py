@@ -44,7 +44,10 @@ def test_rotation_state_matches_reference_generator(d):
     s, q = tq.tq_make_rotation(d, 20260101 + d)
     s2, q2 = R.reference_rotation_state(d, 20260101 + d)
     assert np.array_equal(s, s2)
-    assert np.max(np.abs(q.astype(np.float64) - q2.astype(np.float64)) / (1 + np.abs(q2))) <= 2 ** -23
+    # both round the same float64 Box-Muller value to fp16 (libm and Python may differ in
+    # the last float64 bit, which moves an fp16 result only at an exact rounding tie)
+    assert q.dtype == np.float16 and q2.dtype == np.float16
+    assert np.array_equal(q.view(np.uint16), q2.view(np.uint16))
 
 
 CONFIGS = [(64, "lm_qjl", 3, "group_sym", 2), (128, "lm_qjl", 4, "group_sym", 4), (128, "affine8", 8, "lm_rot", 3),
