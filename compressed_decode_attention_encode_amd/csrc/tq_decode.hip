@@ -1,143 +1,149 @@
-// Decode attention: query preparation, split combination (+ exact recent buffer and the
-// single inverse butterfly), the split plan and the launch sequence.
+// Decode attention: the split merge (one inverse butterfly for rotated-domain value
+// sums), the split plan and the launch sequence.
 //
-//   prep     (TurboQuant-MLX page, GPU kernel optimisation section, pre-rotated query):
-//            once per (batch, q-head): q_r = Pi q and q_s = S q_r for LM + QJL keys, or
-//            32-block sums of q for affine keys; scales 1/sqrt(d), log2(e) and the QJL
-//            factor sqrt(pi/2)/d are folded in here.
-//   main     tq_decode_main.h
-//   combine  log-sum-exp merge of the splits (news page, oMLX section: a two-pass flash
-//            decode); the exact recent tokens (TurboQuant vLLM guide, section 5; benchmark
-//            page, buffering strategy) join under the same normaliser; rotated-domain value
-//            sums are rotated back once (TurboQuant-MLX page, butterfly pulled out).
+//   main     tq_decode_main.h: per (split, kv-head, batch) the query preparation
+//            (TurboQuant-MLX page, GPU kernel optimisation section, pre-rotated query),
+//            scoring on the packed cache, online softmax and value sums; one extra split
+//            per (batch, kv-head) takes the exact recent tokens (TurboQuant vLLM guide,
+//            section 5; benchmark page, buffering strategy).
+//   finish   log-sum-exp merge of the partials of one query head (news page, oMLX
+//            section: a two-pass flash decode), rotated-domain value sums rotated back
+//            once (TurboQuant-MLX page, butterfly pulled out of the loop), plus the
+//            recent buffer's natural-domain sum under the same normaliser.
+#include <algorithm>
+
 #include "tq_decode_main.h"
 
 namespace tq {
 
-constexpr float kLog2e = 1.4426950408889634f;
+// Partials merged by one finish work-group (staged in LDS).
+constexpr int kMaxParts = 512;
 
 // ---------------------------------------------------------------------------------
-// prep: qa (scores against codes), qb (QJL), qn (natural domain, recent tokens), G (affine)
-// ---------------------------------------------------------------------------------
-template <int D, int KK, int DT>
-__global__ void __launch_bounds__(256)
-decode_prep_kernel(const uint16_t* __restrict__ q, const uint32_t* __restrict__ sign_mask,
-                   const uint16_t* __restrict__ S, float* __restrict__ qprep, int Hq) {
-  constexpr int QF = 4 * D;
-  __shared__ float s_x[D];
-  const int h = blockIdx.x, b = blockIdx.y;
-  const int j = threadIdx.x;
-  const float scale = kLog2e * rsqrtf((float)D);
-  float* out = qprep + (size_t)(b * Hq + h) * QF;
-  float qj = 0.f;
-  if (j < D) {
-    qj = in_to_f32<DT>(q[(size_t)(b * Hq + h) * D + j]);
-    out[2 * D + j] = qj * scale;   // qn
-  }
-  if constexpr (KK == TQ_K_LM_QJL) {
-    if (j < D) s_x[j] = ((sign_mask[j >> 5] >> (j & 31)) & 1u) ? -qj : qj;
-    __syncthreads();
-    // in-place fast Walsh-Hadamard transform, one butterfly per thread per stage
-    for (int hs = 1; hs < D; hs <<= 1) {
-      float a = 0.f, c = 0.f;
-      int lo = 0;
-      if (j < D / 2) {
-        lo = (j / hs) * 2 * hs + (j % hs);
-        a = s_x[lo];
-        c = s_x[lo + hs];
-      }
-      __syncthreads();
-      if (j < D / 2) {
-        s_x[lo] = a + c;
-        s_x[lo + hs] = a - c;
-      }
-      __syncthreads();
-    }
-    const float rs = rsqrtf((float)D);
-    if (j < D) out[j] = s_x[j] * rs * scale;   // qa = Pi q
-    // q_s = S q_r; thread i takes row i of S (fp16) with independent 16-byte loads
-    if (j < D) {
-      const uint4* srow = reinterpret_cast<const uint4*>(S + (size_t)j * D);
-      float acc = 0.f;
-#pragma unroll 4
-      for (int k = 0; k < D / 8; ++k) {
-        const uint4 sv = srow[k];
-        const uint32_t w[4] = {sv.x, sv.y, sv.z, sv.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc = fmaf(f16_to_f32(w[i] & 0xFFFFu), s_x[8 * k + 2 * i], acc);
-          acc = fmaf(f16_to_f32(w[i] >> 16), s_x[8 * k + 2 * i + 1], acc);
-        }
-      }
-      const float qjl = 1.2533141373155003f / (float)D;   // sqrt(pi/2)/d
-      out[D + j] = acc * rs * scale * qjl;
-    }
-  } else {
-    if (j < D) out[j] = qj * scale;
-    if (j < D) s_x[j] = qj * scale;
-    __syncthreads();
-    if (j < D / 32) {
-      float gsum = 0.f;
-      for (int k = 0; k < 32; ++k) gsum += s_x[32 * j + k];
-      out[3 * D + j] = gsum;
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------------
-// finish: merge the splits of one (query head, batch), with the recent buffer and the
-// inverse rotation (also the whole decode when nothing is compressed: zero splits).
+// finish: grid (n_q_heads, batch)
 // ---------------------------------------------------------------------------------
 template <int D, int VK>
-__global__ void __launch_bounds__(256) decode_finish_kernel(const DecodeArgs A, int nrep) {
-  __shared__ float sm[finish_floats<D, 1>()];
-  const int h = blockIdx.x;
-  finish_group<D, 1, VK>(A, blockIdx.y, h / nrep, h, sm);
+__global__ void __launch_bounds__(256) decode_finish_kernel(const DecodeArgs A) {
+  constexpr int NG = 256 / D;            // threads per dimension
+  __shared__ float s_w[kMaxParts];       // split maxima -> weights
+  __shared__ float s_l[kMaxParts];
+  __shared__ float s_red[8];
+  __shared__ float s_rot[NG][D];         // per-thread-group sums over the compressed splits
+  __shared__ float s_nat[D];             // recent buffer sum
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int head = blockIdx.x, b = blockIdx.y;
+  const int np = A.n_part, ns = A.nsplit;
+  const float* pp = A.part + (size_t)(b * A.Hq + head) * np * (D + 4);
+  for (int s = tid; s < np; s += 256) {
+    s_w[s] = pp[(size_t)s * (D + 4)];
+    s_l[s] = pp[(size_t)s * (D + 4) + 1];
+  }
+  __syncthreads();
+  float mx = -INFINITY;
+  for (int s = tid; s < np; s += 256) mx = fmaxf(mx, s_w[s]);
+  mx = wave_max(mx);
+  if (lane == 0) s_red[wave] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+  float l = 0.f;
+  for (int s = tid; s < np; s += 256) {
+    const float m = s_w[s];
+    const float w = (m == -INFINITY) ? 0.f : exp2f(m - mx);
+    s_w[s] = w;
+    l = fmaf(s_l[s], w, l);
+  }
+  l = wave_sum(l);
+  if (lane == 0) s_red[4 + wave] = l;
+  __syncthreads();
+  const float L = s_red[4] + s_red[5] + s_red[6] + s_red[7];
+  // value sums: thread group grp takes splits grp, grp + NG, ... of dimension j
+  {
+    const int j = tid % D, grp = tid / D;
+    float a = 0.f;
+#pragma unroll 8
+    for (int s = grp; s < ns; s += NG) a = fmaf(pp[(size_t)s * (D + 4) + 4 + j], s_w[s], a);
+    s_rot[grp][j] = a;
+    if (grp == 0) s_nat[j] = (np > ns) ? pp[(size_t)ns * (D + 4) + 4 + j] * s_w[ns] : 0.f;
+  }
+  __syncthreads();
+  if (tid < D) {
+    float a = 0.f;
+#pragma unroll
+    for (int q = 0; q < NG; ++q) a += s_rot[q][tid];
+    s_rot[0][tid] = a;
+  }
+  __syncthreads();
+  if constexpr (VK == TQ_V_LM_ROT) {
+    // Pi^T acc = diag(s) H acc / sqrt(d): butterflies in LDS
+    float* x = s_rot[0];
+    for (int hs = 1; hs < D; hs <<= 1) {
+      if (tid < D / 2) {
+        const int lo = (tid / hs) * 2 * hs + (tid % hs);
+        const float u = x[lo], v = x[lo + hs];
+        x[lo] = u + v;
+        x[lo + hs] = u - v;
+      }
+      __syncthreads();
+    }
+  }
+  if (tid < D) {
+    float mv = s_rot[0][tid];
+    if constexpr (VK == TQ_V_LM_ROT) {
+      mv *= rsqrtf((float)D);
+      if ((A.vsign[tid >> 5] >> (tid & 31)) & 1u) mv = -mv;
+    }
+    A.out[(size_t)(b * A.Hq + head) * D + tid] = (mv + s_nat[tid]) / L;
+  }
 }
 
 // ---------------------------------------------------------------------------------
 // plan and launch
 // ---------------------------------------------------------------------------------
-// Workspace: prepared queries [B][Hq][4d] | split partials [B][Hq][n_splits][d+4].
+// Workspace: partials [B][Hq][n_splits + 1][d + 4] floats (the last slot: recent buffer).
 static size_t ws_layout_bytes(const tq_layout& L, int batch, int n_splits) {
-  const size_t d = L.head_dim;
-  return sizeof(float) *
-         ((size_t)batch * L.n_q_heads * 4 * d + (size_t)batch * L.n_q_heads * n_splits * (d + 4));
+  return sizeof(float) * (size_t)batch * L.n_q_heads * (n_splits + 1) * (L.head_dim + 4);
+}
+
+// Most splits a launch may use: every split gets >= kMinTilesPerSplit tiles, all
+// (batch, kv-head) units together stay within two rounds of kTargetDecodeGroups, and the
+// merge stages every partial in LDS.
+static int max_splits(const tq_layout& L, int batch, int n_c) {
+  if (n_c <= 0) return 0;
+  const long units = (long)batch * L.n_kv_heads;
+  int s = ceil_div(n_c, kTile * kMinTilesPerSplit);
+  s = std::min(s, ceil_div(2L * kTargetDecodeGroups, units));
+  return std::max(1, std::min(s, kMaxParts - 1));
 }
 
 DecodePlan plan_decode(const tq_layout& L, int batch, int n_c) {
   DecodePlan p{};
-  const int d = L.head_dim;
-  const long units = (long)batch * L.n_kv_heads;
-  const int tiles = ceil_div(n_c, kTile);
-  if (n_c <= 0) {
-    p.n_splits = 0;
-    p.chunk = 0;
-  } else {
-    int want = ceil_div(kTargetDecodeGroups, units);
-    want = std::min(want, kMaxFinishSplits);   // the finishing merge stages every split in LDS
-    want = std::max(1, std::min(want, ceil_div(tiles, kMinTilesPerSplit)));
-    const int tiles_per = ceil_div(tiles, want);
-    p.chunk = tiles_per * kTile;
-    p.n_splits = ceil_div(tiles, tiles_per);
-  }
-  p.q_floats = 4 * (size_t)d;
-  p.part_stride = (size_t)d + 4;
+  p.n_splits = max_splits(L, batch, n_c);
+  p.chunk = 0;
+  p.q_floats = 0;
+  p.part_stride = (size_t)L.head_dim + 4;
   p.ws_bytes = ws_layout_bytes(L, batch, p.n_splits);
   return p;
 }
 
 size_t decode_ws_bound(const tq_layout& L, int batch, int max_c) {
-  // n_splits of any n_c <= max_c is at most min(ceil(target/units), tiles(max_c))
-  const long units = (long)batch * L.n_kv_heads;
-  const int max_splits =
-      std::max(0, std::min(ceil_div(kTargetDecodeGroups, units), ceil_div(std::max(max_c, 0), kTile)));
-  return ws_layout_bytes(L, batch, max_splits);
+  // max_splits is nondecreasing in n_c
+  return ws_layout_bytes(L, batch, max_splits(L, batch, std::max(max_c, 0)));
 }
 
 namespace {
 
-MainLaunch find_main(const tq_layout& L) {
+int device_cus() {
+  static int cus = 0;
+  if (!cus) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+  }
+  return cus;
+}
+
+MainKernel find_main(const tq_layout& L) {
   const int nrep = L.n_q_heads / L.n_kv_heads;
   const int d = L.head_dim, vk = L.v_kind, vb = L.v_bits;
 #define TQ_BY_D(name)                                                   \
@@ -145,35 +151,24 @@ MainLaunch find_main(const tq_layout& L) {
     case 64: return name##_d64(nrep, vk, vb);                           \
     case 128: return name##_d128(nrep, vk, vb);                         \
     case 256: return name##_d256(nrep, vk, vb);                         \
-    default: return nullptr;                                            \
+    default: return MainKernel{nullptr, nullptr};                       \
   }
   if (L.k_kind == TQ_K_LM_QJL) {
     switch (L.k_bits) {
       case 2: TQ_BY_D(find_main_lm2)
       case 3: TQ_BY_D(find_main_lm3)
       case 4: TQ_BY_D(find_main_lm4)
-      default: return nullptr;
+      default: return MainKernel{nullptr, nullptr};
     }
   }
   if (L.k_kind == TQ_K_AFFINE8 && L.k_bits == 8) { TQ_BY_D(find_main_aff8) }
 #undef TQ_BY_D
-  return nullptr;
-}
-
-template <int D, int KK>
-hipError_t run_prep(const tq_layout& L, const tq_state& S, const void* q, float* qprep, int batch, hipStream_t st) {
-  if (L.in_dtype == TQ_F16)
-    hipLaunchKernelGGL((decode_prep_kernel<D, KK, TQ_F16>), dim3(L.n_q_heads, batch), dim3(256), 0, st,
-                       (const uint16_t*)q, S.k_signs, S.qjl, qprep, L.n_q_heads);
-  else
-    hipLaunchKernelGGL((decode_prep_kernel<D, KK, TQ_BF16>), dim3(L.n_q_heads, batch), dim3(256), 0, st,
-                       (const uint16_t*)q, S.k_signs, S.qjl, qprep, L.n_q_heads);
-  return hipGetLastError();
+  return MainKernel{nullptr, nullptr};
 }
 
 template <int D, int VK>
-hipError_t run_finish(const DecodeArgs& A, int nrep, int batch, hipStream_t st) {
-  hipLaunchKernelGGL((decode_finish_kernel<D, VK>), dim3(A.Hq, batch), dim3(256), 0, st, A, nrep);
+hipError_t run_finish(const DecodeArgs& A, int batch, hipStream_t st) {
+  hipLaunchKernelGGL((decode_finish_kernel<D, VK>), dim3(A.Hq, batch), dim3(256), 0, st, A);
   return hipGetLastError();
 }
 
@@ -182,12 +177,23 @@ hipError_t run_decode_d(const tq_layout& L, const tq_state& S, const void* q, co
                         const void* rk, const void* rv, int n_recent, int rcap, float* out, void* ws,
                         const DecodePlan& plan, hipStream_t st) {
   const int batch = C.batch;
-  float* qprep = (float*)ws;
-  float* part = qprep + (size_t)batch * L.n_q_heads * plan.q_floats;
-  hipError_t e = (L.k_kind == TQ_K_LM_QJL) ? run_prep<D, TQ_K_LM_QJL>(L, S, q, qprep, batch, st)
-                                           : run_prep<D, TQ_K_AFFINE8>(L, S, q, qprep, batch, st);
-  if (e != hipSuccess) return e;
+  const MainKernel mk = find_main(L);
+  if (!mk.launch) return hipErrorInvalidDeviceFunction;
+  // splits: one round of resident work-groups over all (batch, kv-head) units, within the
+  // planned maximum; every split a whole number of tiles
+  int nsplit = 0, chunk = 0;
+  if (n_c > 0) {
+    const long units = (long)batch * L.n_kv_heads;
+    const long resident = (long)device_cus() * mk.blocks_per_cu();
+    const int tiles = ceil_div(n_c, kTile);
+    const int want = std::max(1, std::min(plan.n_splits, ceil_div(resident, units)));
+    int tiles_per = ceil_div(tiles, want);
+    if (tiles_per > 4) tiles_per = (tiles_per + 3) & ~3;   // whole rounds of the 4 waves
+    chunk = tiles_per * kTile;
+    nsplit = ceil_div(tiles, tiles_per);
+  }
   DecodeArgs A{};
+  A.q = (const uint16_t*)q;
   A.kc = (const uint32_t*)C.k_codes;
   A.ks = (const uint32_t*)C.k_signs;
   A.ka = (const uint32_t*)C.k_aux;
@@ -195,30 +201,31 @@ hipError_t run_decode_d(const tq_layout& L, const tq_state& S, const void* q, co
   A.va = (const uint32_t*)C.v_aux;
   A.kcent = S.k_centroids;
   A.vcent = S.v_centroids;
+  A.ksign = S.k_signs;
   A.vsign = S.v_signs;
-  A.qprep = qprep;
-  A.part = part;
+  A.S = S.qjl;
+  A.part = (float*)ws;
   A.rk = (const uint16_t*)rk;
   A.rv = (const uint16_t*)rv;
   A.out = out;
   A.Hq = L.n_q_heads;
   A.Hkv = L.n_kv_heads;
+  A.batch = batch;
   A.cap = C.capacity;
   A.n_c = n_c;
-  A.chunk = plan.chunk;
-  A.nsplit = plan.n_splits;
+  A.chunk = chunk;
+  A.nsplit = nsplit;
+  A.n_part = nsplit + (n_recent > 0 ? 1 : 0);
   A.n_recent = n_recent;
   A.recent_cap = rcap;
   A.recent_bf16 = (L.recent_dtype == TQ_BF16) ? 1 : 0;
-  if (n_c > 0) {
-    MainLaunch fn = find_main(L);
-    if (!fn) return hipErrorInvalidDeviceFunction;
-    e = fn(dim3(plan.n_splits, L.n_kv_heads, batch), st, A);
-    if (e != hipSuccess) return e;
-  }
-  const int nrep = L.n_q_heads / L.n_kv_heads;
-  return (L.v_kind == TQ_V_GROUP_SYM) ? run_finish<D, TQ_V_GROUP_SYM>(A, nrep, batch, st)
-                                      : run_finish<D, TQ_V_LM_ROT>(A, nrep, batch, st);
+  A.q_bf16 = (L.in_dtype == TQ_BF16) ? 1 : 0;
+  const long groups = (long)A.n_part * L.n_kv_heads * batch;
+  if (groups > 0x7FFFFFFFL) return hipErrorInvalidConfiguration;
+  hipError_t e = mk.launch(dim3((unsigned)groups), st, A);
+  if (e != hipSuccess) return e;
+  return (L.v_kind == TQ_V_GROUP_SYM) ? run_finish<D, TQ_V_GROUP_SYM>(A, batch, st)
+                                      : run_finish<D, TQ_V_LM_ROT>(A, batch, st);
 }
 
 }  // namespace
@@ -226,7 +233,7 @@ hipError_t run_decode_d(const tq_layout& L, const tq_state& S, const void* q, co
 bool decode_compiled(const tq_layout& L) {
   if (!(L.head_dim == 64 || L.head_dim == 128 || L.head_dim == 256)) return false;
   if (L.n_kv_heads <= 0 || L.n_q_heads % L.n_kv_heads) return false;
-  return find_main(L) != nullptr;
+  return find_main(L).launch != nullptr;
 }
 
 hipError_t launch_decode(const tq_layout& L, const tq_state& S, const void* q, const tq_cache& C, int n_c,

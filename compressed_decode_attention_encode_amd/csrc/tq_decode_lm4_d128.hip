@@ -6,25 +6,25 @@ namespace tq {
 
 namespace {
 template <int KK, int KB, int VK, int VB>
-MainLaunch pick(int nrep) {
+MainKernel pick(int nrep) {
   switch (nrep) {
-    case 1: return &main_launch<128, 1, KK, KB, VK, VB>;
-    case 2: return &main_launch<128, 2, KK, KB, VK, VB>;
-    case 3: return &main_launch<128, 3, KK, KB, VK, VB>;
-    case 4: return &main_launch<128, 4, KK, KB, VK, VB>;
-    case 5: return &main_launch<128, 5, KK, KB, VK, VB>;
-    case 6: return &main_launch<128, 6, KK, KB, VK, VB>;
-    case 7: return &main_launch<128, 7, KK, KB, VK, VB>;
-    case 8: return &main_launch<128, 8, KK, KB, VK, VB>;
-    default: return nullptr;
+    case 1: return main_kernel<128, 1, KK, KB, VK, VB>();
+    case 2: return main_kernel<128, 2, KK, KB, VK, VB>();
+    case 3: return main_kernel<128, 3, KK, KB, VK, VB>();
+    case 4: return main_kernel<128, 4, KK, KB, VK, VB>();
+    case 5: return main_kernel<128, 5, KK, KB, VK, VB>();
+    case 6: return main_kernel<128, 6, KK, KB, VK, VB>();
+    case 7: return main_kernel<128, 7, KK, KB, VK, VB>();
+    case 8: return main_kernel<128, 8, KK, KB, VK, VB>();
+    default: return MainKernel{nullptr, nullptr};
   }
 }
 }  // namespace
 
-MainLaunch find_main_lm4_d128(int nrep, int vk, int vb) {
+MainKernel find_main_lm4_d128(int nrep, int vk, int vb) {
   if (vk == TQ_V_GROUP_SYM && vb == 2) return pick<TQ_K_LM_QJL, 4, TQ_V_GROUP_SYM, 2>(nrep);
   if (vk == TQ_V_GROUP_SYM && vb == 4) return pick<TQ_K_LM_QJL, 4, TQ_V_GROUP_SYM, 4>(nrep);
-  return nullptr;
+  return MainKernel{nullptr, nullptr};
 }
 
 }  // namespace tq

@@ -7,26 +7,36 @@
 // butterfly afterwards, wave-level reductions, GQA n_rep handled without repeating KV;
 // TurboQuant vLLM guide (kwkr.cn), section 2: the unbiased LM + QJL inner product.
 //
-// One work-group = one (batch, kv-head, split) and 4 independent waves.  A wave takes
-// 64-token tiles of the split in turn:
+// One work-group = one (batch, kv-head, split), 4 waves.  It first prepares the n_rep
+// queries of its kv-head in LDS (sign flip, Walsh-Hadamard, QJL projection S q, all
+// scales folded in) and turns them into lookup tables:
+// a QJL table: for every 4 consecutive dimensions and each of the 16 sign patterns, the
+// signed sum of the projected query for all n_rep heads (padded to 1, 2, 4 or 8 floats,
+// one LDS read) -- one read replaces 4 n_rep FMAs.  The 16 entries of a 4-dimension
+// block span the LDS banks once, so random entries rarely collide.  (A table over pairs
+// of 3-bit codes would replace more FMAs, but its 64 entries per pair collide in the
+// banks and its size halves the resident work-groups: slower on this part.)
+// Then every wave takes 64-token tiles of the split in turn:
 //   1. stage the tile's packed rows (every plane) from HBM into its own LDS area with
 //      coalesced loads (rows padded to an odd word stride: conflict-free row reads);
-//   2. scores, one token per lane, for all n_rep query heads of the group at once: the
-//      codes are unpacked once and the prepared query (uniform across the wave) comes in
-//      through scalar registers, so each code element costs one FMA per head;
-//   3. online softmax in the log2 domain (scores carry log2(e)/sqrt(d) from the prep);
+//   2. scores, one token per lane, for all n_rep query heads at once;
+//   3. online softmax in the log2 domain (the scales carry log2(e)/sqrt(d));
 //   4. weighted value sum, 8 dimensions per lane: each decoded value element is used by
 //      all n_rep heads; group-scaled values fold the scale into the weight and the
 //      (L-1)/2 offset into one per-group running sum.
-// The four waves then merge (m, l, acc) through LDS and write one partial per head; a
-// second kernel (one work-group per (batch, kv-head)) merges the splits: the kernel
-// boundary makes every partial visible without device-wide cache flushes.
+// The four waves merge (m, l, acc) through LDS and write one partial per head.  One more
+// split per (batch, kv-head) scores the exact fp16 recent buffer.  A second kernel (one
+// work-group per query head) merges the partials: the kernel boundary makes them visible
+// without device-wide cache flushes.
 #pragma once
 
 #include "tq_device.h"
 #include "tq_internal.h"
 
 namespace tq {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kSqrtHalfPi = 1.2533141373155003f;   // sqrt(pi/2)
 
 template <int D, int NREP, int KK, int KB, int VK, int VB>
 struct DecodeGeom {
@@ -43,8 +53,21 @@ struct DecodeGeom {
   static constexpr int STAGE = kTile * (SK + SS + SAK + SV + SAV);   // words per wave
   static constexpr int LPT = D / 8;                                 // value lanes per token
   static constexpr int SLOTS = kWave / LPT;                         // tokens per value step
-  static constexpr int QF = 4 * D;                                  // prepared-query floats per head
   static constexpr int PS = D + 4;                                  // partial stride (floats)
+  // lookup tables
+  static constexpr int NE = NREP == 1 ? 1 : (NREP == 2 ? 2 : (NREP <= 4 ? 4 : 8));   // floats per entry
+  static constexpr int LK = (KK == TQ_K_LM_QJL) ? (1 << KB) : 1;
+  static constexpr int TQ_FLOATS = (KK == TQ_K_LM_QJL) ? (D / 4) * 16 * NE : 0;
+  // LDS carve-out (floats): queries, second query block (QJL projection / affine block
+  // sums), QJL table, staging, softmax weights, codebooks, merge scalars
+  static constexpr int OFF_QA = 0;
+  static constexpr int OFF_QB = OFF_QA + NREP * D;
+  static constexpr int OFF_TQ = OFF_QB + ((NREP * D + 3) & ~3);
+  static constexpr int OFF_ST = OFF_TQ + TQ_FLOATS;
+  static constexpr int OFF_P = OFF_ST + 4 * STAGE;
+  static constexpr int OFF_CENT = OFF_P + 4 * NREP * kWave;
+  static constexpr int OFF_MRG = OFF_CENT + 32;
+  static constexpr int FLOATS = OFF_MRG + 8 * NREP + 16;
 };
 
 // Register double-buffer for one plane of a 64-token tile: load() issues the global
@@ -106,199 +129,341 @@ struct RowLoader {
 
 // Everything the decode kernels need, passed by value.
 struct DecodeArgs {
-  const uint32_t *kc, *ks, *ka, *vc, *va;   // packed planes
+  const uint16_t* q;                          // queries [B][Hq][d], fp16 / bf16
+  const uint32_t *kc, *ks, *ka, *vc, *va;     // packed planes
   const float *kcent, *vcent;                 // codebooks (LM keys / rotated LM values)
-  const uint32_t* vsign;                      // value rotation signs (rotated LM values)
-  const float* qprep;                         // prepared queries [B][Hq][QF]
-  float* part;                                // split partials [B][Hq][nsplit][PS]
+  const uint32_t *ksign, *vsign;              // rotation signs (keys / rotated LM values)
+  const uint16_t* S;                          // QJL matrix, fp16 [d][d]
+  float* part;                                // partials [B][Hq][n_part][PS]
   const uint16_t *rk, *rv;                    // recent buffer [B][Hkv][recent_cap][d]
   float* out;                                 // [B][Hq][d]
-  int Hq, Hkv, cap, n_c, chunk, nsplit, n_recent, recent_cap, recent_bf16;
+  int Hq, Hkv, batch, cap, n_c, chunk, nsplit, n_part, n_recent, recent_cap, recent_bf16, q_bf16;
 };
 
-__device__ __forceinline__ float recent_to_f32(uint32_t bits, int bf16) {
+__device__ __forceinline__ float bits16_to_f32(uint32_t bits, int bf16) {
   return bf16 ? __uint_as_float(bits << 16) : f16_to_f32(bits);
 }
 
-// Merge the n_split partials of NREP consecutive query heads h0.. of kv-head g (batch b),
-// fold in the
-// exact recent tokens under the same normaliser, rotate rotated-domain value sums back
-// with one inverse Walsh-Hadamard transform, normalise and write the output.
-// Uses all 256 threads.  Every global load is independent of the others: split maxima,
-// normalisers and queries are staged in LDS first, weights are computed once per head,
-// and each (head, dimension) sum is spread over 256/(n_rep d) threads.
-// Needs NREP * nsplit <= kMaxFinishSplits; `sm` holds finish_floats<D, NREP>() floats.
-constexpr int kMaxFinishSplits = 512;
-
-template <int D, int NREP>
-constexpr int finish_floats() {
-  constexpr int items = NREP * D;
-  return items + 2 * kMaxFinishSplits + NREP * kMaxRecent + 2 * NREP + 2 * (items > 256 ? items : 256);
+// NE consecutive floats of a table entry (16-byte aligned for NE >= 4).
+template <int NE>
+__device__ __forceinline__ void read_entry(const float* p, float (&e)[NE]) {
+  if constexpr (NE == 1) {
+    e[0] = p[0];
+  } else if constexpr (NE == 2) {
+    const float2 v = *reinterpret_cast<const float2*>(p);
+    e[0] = v.x; e[1] = v.y;
+  } else {
+#pragma unroll
+    for (int i = 0; i < NE / 4; ++i) {
+      const float4 v = reinterpret_cast<const float4*>(p)[i];
+      e[4 * i] = v.x; e[4 * i + 1] = v.y; e[4 * i + 2] = v.z; e[4 * i + 3] = v.w;
+    }
+  }
 }
 
-template <int D, int NREP, int VK>
-__device__ void finish_group(const DecodeArgs& A, int b, int g, int h0, float* sm) {
-  constexpr int QF = 4 * D, PS = D + 4;
-  constexpr int ITEMS = NREP * D;
-  constexpr int NG = (ITEMS >= 256) ? 1 : 256 / ITEMS;   // threads per (head, dimension) item
-  constexpr int PART = (ITEMS > 256 ? ITEMS : 256);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int Hq = A.Hq;
-  const int R = A.n_recent, ns = A.nsplit;
-  float* s_qn = sm;                         // [NREP][D]
-  float* s_w = s_qn + ITEMS;                // [NREP][ns] split maxima -> weights
-  float* s_l = s_w + kMaxFinishSplits;      // [NREP][ns] split normalisers
-  float* s_sr = s_l + kMaxFinishSplits;     // [NREP][kMaxRecent] recent scores -> weights
-  float* s_M = s_sr + NREP * kMaxRecent;    // [NREP]
-  float* s_L = s_M + NREP;                  // [NREP]
-  float* s_pa = s_L + NREP;                 // [NG][ITEMS] partial sums (compressed part)
-  float* s_pr = s_pa + PART;                // [NG][ITEMS] partial sums (recent part)
-  const size_t rbase = ((size_t)b * A.Hkv + g) * A.recent_cap;
-  const float* pp0 = A.part + (size_t)(b * Hq + h0) * ns * PS;
-  const float* qn0 = A.qprep + (size_t)(b * Hq + h0) * QF + 2 * D;
-  for (int i = tid; i < ITEMS; i += 256) s_qn[i] = qn0[(size_t)(i / D) * QF + (i % D)];
-  for (int i = tid; i < NREP * ns; i += 256) {
-    const float* pp = pp0 + (size_t)i * PS;    // head i / ns, split i % ns
-    s_w[i] = pp[0];
-    s_l[i] = pp[1];
-  }
-  __syncthreads();
-  // recent-token scores, one (head, token) pair per thread
-  for (int i = tid; i < NREP * R; i += 256) {
-    const int h = i / R, r = i % R;
-    const uint4* kr = reinterpret_cast<const uint4*>(A.rk + (rbase + r) * D);
-    const float* qn = s_qn + h * D;
-    float a = 0.f;
-#pragma unroll 4
-    for (int c = 0; c < D / 8; ++c) {
-      const uint4 u = kr[c];
-      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+// Query preparation for the n_rep heads h0.. of one kv-head, into LDS (256 threads):
+//   LM + QJL keys: qa = Pi q * log2(e)/sqrt(d), qb = S Pi q * log2(e)/sqrt(d) * sqrt(pi/2)/d,
+//                  then the QJL table;
+//   affine keys:   qa = q * log2(e)/sqrt(d), qb[h][blk] = sum of qa over the 32-block.
+template <int D, int NREP, int KK, int KB, int VK, int VB>
+__device__ void prepare_queries(const DecodeArgs& A, int b, int g, float* sm) {
+  using G = DecodeGeom<D, NREP, KK, KB, VK, VB>;
+  constexpr int NE = G::NE;
+  const int tid = threadIdx.x;
+  float* qa = sm + G::OFF_QA;
+  float* qb = sm + G::OFF_QB;
+  const float scale = kLog2e * rsqrtf((float)D);
+  const uint16_t* qsrc = A.q + (size_t)(b * A.Hq + g * NREP) * D;
+  if constexpr (KK == TQ_K_LM_QJL) {
+    // this thread's slice of S (row i, columns part*KL ..): its first reads go out first
+    constexpr int KS = (256 / D) > 0 ? 256 / D : 1;
+    constexpr int KL = D / KS;
+    constexpr int PRE = (KL / 8 < 8) ? KL / 8 : 8;   // 16-byte reads issued up front
+    const int i = tid / KS, part = tid % KS;
+    const uint4* srow = reinterpret_cast<const uint4*>(A.S + (size_t)i * D + part * KL);
+    uint4 spre[PRE];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        a = fmaf(qn[8 * c + 2 * k], recent_to_f32(w[k] & 0xFFFFu, A.recent_bf16), a);
-        a = fmaf(qn[8 * c + 2 * k + 1], recent_to_f32(w[k] >> 16, A.recent_bf16), a);
+    for (int c = 0; c < PRE; ++c) spre[c] = srow[c];
+    // H (s * q) per head, one wave per head: lane holds E = d/64 consecutive coordinates;
+    // strides below E inside the lane, the others across lanes (xor exchanges)
+    {
+      constexpr int E = D / 64;
+      const int lane = tid & 63, wave = tid >> 6;
+      for (int h = wave; h < NREP; h += 4) {
+        float x[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int j = lane * E + e;
+          const float v = bits16_to_f32(qsrc[h * D + j], A.q_bf16);
+          x[e] = ((A.ksign[j >> 5] >> (j & 31)) & 1u) ? -v : v;
+        }
+#pragma unroll
+        for (int hs = 1; hs < E; hs <<= 1) {
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            if ((e & hs) == 0) {
+              const float u = x[e], v = x[e + hs];
+              x[e] = u + v;
+              x[e + hs] = u - v;
+            }
+          }
+        }
+#pragma unroll
+        for (int m = 1; m < 64; m <<= 1) {
+          const bool up = (lane & m) != 0;
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            const float o = __shfl_xor(x[e], m);
+            x[e] = up ? (o - x[e]) : (x[e] + o);
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) qa[h * D + lane * E + e] = x[e];
       }
     }
-    s_sr[h * kMaxRecent + r] = a;
+    __syncthreads();
+    // qb = S (H s q): row i of S per group of KS threads, each a 1/KS slice of k
+    {
+      float acc[NREP];
+#pragma unroll
+      for (int h = 0; h < NREP; ++h) acc[h] = 0.f;
+      if (i < D) {
+#pragma unroll 2
+        for (int k8 = 0; k8 < KL / 8; ++k8) {
+          uint4 sv;
+          if (k8 < PRE) {
+#pragma unroll
+            for (int c = 0; c < PRE; ++c)
+              if (c == k8) sv = spre[c];
+          } else {
+            sv = srow[k8];
+          }
+          const uint32_t w[4] = {sv.x, sv.y, sv.z, sv.w};
+          float sf[8];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            sf[2 * t] = f16_to_f32(w[t] & 0xFFFFu);
+            sf[2 * t + 1] = f16_to_f32(w[t] >> 16);
+          }
+          const int k0 = part * KL + 8 * k8;
+#pragma unroll
+          for (int h = 0; h < NREP; ++h) {
+#pragma unroll
+            for (int t = 0; t < 8; ++t) acc[h] = fmaf(sf[t], qa[h * D + k0 + t], acc[h]);
+          }
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < NREP; ++h) {
+        if constexpr (KS >= 2) acc[h] += xor_lanes<1>(acc[h]);
+        if constexpr (KS >= 4) acc[h] += xor_lanes<2>(acc[h]);
+      }
+      const float sq = rsqrtf((float)D) * scale * (kSqrtHalfPi / (float)D);
+      if (i < D && part == 0) {
+#pragma unroll
+        for (int h = 0; h < NREP; ++h) qb[h * D + i] = acc[h] * sq;
+      }
+    }
+    __syncthreads();
+    for (int i = tid; i < NREP * D; i += 256) qa[i] *= rsqrtf((float)D) * scale;
+    __syncthreads();
+    // QJL table: entry (nib, v), head h = sum_t (bit t of v ? +1 : -1) qb[h][4 nib + t]
+    float* tq = sm + G::OFF_TQ;
+    for (int i = tid; i < (D / 4) * 16; i += 256) {
+      const int nib = i / 16, v = i % 16;
+#pragma unroll
+      for (int h = 0; h < NREP; ++h) {
+        const float* qq = qb + h * D + 4 * nib;
+        float a = 0.f;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) a += ((v >> t) & 1) ? qq[t] : -qq[t];
+        tq[i * NE + h] = a;
+      }
+    }
+  } else {
+    for (int i = tid; i < NREP * D; i += 256) qa[i] = bits16_to_f32(qsrc[i], A.q_bf16) * scale;
+    __syncthreads();
+    for (int i = tid; i < NREP * (D / 32); i += 256) {
+      const int h = i / (D / 32), blk = i % (D / 32);
+      float s = 0.f;
+      for (int k = 0; k < 32; ++k) s += qa[h * D + 32 * blk + k];
+      qb[i] = s;
+    }
   }
   __syncthreads();
-  // per head: max, weights, normaliser (one wave per head, heads strided over 4 waves)
+}
+
+// Write (m, l, acc[d]) of head h0 + h (partial index `pi`) from LDS-merged values.
+template <int D>
+__device__ __forceinline__ float* partial_ptr(const DecodeArgs& A, int b, int head, int pi) {
+  return A.part + ((size_t)(b * A.Hq + head) * A.n_part + pi) * (D + 4);
+}
+
+// The exact recent tokens of kv-head g: scores with the natural-domain query, softmax,
+// value sum (natural domain), one partial per head at index nsplit.  Every global read is
+// issued on entry, before any is used: two threads per token row (half a row each) for
+// the scores, and value columns as thread = (dimension, token subset), 32 rows at a time.
+template <int D, int NREP, int KK, int KB, int VK, int VB>
+__device__ void recent_split(const DecodeArgs& A, int b, int g, float* sm) {
+  using G = DecodeGeom<D, NREP, KK, KB, VK, VB>;
+  static_assert(kMaxRecent * 2 <= 256, "two threads per recent token");
+  constexpr int NG = 256 / D;                 // threads per dimension in the value sums
+  constexpr int VCH = 32;                     // value rows in flight per thread
+  constexpr int HU = D / 16;                  // 16-byte reads per half row
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int R = A.n_recent;
+  const int bf = A.recent_bf16;
+  float* qn = sm + G::OFF_QA;
+  float* sr = sm + G::OFF_ST;                 // [NREP][kMaxRecent] scores -> weights
+  float* sML = sr + NREP * kMaxRecent;        // [NREP] max, [NREP] normaliser
+  float* sacc = sML + 2 * NREP;               // [NG][NREP][D] partial value sums
+  static_assert(4 * G::STAGE >= NREP * kMaxRecent + 2 * NREP + NG * NREP * D,
+                "recent scratch does not fit the staging area");
+  const size_t rbase = ((size_t)b * A.Hkv + g) * A.recent_cap;
+  // key half rows
+  const int r_k = tid >> 1, half = tid & 1;
+  uint4 kr[HU];
+  if (r_k < R) {
+    const uint4* src = reinterpret_cast<const uint4*>(A.rk + (rbase + r_k) * D + half * (D / 2));
+#pragma unroll
+    for (int c = 0; c < HU; ++c) kr[c] = src[c];
+  } else {
+#pragma unroll
+    for (int c = 0; c < HU; ++c) kr[c] = make_uint4(0u, 0u, 0u, 0u);
+  }
+  // first block of value rows
+  const int j = tid % D, grp = tid / D;
+  float vv[VCH];
+#pragma unroll
+  for (int i = 0; i < VCH; ++i) {
+    const int r = grp + NG * i;
+    vv[i] = (r < R) ? bits16_to_f32(A.rv[(rbase + r) * D + j], bf) : 0.f;
+  }
+  const float scale = kLog2e * rsqrtf((float)D);
+  const uint16_t* qsrc = A.q + (size_t)(b * A.Hq + g * NREP) * D;
+  for (int i = tid; i < NREP * D; i += 256) qn[i] = bits16_to_f32(qsrc[i], A.q_bf16) * scale;
+  __syncthreads();
+  // scores: each thread dots its half row with every head, the pair adds its halves
+#pragma unroll 1
+  for (int h = 0; h < NREP; ++h) {
+    const float* q = qn + h * D + half * (D / 2);
+    float a = 0.f;
+#pragma unroll
+    for (int c = 0; c < HU; ++c) {
+      const uint32_t w[4] = {kr[c].x, kr[c].y, kr[c].z, kr[c].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        a = fmaf(q[8 * c + 2 * k], bits16_to_f32(w[k] & 0xFFFFu, bf), a);
+        a = fmaf(q[8 * c + 2 * k + 1], bits16_to_f32(w[k] >> 16, bf), a);
+      }
+    }
+    a += xor_lanes<1>(a);
+    if (half == 0 && r_k < R) sr[h * kMaxRecent + r_k] = a;
+  }
+  __syncthreads();
   for (int h = wave; h < NREP; h += 4) {
     float mx = -INFINITY;
-    for (int s = lane; s < ns; s += 64) mx = fmaxf(mx, s_w[h * ns + s]);
-    for (int r = lane; r < R; r += 64) mx = fmaxf(mx, s_sr[h * kMaxRecent + r]);
+    for (int r = lane; r < R; r += 64) mx = fmaxf(mx, sr[h * kMaxRecent + r]);
     mx = wave_max(mx);
     float l = 0.f;
-    for (int s = lane; s < ns; s += 64) {
-      const float m = s_w[h * ns + s];
-      const float w = (m == -INFINITY) ? 0.f : exp2f(m - mx);
-      s_w[h * ns + s] = w;
-      l = fmaf(s_l[h * ns + s], w, l);
-    }
     for (int r = lane; r < R; r += 64) {
-      const float p = exp2f(s_sr[h * kMaxRecent + r] - mx);
-      s_sr[h * kMaxRecent + r] = p;
+      const float p = exp2f(sr[h * kMaxRecent + r] - mx);
+      sr[h * kMaxRecent + r] = p;
       l += p;
     }
     l = wave_sum(l);
-    if (lane == 0) { s_M[h] = mx; s_L[h] = l; }
+    if (lane == 0) { sML[h] = mx; sML[NREP + h] = l; }
   }
   __syncthreads();
-  // (head, dimension) sums: thread group `grp` takes splits / recent tokens grp, grp+NG, ...
-  for (int it = tid; it < ITEMS * NG; it += 256) {
-    const int item = it % ITEMS, grp = it / ITEMS;
-    const int h = item / D, j = item % D;
-    const float* pp = pp0 + (size_t)h * ns * PS + 4 + j;
-    const float* w = s_w + h * ns;
-    float a = 0.f;
-#pragma unroll 8
-    for (int s = grp; s < ns; s += NG) a = fmaf(pp[(size_t)s * PS], w[s], a);
-    const uint16_t* vr = A.rv + rbase * D + j;
-    const float* pr = s_sr + h * kMaxRecent;
-    float rs = 0.f;
-#pragma unroll 8
-    for (int r = grp; r < R; r += NG) rs = fmaf(pr[r], recent_to_f32(vr[(size_t)r * D], A.recent_bf16), rs);
-    s_pa[grp * ITEMS + item] = a;
-    s_pr[grp * ITEMS + item] = rs;
-  }
-  __syncthreads();
-  if constexpr (NG > 1) {
-    for (int i = tid; i < ITEMS; i += 256) {
-      float a = 0.f, rs = 0.f;
+  // value sums: thread (j, grp) over tokens grp, grp + NG, ... for every head
+  float acc[NREP];
 #pragma unroll
-      for (int q = 0; q < NG; ++q) { a += s_pa[q * ITEMS + i]; rs += s_pr[q * ITEMS + i]; }
-      s_pa[i] = a;
-      s_pr[i] = rs;
-    }
-    __syncthreads();
-  }
-  if constexpr (VK == TQ_V_LM_ROT) {
-    // Pi^T acc = diag(s) H acc / sqrt(d) for every head: butterflies in LDS
-    for (int hs = 1; hs < D; hs <<= 1) {
-      for (int i = tid; i < ITEMS / 2; i += 256) {
-        const int h = i / (D / 2), t = i % (D / 2);
-        const int lo = h * D + (t / hs) * 2 * hs + (t % hs);
-        const float x = s_pa[lo], y = s_pa[lo + hs];
-        s_pa[lo] = x + y;
-        s_pa[lo + hs] = x - y;
+  for (int h = 0; h < NREP; ++h) acc[h] = 0.f;
+  for (int r0 = 0; r0 < R; r0 += NG * VCH) {
+    if (r0 > 0) {
+#pragma unroll
+      for (int i = 0; i < VCH; ++i) {
+        const int r = r0 + grp + NG * i;
+        vv[i] = (r < R) ? bits16_to_f32(A.rv[(rbase + r) * D + j], bf) : 0.f;
       }
-      __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < VCH; ++i) {
+      const int r = r0 + grp + NG * i;
+      if (r < R) {
+#pragma unroll
+        for (int h = 0; h < NREP; ++h) acc[h] = fmaf(sr[h * kMaxRecent + r], vv[i], acc[h]);
+      }
     }
   }
-  for (int i = tid; i < ITEMS; i += 256) {
-    const int h = i / D, j = i % D;
-    float mv = s_pa[i];
-    if constexpr (VK == TQ_V_LM_ROT) {
-      mv *= rsqrtf((float)D);
-      if ((A.vsign[j >> 5] >> (j & 31)) & 1u) mv = -mv;
-    }
-    A.out[(size_t)(b * Hq + h0 + h) * D + j] = (mv + s_pr[i]) / s_L[h];
+#pragma unroll
+  for (int h = 0; h < NREP; ++h) sacc[(grp * NREP + h) * D + j] = acc[h];
+  __syncthreads();
+  for (int i = tid; i < NREP * D; i += 256) {
+    const int h = i / D, jj = i % D;
+    float a = 0.f;
+#pragma unroll
+    for (int q = 0; q < NG; ++q) a += sacc[(q * NREP + h) * D + jj];
+    float* dst = partial_ptr<D>(A, b, g * NREP + h, A.nsplit);
+    dst[4 + jj] = a;
+    if (jj == 0) { dst[0] = sML[h]; dst[1] = sML[NREP + h]; }
   }
 }
 
 template <int D, int NREP, int KK, int KB, int VK, int VB>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 decode_main_kernel(const DecodeArgs A) {
   using G = DecodeGeom<D, NREP, KK, KB, VK, VB>;
   constexpr int LK = 1 << KB;
   constexpr int LV = 1 << VB;
+  constexpr int NE = G::NE;
 
-  __shared__ __attribute__((aligned(16))) uint32_t s_stage[4 * G::STAGE];
-  __shared__ float s_p[4][NREP * kWave];
-  __shared__ float s_kcent[16], s_vcent[16];
-  __shared__ float s_mrg_m[4][NREP], s_mrg_l[4][NREP];
+  __shared__ __attribute__((aligned(16))) float sm[G::FLOATS];
   // the four waves' value sums reuse the staging area once the tile loop is done
   static_assert(4 * G::STAGE >= 4 * NREP * D, "merge buffer does not fit in the staging area");
-  float(*s_mrg_acc)[NREP * D] = reinterpret_cast<float(*)[NREP * D]>(s_stage);
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int Hkv = A.Hkv, cap = A.cap, n_c = A.n_c, chunk = A.chunk, nsplit = A.nsplit;
+  // 1-D grid: the n_splits x (batch, kv-head) compressed groups first, then one short
+  // recent-buffer group per (batch, kv-head), so that the recent groups are dispatched
+  // last and never hold back a compressed group
+  const int n_comp = A.nsplit * A.Hkv * A.batch;
+  if ((int)blockIdx.x >= n_comp) {
+    const int u = blockIdx.x - n_comp;
+    recent_split<D, NREP, KK, KB, VK, VB>(A, u / A.Hkv, u % A.Hkv, sm);
+    return;
+  }
+  const int split = blockIdx.x % A.nsplit;
+  const int g = (blockIdx.x / A.nsplit) % A.Hkv;
+  const int b = blockIdx.x / (A.nsplit * A.Hkv);
+
+  float* s_kcent = sm + G::OFF_CENT;
+  float* s_vcent = s_kcent + 16;
+  if (threadIdx.x < 16) {
+    if constexpr (KK == TQ_K_LM_QJL) s_kcent[threadIdx.x] = (threadIdx.x < LK) ? A.kcent[threadIdx.x] : 0.f;
+    if constexpr (VK == TQ_V_LM_ROT) s_vcent[threadIdx.x] = (threadIdx.x < LV) ? A.vcent[threadIdx.x] : 0.f;
+  }
+  const float* qa = sm + G::OFF_QA;
+  const float* qb = sm + G::OFF_QB;
+  const float* tq = sm + G::OFF_TQ;
+  const int Hkv = A.Hkv, cap = A.cap, n_c = A.n_c, chunk = A.chunk;
   const uint32_t* __restrict__ kc = A.kc;
   const uint32_t* __restrict__ ks = A.ks;
   const uint32_t* __restrict__ ka = A.ka;
   const uint32_t* __restrict__ vc = A.vc;
   const uint32_t* __restrict__ va = A.va;
-  const int Hq = Hkv * NREP;
 
-  if (threadIdx.x < 16) {
-    if constexpr (KK == TQ_K_LM_QJL) s_kcent[threadIdx.x] = (threadIdx.x < LK) ? A.kcent[threadIdx.x] : 0.f;
-    if constexpr (VK == TQ_V_LM_ROT) s_vcent[threadIdx.x] = (threadIdx.x < LV) ? A.vcent[threadIdx.x] : 0.f;
-  }
-  __syncthreads();
-
-  const float* __restrict__ qp = A.qprep + (size_t)(b * Hq + g * NREP) * G::QF;
   const size_t slice = (size_t)b * Hkv + g;
   const int tb = split * chunk;
   const int te = min(n_c, tb + chunk);
 
-  uint32_t* st_k = s_stage + wave * G::STAGE;
+  uint32_t* stage = reinterpret_cast<uint32_t*>(sm + G::OFF_ST);
+  uint32_t* st_k = stage + wave * G::STAGE;
   uint32_t* st_s = st_k + kTile * G::SK;
   uint32_t* st_ak = st_s + kTile * G::SS;
   uint32_t* st_v = st_ak + kTile * G::SAK;
   uint32_t* st_av = st_v + kTile * G::SV;
-  float* sp = s_p[wave];
+  float* sp = sm + G::OFF_P + wave * NREP * kWave;
 
   float m_run[NREP], l_run[NREP], off[NREP];
   float acc[NREP][8];
@@ -327,7 +492,9 @@ decode_main_kernel(const DecodeArgs A) {
     ld_v.load(vc + row0 * G::WV, nv, lane);
     ld_av.load(va + row0 * G::WAV, nv, lane);
   };
+  // the first tile's loads overlap the query preparation
   if (tb + wave * kTile < te) issue(tb + wave * kTile);
+  prepare_queries<D, NREP, KK, KB, VK, VB>(A, b, g, sm);
 
   for (int t0 = tb + wave * kTile; t0 < te; t0 += 4 * kTile) {
     const int nv = min(kTile, te - t0);
@@ -343,41 +510,57 @@ decode_main_kernel(const DecodeArgs A) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
     // ---- 2. scores: lane = token ----------------------------------------------------------
-    // The query block is uniform across the wave and is read through scalar loads; the
-    // outer loop walks CH dimensions at a time and is not unrolled, so only one chunk of
-    // query values is live in scalar registers (a fully unrolled loop would hoist all of
-    // them and spill).  Codes come from the lane's staged row in LDS.
     float s2[NREP];
     {
-      constexpr int CH = (NREP <= 4) ? 8 : 4;
       const uint32_t* krow = st_k + lane * G::SK;
       if constexpr (KK == TQ_K_LM_QJL) {
-        const uint32_t* srow = st_s + lane * G::SS;
         const uint32_t aux = st_ak[lane * G::SAK];
         float alm[NREP], aqj[NREP];
 #pragma unroll
         for (int h = 0; h < NREP; ++h) { alm[h] = 0.f; aqj[h] = 0.f; }
+        // QJL term: one table entry per 4 dimensions (stored bit 1 <=> sigma = +1)
+        {
+          const uint32_t* srow = st_s + lane * G::SS;
+          // one sign word (8 table reads) per iteration: a fully unrolled loop would
+          // hoist every read and hold all entries in registers
 #pragma unroll 1
-        for (int j0 = 0; j0 < D; j0 += CH) {
-          uint32_t x;   // code j0 + i at bits KB*i
-          if constexpr (KB == 3) {
-            const int w0 = j0 / 10, r0 = j0 % 10, k0 = 10 - r0;   // codes left in word w0
-            const uint32_t lo = krow[w0] >> (3 * r0);
-            x = (k0 >= CH) ? lo : ((lo & ((1u << (3 * k0)) - 1u)) | (krow[w0 + 1] << (3 * k0)));
-          } else {
-            constexpr int PER = 32 / KB;
-            x = krow[j0 / PER] >> (KB * (j0 % PER));
-          }
-          const uint32_t nsw = ~(srow[j0 >> 5] >> (j0 & 31));   // inverted QJL bits, dim j0 at bit 0
+          for (int w = 0; w < D / 32; ++w) {
+            const uint32_t sw = srow[w];
 #pragma unroll
-          for (int i = 0; i < CH; ++i) {
-            const float c = s_kcent[(x >> (KB * i)) & (LK - 1)];
-            // sigma = +1 where the stored bit is 1: +-1.0f from the inverted bit
-            const float sg = __uint_as_float(((nsw << (31 - i)) & 0x80000000u) | 0x3F800000u);
+            for (int n = 0; n < 8; ++n) {
+              const uint32_t v = (sw >> (4 * n)) & 15u;
+              float e[NE];
+              read_entry<NE>(tq + ((8 * w + n) * 16 + v) * NE, e);
+#pragma unroll
+              for (int h = 0; h < NREP; ++h) aqj[h] += e[h];
+            }
+          }
+        }
+        {
+          // codebook term, one code at a time: centroid from LDS, query from LDS broadcast
+          constexpr int CH = 8;
+#pragma unroll 1
+          for (int j0 = 0; j0 < D; j0 += CH) {
+            uint32_t x;   // code j0 + i at bits KB*i
+            if constexpr (KB == 3) {
+              const int w0 = j0 / 10, r0 = j0 % 10, k0 = 10 - r0;   // codes left in word w0
+              const uint32_t lo = krow[w0] >> (3 * r0);
+              x = (k0 >= CH) ? lo : ((lo & ((1u << (3 * k0)) - 1u)) | (krow[w0 + 1] << (3 * k0)));
+            } else {
+              constexpr int PER = 32 / KB;
+              x = krow[j0 / PER] >> (KB * (j0 % PER));
+            }
+            float c[CH];
+#pragma unroll
+            for (int i = 0; i < CH; ++i) c[i] = s_kcent[(x >> (KB * i)) & (LK - 1)];
 #pragma unroll
             for (int h = 0; h < NREP; ++h) {
-              alm[h] = fmaf(qp[h * G::QF + j0 + i], c, alm[h]);
-              aqj[h] = fmaf(qp[h * G::QF + D + j0 + i], sg, aqj[h]);
+              const float4 q0 = *reinterpret_cast<const float4*>(qa + h * D + j0);
+              const float4 q1 = *reinterpret_cast<const float4*>(qa + h * D + j0 + 4);
+              float a = alm[h];
+              a = fmaf(q0.x, c[0], a); a = fmaf(q0.y, c[1], a); a = fmaf(q0.z, c[2], a); a = fmaf(q0.w, c[3], a);
+              a = fmaf(q1.x, c[4], a); a = fmaf(q1.y, c[5], a); a = fmaf(q1.z, c[6], a); a = fmaf(q1.w, c[7], a);
+              alm[h] = a;
             }
           }
         }
@@ -390,25 +573,31 @@ decode_main_kernel(const DecodeArgs A) {
 #pragma unroll
         for (int h = 0; h < NREP; ++h) { s2[h] = 0.f; ag[h] = 0.f; }
 #pragma unroll 1
-        for (int j0 = 0; j0 < D; j0 += CH) {
+        for (int j0 = 0; j0 < D; j0 += 8) {
+          const uint32_t w0 = krow[j0 / 4], w1 = krow[j0 / 4 + 1];
+          float c[8];
 #pragma unroll
-          for (int wi = 0; wi < CH / 4; ++wi) {
-            const uint32_t word = krow[j0 / 4 + wi];
-#pragma unroll
-            for (int bsel = 0; bsel < 4; ++bsel) {
-              const float q8 = (float)((word >> (8 * bsel)) & 0xFFu);
-#pragma unroll
-              for (int h = 0; h < NREP; ++h) ag[h] = fmaf(qp[h * G::QF + j0 + 4 * wi + bsel], q8, ag[h]);
-            }
+          for (int i = 0; i < 4; ++i) {
+            c[i] = (float)((w0 >> (8 * i)) & 0xFFu);
+            c[4 + i] = (float)((w1 >> (8 * i)) & 0xFFu);
           }
-          if (((j0 + CH) & 31) == 0) {   // end of a 32-block: fold in its scale and offset
+#pragma unroll
+          for (int h = 0; h < NREP; ++h) {
+            const float4 q0 = *reinterpret_cast<const float4*>(qa + h * D + j0);
+            const float4 q1 = *reinterpret_cast<const float4*>(qa + h * D + j0 + 4);
+            float a = ag[h];
+            a = fmaf(q0.x, c[0], a); a = fmaf(q0.y, c[1], a); a = fmaf(q0.z, c[2], a); a = fmaf(q0.w, c[3], a);
+            a = fmaf(q1.x, c[4], a); a = fmaf(q1.y, c[5], a); a = fmaf(q1.z, c[6], a); a = fmaf(q1.w, c[7], a);
+            ag[h] = a;
+          }
+          if (((j0 + 8) & 31) == 0) {   // end of a 32-block: fold in its scale and offset
             const int gi = j0 >> 5;
             const uint32_t aux = st_ak[lane * G::SAK + gi];
             const float a = f16_to_f32(aux & 0xFFFFu);
             const float m = f16_to_f32(aux >> 16);
 #pragma unroll
             for (int h = 0; h < NREP; ++h) {
-              s2[h] = fmaf(a, ag[h], fmaf(m, qp[h * G::QF + 3 * D + gi], s2[h]));
+              s2[h] = fmaf(a, ag[h], fmaf(m, qb[h * (D / 32) + gi], s2[h]));
               ag[h] = 0.f;
             }
           }
@@ -497,6 +686,9 @@ decode_main_kernel(const DecodeArgs A) {
     }
   }
   __syncthreads();   // every wave is done with its staging area
+  float(*s_mrg_acc)[NREP * D] = reinterpret_cast<float(*)[NREP * D]>(stage);
+  float* s_mrg_m = sm + G::OFF_MRG;            // [4][NREP]
+  float* s_mrg_l = s_mrg_m + 4 * NREP;         // [4][NREP]
   if (lane < G::LPT) {
 #pragma unroll
     for (int h = 0; h < NREP; ++h) {
@@ -507,8 +699,8 @@ decode_main_kernel(const DecodeArgs A) {
   if (lane == 0) {
 #pragma unroll
     for (int h = 0; h < NREP; ++h) {
-      s_mrg_m[wave][h] = m_run[h];
-      s_mrg_l[wave][h] = l_run[h];
+      s_mrg_m[wave * NREP + h] = m_run[h];
+      s_mrg_l[wave * NREP + h] = l_run[h];
     }
   }
   __syncthreads();
@@ -516,27 +708,31 @@ decode_main_kernel(const DecodeArgs A) {
   // ---- merge the four waves, write one partial per head ----------------------------------
   for (int i = threadIdx.x; i < NREP * D; i += blockDim.x) {
     const int h = i / D, j = i % D;
-    float mx = s_mrg_m[0][h];
+    float mx = s_mrg_m[h];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) mx = fmaxf(mx, s_mrg_m[w][h]);
+    for (int w = 1; w < 4; ++w) mx = fmaxf(mx, s_mrg_m[w * NREP + h]);
     float a = 0.f, l = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const float sc = (s_mrg_m[w][h] == -INFINITY) ? 0.f : exp2f(s_mrg_m[w][h] - mx);
+      const float mw = s_mrg_m[w * NREP + h];
+      const float sc = (mw == -INFINITY) ? 0.f : exp2f(mw - mx);
       a = fmaf(s_mrg_acc[w][h * D + j], sc, a);
-      l = fmaf(s_mrg_l[w][h], sc, l);
+      l = fmaf(s_mrg_l[w * NREP + h], sc, l);
     }
-    float* dst = A.part + ((size_t)(b * Hq + g * NREP + h) * nsplit + split) * G::PS;
+    float* dst = partial_ptr<D>(A, b, g * NREP + h, split);
     dst[4 + j] = a;
     if (j == 0) {
       dst[0] = mx;
       dst[1] = l;
     }
   }
-
 }
 
-using MainLaunch = hipError_t (*)(dim3 grid, hipStream_t st, const DecodeArgs& A);
+// One instantiation: its launcher and its resident work-groups per CU.
+struct MainKernel {
+  hipError_t (*launch)(dim3 grid, hipStream_t st, const DecodeArgs& A);
+  int (*blocks_per_cu)();
+};
 
 template <int D, int NREP, int KK, int KB, int VK, int VB>
 hipError_t main_launch(dim3 grid, hipStream_t st, const DecodeArgs& A) {
@@ -544,18 +740,35 @@ hipError_t main_launch(dim3 grid, hipStream_t st, const DecodeArgs& A) {
   return hipGetLastError();
 }
 
+template <int D, int NREP, int KK, int KB, int VK, int VB>
+int main_blocks_per_cu() {
+  static const int n = [] {
+    int b = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, decode_main_kernel<D, NREP, KK, KB, VK, VB>, 256, 0) !=
+            hipSuccess || b <= 0)
+      b = 1;
+    return b;
+  }();
+  return n;
+}
+
+template <int D, int NREP, int KK, int KB, int VK, int VB>
+constexpr MainKernel main_kernel() {
+  return MainKernel{&main_launch<D, NREP, KK, KB, VK, VB>, &main_blocks_per_cu<D, NREP, KK, KB, VK, VB>};
+}
+
 // Lookup of the compiled instantiations (one file per key kind and head_dim).
-MainLaunch find_main_lm2_d64(int nrep, int vk, int vb);
-MainLaunch find_main_lm3_d64(int nrep, int vk, int vb);
-MainLaunch find_main_lm4_d64(int nrep, int vk, int vb);
-MainLaunch find_main_aff8_d64(int nrep, int vk, int vb);
-MainLaunch find_main_lm2_d128(int nrep, int vk, int vb);
-MainLaunch find_main_lm3_d128(int nrep, int vk, int vb);
-MainLaunch find_main_lm4_d128(int nrep, int vk, int vb);
-MainLaunch find_main_aff8_d128(int nrep, int vk, int vb);
-MainLaunch find_main_lm2_d256(int nrep, int vk, int vb);
-MainLaunch find_main_lm3_d256(int nrep, int vk, int vb);
-MainLaunch find_main_lm4_d256(int nrep, int vk, int vb);
-MainLaunch find_main_aff8_d256(int nrep, int vk, int vb);
+MainKernel find_main_lm2_d64(int nrep, int vk, int vb);
+MainKernel find_main_lm3_d64(int nrep, int vk, int vb);
+MainKernel find_main_lm4_d64(int nrep, int vk, int vb);
+MainKernel find_main_aff8_d64(int nrep, int vk, int vb);
+MainKernel find_main_lm2_d128(int nrep, int vk, int vb);
+MainKernel find_main_lm3_d128(int nrep, int vk, int vb);
+MainKernel find_main_lm4_d128(int nrep, int vk, int vb);
+MainKernel find_main_aff8_d128(int nrep, int vk, int vb);
+MainKernel find_main_lm2_d256(int nrep, int vk, int vb);
+MainKernel find_main_lm3_d256(int nrep, int vk, int vb);
+MainKernel find_main_lm4_d256(int nrep, int vk, int vb);
+MainKernel find_main_aff8_d256(int nrep, int vk, int vb);
 
 }  // namespace tq

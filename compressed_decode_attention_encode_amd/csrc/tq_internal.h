@@ -14,8 +14,9 @@ namespace tq {
 constexpr int kTile = 64;
 // Largest recent buffer accepted by the decode (vLLM guide, section 5: 128-token buffer).
 constexpr int kMaxRecent = 128;
-// Decode work-group count the split policy aims for (4 per CU on 256 CUs), and the
-// fewest 64-token tiles a split gets (two per wave, so a wave's loads overlap compute).
+// Decode work-group count the split bound is sized for (4 per CU on 256 CUs), and the
+// fewest 64-token tiles a split gets (two per wave: the query preparation is amortised
+// over eight tiles).
 constexpr int kTargetDecodeGroups = 1024;
 constexpr int kMinTilesPerSplit = 8;
 
