@@ -25,6 +25,7 @@ constexpr int kMaxParts = 512;
 template <int D, int VK>
 __global__ void __launch_bounds__(256) decode_finish_kernel(const DecodeArgs A) {
   constexpr int NG = 256 / D;            // threads per dimension
+  constexpr int PF = 32;                 // partial values prefetched per thread
   __shared__ float s_w[kMaxParts];       // split maxima -> weights
   __shared__ float s_l[kMaxParts];
   __shared__ float s_red[8];
@@ -34,6 +35,16 @@ __global__ void __launch_bounds__(256) decode_finish_kernel(const DecodeArgs A) 
   const int head = blockIdx.x, b = blockIdx.y;
   const int np = A.n_part, ns = A.nsplit;
   const float* pp = A.part + (size_t)(b * A.Hq + head) * np * (D + 4);
+  // thread (j, grp) sums splits grp, grp + NG, ... of dimension j; its first PF values are
+  // read together with the split maxima, so the merge waits on one round of reads
+  const int j = tid % D, grp = tid / D;
+  float pv[PF];
+#pragma unroll
+  for (int i = 0; i < PF; ++i) {
+    const int s = grp + NG * i;
+    pv[i] = (s < ns) ? pp[(size_t)s * (D + 4) + 4 + j] : 0.f;
+  }
+  const float nat = (np > ns && grp == 0) ? pp[(size_t)ns * (D + 4) + 4 + j] : 0.f;
   for (int s = tid; s < np; s += 256) {
     s_w[s] = pp[(size_t)s * (D + 4)];
     s_l[s] = pp[(size_t)s * (D + 4) + 1];
@@ -56,14 +67,16 @@ __global__ void __launch_bounds__(256) decode_finish_kernel(const DecodeArgs A) 
   if (lane == 0) s_red[4 + wave] = l;
   __syncthreads();
   const float L = s_red[4] + s_red[5] + s_red[6] + s_red[7];
-  // value sums: thread group grp takes splits grp, grp + NG, ... of dimension j
   {
-    const int j = tid % D, grp = tid / D;
     float a = 0.f;
-#pragma unroll 8
-    for (int s = grp; s < ns; s += NG) a = fmaf(pp[(size_t)s * (D + 4) + 4 + j], s_w[s], a);
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      const int s = grp + NG * i;
+      if (s < ns) a = fmaf(pv[i], s_w[s], a);
+    }
+    for (int s = grp + NG * PF; s < ns; s += NG) a = fmaf(pp[(size_t)s * (D + 4) + 4 + j], s_w[s], a);
     s_rot[grp][j] = a;
-    if (grp == 0) s_nat[j] = (np > ns) ? pp[(size_t)ns * (D + 4) + 4 + j] * s_w[ns] : 0.f;
+    if (grp == 0) s_nat[j] = (np > ns) ? nat * s_w[ns] : 0.f;
   }
   __syncthreads();
   if (tid < D) {

@@ -63,8 +63,14 @@ __device__ __forceinline__ uint32_t magnitude_cell(float ay, const float (&p)[(1
   }
 }
 
+// Coordinates per lane (a vector spans d / coordinates lanes).  32: five butterfly stages
+// inside a lane and a 64-VGPR float64 rotation state.  (16 per lane fits a third wave per
+// SIMD but adds a cross-lane stage; measured no faster at d = 64 and slower at d = 128.)
+template <int D>
+constexpr int lm_coords() { return 32; }
+
 template <int D, int KB, int DT, bool QJL>
-__global__ void __launch_bounds__(2 * D) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1)))
+__global__ void __launch_bounds__(64 * D / lm_coords<D>()) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1)))
 encode_lm_kernel(const uint16_t* __restrict__ x, int T, int tiles_per_slice, int n_tiles,
                  int dst_offset, int cap,
                  const float* __restrict__ cent, const float* __restrict__ thr,
@@ -75,16 +81,23 @@ encode_lm_kernel(const uint16_t* __restrict__ x, int T, int tiles_per_slice, int
   // float64 evaluation; values: float32 rotation (only the decisions depend on it) and a
   // float64 norm
   using W = typename std::conditional<QJL, double, float>::type;
-  constexpr int P = D / 32;            // lanes per vector
+  constexpr int C = lm_coords<D>();        // coordinates per lane
+  constexpr int P = D / C;                 // lanes per vector (= waves per group)
+  constexpr int NT = 64 * P;               // threads: one 64-token tile
   constexpr int L = 1 << KB;
   constexpr int PER = (KB == 3) ? 10 : 32 / KB;   // codes per word
   constexpr int WK = (D + PER - 1) / PER;          // words per row
-  constexpr int SW = D / 32;                       // sign words per row
+  constexpr int SW = D / 32;                       // sign words per row (= MFMA n-blocks)
   constexpr int RH = D + 8;                        // LDS row stride of the residual halves
   constexpr int NKB = D / 16;                      // MFMA k-blocks
+  constexpr int LW = C * KB / 32;                  // whole stream words of a lane's codes
+  constexpr int LSH = (C * KB) % 32;               // bits of a partial last stream word
+  constexpr int MPW = 2 * SW / P;                  // projection m-blocks per wave
+  static_assert(P >= 2 && P <= 16 && NT <= 1024, "lane split");
+  static_assert(MPW == 1 || MPW == 2, "each wave takes one n-block and one or both m-blocks");
 
   __shared__ double s_cent[16];
-  __shared__ __attribute__((aligned(16))) uint32_t s_xm[P * 16];
+  __shared__ __attribute__((aligned(16))) uint32_t s_xm[P * (C / 2)];
   __shared__ __attribute__((aligned(16))) _Float16 s_rhi[QJL ? kTile * RH : 8];
   __shared__ __attribute__((aligned(16))) _Float16 s_rlo[QJL ? kTile * RH : 8];
 
@@ -92,16 +105,17 @@ encode_lm_kernel(const uint16_t* __restrict__ x, int T, int tiles_per_slice, int
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int vec = tid / P;     // vector within the tile
-  const int part = tid % P;    // which 32 coordinates
+  const int part = tid % P;    // which C coordinates
 
   constexpr double kPre = QJL ? kKeyScale : 1.0;
   if (tid < L) s_cent[tid] = (double)cent[tid] * kPre;
-  if (tid < P * 16) {
-    // sign flips as xor masks on pairs of packed 16-bit inputs: coordinate 32 p + 2 i at
-    // bit 15, 32 p + 2 i + 1 at bit 31
-    const uint32_t sm = sign_mask[tid / 16];
-    const int i = tid % 16;
-    s_xm[tid] = (((sm >> (2 * i)) & 1u) << 15) | (((sm >> (2 * i + 1)) & 1u) << 31);
+  if (tid < P * (C / 2)) {
+    // sign flips as xor masks on pairs of packed 16-bit inputs: coordinate C p + 2 i at
+    // bit 15, C p + 2 i + 1 at bit 31
+    const int pp = tid / (C / 2), i = tid % (C / 2);
+    const int j = C * pp + 2 * i;
+    const uint32_t sm = sign_mask[j >> 5] >> (j & 31);
+    s_xm[tid] = ((sm & 1u) << 15) | (((sm >> 1) & 1u) << 31);
   }
   // symmetric codebook: t[L/2-1] = 0 and t[L/2-1+i] = -t[L/2-1-i]; only the positive
   // thresholds are compared, against |y|
@@ -109,36 +123,38 @@ encode_lm_kernel(const uint16_t* __restrict__ x, int T, int tiles_per_slice, int
 #pragma unroll
   for (int i = 0; i < L / 2 - 1; ++i) thp[i] = thr[L / 2 + i] * (float)kPre;
 
-  // QJL: the wave's 32 rows of S (projection outputs 32 wave .. 32 wave + 31), fp16, as
-  // MFMA A operands: lane l holds S[32 wave + l % 32][16 kb + 8 (l / 32) + i], i = 0..7.
+  // QJL: wave w computes projection outputs 32 nb .. 32 nb + 31 (nb = w % SW) for the
+  // 32-token m-blocks mb0 .. mb0 + MPW - 1 (mb0 = w / SW).  Its rows of S, fp16, as MFMA A
+  // operands: lane l holds S[32 nb + l % 32][16 kb + 8 (l / 32) + i], i = 0..7.
+  const int nb = wave % SW, mb0 = wave / SW;
   half8 sop[QJL ? NKB : 1];
   if constexpr (QJL) {
-    const uint16_t* srow = S + (size_t)(32 * wave + (lane & 31)) * D + 8 * (lane >> 5);
+    const uint16_t* srow = S + (size_t)(32 * nb + (lane & 31)) * D + 8 * (lane >> 5);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) sop[kb] = __builtin_bit_cast(half8, *reinterpret_cast<const uint4*>(srow + 16 * kb));
   }
 
   // 3-bit codes: word kw holds codes 10 kw .. 10 kw + 9, so words straddle the lanes'
-  // 32-code ranges.  A lane writes the words that start in its range, kw0 .. kw1, taking
+  // C-code ranges.  A lane writes the words that start in its range, kw0 .. kw1, taking
   // the first bits of the next lane's stream where a word runs past its own.
-  const int kw0 = (32 * part + PER - 1) / PER;
-  const int kw1 = min((32 * part + 31) / PER, WK - 1);
-  const int b0 = KB * (PER * kw0 - 32 * part);     // bit offset of word kw0 in the lane's stream
+  const int kw0 = (C * part + PER - 1) / PER;
+  const int kw1 = min((C * part + C - 1) / PER, WK - 1);
+  const int b0 = KB * (PER * kw0 - C * part);     // bit offset of word kw0 in the lane's stream
 
-  auto load_tile = [&](int tile, uint4 (&raw)[4]) {
+  auto load_tile = [&](int tile, uint4 (&raw)[C / 8]) {
     const int slice = tile / tiles_per_slice;
     const int t0 = (tile % tiles_per_slice) * kTile;
     if (tile < n_tiles && vec < min(kTile, T - t0)) {
-      const uint4* src = reinterpret_cast<const uint4*>(x + ((size_t)slice * T + t0 + vec) * D + 32 * part);
+      const uint4* src = reinterpret_cast<const uint4*>(x + ((size_t)slice * T + t0 + vec) * D + C * part);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) raw[i] = src[i];
+      for (int i = 0; i < C / 8; ++i) raw[i] = src[i];
     } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) raw[i] = make_uint4(0u, 0u, 0u, 0u);
+      for (int i = 0; i < C / 8; ++i) raw[i] = make_uint4(0u, 0u, 0u, 0u);
     }
   };
 
-  uint4 raw[4];
+  uint4 raw[C / 8];
   load_tile(blockIdx.x, raw);
   __syncthreads();
 
@@ -149,12 +165,12 @@ encode_lm_kernel(const uint16_t* __restrict__ x, int T, int tiles_per_slice, int
     const bool valid = vec < nv;
     const size_t row0 = (size_t)slice * cap + dst_offset + t0;
 
-    uint32_t w[16];
+    uint32_t w[C / 2];
     {
       const uint32_t* rw = reinterpret_cast<const uint32_t*>(raw);
-      const uint4* xm4 = reinterpret_cast<const uint4*>(&s_xm[part * 16]);
+      const uint4* xm4 = reinterpret_cast<const uint4*>(&s_xm[part * (C / 2)]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < C / 8; ++i) {
         const uint4 m = xm4[i];
         w[4 * i] = rw[4 * i] ^ m.x;
         w[4 * i + 1] = rw[4 * i + 1] ^ m.y;
@@ -166,10 +182,10 @@ encode_lm_kernel(const uint16_t* __restrict__ x, int T, int tiles_per_slice, int
     load_tile(tile + gridDim.x, raw);
 
     // ---- phase A: sign flip, norm (float64), Walsh-Hadamard ----------------------------
-    W xv[32];
+    W xv[C];
     double ss = 0.0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < C / 2; ++i) {
       const float a = in_to_f32<DT>(w[i] & 0xFFFFu);
       const float b = in_to_f32<DT>(w[i] >> 16);
       ss = fma((double)a, (double)a, ss);
@@ -178,9 +194,9 @@ encode_lm_kernel(const uint16_t* __restrict__ x, int T, int tiles_per_slice, int
       xv[2 * i + 1] = (W)b;
     }
 #pragma unroll
-    for (int h = 1; h < 32; h <<= 1) {
+    for (int h = 1; h < C; h <<= 1) {
 #pragma unroll
-      for (int e = 0; e < 32; ++e) {
+      for (int e = 0; e < C; ++e) {
         if ((e & h) == 0) {
           const W a = xv[e], b = xv[e + h];
           xv[e] = a + b;
@@ -188,12 +204,12 @@ encode_lm_kernel(const uint16_t* __restrict__ x, int T, int tiles_per_slice, int
         }
       }
     }
-    // butterflies across the P lanes of the vector (stride 32 m <-> lane xor m): the upper
+    // butterflies across the P lanes of the vector (stride C m <-> lane xor m): the upper
     // lane of each pair keeps partner - own, the lower own + partner
 #define TQ_XSTAGE(M)                                              \
     if constexpr (P > M) {                                        \
       const W sg = (part & M) ? W(-1) : W(1);                     \
-      _Pragma("unroll") for (int e = 0; e < 32; ++e) {            \
+      _Pragma("unroll") for (int e = 0; e < C; ++e) {             \
         const W o = xor_lanes<M>(xv[e]);                          \
         xv[e] = fma(xv[e], sg, o);                                \
       }                                                           \
@@ -201,6 +217,7 @@ encode_lm_kernel(const uint16_t* __restrict__ x, int T, int tiles_per_slice, int
     TQ_XSTAGE(1)
     TQ_XSTAGE(2)
     TQ_XSTAGE(4)
+    TQ_XSTAGE(8)
 #undef TQ_XSTAGE
     ss = group_sum_dpp<P>(ss);
     const double n = sqrt(ss);
@@ -208,14 +225,16 @@ encode_lm_kernel(const uint16_t* __restrict__ x, int T, int tiles_per_slice, int
     const W scale = (W)scale64;
 
     // ---- Lloyd-Max decision, packed codes, residual -----------------------------------
-    uint32_t cw[4] = {0u, 0u, 0u, 0u};   // the lane's 32 codes as a KB-bit stream
+    uint32_t cw[LW + 1];                // the lane's C codes as a KB-bit stream
+#pragma unroll
+    for (int i = 0; i <= LW; ++i) cw[i] = 0u;
     double gg = 0.0;
     // eight coordinates at a time (keeps the centroid reads and residuals of one chunk
     // in registers); keys write each chunk's residual halves to LDS:
     // hi = fp16(r) and lo = fp16(r - hi), both rounded toward zero -- the pair carries 21+
     // significant bits and every product of halves is exact in float32
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < C / 8; ++c) {
       float rf[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
@@ -246,31 +265,47 @@ encode_lm_kernel(const uint16_t* __restrict__ x, int T, int tiles_per_slice, int
           hw[q] = __builtin_bit_cast(uint32_t, h);
           lw[q] = __builtin_bit_cast(uint32_t, l);
         }
-        *reinterpret_cast<uint4*>(&s_rhi[vec * RH + 32 * part + 8 * c]) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-        *reinterpret_cast<uint4*>(&s_rlo[vec * RH + 32 * part + 8 * c]) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+        *reinterpret_cast<uint4*>(&s_rhi[vec * RH + C * part + 8 * c]) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        *reinterpret_cast<uint4*>(&s_rlo[vec * RH + C * part + 8 * c]) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (valid) {
-      uint32_t* crow = codes_out + (row0 + vec) * WK;
-      if constexpr (KB == 2) {
-        *reinterpret_cast<uint2*>(crow + 2 * part) = make_uint2(cw[0], cw[1]);
-      } else if constexpr (KB == 4) {
-        *reinterpret_cast<uint4*>(crow + 4 * part) = make_uint4(cw[0], cw[1], cw[2], cw[3]);
+    if constexpr (KB != 3) {
+      // whole words: 16 / 8 codes per word, C codes per lane
+      if (valid) {
+        uint32_t* crow = codes_out + (row0 + vec) * WK + LW * part;
+        if constexpr (LW == 1) {
+          crow[0] = cw[0];
+        } else if constexpr (LW == 2) {
+          *reinterpret_cast<uint2*>(crow) = make_uint2(cw[0], cw[1]);
+        } else {
+          *reinterpret_cast<uint4*>(crow) = make_uint4(cw[0], cw[1], cw[2], cw[3]);
+        }
       }
-    }
-    if constexpr (KB == 3) {
-      // the lane's stream is 96 bits; word kw0 + j starts at bit b0 + 30 j (< 118)
-      const uint32_t nx = next_lane_u32(cw[0]);
-      const uint32_t s3 = (part == P - 1) ? 0u : nx;
-      const uint32_t st[4] = {cw[0], cw[1], cw[2], s3};
+    } else {
+      // the lane's stream is C * 3 bits; append the next lane's first word behind it (the
+      // last lane of a vector appends zeros), then word kw0 + j starts at bit b0 + 30 j
+      const uint32_t nx0 = next_lane_u32(cw[0]);
+      const uint32_t nx = (part == P - 1) ? 0u : nx0;
+      constexpr int NS = LW + (LSH ? 2 : 1);
+      uint32_t st[NS + 1];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int i = 0; i < LW; ++i) st[i] = cw[i];
+      if constexpr (LSH) {
+        st[LW] = cw[LW] | (nx << LSH);
+        st[LW + 1] = nx >> (32 - LSH);
+      } else {
+        st[LW] = nx;
+      }
+      st[NS] = 0u;
+      constexpr int NJ = (C + PER - 1) / PER + 1;   // most words starting in a lane's range
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
         // bit bb of the stream lies in stream word j (j = 0 always) or j - 1
         const int bb = b0 + 30 * j;
         const bool up = j == 0 || (bb >> 5) == j;
-        const uint32_t lo = up ? st[j] : st[j - 1];
-        const uint32_t hi = up ? (j < 3 ? st[j + 1] : 0u) : st[j];
+        const uint32_t lo = up ? st[j < NS ? j : NS] : st[j - 1];
+        const uint32_t hi = up ? st[j + 1 <= NS ? j + 1 : NS] : st[j < NS ? j : NS];
         const uint32_t word = __builtin_amdgcn_alignbit(hi, lo, (uint32_t)(bb & 31)) & 0x3FFFFFFFu;
         if (valid && kw0 + j <= kw1) codes_out[(row0 + vec) * WK + kw0 + j] = word;
       }
@@ -284,11 +319,12 @@ encode_lm_kernel(const uint16_t* __restrict__ x, int T, int tiles_per_slice, int
     }
 
     // ---- phase B: QJL projection on the matrix cores, sign bits packed per lane --------
-    // Z^T = S R^T per 32-token block: A = the wave's S rows (outputs), B = residual rows.
+    // Z^T = S R^T for the wave's 32 outputs x 32 tokens: A = rows of S, B = residual rows.
     if constexpr (QJL) {
       __syncthreads();
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
+      for (int m = 0; m < MPW; ++m) {
+        const int mb = mb0 + m;
         floatx16 acc = {};
         const _Float16* ah = &s_rhi[(32 * mb + (lane & 31)) * RH + 8 * (lane >> 5)];
         const _Float16* al = &s_rlo[(32 * mb + (lane & 31)) * RH + 8 * (lane >> 5)];
@@ -300,14 +336,14 @@ encode_lm_kernel(const uint16_t* __restrict__ x, int T, int tiles_per_slice, int
           acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(sop[kb], r_l, acc, 0, 0, 0);
         }
         // acc register r of lane l: token 32 mb + l % 32, projection output
-        // 32 wave + 8 (r / 4) + 4 (l / 32) + r % 4.  Stored bit = (z >= 0), from the sign bit.
+        // 32 nb + 8 (r / 4) + 4 (l / 32) + r % 4.  Stored bit = (z >= 0), from the sign bit.
         uint32_t neg = 0u;
 #pragma unroll
         for (int r = 0; r < 16; ++r) neg |= (__float_as_uint(acc[r]) >> 31) << (8 * (r >> 2) + (r & 3));
         const uint32_t half_bits = (~neg & 0x0F0F0F0Fu) << (4 * (lane >> 5));
         const uint32_t word = half_bits | (uint32_t)__shfl_xor((int)half_bits, 32);
         const int t = 32 * mb + lane;
-        if (lane < 32 && t < nv) signs_out[(row0 + t) * SW + wave] = word;
+        if (lane < 32 && t < nv) signs_out[(row0 + t) * SW + nb] = word;
       }
       __syncthreads();   // the residual tile is overwritten by the next tile
     }
@@ -520,7 +556,8 @@ template <int D, int KB, int DT, bool QJL>
 int lm_blocks_per_cu() {
   static const int n = [] {
     int b = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, encode_lm_kernel<D, KB, DT, QJL>, 2 * D, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, encode_lm_kernel<D, KB, DT, QJL>, 64 * D / lm_coords<D>(), 0) !=
+            hipSuccess ||
         b <= 0)
       b = 1;
     return b;
@@ -538,12 +575,12 @@ hipError_t run_lm(const tq_layout& Lay, const tq_state& S, const void* x, int ba
   // (keys) once and walks the tiles with a stride of the grid size
   const int grid = std::min(n_tiles, device_cus() * lm_blocks_per_cu<D, KB, DT, QJL>());
   if (values) {
-    hipLaunchKernelGGL((encode_lm_kernel<D, KB, DT, QJL>), dim3(grid), dim3(2 * D), 0, st,
+    hipLaunchKernelGGL((encode_lm_kernel<D, KB, DT, QJL>), dim3(grid), dim3(64 * D / lm_coords<D>()), 0, st,
                        (const uint16_t*)x, T, tps, n_tiles, dst, C.capacity, S.v_centroids, S.v_thresholds,
                        S.v_signs, (const uint16_t*)nullptr, (uint32_t*)C.v_codes, (uint32_t*)nullptr,
                        (uint32_t*)C.v_aux);
   } else {
-    hipLaunchKernelGGL((encode_lm_kernel<D, KB, DT, QJL>), dim3(grid), dim3(2 * D), 0, st,
+    hipLaunchKernelGGL((encode_lm_kernel<D, KB, DT, QJL>), dim3(grid), dim3(64 * D / lm_coords<D>()), 0, st,
                        (const uint16_t*)x, T, tps, n_tiles, dst, C.capacity, S.k_centroids, S.k_thresholds,
                        S.k_signs, S.qjl, (uint32_t*)C.k_codes, (uint32_t*)C.k_signs, (uint32_t*)C.k_aux);
   }
