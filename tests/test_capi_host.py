@@ -150,6 +150,10 @@ def test_decode_rejects_bad_arguments():
         tq.tq_decode_attn(_layout(n_q_heads=18, n_kv_heads=2), _state(), FAKE, _cache(), 100, None, None, 0, 0,
                           FAKE, FAKE, 1 << 30)       # n_rep 9: no kernel compiled
     assert e.value.status == tq.TQ_ERR_UNSUPPORTED
+    with pytest.raises(tq.TQError) as e:              # LM + QJL keys with rotated values: not compiled
+        tq.tq_decode_attn(_layout(v_kind="lm_rot", v_bits=3), _state(), FAKE, _cache(), 100, None, None, 0, 0,
+                          FAKE, FAKE, 1 << 30)
+    assert e.value.status == tq.TQ_ERR_UNSUPPORTED
 
 
 def test_workspace_bound_covers_every_length():

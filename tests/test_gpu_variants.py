@@ -1,0 +1,117 @@
+"""GPU parity over the compiled variants the benchmark workloads do not reach.
+
+Every kernel family (2/3/4-bit Lloyd-Max + QJL keys, per-block affine keys, group-32
+and rotated Lloyd-Max values, head_dim 64/128/256, n_rep 1..8, fp16/bf16 inputs) is
+encoded and decoded at a small, ragged size against the CPU oracle, and degenerate
+vectors (all zero, constant, a single non-zero element, signed zeros, subnormals) go
+through both sides.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+
+from compressed_decode_attention_encode_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu_ok():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+if not _gpu_ok():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import gpu_harness as H  # noqa: E402
+
+# d, key kind/bits, value kind/bits, Hq, Hkv, input dtype, context, recent tokens
+VARIANTS = [
+    (64, "lm_qjl", 2, "group_sym", 2, 4, 2, "f16", 300, 17),
+    (64, "lm_qjl", 4, "group_sym", 4, 24, 3, "bf16", 260, 0),
+    (128, "lm_qjl", 2, "group_sym", 4, 6, 2, "f16", 200, 64),
+    (128, "lm_qjl", 4, "group_sym", 2, 12, 2, "bf16", 333, 5),
+    (256, "lm_qjl", 3, "group_sym", 2, 2, 2, "f16", 150, 31),
+    (256, "lm_qjl", 2, "group_sym", 4, 8, 1, "f16", 190, 0),
+    (64, "affine8", 8, "lm_rot", 2, 8, 2, "f16", 280, 0),
+    (64, "affine8", 8, "lm_rot", 4, 2, 2, "bf16", 200, 20),
+    (128, "affine8", 8, "lm_rot", 2, 14, 2, "f16", 222, 100),
+    (256, "affine8", 8, "lm_rot", 4, 6, 3, "bf16", 170, 9),
+]
+
+
+def make(v, seed=4242):
+    d, kk, kb, vk, vb, hq, hkv, dt, n_ctx, n_rec = v
+    return W.Workload(name=f"var_d{d}_{kk}{kb}_{vk}{vb}_h{hq}x{hkv}_{dt}", seed=seed, batch=2, n_q_heads=hq,
+                      n_kv_heads=hkv, head_dim=d, n_ctx=n_ctx, n_recent=n_rec, k_kind=kk, k_bits=kb, v_kind=vk,
+                      v_bits=vb, in_dtype=dt, recent_dtype="f16")
+
+
+@pytest.mark.parametrize("v", VARIANTS, ids=lambda v: make(v).name)
+def test_variant_encode_and_decode(v):
+    wl = make(v)
+    s = H.Setup(wl)
+    K, V = s.kv()
+    n = wl.n_compressed
+    off, cap = 3, n + 7
+    H.log(f"[variant] {wl.name} n_c={n} n_recent={wl.n_recent}")
+    cache = s.gpu_encode(K[:, :, :n], V[:, :, :n], n, cap, dst_offset=off)
+    gpu = H.download(cache, wl, K.shape[0], cap)
+    planes, ek, ev = s.oracle_encode(K[:, :, :n], V[:, :, :n])
+    st = H.compare_encode(wl, gpu, ek, ev, rows=slice(off, off + n))
+    H.log(f"  encode {st}")
+    assert H.untouched(gpu, slice(off, off + n), cap)
+    rk, rv, R = s.recent(K, V)
+    for variant in ("normal", "needle"):
+        Q = W.q_bits(wl, variant)
+        c2 = s.tq.alloc_cache(s.layout, K.shape[0], n)
+        H.upload_planes(c2, planes)
+        out = s.gpu_decode(c2, Q, n, rk, rv, R)
+        ref = s.oracle_decode(planes, Q, n, rk, rv, R)
+        err = H.rel_err(out, ref)
+        H.log(f"  decode {variant}: max rel err {err:.3e}")
+        assert err <= H.ATTN_TOL
+
+
+def _bits(dt, x):
+    return int(W.to_storage(np.array([x], dtype=np.float32), dt)[0])
+
+
+@pytest.mark.parametrize("name", ["llama1b_h32x8_d64_t32k", "qwen0p6b_h16x4_d128_b8_t64k",
+                                  "qwen32b_h40x8_d128_b4_t128k"])
+def test_degenerate_vectors(name):
+    """Zero, constant, one-hot, signed-zero and subnormal vectors through encode and decode."""
+    wl = dataclasses.replace(W.WORKLOADS[name].scaled(200, batch=1), n_recent=0)
+    s = H.Setup(wl)
+    K, V = s.kv()
+    dt, d = wl.in_dtype, wl.head_dim
+    one, big, neg_small = _bits(dt, 1.0), _bits(dt, 6.0e4), _bits(dt, -3.0e-3)
+    tiny = 0x0001                                   # the smallest subnormal of either format
+    for X in (K, V):
+        X[:, :, 0] = 0                              # all zero
+        X[:, :, 1] = one                            # constant
+        X[:, :, 2] = 0
+        X[:, :, 2, 5] = big                         # one non-zero element, large
+        X[:, :, 3] = 0x8000                         # negative zeros
+        X[:, :, 4] = tiny                           # subnormals
+        X[:, :, 4, 1::2] = tiny | 0x8000
+        X[:, :, 5] = neg_small                      # constant negative
+        X[:, :, 6, : d // 2] = one                  # half constant, half random
+    n = wl.n_compressed
+    cache = s.gpu_encode(K[:, :, :n], V[:, :, :n], n, n)
+    gpu = H.download(cache, wl, 1, n)
+    planes, ek, ev = s.oracle_encode(K[:, :, :n], V[:, :, :n])
+    st = H.compare_encode(wl, gpu, ek, ev)
+    H.log(f"[degenerate] {name}: {st}")
+    Q = W.q_bits(wl)
+    c2 = s.tq.alloc_cache(s.layout, 1, n)
+    H.upload_planes(c2, planes)
+    out = s.gpu_decode(c2, Q, n)
+    ref = s.oracle_decode(planes, Q, n)
+    err = H.rel_err(out, ref)
+    H.log(f"  decode max rel err {err:.3e}")
+    assert err <= H.ATTN_TOL
