@@ -519,7 +519,7 @@ decode_main_kernel(const DecodeArgs A) {
 #pragma unroll
         for (int h = 0; h < NREP; ++h) { alm[h] = 0.f; aqj[h] = 0.f; }
         // QJL term: one table entry per 4 dimensions (stored bit 1 <=> sigma = +1)
-        {
+        if constexpr (NREP <= 4) {
           const uint32_t* srow = st_s + lane * G::SS;
           // one sign word (8 table reads) per iteration: a fully unrolled loop would
           // hoist every read and hold all entries in registers
@@ -535,9 +535,41 @@ decode_main_kernel(const DecodeArgs A) {
               for (int h = 0; h < NREP; ++h) aqj[h] += e[h];
             }
           }
+        } else {
+          // n_rep > 4: reads go out in batches into separate registers, the next batch
+          // before the current one is added, so their LDS latencies overlap
+          const uint32_t* srow = st_s + lane * G::SS;
+          constexpr int NB = D / 4;                       // 4-dimension blocks
+          constexpr int QB = 4;                           // entries per batch
+          uint32_t sw[D / 32];
+#pragma unroll
+          for (int w = 0; w < D / 32; ++w) sw[w] = srow[w];
+          float e[2][QB][NE];
+          auto fetch = [&](int b0, float (&dst)[QB][NE]) {
+#pragma unroll
+            for (int k = 0; k < QB; ++k) {
+              const int blk = b0 + k;
+              const uint32_t v = (sw[blk / 8] >> (4 * (blk % 8))) & 15u;
+              read_entry<NE>(tq + (blk * 16 + v) * NE, dst[k]);
+            }
+          };
+          fetch(0, e[0]);
+#pragma unroll
+          for (int b0 = 0; b0 < NB; b0 += QB) {
+            const int cur = (b0 / QB) & 1;
+            if (b0 + QB < NB) fetch(b0 + QB, e[cur ^ 1]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int k = 0; k < QB; ++k)
+#pragma unroll
+              for (int h = 0; h < NREP; ++h) aqj[h] += e[cur][k][h];
+            __builtin_amdgcn_sched_barrier(0);
+          }
         }
-        {
-          // codebook term, one code at a time: centroid from LDS, query from LDS broadcast
+        if constexpr (NREP <= 4) {
+          // codebook term, one code at a time: centroid from LDS, query from LDS broadcast,
+          // 8 codes per loop trip (a rolled loop: measured faster than the batched form
+          // below for n_rep <= 4)
           constexpr int CH = 8;
 #pragma unroll 1
           for (int j0 = 0; j0 < D; j0 += CH) {
@@ -562,6 +594,38 @@ decode_main_kernel(const DecodeArgs A) {
               a = fmaf(q1.x, c[4], a); a = fmaf(q1.y, c[5], a); a = fmaf(q1.z, c[6], a); a = fmaf(q1.w, c[7], a);
               alm[h] = a;
             }
+          }
+        } else {
+          // codebook term for n_rep > 4: the row's code words are read once; chunks of 4
+          // codes read their centroids and query values as one batch before the FMAs
+          constexpr int CH = 4;
+          constexpr int NCH = D / CH;
+          uint32_t kw[G::WK];
+#pragma unroll
+          for (int w = 0; w < G::WK; ++w) kw[w] = krow[w];
+#pragma unroll
+          for (int c = 0; c < NCH; ++c) {
+            float cb[CH], qv[NREP][CH];
+#pragma unroll
+            for (int i = 0; i < CH; ++i) {
+              const int j = c * CH + i;
+              const uint32_t code = (kw[j / G::KPER] >> (KB * (j % G::KPER))) & (LK - 1);
+              cb[i] = s_kcent[code];
+            }
+#pragma unroll
+            for (int h = 0; h < NREP; ++h) {
+              const float4 q4 = *reinterpret_cast<const float4*>(qa + h * D + c * CH);
+              qv[h][0] = q4.x; qv[h][1] = q4.y; qv[h][2] = q4.z; qv[h][3] = q4.w;
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int h = 0; h < NREP; ++h) {
+              float a = alm[h];
+#pragma unroll
+              for (int i = 0; i < CH; ++i) a = fmaf(qv[h][i], cb[i], a);
+              alm[h] = a;
+            }
+            __builtin_amdgcn_sched_barrier(0);
           }
         }
         const float nn = f16_to_f32(aux & 0xFFFFu);
