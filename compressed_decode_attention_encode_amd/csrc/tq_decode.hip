@@ -22,71 +22,96 @@ constexpr int kMaxParts = 512;
 // ---------------------------------------------------------------------------------
 // finish: grid (n_q_heads, batch)
 // ---------------------------------------------------------------------------------
+// One work-group per (query head, batch): the log-sum-exp merge of the compressed
+// splits' partials and the recent buffer's partial (slot nsplit, natural domain) under
+// one normaliser.  Every read is issued on entry, 16 bytes at a time, so the kernel waits
+// on one round of reads before its arithmetic.
 template <int D, int VK>
 __global__ void __launch_bounds__(256) decode_finish_kernel(const DecodeArgs A) {
-  constexpr int NG = 256 / D;            // threads per dimension
-  constexpr int PF = 32;                 // partial values prefetched per thread
-  __shared__ float s_w[kMaxParts];       // split maxima -> weights
-  __shared__ float s_l[kMaxParts];
+  static_assert(kMaxParts <= 2 * 256, "two split (m, l) pairs per thread");
+  constexpr int SG = 1024 / D;           // split groups: thread = (4-dimension quad, split group)
+  constexpr int PF = 8;                  // partial quads held per thread and pass
+  __shared__ float s_w[kMaxParts];       // split weights
   __shared__ float s_red[8];
-  __shared__ float s_rot[NG][D];         // per-thread-group sums over the compressed splits
-  __shared__ float s_nat[D];             // recent buffer sum
+  __shared__ __attribute__((aligned(16))) float s_rot[SG][D];   // per split group sums
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int head = blockIdx.x, b = blockIdx.y;
-  const int np = A.n_part, ns = A.nsplit;
+  const int ns = A.nsplit, np = A.n_part;   // np = ns + 1 with a recent partial
   const float* pp = A.part + (size_t)(b * A.Hq + head) * np * (D + 4);
-  // thread (j, grp) sums splits grp, grp + NG, ... of dimension j; its first PF values are
-  // read together with the split maxima, so the merge waits on one round of reads
-  const int j = tid % D, grp = tid / D;
-  float pv[PF];
+  // Reads past the last split are clamped to it (never out of bounds, never a branch
+  // around a load: that would make the compiler wait on each load in turn) and their
+  // values are not used.
+  // thread s (and s + 256): split s's maximum and normaliser
+  float2 ml[2];
 #pragma unroll
-  for (int i = 0; i < PF; ++i) {
-    const int s = grp + NG * i;
-    pv[i] = (s < ns) ? pp[(size_t)s * (D + 4) + 4 + j] : 0.f;
+  for (int k = 0; k < 2; ++k) ml[k] = *reinterpret_cast<const float2*>(pp + (size_t)min(tid + 256 * k, np - 1) * (D + 4));
+  // the recent partial's values, 4 dimensions per thread
+  float4 nat = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (np > ns && tid < D / 4) nat = *reinterpret_cast<const float4*>(pp + (size_t)ns * (D + 4) + 4 + 4 * tid);
+  // thread (quad dq, split group sg): splits sg, sg + SG, ..., dimensions 4dq..4dq+3
+  const int dq = tid % (D / 4), sg = tid / (D / 4);
+  float4 pv[PF];
+  if (ns > 0) {
+#pragma unroll
+    for (int i = 0; i < PF; ++i)
+      pv[i] = *reinterpret_cast<const float4*>(pp + (size_t)min(sg + SG * i, ns - 1) * (D + 4) + 4 + 4 * dq);
   }
-  const float nat = (np > ns && grp == 0) ? pp[(size_t)ns * (D + 4) + 4 + j] : 0.f;
-  for (int s = tid; s < np; s += 256) {
-    s_w[s] = pp[(size_t)s * (D + 4)];
-    s_l[s] = pp[(size_t)s * (D + 4) + 1];
-  }
-  __syncthreads();
   float mx = -INFINITY;
-  for (int s = tid; s < np; s += 256) mx = fmaxf(mx, s_w[s]);
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+    if (tid + 256 * k < np) mx = fmaxf(mx, ml[k].x);
   mx = wave_max(mx);
   if (lane == 0) s_red[wave] = mx;
   __syncthreads();
   mx = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
   float l = 0.f;
-  for (int s = tid; s < np; s += 256) {
-    const float m = s_w[s];
-    const float w = (m == -INFINITY) ? 0.f : exp2f(m - mx);
-    s_w[s] = w;
-    l = fmaf(s_l[s], w, l);
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    if (tid + 256 * k < np) {
+      const float m = ml[k].x;
+      const float w = (m == -INFINITY) ? 0.f : exp2f(m - mx);
+      s_w[tid + 256 * k] = w;
+      l = fmaf(ml[k].y, w, l);
+    }
   }
   l = wave_sum(l);
   if (lane == 0) s_red[4 + wave] = l;
   __syncthreads();
   const float L = s_red[4] + s_red[5] + s_red[6] + s_red[7];
   {
-    float a = 0.f;
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s0 = 0; s0 < ns; s0 += SG * PF) {
+      if (s0 > 0) {
 #pragma unroll
-    for (int i = 0; i < PF; ++i) {
-      const int s = grp + NG * i;
-      if (s < ns) a = fmaf(pv[i], s_w[s], a);
+        for (int i = 0; i < PF; ++i)
+          pv[i] = *reinterpret_cast<const float4*>(pp + (size_t)min(s0 + sg + SG * i, ns - 1) * (D + 4) + 4 + 4 * dq);
+      }
+#pragma unroll
+      for (int i = 0; i < PF; ++i) {
+        const int s = s0 + sg + SG * i;
+        if (s < ns) {
+          const float w = s_w[s];
+          a.x = fmaf(pv[i].x, w, a.x); a.y = fmaf(pv[i].y, w, a.y);
+          a.z = fmaf(pv[i].z, w, a.z); a.w = fmaf(pv[i].w, w, a.w);
+        }
+      }
     }
-    for (int s = grp + NG * PF; s < ns; s += NG) a = fmaf(pp[(size_t)s * (D + 4) + 4 + j], s_w[s], a);
-    s_rot[grp][j] = a;
-    if (grp == 0) s_nat[j] = (np > ns) ? nat * s_w[ns] : 0.f;
+    *reinterpret_cast<float4*>(&s_rot[sg][4 * dq]) = a;
   }
-  __syncthreads();
-  if (tid < D) {
-    float a = 0.f;
-#pragma unroll
-    for (int q = 0; q < NG; ++q) a += s_rot[q][tid];
-    s_rot[0][tid] = a;
+  // the recent partial under the common normaliser, kept in registers of threads < D/4
+  if (np > ns && tid < D / 4) {
+    const float w = s_w[ns];
+    nat.x *= w; nat.y *= w; nat.z *= w; nat.w *= w;
   }
   __syncthreads();
   if constexpr (VK == TQ_V_LM_ROT) {
+    if (tid < D) {
+      float a = 0.f;
+#pragma unroll
+      for (int q = 0; q < SG; ++q) a += s_rot[q][tid];
+      s_rot[0][tid] = a;
+    }
+    __syncthreads();
     // Pi^T acc = diag(s) H acc / sqrt(d): butterflies in LDS
     float* x = s_rot[0];
     for (int hs = 1; hs < D; hs <<= 1) {
@@ -99,13 +124,29 @@ __global__ void __launch_bounds__(256) decode_finish_kernel(const DecodeArgs A) 
       __syncthreads();
     }
   }
-  if (tid < D) {
-    float mv = s_rot[0][tid];
+  if (tid < D / 4) {
+    float4 mv;
     if constexpr (VK == TQ_V_LM_ROT) {
-      mv *= rsqrtf((float)D);
-      if ((A.vsign[tid >> 5] >> (tid & 31)) & 1u) mv = -mv;
+      const float r = rsqrtf((float)D);
+      float e[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int jj = 4 * tid + k;
+        e[k] = s_rot[0][jj] * r;
+        if ((A.vsign[jj >> 5] >> (jj & 31)) & 1u) e[k] = -e[k];
+      }
+      mv = make_float4(e[0], e[1], e[2], e[3]);
+    } else {
+      mv = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int q = 0; q < SG; ++q) {
+        const float4 v = *reinterpret_cast<const float4*>(&s_rot[q][4 * tid]);
+        mv.x += v.x; mv.y += v.y; mv.z += v.z; mv.w += v.w;
+      }
     }
-    A.out[(size_t)(b * A.Hq + head) * D + tid] = (mv + s_nat[tid]) / L;
+    const float il = 1.f / L;
+    *reinterpret_cast<float4*>(A.out + (size_t)(b * A.Hq + head) * D + 4 * tid) =
+        make_float4((mv.x + nat.x) * il, (mv.y + nat.y) * il, (mv.z + nat.z) * il, (mv.w + nat.w) * il);
   }
 }
 
@@ -235,8 +276,10 @@ hipError_t run_decode_d(const tq_layout& L, const tq_state& S, const void* q, co
   A.q_bf16 = (L.in_dtype == TQ_BF16) ? 1 : 0;
   const long groups = (long)A.n_part * L.n_kv_heads * batch;
   if (groups > 0x7FFFFFFFL) return hipErrorInvalidConfiguration;
-  hipError_t e = mk.launch(dim3((unsigned)groups), st, A);
-  if (e != hipSuccess) return e;
+  if (groups > 0) {
+    const hipError_t e = mk.launch(dim3((unsigned)groups), st, A);
+    if (e != hipSuccess) return e;
+  }
   return (L.v_kind == TQ_V_GROUP_SYM) ? run_finish<D, TQ_V_GROUP_SYM>(A, batch, st)
                                       : run_finish<D, TQ_V_LM_ROT>(A, batch, st);
 }

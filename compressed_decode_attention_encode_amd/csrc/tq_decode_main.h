@@ -22,8 +22,12 @@
 //   2. scores, one token per lane, for all n_rep query heads at once;
 //   3. online softmax in the log2 domain (the scales carry log2(e)/sqrt(d));
 //   4. weighted value sum, 8 dimensions per lane: each decoded value element is used by
-//      all n_rep heads; group-scaled values fold the scale into the weight and the
-//      (L-1)/2 offset into one per-group running sum.
+//      all n_rep heads.  Group-scaled values fold the scale into the weight, rounded to
+//      fp16, and take two tokens per dot instruction (fp16 operands, exact products, fp32
+//      sums), the (L-1)/2 offset going into a per-group running sum of the same weights.
+//      The weight rounding moves an output by a relative 2^-12 per token, with errors of
+//      independent sign; scores stay in fp32 (fp16 queries or centroids cost too much of
+//      the 2e-3 attention tolerance where keys carry outlier channels).
 // The four waves merge (m, l, acc) through LDS and write one partial per head.  One more
 // split per (batch, kv-head) scores the exact fp16 recent buffer.  A second kernel (one
 // work-group per query head) merges the partials: the kernel boundary makes them visible
@@ -299,10 +303,11 @@ __device__ __forceinline__ float* partial_ptr(const DecodeArgs& A, int b, int he
   return A.part + ((size_t)(b * A.Hq + head) * A.n_part + pi) * (D + 4);
 }
 
-// The exact recent tokens of kv-head g: scores with the natural-domain query, softmax,
-// value sum (natural domain), one partial per head at index nsplit.  Every global read is
-// issued on entry, before any is used: two threads per token row (half a row each) for
-// the scores, and value columns as thread = (dimension, token subset), 32 rows at a time.
+// The exact recent tokens of kv-head g (n_recent >= 1): scores with the natural-domain
+// query, softmax, value sum (natural domain), one partial per head at index nsplit.  Every
+// global read is issued on entry, before any is used: two threads per token row (half a
+// row each) for the scores, and value columns as thread = (dimension, token subset), 32
+// rows at a time.
 template <int D, int NREP, int KK, int KB, int VK, int VB>
 __device__ void recent_split(const DecodeArgs& A, int b, int g, float* sm) {
   using G = DecodeGeom<D, NREP, KK, KB, VK, VB>;
@@ -320,25 +325,22 @@ __device__ void recent_split(const DecodeArgs& A, int b, int g, float* sm) {
   static_assert(4 * G::STAGE >= NREP * kMaxRecent + 2 * NREP + NG * NREP * D,
                 "recent scratch does not fit the staging area");
   const size_t rbase = ((size_t)b * A.Hkv + g) * A.recent_cap;
+  // Reads past the last row are clamped to it (never out of bounds, never a branch
+  // around a load: that would make the compiler wait on each load in turn) and their
+  // values are not used.
   // key half rows
   const int r_k = tid >> 1, half = tid & 1;
   uint4 kr[HU];
-  if (r_k < R) {
-    const uint4* src = reinterpret_cast<const uint4*>(A.rk + (rbase + r_k) * D + half * (D / 2));
+  {
+    const uint4* src = reinterpret_cast<const uint4*>(A.rk + (rbase + min(r_k, R - 1)) * D + half * (D / 2));
 #pragma unroll
     for (int c = 0; c < HU; ++c) kr[c] = src[c];
-  } else {
-#pragma unroll
-    for (int c = 0; c < HU; ++c) kr[c] = make_uint4(0u, 0u, 0u, 0u);
   }
-  // first block of value rows
+  // first block of value rows (fp16 / bf16 bits, one per register)
   const int j = tid % D, grp = tid / D;
-  float vv[VCH];
+  uint32_t vv[VCH];
 #pragma unroll
-  for (int i = 0; i < VCH; ++i) {
-    const int r = grp + NG * i;
-    vv[i] = (r < R) ? bits16_to_f32(A.rv[(rbase + r) * D + j], bf) : 0.f;
-  }
+  for (int i = 0; i < VCH; ++i) vv[i] = A.rv[(rbase + min(grp + NG * i, R - 1)) * D + j];
   const float scale = kLog2e * rsqrtf((float)D);
   const uint16_t* qsrc = A.q + (size_t)(b * A.Hq + g * NREP) * D;
   for (int i = tid; i < NREP * D; i += 256) qn[i] = bits16_to_f32(qsrc[i], A.q_bf16) * scale;
@@ -382,17 +384,15 @@ __device__ void recent_split(const DecodeArgs& A, int b, int g, float* sm) {
   for (int r0 = 0; r0 < R; r0 += NG * VCH) {
     if (r0 > 0) {
 #pragma unroll
-      for (int i = 0; i < VCH; ++i) {
-        const int r = r0 + grp + NG * i;
-        vv[i] = (r < R) ? bits16_to_f32(A.rv[(rbase + r) * D + j], bf) : 0.f;
-      }
+      for (int i = 0; i < VCH; ++i) vv[i] = A.rv[(rbase + min(r0 + grp + NG * i, R - 1)) * D + j];
     }
 #pragma unroll
     for (int i = 0; i < VCH; ++i) {
-      const int r = r0 + grp + NG * i;
+      const int r = r0 + grp + NG * i;   // uniform over a wave (grp is)
       if (r < R) {
+        const float v = bits16_to_f32(vv[i], bf);
 #pragma unroll
-        for (int h = 0; h < NREP; ++h) acc[h] = fmaf(sr[h * kMaxRecent + r], vv[i], acc[h]);
+        for (int h = 0; h < NREP; ++h) acc[h] = fmaf(sr[h * kMaxRecent + r], v, acc[h]);
       }
     }
   }
@@ -421,12 +421,14 @@ decode_main_kernel(const DecodeArgs A) {
   __shared__ __attribute__((aligned(16))) float sm[G::FLOATS];
   // the four waves' value sums reuse the staging area once the tile loop is done
   static_assert(4 * G::STAGE >= 4 * NREP * D, "merge buffer does not fit in the staging area");
+  static_assert(VK != TQ_V_GROUP_SYM || VB == 2 || VB == 4, "group-scaled values are 2 or 4 bits");
+  static_assert((kTile / G::SLOTS) % 2 == 0, "value steps go in token pairs");
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   // 1-D grid: the n_splits x (batch, kv-head) compressed groups first, then one short
-  // recent-buffer group per (batch, kv-head), so that the recent groups are dispatched
-  // last and never hold back a compressed group
+  // recent-buffer group per (batch, kv-head), dispatched last: they take the slots of the
+  // first compressed groups to finish
   const int n_comp = A.nsplit * A.Hkv * A.batch;
   if ((int)blockIdx.x >= n_comp) {
     const int u = blockIdx.x - n_comp;
@@ -520,20 +522,55 @@ decode_main_kernel(const DecodeArgs A) {
         for (int h = 0; h < NREP; ++h) { alm[h] = 0.f; aqj[h] = 0.f; }
         // QJL term: one table entry per 4 dimensions (stored bit 1 <=> sigma = +1)
         if constexpr (NREP <= 4) {
+          // QJL and codebook terms together, every LDS read issued one chunk (8 dimensions)
+          // ahead of its use: the row's code and sign words first, then per chunk its 8
+          // centroids, its 2 QJL entries and its query values.  With one token per lane
+          // and two waves per SIMD, little else can hide the LDS latency.
+          constexpr int CH = 8;
+          constexpr int NCH = D / CH;
           const uint32_t* srow = st_s + lane * G::SS;
-          // one sign word (8 table reads) per iteration: a fully unrolled loop would
-          // hoist every read and hold all entries in registers
-#pragma unroll 1
-          for (int w = 0; w < D / 32; ++w) {
-            const uint32_t sw = srow[w];
+          uint32_t kw[G::WK], sw[D / 32];
 #pragma unroll
-            for (int n = 0; n < 8; ++n) {
-              const uint32_t v = (sw >> (4 * n)) & 15u;
-              float e[NE];
-              read_entry<NE>(tq + ((8 * w + n) * 16 + v) * NE, e);
+          for (int w = 0; w < G::WK; ++w) kw[w] = krow[w];
 #pragma unroll
-              for (int h = 0; h < NREP; ++h) aqj[h] += e[h];
+          for (int w = 0; w < D / 32; ++w) sw[w] = srow[w];
+          float cb[2][CH], qj[2][2][NE];
+          float4 qv[2][NREP][2];
+          auto fetch = [&](int c, int buf) {
+#pragma unroll
+            for (int i = 0; i < CH; ++i) {
+              const int j = c * CH + i;
+              cb[buf][i] = s_kcent[(kw[j / G::KPER] >> (KB * (j % G::KPER))) & (LK - 1)];
             }
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+              const int blk = 2 * c + n;
+              const uint32_t v = (sw[blk / 8] >> (4 * (blk % 8))) & 15u;
+              read_entry<NE>(tq + (blk * 16 + v) * NE, qj[buf][n]);
+            }
+#pragma unroll
+            for (int h = 0; h < NREP; ++h) {
+              qv[buf][h][0] = *reinterpret_cast<const float4*>(qa + h * D + c * CH);
+              qv[buf][h][1] = *reinterpret_cast<const float4*>(qa + h * D + c * CH + 4);
+            }
+          };
+          fetch(0, 0);
+#pragma unroll
+          for (int c = 0; c < NCH; ++c) {
+            const int cur = c & 1;
+            if (c + 1 < NCH) fetch(c + 1, cur ^ 1);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int h = 0; h < NREP; ++h) {
+              const float4 q0 = qv[cur][h][0], q1 = qv[cur][h][1];
+              const float* cc = cb[cur];
+              float a = alm[h];
+              a = fmaf(q0.x, cc[0], a); a = fmaf(q0.y, cc[1], a); a = fmaf(q0.z, cc[2], a); a = fmaf(q0.w, cc[3], a);
+              a = fmaf(q1.x, cc[4], a); a = fmaf(q1.y, cc[5], a); a = fmaf(q1.z, cc[6], a); a = fmaf(q1.w, cc[7], a);
+              alm[h] = a;
+              aqj[h] += qj[cur][0][h] + qj[cur][1][h];
+            }
+            __builtin_amdgcn_sched_barrier(0);
           }
         } else {
           // n_rep > 4: reads go out in batches into separate registers, the next batch
@@ -566,36 +603,7 @@ decode_main_kernel(const DecodeArgs A) {
             __builtin_amdgcn_sched_barrier(0);
           }
         }
-        if constexpr (NREP <= 4) {
-          // codebook term, one code at a time: centroid from LDS, query from LDS broadcast,
-          // 8 codes per loop trip (a rolled loop: measured faster than the batched form
-          // below for n_rep <= 4)
-          constexpr int CH = 8;
-#pragma unroll 1
-          for (int j0 = 0; j0 < D; j0 += CH) {
-            uint32_t x;   // code j0 + i at bits KB*i
-            if constexpr (KB == 3) {
-              const int w0 = j0 / 10, r0 = j0 % 10, k0 = 10 - r0;   // codes left in word w0
-              const uint32_t lo = krow[w0] >> (3 * r0);
-              x = (k0 >= CH) ? lo : ((lo & ((1u << (3 * k0)) - 1u)) | (krow[w0 + 1] << (3 * k0)));
-            } else {
-              constexpr int PER = 32 / KB;
-              x = krow[j0 / PER] >> (KB * (j0 % PER));
-            }
-            float c[CH];
-#pragma unroll
-            for (int i = 0; i < CH; ++i) c[i] = s_kcent[(x >> (KB * i)) & (LK - 1)];
-#pragma unroll
-            for (int h = 0; h < NREP; ++h) {
-              const float4 q0 = *reinterpret_cast<const float4*>(qa + h * D + j0);
-              const float4 q1 = *reinterpret_cast<const float4*>(qa + h * D + j0 + 4);
-              float a = alm[h];
-              a = fmaf(q0.x, c[0], a); a = fmaf(q0.y, c[1], a); a = fmaf(q0.z, c[2], a); a = fmaf(q0.w, c[3], a);
-              a = fmaf(q1.x, c[4], a); a = fmaf(q1.y, c[5], a); a = fmaf(q1.z, c[6], a); a = fmaf(q1.w, c[7], a);
-              alm[h] = a;
-            }
-          }
-        } else {
+        if constexpr (NREP > 4) {
           // codebook term for n_rep > 4: the row's code words are read once; chunks of 4
           // codes read their centroids and query values as one batch before the FMAs
           constexpr int CH = 4;
@@ -691,29 +699,66 @@ decode_main_kernel(const DecodeArgs A) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
     // ---- 4. weighted values: lane = (token slot, 8 dimensions) ---------------------------
-#pragma unroll 2
-    for (int stp = 0; stp < kTile / G::SLOTS; ++stp) {
-      const int t = stp * G::SLOTS + slot;
-      float pw[NREP];
-#pragma unroll
-      for (int h = 0; h < NREP; ++h) pw[h] = sp[h * kWave + t];
-      float cv[8];
-      if constexpr (VK == TQ_V_GROUP_SYM) {
-        // 8 codes of VB bits, all inside one word
-        const int bit0 = 8 * prt * VB;
-        const uint32_t w = st_v[t * G::SV + (bit0 >> 5)] >> (bit0 & 31);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) cv[e] = (float)((w >> (VB * e)) & (LV - 1));
-        const int gi = prt / 4;   // 32-group of these 8 dimensions
-        const float dl = f16_to_f32((st_av[t * G::SAV + (gi >> 1)] >> (16 * (gi & 1))) & 0xFFFFu);
+    if constexpr (VK == TQ_V_GROUP_SYM) {
+      // two token slots per step.  Each token's weight (softmax weight times the group
+      // scale) is rounded once to fp16, the pair packed; each code c becomes the fp16 value
+      // 1 + c / 2^MV (the code dropped into the top mantissa bits under the exponent of
+      // 1.0), the two tokens' values of one dimension packed alike; one dot instruction
+      // adds both tokens' terms in fp32.  off[h] sums the same fp16 weights, so the 1 and
+      // the (L-1)/2 offset are taken out exactly after the loop.
+      constexpr uint32_t kOne = 0x3C003C00u;     // fp16 pair (1, 1)
+      const int gi = prt / 4;                     // 32-group of these 8 dimensions
+#pragma unroll 1
+      for (int stp = 0; stp < kTile / G::SLOTS; stp += 2) {
+        const int t1 = stp * G::SLOTS + slot, t2 = t1 + G::SLOTS;
+        const uint32_t aw1 = st_av[t1 * G::SAV + (gi >> 1)], aw2 = st_av[t2 * G::SAV + (gi >> 1)];
+        const float dl1 = f16_to_f32((aw1 >> (16 * (gi & 1))) & 0xFFFFu);
+        const float dl2 = f16_to_f32((aw2 >> (16 * (gi & 1))) & 0xFFFFu);
+        uint32_t wp[NREP];
 #pragma unroll
         for (int h = 0; h < NREP; ++h) {
-          const float wgt = pw[h] * dl;
-          off[h] += wgt;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(wgt, cv[e], acc[h][e]);
+          wp[h] = pack_f16x2(sp[h * kWave + t1] * dl1, sp[h * kWave + t2] * dl2);
+          off[h] = dot2_f16(wp[h], kOne, off[h]);
         }
-      } else {
+        uint32_t y[8];
+        if constexpr (VB == 2) {
+          // this lane's 8 codes are one half-word of each row: token 1's half below token
+          // 2's, code e at bits 2e of its half, moved to the mantissa bits 8..9
+          const uint32_t c1 = st_v[t1 * G::SV + (prt >> 1)], c2 = st_v[t2 * G::SV + (prt >> 1)];
+          const uint32_t x = __builtin_amdgcn_perm(c2, c1, (prt & 1) ? 0x07060302u : 0x05040100u);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t m = (e < 4) ? (x << (8 - 2 * e)) : (x >> (2 * e - 8));
+            y[e] = (m & 0x03000300u) | kOne;
+          }
+        } else {
+          // 4-bit codes: the 8 codes fill the word; the low and the high half-words of the
+          // two rows are paired, code e at bits 4 (e % 4) of its half, moved to bits 6..9
+          const uint32_t c1 = st_v[t1 * G::SV + prt], c2 = st_v[t2 * G::SV + prt];
+          const uint32_t xl = __builtin_amdgcn_perm(c2, c1, 0x05040100u);
+          const uint32_t xh = __builtin_amdgcn_perm(c2, c1, 0x07060302u);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t x = (e < 4) ? xl : xh;
+            const int sh = 6 - 4 * (e % 4);
+            const uint32_t m = (sh >= 0) ? (x << sh) : (x >> (-sh));
+            y[e] = (m & 0x03C003C0u) | kOne;
+          }
+        }
+#pragma unroll
+        for (int h = 0; h < NREP; ++h) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[h][e] = dot2_f16(wp[h], y[e], acc[h][e]);
+        }
+      }
+    } else {
+#pragma unroll 2
+      for (int stp = 0; stp < kTile / G::SLOTS; ++stp) {
+        const int t = stp * G::SLOTS + slot;
+        float pw[NREP];
+#pragma unroll
+        for (int h = 0; h < NREP; ++h) pw[h] = sp[h * kWave + t];
+        float cv[8];
         const float nv_t = __uint_as_float(st_av[t * G::SAV]);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -739,9 +784,11 @@ decode_main_kernel(const DecodeArgs A) {
   for (int h = 0; h < NREP; ++h) {
     l_run[h] = wave_sum(l_run[h]);
     if constexpr (VK == TQ_V_GROUP_SYM) {
-      const float o = 0.5f * (float)(LV - 1) * off[h];
+      // acc = sum w (1 + c / 2^MV), off = sum w  ->  sum w (c - (L-1)/2)
+      constexpr float F = (VB == 2) ? 4.f : 16.f;
+      const float o = (F + 0.5f * (float)(LV - 1)) * off[h];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] -= o;
+      for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(F, acc[h][e], -o);
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {

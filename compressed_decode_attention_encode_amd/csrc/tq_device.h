@@ -90,6 +90,22 @@ __device__ __forceinline__ uint32_t next_lane_u32(uint32_t v) {
 }
 
 // Sum over the N consecutive lanes sharing lane / N (N <= 16), by DPP exchanges.
+// Packed fp16 pairs held in a 32-bit word (low half = first element).
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+// c + a.lo * b.lo + a.hi * b.hi: fp16 products (exact in fp32), fp32 sum.
+__device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b), c, false);
+}
+
+// Two floats rounded to fp16 (nearest-even) and packed, lo in the low half.
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  f16x2_t r;
+  r.x = (_Float16)lo;
+  r.y = (_Float16)hi;
+  return __builtin_bit_cast(uint32_t, r);
+}
+
 template <int N>
 __device__ __forceinline__ double group_sum_dpp(double v) {
   if constexpr (N >= 2) v += xor_lanes<1>(v);
