@@ -17,6 +17,8 @@ synchronized wall clock around exactly K steps.
 Prints one JSON line on stdout:
   value       decode-attention KV GB/s (algorithmic bytes / decode kernel time)
   roofline    the dominant kernel against its MI355X peak
+  materialize tq_materialize of the whole history to fp16 rows (timed apart from the
+              step: the dequantise path ahead of a dense prefill)
   cpu_baseline  the CPU oracle timed on a bounded sample of the same workload
 """
 from __future__ import annotations
@@ -53,11 +55,20 @@ def source_digest() -> str:
     return h.hexdigest()[:16]
 
 
+def plane_bytes_per_token_head(wl) -> dict:
+    """Bytes of each packed plane for one token of one kv-head (the library's own layout
+    accounting, tq_cache_plane_bytes)."""
+    from compressed_decode_attention_encode_amd import tq
+    names = ("k_codes", "k_signs", "k_aux", "v_codes", "v_aux")
+    cap = 4096
+    sizes = tq.tq_cache_plane_bytes(tq.layout_of(wl), 1, cap)
+    return {nm: sz // (wl.n_kv_heads * cap) for nm, sz in zip(names, sizes)}
+
+
 def algorithmic(wl):
     """Bytes / flops the method must move or compute per step, per kernel group."""
-    from oracle import layout as OL   # byte accounting of the documented layout
     B, Hkv, Hq, d, n, R = wl.batch, wl.n_kv_heads, wl.n_q_heads, wl.head_dim, wl.n_compressed, wl.n_recent
-    per = OL.bytes_per_token_head(d, wl.k_kind, wl.k_bits, wl.v_kind, wl.v_bits)
+    per = plane_bytes_per_token_head(wl)
     rows = B * Hkv * n
     k_out = rows * (per["k_codes"] + per["k_signs"] + per["k_aux"])
     v_out = rows * (per["v_codes"] + per["v_aux"])
@@ -90,6 +101,48 @@ def read_traffic(workload: str, digest: str):
             except ValueError:
                 pass
     return out
+
+
+def bench_materialize(tq, lay, state, caches, wl, stream, steps: int, warmup: int) -> dict:
+    """tq_materialize of the whole compressed history (keys and values, fp16 rows), timed
+    apart from the step: caches and output buffers rotate over more than the Infinity Cache."""
+    import torch
+    B, Hkv, d, n = wl.batch, wl.n_kv_heads, wl.head_dim, wl.n_compressed
+    rows = B * Hkv * n
+    per = plane_bytes_per_token_head(wl)
+    out_bytes = 2 * rows * d * 2
+    alg = rows * sum(per.values()) + out_bytes
+    n_out = max(1, min(8, -(-(512 << 20) // out_bytes)))
+    outs = [(torch.empty((B, Hkv, n, d), dtype=torch.int16, device="cuda"),
+             torch.empty((B, Hkv, n, d), dtype=torch.int16, device="cuda")) for _ in range(n_out)]
+
+    def run(i):
+        ok, ov = outs[i % n_out]
+        tq.tq_materialize(lay, state.struct, caches[(3 * i + 1) % len(caches)].struct, 0, n, ok, ov, tq.TQ_F16,
+                          stream)
+
+    for i in range(warmup):
+        run(i)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        evs[i][0].record(stream)
+        run(i)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    gb = alg / (ms * 1e-3) / 1e9
+    res = {"us": ms * 1e3, "gbps": gb, "algorithmic_bytes": alg, "steps": steps,
+           "kernels": ("materialize_lm_kernel (keys, QJL term on fp16 matrix cores)" if wl.k_kind == "lm_qjl"
+                       else "materialize_elem_kernel (keys)") + " + " +
+                      ("materialize_elem_kernel (values)" if wl.v_kind == "group_sym"
+                       else "materialize_lm_kernel (values)"),
+           "roofline": {"bound": "hbm", "achieved": gb, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": gb / HBM_PEAK_GBS, "traffic": None}}
+    if wl.k_kind == "lm_qjl":
+        res["qjl_tflops_fp16"] = 2.0 * d * d * rows / (ms * 1e-3) / 1e12
+    del outs
+    return res
 
 
 def cpu_baseline(wl, budget_s: float = 15.0):
@@ -157,6 +210,8 @@ def main():
     ap.add_argument("--workload", default=W.BENCH_WORKLOAD, choices=sorted(W.WORKLOADS))
     ap.add_argument("--ring-gib", type=float, default=1.0, help="distinct input/cache bytes to rotate over")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-materialize", action="store_true",
+                    help="skip the separate timing of tq_materialize (dequantisation of the whole cache)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run 10 plain device-to-device copies of MIB MiB (counter calibration) and exit")
     a = ap.parse_args()
@@ -309,6 +364,9 @@ def main():
         "rooflines": rl,
         "source_digest": digest,
     }
+    if not a.no_materialize:
+        line["materialize"] = bench_materialize(tq, lay, state, caches, wl, stream, max(10, a.steps // 4),
+                                                max(2, a.warmup // 4))
     if not a.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample ...")
         line["cpu_baseline"] = cpu_baseline(wl)

@@ -220,6 +220,36 @@ uint16_t f64_to_f16_bits(double x) {
 
 extern "C" {
 
+int tq_materialize(const tq_layout* L, const tq_state* S, const tq_cache* C, int t0, int n_tokens, void* out_k,
+                   void* out_v, int out_dtype, void* stream) {
+  int rc = check_layout(L);
+  if (rc) return rc;
+  if (!out_k && !out_v) return fail(TQ_ERR_INVALID, "both out_k and out_v are NULL");
+  if ((out_k && !aligned16(out_k)) || (out_v && !aligned16(out_v)))
+    return fail(TQ_ERR_INVALID, "out_k/out_v must be 16-byte aligned");
+  if (out_dtype != TQ_F16 && out_dtype != TQ_BF16) return fail(TQ_ERR_UNSUPPORTED, "out_dtype %d", out_dtype);
+  if ((rc = check_cache(C, out_k != nullptr, out_v != nullptr, L))) return rc;
+  if ((rc = check_state(S, L, out_k != nullptr, out_v != nullptr))) return rc;
+  if (t0 < 0 || n_tokens < 0) return fail(TQ_ERR_INVALID, "t0 %d / n_tokens %d negative", t0, n_tokens);
+  if ((long)t0 + n_tokens > C->capacity)
+    return fail(TQ_ERR_CAPACITY, "t0 %d + n_tokens %d > capacity %d", t0, n_tokens, C->capacity);
+  if ((long)C->batch * L->n_kv_heads * n_tokens * (L->head_dim / 8) > 0x7FFFFFFFL)
+    return fail(TQ_ERR_UNSUPPORTED, "batch x kv-heads x n_tokens too large for one call (split it)");
+  if (!materialize_compiled(*L))
+    return fail(TQ_ERR_UNSUPPORTED, "no materialisation kernel compiled for head_dim %d", L->head_dim);
+  if (n_tokens == 0) return TQ_OK;
+  hipStream_t st = (hipStream_t)stream;
+  if (out_k) {
+    hipError_t e = launch_materialize_k(*L, *S, *C, t0, n_tokens, out_k, out_dtype, st);
+    if (e != hipSuccess) return fail(TQ_ERR_HIP, "key materialisation launch: %s", hipGetErrorString(e));
+  }
+  if (out_v) {
+    hipError_t e = launch_materialize_v(*L, *S, *C, t0, n_tokens, out_v, out_dtype, st);
+    if (e != hipSuccess) return fail(TQ_ERR_HIP, "value materialisation launch: %s", hipGetErrorString(e));
+  }
+  return TQ_OK;
+}
+
 const char* tq_strerror(int status) {
   switch (status) {
     case TQ_OK: return "ok";

@@ -50,10 +50,16 @@ hipError_t launch_decode(const tq_layout& L, const tq_state& S, const void* q, c
                          int n_compressed, const void* rk, const void* rv, int n_recent, int recent_cap,
                          float* out, void* ws, const DecodePlan& plan, hipStream_t st);
 
+hipError_t launch_materialize_k(const tq_layout& L, const tq_state& S, const tq_cache& C, int t0, int n_tokens,
+                                void* out, int out_dtype, hipStream_t st);
+hipError_t launch_materialize_v(const tq_layout& L, const tq_state& S, const tq_cache& C, int t0, int n_tokens,
+                                void* out, int out_dtype, hipStream_t st);
+
 // Whether a kernel instantiation exists for this layout.
 bool encode_k_compiled(const tq_layout& L);
 bool encode_v_compiled(const tq_layout& L);
 bool decode_compiled(const tq_layout& L);
+bool materialize_compiled(const tq_layout& L);
 
 // Per-thread error message (set by the C-ABI entry points and launchers).
 void set_error(const char* fmt, ...);

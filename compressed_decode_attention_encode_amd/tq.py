@@ -46,7 +46,7 @@ TQ_K_LM_QJL, TQ_K_AFFINE8 = 0, 1
 TQ_V_GROUP_SYM, TQ_V_LM_ROT = 0, 1
 
 EXPORTED = ("tq_make_codebook", "tq_make_rotation", "tq_cache_plane_bytes", "tq_encode",
-            "tq_decode_workspace_bytes", "tq_decode_attn", "tq_strerror", "tq_last_error")
+            "tq_decode_workspace_bytes", "tq_decode_attn", "tq_materialize", "tq_strerror", "tq_last_error")
 
 
 class tq_layout(ctypes.Structure):
@@ -77,6 +77,8 @@ _lib.tq_decode_workspace_bytes.argtypes = [ctypes.POINTER(tq_layout), ctypes.c_i
 _lib.tq_decode_workspace_bytes.restype = ctypes.c_size_t
 _lib.tq_decode_attn.argtypes = [ctypes.POINTER(tq_layout), ctypes.POINTER(tq_state), _P, ctypes.POINTER(tq_cache),
                                 ctypes.c_int, _P, _P, ctypes.c_int, ctypes.c_int, _P, _P, ctypes.c_size_t, _P]
+_lib.tq_materialize.argtypes = [ctypes.POINTER(tq_layout), ctypes.POINTER(tq_state), ctypes.POINTER(tq_cache),
+                                ctypes.c_int, ctypes.c_int, _P, _P, ctypes.c_int, _P]
 _lib.tq_strerror.argtypes = [ctypes.c_int]
 _lib.tq_strerror.restype = ctypes.c_char_p
 _lib.tq_last_error.argtypes = []
@@ -163,6 +165,12 @@ def tq_decode_attn(layout: tq_layout, state: tq_state, q, cache: tq_cache, n_com
     _check(_lib.tq_decode_attn(ctypes.byref(layout), ctypes.byref(state), _ptr(q), ctypes.byref(cache), n_compressed,
                                _ptr(recent_k), _ptr(recent_v), n_recent, recent_capacity, _ptr(out), _ptr(workspace),
                                workspace_bytes, _stream(stream)))
+
+
+def tq_materialize(layout: tq_layout, state: tq_state, cache: tq_cache, t0: int, n_tokens: int, out_k, out_v,
+                   out_dtype: int = TQ_F16, stream=None) -> None:
+    _check(_lib.tq_materialize(ctypes.byref(layout), ctypes.byref(state), ctypes.byref(cache), t0, n_tokens,
+                               _ptr(out_k), _ptr(out_v), out_dtype, _stream(stream)))
 
 
 # ---------------------------------------------------------------------------- marshalling helpers

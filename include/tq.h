@@ -23,9 +23,9 @@
  *   - Pointers marked "device" are HIP device memory; "host" pointers are CPU memory.
  *     The caller owns all memory.  The library allocates nothing and keeps no state
  *     between calls; it is reentrant.
- *   - `stream` is a hipStream_t (NULL = the default stream).  tq_encode and
- *     tq_decode_attn validate their arguments on the host, then enqueue kernels on
- *     `stream` and return without synchronising.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  tq_encode,
+ *     tq_decode_attn and tq_materialize validate their arguments on the host, then
+ *     enqueue kernels on `stream` and return without synchronising.
  *   - Every call returns TQ_OK or a negative tq_status.  Argument checks run before
  *     any HIP call, so an invalid or unsupported configuration fails immediately and
  *     loudly instead of degrading.  tq_last_error() returns a message for the most
@@ -194,6 +194,29 @@ int tq_decode_attn(const tq_layout* layout, const tq_state* state, const void* q
                    const tq_cache* cache, int n_compressed,
                    const void* recent_k, const void* recent_v, int n_recent, int recent_capacity,
                    float* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Materialisation: dequantise cache slots [t0, t0 + n_tokens) of every (batch,
+ * kv-head) slice into natural-domain rows (vllm-metal guide, prefill section: long
+ * prefills materialise the compressed history and run ordinary attention on it; vLLM
+ * guide, section 7: the hybrid path dequantises the whole history).  Row t of slice
+ * (b, g) is exactly the decoded vector the decode attention uses:
+ *   LM_QJL keys:    k = n Pi^T (c[idx] + gamma sqrt(pi/2)/d S^T sigma)
+ *   AFFINE8 keys:   k_j = m + a q8_j
+ *   GROUP_SYM vals: v_j = Delta (idx_j - (L-1)/2)
+ *   LM_ROT values:  v = n Pi_v^T c[idx]
+ * computed in float32 (the S^T sigma term on fp16 matrix cores: sigma and S are exact
+ * in fp16, the products exact, the sums fp32) and rounded once to out_dtype (nearest
+ * even).
+ *   out_k, out_v  device, [batch][n_kv_heads][n_tokens][head_dim] of out_dtype bits,
+ *                 contiguous; either may be NULL to materialise only the other half
+ *   out_dtype     TQ_F16 or TQ_BF16
+ * The state fields the decode needs for a half are needed here too.  Errors:
+ * TQ_ERR_INVALID for both outputs NULL, null/misaligned pointers or negative sizes;
+ * TQ_ERR_CAPACITY if t0 + n_tokens > cache->capacity; TQ_ERR_UNSUPPORTED for head_dim
+ * 512, an unknown out_dtype or batch * n_kv_heads * n_tokens * head_dim / 8 >= 2^31
+ * (split such a call); TQ_ERR_HIP.  n_tokens == 0 is a no-op.                       */
+int tq_materialize(const tq_layout* layout, const tq_state* state, const tq_cache* cache, int t0, int n_tokens,
+                   void* out_k, void* out_v, int out_dtype, void* stream);
 
 /* Static description of a status code. */
 const char* tq_strerror(int status);

@@ -156,6 +156,31 @@ def test_decode_rejects_bad_arguments():
     assert e.value.status == tq.TQ_ERR_UNSUPPORTED
 
 
+def test_materialize_rejects_bad_arguments():
+    """Host-side checks of tq_materialize: every rejection happens before any HIP call."""
+    L = _layout()
+    base = dict(t0=0, n=16, ok=FAKE, ov=FAKE, dt=tq.TQ_F16, cache=_cache(), state=_state())
+    cases = [
+        (dict(ok=None, ov=None), tq.TQ_ERR_INVALID),
+        (dict(ok=FAKE + 4), tq.TQ_ERR_INVALID),                     # misaligned output
+        (dict(t0=-1), tq.TQ_ERR_INVALID),
+        (dict(n=-2), tq.TQ_ERR_INVALID),
+        (dict(t0=250, n=16), tq.TQ_ERR_CAPACITY),                   # 266 > 256
+        (dict(dt=7), tq.TQ_ERR_UNSUPPORTED),
+        (dict(cache=tq.tq_cache(None, FAKE, FAKE, FAKE, FAKE, 1, 256)), tq.TQ_ERR_INVALID),
+        (dict(state=tq.tq_state(FAKE, FAKE, None, None, FAKE, None, None)), tq.TQ_ERR_INVALID),  # no QJL matrix
+    ]
+    for over, code in cases:
+        a = dict(base)
+        a.update(over)
+        with pytest.raises(tq.TQError) as e:
+            tq.tq_materialize(L, a["state"], a["cache"], a["t0"], a["n"], a["ok"], a["ov"], a["dt"])
+        assert e.value.status == code, (over, e.value)
+    with pytest.raises(tq.TQError) as e:
+        tq.tq_materialize(_layout(head_dim=512), _state(), _cache(), 0, 16, FAKE, FAKE, tq.TQ_F16)
+    assert e.value.status == tq.TQ_ERR_UNSUPPORTED
+
+
 def test_workspace_bound_covers_every_length():
     L = _layout(head_dim=64, n_q_heads=32, n_kv_heads=8)
     import ctypes
