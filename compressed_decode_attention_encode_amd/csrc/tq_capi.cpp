@@ -29,7 +29,7 @@ int lm_words(int d, int bits) {
 }
 int k_code_words(const tq_layout& L) { return L.k_kind == TQ_K_AFFINE8 ? L.head_dim / 4 : lm_words(L.head_dim, L.k_bits); }
 int k_sign_words(const tq_layout& L) { return L.k_kind == TQ_K_LM_QJL ? L.head_dim / 32 : 0; }
-int k_aux_words(const tq_layout& L) { return L.k_kind == TQ_K_LM_QJL ? 1 : L.head_dim / 32; }
+int k_aux_words(const tq_layout& L) { return L.k_kind == TQ_K_AFFINE8 ? L.head_dim / 32 : 1; }
 int v_code_words(const tq_layout& L) { return lm_words(L.head_dim, L.v_bits); }
 int v_aux_bytes(const tq_layout& L) { return L.v_kind == TQ_V_GROUP_SYM ? (L.head_dim / 32) * 2 : 4; }
 
@@ -63,8 +63,8 @@ int check_layout(const tq_layout* L) {
                 L->n_kv_heads);
   if (L->n_q_heads % L->n_kv_heads)
     return fail(TQ_ERR_UNSUPPORTED, "n_q_heads %d is not a multiple of n_kv_heads %d", L->n_q_heads, L->n_kv_heads);
-  if (L->k_kind == TQ_K_LM_QJL) {
-    if (L->k_bits < 2 || L->k_bits > 4) return fail(TQ_ERR_UNSUPPORTED, "LM+QJL keys need k_bits 2..4, got %d", L->k_bits);
+  if (L->k_kind == TQ_K_LM_QJL || L->k_kind == TQ_K_LM_MSE) {
+    if (L->k_bits < 2 || L->k_bits > 4) return fail(TQ_ERR_UNSUPPORTED, "LM keys need k_bits 2..4, got %d", L->k_bits);
   } else if (L->k_kind == TQ_K_AFFINE8) {
     if (L->k_bits != 8) return fail(TQ_ERR_UNSUPPORTED, "affine keys need k_bits 8, got %d", L->k_bits);
   } else {
@@ -104,6 +104,12 @@ int check_state(const tq_state* S, const tq_layout* L, bool need_k, bool need_v)
     if (!S->k_centroids || !S->k_thresholds || !S->k_signs || !S->qjl)
       return fail(TQ_ERR_INVALID, "LM+QJL keys need k_centroids, k_thresholds, k_signs and qjl");
     if (!aligned4(S->k_centroids) || !aligned4(S->k_thresholds) || !aligned4(S->k_signs) || !aligned16(S->qjl))
+      return fail(TQ_ERR_INVALID, "state arrays must be 4-byte aligned");
+  }
+  if (need_k && L->k_kind == TQ_K_LM_MSE) {
+    if (!S->k_centroids || !S->k_thresholds || !S->k_signs)
+      return fail(TQ_ERR_INVALID, "MSE-only LM keys need k_centroids, k_thresholds and k_signs");
+    if (!aligned4(S->k_centroids) || !aligned4(S->k_thresholds) || !aligned4(S->k_signs))
       return fail(TQ_ERR_INVALID, "state arrays must be 4-byte aligned");
   }
   if (need_v && L->v_kind == TQ_V_LM_ROT) {

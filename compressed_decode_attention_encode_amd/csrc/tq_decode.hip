@@ -215,6 +215,14 @@ MainKernel find_main(const tq_layout& L) {
       default: return MainKernel{nullptr, nullptr};
     }
   }
+  if (L.k_kind == TQ_K_LM_MSE) {
+    switch (L.k_bits) {
+      case 2: TQ_BY_D(find_main_lmm2)
+      case 3: TQ_BY_D(find_main_lmm3)
+      case 4: TQ_BY_D(find_main_lmm4)
+      default: return MainKernel{nullptr, nullptr};
+    }
+  }
   if (L.k_kind == TQ_K_AFFINE8 && L.k_bits == 8) { TQ_BY_D(find_main_aff8) }
 #undef TQ_BY_D
   return MainKernel{nullptr, nullptr};

@@ -47,7 +47,7 @@ struct DecodeGeom {
   static constexpr int KPER = (KB == 3) ? 10 : (KK == TQ_K_AFFINE8 ? 4 : 32 / KB);
   static constexpr int WK = (KK == TQ_K_AFFINE8) ? D / 4 : (D + KPER - 1) / KPER;
   static constexpr int WS = (KK == TQ_K_LM_QJL) ? D / 32 : 0;
-  static constexpr int WAK = (KK == TQ_K_LM_QJL) ? 1 : D / 32;
+  static constexpr int WAK = (KK == TQ_K_AFFINE8) ? D / 32 : 1;
   static constexpr int VPER = (VB == 3) ? 10 : 32 / VB;
   static constexpr int WV = (D + VPER - 1) / VPER;
   static constexpr int WAV = (VK == TQ_V_GROUP_SYM) ? D / 64 : 1;
@@ -60,7 +60,7 @@ struct DecodeGeom {
   static constexpr int PS = D + 4;                                  // partial stride (floats)
   // lookup tables
   static constexpr int NE = NREP == 1 ? 1 : (NREP == 2 ? 2 : (NREP <= 4 ? 4 : 8));   // floats per entry
-  static constexpr int LK = (KK == TQ_K_LM_QJL) ? (1 << KB) : 1;
+  static constexpr int LK = (KK == TQ_K_AFFINE8) ? 1 : (1 << KB);
   static constexpr int TQ_FLOATS = (KK == TQ_K_LM_QJL) ? (D / 4) * 16 * NE : 0;
   // LDS carve-out (floats): queries, second query block (QJL projection / affine block
   // sums), QJL table, staging, softmax weights, codebooks, merge scalars
@@ -68,7 +68,10 @@ struct DecodeGeom {
   static constexpr int OFF_QB = OFF_QA + NREP * D;
   static constexpr int OFF_TQ = OFF_QB + ((NREP * D + 3) & ~3);
   static constexpr int OFF_ST = OFF_TQ + TQ_FLOATS;
-  static constexpr int OFF_P = OFF_ST + 4 * STAGE;
+  // the staging area also holds the recent split's scratch and the waves' merge buffer
+  static constexpr int RECENT_SCRATCH = NREP * kMaxRecent + 2 * NREP + (256 / D) * NREP * D;
+  static constexpr int STAGE_ALL = (4 * STAGE > RECENT_SCRATCH) ? 4 * STAGE : RECENT_SCRATCH;
+  static constexpr int OFF_P = OFF_ST + STAGE_ALL;
   static constexpr int OFF_CENT = OFF_P + 4 * NREP * kWave;
   static constexpr int OFF_MRG = OFF_CENT + 32;
   static constexpr int FLOATS = OFF_MRG + 8 * NREP + 16;
@@ -178,16 +181,19 @@ __device__ void prepare_queries(const DecodeArgs& A, int b, int g, float* sm) {
   float* qb = sm + G::OFF_QB;
   const float scale = kLog2e * rsqrtf((float)D);
   const uint16_t* qsrc = A.q + (size_t)(b * A.Hq + g * NREP) * D;
-  if constexpr (KK == TQ_K_LM_QJL) {
+  if constexpr (KK != TQ_K_AFFINE8) {
+    constexpr bool QJL = KK == TQ_K_LM_QJL;
     // this thread's slice of S (row i, columns part*KL ..): its first reads go out first
     constexpr int KS = (256 / D) > 0 ? 256 / D : 1;
     constexpr int KL = D / KS;
-    constexpr int PRE = (KL / 8 < 8) ? KL / 8 : 8;   // 16-byte reads issued up front
+    constexpr int PRE = QJL ? ((KL / 8 < 8) ? KL / 8 : 8) : 1;   // 16-byte reads issued up front
     const int i = tid / KS, part = tid % KS;
-    const uint4* srow = reinterpret_cast<const uint4*>(A.S + (size_t)i * D + part * KL);
+    const uint4* srow = QJL ? reinterpret_cast<const uint4*>(A.S + (size_t)i * D + part * KL) : nullptr;
     uint4 spre[PRE];
+    if constexpr (QJL) {
 #pragma unroll
-    for (int c = 0; c < PRE; ++c) spre[c] = srow[c];
+      for (int c = 0; c < PRE; ++c) spre[c] = srow[c];
+    }
     // H (s * q) per head, one wave per head: lane holds E = d/64 consecutive coordinates;
     // strides below E inside the lane, the others across lanes (xor exchanges)
     {
@@ -227,6 +233,7 @@ __device__ void prepare_queries(const DecodeArgs& A, int b, int g, float* sm) {
     }
     __syncthreads();
     // qb = S (H s q): row i of S per group of KS threads, each a 1/KS slice of k
+    if constexpr (QJL) {
     {
       float acc[NREP];
 #pragma unroll
@@ -268,12 +275,13 @@ __device__ void prepare_queries(const DecodeArgs& A, int b, int g, float* sm) {
         for (int h = 0; h < NREP; ++h) qb[h * D + i] = acc[h] * sq;
       }
     }
+    }
     __syncthreads();
     for (int i = tid; i < NREP * D; i += 256) qa[i] *= rsqrtf((float)D) * scale;
     __syncthreads();
     // QJL table: entry (nib, v), head h = sum_t (bit t of v ? +1 : -1) qb[h][4 nib + t]
     float* tq = sm + G::OFF_TQ;
-    for (int i = tid; i < (D / 4) * 16; i += 256) {
+    for (int i = tid; QJL && i < (D / 4) * 16; i += 256) {
       const int nib = i / 16, v = i % 16;
 #pragma unroll
       for (int h = 0; h < NREP; ++h) {
@@ -322,7 +330,7 @@ __device__ void recent_split(const DecodeArgs& A, int b, int g, float* sm) {
   float* sr = sm + G::OFF_ST;                 // [NREP][kMaxRecent] scores -> weights
   float* sML = sr + NREP * kMaxRecent;        // [NREP] max, [NREP] normaliser
   float* sacc = sML + 2 * NREP;               // [NG][NREP][D] partial value sums
-  static_assert(4 * G::STAGE >= NREP * kMaxRecent + 2 * NREP + NG * NREP * D,
+  static_assert(G::STAGE_ALL >= NREP * kMaxRecent + 2 * NREP + NG * NREP * D,
                 "recent scratch does not fit the staging area");
   const size_t rbase = ((size_t)b * A.Hkv + g) * A.recent_cap;
   // Reads past the last row are clamped to it (never out of bounds, never a branch
@@ -420,7 +428,7 @@ decode_main_kernel(const DecodeArgs A) {
 
   __shared__ __attribute__((aligned(16))) float sm[G::FLOATS];
   // the four waves' value sums reuse the staging area once the tile loop is done
-  static_assert(4 * G::STAGE >= 4 * NREP * D, "merge buffer does not fit in the staging area");
+  static_assert(G::STAGE_ALL >= 4 * NREP * D, "merge buffer does not fit in the staging area");
   static_assert(VK != TQ_V_GROUP_SYM || VB == 2 || VB == 4, "group-scaled values are 2 or 4 bits");
   static_assert((kTile / G::SLOTS) % 2 == 0, "value steps go in token pairs");
 
@@ -442,7 +450,7 @@ decode_main_kernel(const DecodeArgs A) {
   float* s_kcent = sm + G::OFF_CENT;
   float* s_vcent = s_kcent + 16;
   if (threadIdx.x < 16) {
-    if constexpr (KK == TQ_K_LM_QJL) s_kcent[threadIdx.x] = (threadIdx.x < LK) ? A.kcent[threadIdx.x] : 0.f;
+    if constexpr (KK != TQ_K_AFFINE8) s_kcent[threadIdx.x] = (threadIdx.x < LK) ? A.kcent[threadIdx.x] : 0.f;
     if constexpr (VK == TQ_V_LM_ROT) s_vcent[threadIdx.x] = (threadIdx.x < LV) ? A.vcent[threadIdx.x] : 0.f;
   }
   const float* qa = sm + G::OFF_QA;
@@ -515,7 +523,8 @@ decode_main_kernel(const DecodeArgs A) {
     float s2[NREP];
     {
       const uint32_t* krow = st_k + lane * G::SK;
-      if constexpr (KK == TQ_K_LM_QJL) {
+      if constexpr (KK != TQ_K_AFFINE8) {
+        constexpr bool QJL = KK == TQ_K_LM_QJL;   // MSE-only keys: the codebook term alone
         const uint32_t aux = st_ak[lane * G::SAK];
         float alm[NREP], aqj[NREP];
 #pragma unroll
@@ -529,11 +538,13 @@ decode_main_kernel(const DecodeArgs A) {
           constexpr int CH = 8;
           constexpr int NCH = D / CH;
           const uint32_t* srow = st_s + lane * G::SS;
-          uint32_t kw[G::WK], sw[D / 32];
+          uint32_t kw[G::WK], sw[QJL ? D / 32 : 1];
 #pragma unroll
           for (int w = 0; w < G::WK; ++w) kw[w] = krow[w];
+          if constexpr (QJL) {
 #pragma unroll
-          for (int w = 0; w < D / 32; ++w) sw[w] = srow[w];
+            for (int w = 0; w < D / 32; ++w) sw[w] = srow[w];
+          }
           float cb[2][CH], qj[2][2][NE];
           float4 qv[2][NREP][2];
           auto fetch = [&](int c, int buf) {
@@ -542,11 +553,13 @@ decode_main_kernel(const DecodeArgs A) {
               const int j = c * CH + i;
               cb[buf][i] = s_kcent[(kw[j / G::KPER] >> (KB * (j % G::KPER))) & (LK - 1)];
             }
+            if constexpr (QJL) {
 #pragma unroll
-            for (int n = 0; n < 2; ++n) {
-              const int blk = 2 * c + n;
-              const uint32_t v = (sw[blk / 8] >> (4 * (blk % 8))) & 15u;
-              read_entry<NE>(tq + (blk * 16 + v) * NE, qj[buf][n]);
+              for (int n = 0; n < 2; ++n) {
+                const int blk = 2 * c + n;
+                const uint32_t v = (sw[blk / 8] >> (4 * (blk % 8))) & 15u;
+                read_entry<NE>(tq + (blk * 16 + v) * NE, qj[buf][n]);
+              }
             }
 #pragma unroll
             for (int h = 0; h < NREP; ++h) {
@@ -568,11 +581,11 @@ decode_main_kernel(const DecodeArgs A) {
               a = fmaf(q0.x, cc[0], a); a = fmaf(q0.y, cc[1], a); a = fmaf(q0.z, cc[2], a); a = fmaf(q0.w, cc[3], a);
               a = fmaf(q1.x, cc[4], a); a = fmaf(q1.y, cc[5], a); a = fmaf(q1.z, cc[6], a); a = fmaf(q1.w, cc[7], a);
               alm[h] = a;
-              aqj[h] += qj[cur][0][h] + qj[cur][1][h];
+              if constexpr (QJL) aqj[h] += qj[cur][0][h] + qj[cur][1][h];
             }
             __builtin_amdgcn_sched_barrier(0);
           }
-        } else {
+        } else if constexpr (QJL) {
           // n_rep > 4: reads go out in batches into separate registers, the next batch
           // before the current one is added, so their LDS latencies overlap
           const uint32_t* srow = st_s + lane * G::SS;
@@ -636,10 +649,16 @@ decode_main_kernel(const DecodeArgs A) {
             __builtin_amdgcn_sched_barrier(0);
           }
         }
-        const float nn = f16_to_f32(aux & 0xFFFFu);
-        const float gm = f16_to_f32(aux >> 16);
+        if constexpr (QJL) {
+          const float nn = f16_to_f32(aux & 0xFFFFu);
+          const float gm = f16_to_f32(aux >> 16);
 #pragma unroll
-        for (int h = 0; h < NREP; ++h) s2[h] = nn * fmaf(gm, aqj[h], alm[h]);
+          for (int h = 0; h < NREP; ++h) s2[h] = nn * fmaf(gm, aqj[h], alm[h]);
+        } else {
+          const float nn = __uint_as_float(aux);   // fp32 n
+#pragma unroll
+          for (int h = 0; h < NREP; ++h) s2[h] = nn * alm[h];
+        }
       } else {
         float ag[NREP];
 #pragma unroll
@@ -881,5 +900,14 @@ MainKernel find_main_lm2_d256(int nrep, int vk, int vb);
 MainKernel find_main_lm3_d256(int nrep, int vk, int vb);
 MainKernel find_main_lm4_d256(int nrep, int vk, int vb);
 MainKernel find_main_aff8_d256(int nrep, int vk, int vb);
+MainKernel find_main_lmm2_d64(int nrep, int vk, int vb);
+MainKernel find_main_lmm3_d64(int nrep, int vk, int vb);
+MainKernel find_main_lmm4_d64(int nrep, int vk, int vb);
+MainKernel find_main_lmm2_d128(int nrep, int vk, int vb);
+MainKernel find_main_lmm3_d128(int nrep, int vk, int vb);
+MainKernel find_main_lmm4_d128(int nrep, int vk, int vb);
+MainKernel find_main_lmm2_d256(int nrep, int vk, int vb);
+MainKernel find_main_lmm3_d256(int nrep, int vk, int vb);
+MainKernel find_main_lmm4_d256(int nrep, int vk, int vb);
 
 }  // namespace tq

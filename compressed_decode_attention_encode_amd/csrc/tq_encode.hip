@@ -582,7 +582,8 @@ hipError_t run_lm(const tq_layout& Lay, const tq_state& S, const void* x, int ba
   } else {
     hipLaunchKernelGGL((encode_lm_kernel<D, KB, DT, QJL>), dim3(grid), dim3(64 * D / lm_coords<D>()), 0, st,
                        (const uint16_t*)x, T, tps, n_tiles, dst, C.capacity, S.k_centroids, S.k_thresholds,
-                       S.k_signs, S.qjl, (uint32_t*)C.k_codes, (uint32_t*)C.k_signs, (uint32_t*)C.k_aux);
+                       S.k_signs, QJL ? S.qjl : (const uint16_t*)nullptr, (uint32_t*)C.k_codes,
+                       QJL ? (uint32_t*)C.k_signs : (uint32_t*)nullptr, (uint32_t*)C.k_aux);
   }
   return hipGetLastError();
 }
@@ -639,7 +640,7 @@ hipError_t run_affine(const tq_layout& Lay, const void* x, int batch, int T, int
 bool encode_k_compiled(const tq_layout& L) {
   const bool d_ok = L.head_dim == 64 || L.head_dim == 128 || L.head_dim == 256;
   const bool dt_ok = L.in_dtype == TQ_F16 || L.in_dtype == TQ_BF16;
-  if (L.k_kind == TQ_K_LM_QJL) return d_ok && dt_ok && L.k_bits >= 2 && L.k_bits <= 4;
+  if (L.k_kind == TQ_K_LM_QJL || L.k_kind == TQ_K_LM_MSE) return d_ok && dt_ok && L.k_bits >= 2 && L.k_bits <= 4;
   if (L.k_kind == TQ_K_AFFINE8) return d_ok && dt_ok && L.k_bits == 8;
   return false;
 }
@@ -658,6 +659,10 @@ hipError_t launch_encode_k(const tq_layout& L, const tq_state& S, const void* k,
   if (L.k_kind == TQ_K_LM_QJL) {
     TQ_D_SWITCH(L.head_dim, TQ_B_SWITCH(L.k_bits, TQ_DT_SWITCH(L.in_dtype,
         err = (run_lm<DD, BB, DTT, true>(L, S, k, batch, n_tokens, dst_offset, C, st, false));)))
+  } else if (L.k_kind == TQ_K_LM_MSE) {
+    // the rotated-LM kernel without the QJL stage (fp32 n in the aux plane), key state
+    TQ_D_SWITCH(L.head_dim, TQ_B_SWITCH(L.k_bits, TQ_DT_SWITCH(L.in_dtype,
+        err = (run_lm<DD, BB, DTT, false>(L, S, k, batch, n_tokens, dst_offset, C, st, false));)))
   } else {
     TQ_D_SWITCH(L.head_dim, TQ_DT_SWITCH(L.in_dtype,
         err = (run_affine<DD, DTT>(L, k, batch, n_tokens, dst_offset, C, st));))

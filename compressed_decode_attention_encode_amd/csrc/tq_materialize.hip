@@ -379,21 +379,22 @@ hipError_t launch_materialize_k(const tq_layout& L, const tq_state& S, const tq_
     return (out_dtype == TQ_BF16) ? run_elem_d<0, 8, TQ_BF16>(L.head_dim, codes, aux, slices, C.capacity, t0, n, o, st)
                                   : run_elem_d<0, 8, TQ_F16>(L.head_dim, codes, aux, slices, C.capacity, t0, n, o, st);
   }
+  const bool qjl = L.k_kind == TQ_K_LM_QJL;   // MSE-only keys: centroids and fp32 n alone
   LmArgs A{};
   A.codes = static_cast<const uint32_t*>(C.k_codes);
-  A.signs = static_cast<const uint32_t*>(C.k_signs);
+  A.signs = qjl ? static_cast<const uint32_t*>(C.k_signs) : nullptr;
   A.aux = static_cast<const uint32_t*>(C.k_aux);
   A.cent = S.k_centroids;
   A.rsign = S.k_signs;
-  A.S = S.qjl;
+  A.S = qjl ? S.qjl : nullptr;
   A.out = o;
   A.slices = slices;
   A.cap = C.capacity;
   A.t0 = t0;
   A.n = n;
   A.tiles_per_slice = ceil_div(n, 8192 / L.head_dim);
-  return (out_dtype == TQ_BF16) ? run_lm_any<TQ_BF16>(A, L.head_dim, L.k_bits, true, st)
-                                : run_lm_any<TQ_F16>(A, L.head_dim, L.k_bits, true, st);
+  return (out_dtype == TQ_BF16) ? run_lm_any<TQ_BF16>(A, L.head_dim, L.k_bits, qjl, st)
+                                : run_lm_any<TQ_F16>(A, L.head_dim, L.k_bits, qjl, st);
 }
 
 hipError_t launch_materialize_v(const tq_layout& L, const tq_state& S, const tq_cache& C, int t0, int n,

@@ -38,7 +38,7 @@ class Workload:
     head_dim: int
     n_ctx: int            # total cached tokens (compressed + recent buffer)
     n_recent: int         # last n_recent tokens stay exact in the recent buffer
-    k_kind: str           # "lm_qjl" | "affine8"
+    k_kind: str           # "lm_qjl" | "affine8" | "lm_mse"
     k_bits: int
     v_kind: str           # "group_sym" | "lm_rot"
     v_bits: int

@@ -53,6 +53,10 @@ typedef enum {
 typedef enum { TQ_F16 = 0, TQ_BF16 = 1 } tq_dtype;
 
 /* Key encodings.
+ * TQ_K_LM_MSE  (vLLM guide section 2 steps 1-2 only: the MSE-optimal codes without the
+ *   QJL residual sketch; vLLM guide, MSE score kernel): n = |k| stored fp32, y = Pi k/n,
+ *   idx_j = #{i : t_i < y_j} (k_bits in {2,3,4}); decoded key n Pi^T c[idx].  Its
+ *   scores are the codebook term only (a biased, shrunk inner-product estimate).
  * TQ_K_LM_QJL  (vLLM guide section 2 steps 1-3): n = |k|, y = Pi k/n with the
  *   randomised Hadamard rotation Pi = H diag(s)/sqrt(d), idx_j = #{i : t_i < y_j}
  *   (Lloyd-Max, k_bits in {2,3,4}), r = y - c[idx], gamma = |r|, one QJL bit per
@@ -60,7 +64,7 @@ typedef enum { TQ_F16 = 0, TQ_BF16 = 1 } tq_dtype;
  * TQ_K_AFFINE8 (vllm-metal guide, quantisation principle table: per-block affine,
  *   no rotation): per 32-block a = fp16((max-min)/255), m = fp16(min),
  *   q = clamp(rne((k - m)/a), 0, 255)  (q = 0 where a = 0). k_bits must be 8.      */
-typedef enum { TQ_K_LM_QJL = 0, TQ_K_AFFINE8 = 1 } tq_kkind;
+typedef enum { TQ_K_LM_QJL = 0, TQ_K_AFFINE8 = 1, TQ_K_LM_MSE = 2 } tq_kkind;
 
 /* Value encodings.
  * TQ_V_GROUP_SYM (vLLM guide section 2 step 4, symmetric group-of-32 scaling):
@@ -87,10 +91,10 @@ typedef struct {
 
 /* Per-layer method state (device pointers, read-only).  Shared by every head and
  * token of the layer: one key rotation, one value rotation, one QJL matrix.
- *   k_centroids  float[2^k_bits], ascending       (TQ_K_LM_QJL; else may be NULL)
+ *   k_centroids  float[2^k_bits], ascending       (TQ_K_LM_QJL / LM_MSE; else may be NULL)
  *   k_thresholds float[2^k_bits - 1]              (midpoints, from tq_make_codebook)
  *   v_centroids, v_thresholds                     (TQ_V_LM_ROT; else may be NULL)
- *   k_signs      uint32[d/32]: bit j%32 of word j/32 set <=> s_j = -1  (TQ_K_LM_QJL)
+ *   k_signs      uint32[d/32]: bit j%32 of word j/32 set <=> s_j = -1  (TQ_K_LM_QJL / LM_MSE)
  *   v_signs      uint32[d/32], same convention     (TQ_V_LM_ROT)
  *   qjl          fp16 bits [d*d], row-major S, S[i*d + j] (TQ_K_LM_QJL), 16-byte
  *                aligned: the Gaussian sketch is stored at fp16 resolution (its
@@ -113,7 +117,8 @@ typedef struct {
  *                    ten 3-bit codes per uint32; vLLM guide: four 2-bit codes per byte)
  *            AFFINE8: uint8[d], byte j = code j
  *   k_signs  LM_QJL: uint32[d/32], bit j%32 of word j/32 = QJL bit j   (else unused)
- *   k_aux    LM_QJL: fp16[2] = (n, gamma);  AFFINE8: fp16[d/32][2] = (a, m) per block
+ *   k_aux    LM_QJL: fp16[2] = (n, gamma);  AFFINE8: fp16[d/32][2] = (a, m) per block;
+ *            LM_MSE: fp32 n  (LM_MSE codes are packed like LM_QJL codes)
  *   v_codes  uint32[W], same packing as LM codes (GROUP_SYM v_bits 2/4, LM_ROT 2/3/4)
  *   v_aux    GROUP_SYM: fp16[d/32] scales Delta;  LM_ROT: fp32 n
  * tq_cache_plane_bytes gives each plane's size.                                        */
@@ -177,6 +182,7 @@ size_t tq_decode_workspace_bytes(const tq_layout* layout, int batch, int max_com
  * domain then one inverse butterfly, GQA n_rep without replicating KV; vLLM guide
  * section 5: exact recent buffer).  For q-head h of batch b, kv-head g = h / n_rep:
  *   LM_QJL keys:  s_t = n_t/sqrt(d) (<Pi q, c[idx_t]> + gamma_t sqrt(pi/2)/d <S Pi q, sigma_t>)
+ *   LM_MSE keys:  s_t = n_t/sqrt(d) <Pi q, c[idx_t]>
  *   AFFINE8 keys: s_t = <q, m + a q8_t>/sqrt(d);  recent keys: s_r = <q, k_r>/sqrt(d)
  *   out = softmax-weighted sum of decoded values over all n_compressed + n_recent
  *   tokens (GROUP_SYM: Delta (idx-(L-1)/2); LM_ROT: n Pi_v^T c[idx]; recent: v_r).
@@ -201,6 +207,7 @@ int tq_decode_attn(const tq_layout* layout, const tq_state* state, const void* q
  * guide, section 7: the hybrid path dequantises the whole history).  Row t of slice
  * (b, g) is exactly the decoded vector the decode attention uses:
  *   LM_QJL keys:    k = n Pi^T (c[idx] + gamma sqrt(pi/2)/d S^T sigma)
+ *   LM_MSE keys:    k = n Pi^T c[idx]
  *   AFFINE8 keys:   k_j = m + a q8_j
  *   GROUP_SYM vals: v_j = Delta (idx_j - (L-1)/2)
  *   LM_ROT values:  v = n Pi_v^T c[idx]

@@ -21,6 +21,11 @@ def encode_k(lay, k: np.ndarray, state: dict) -> dict:
         aux = np.stack([e["n16"].view(np.uint16), e["g16"].view(np.uint16)], axis=-1)
         return {"k_codes": L.pack_codes(e["idx"], lay.k_bits), "k_signs": L.pack_signs(e["qjl"]),
                 "k_aux": aux, "near_idx": e["near_idx"], "near_qjl": e["near_qjl"], "enc": e}
+    if lay.k_kind == "lm_mse":
+        c, t = state["cb_k"]
+        e = enc.encode_k_lm_mse(k, state["signs_k"], c, t)
+        return {"k_codes": L.pack_codes(e["idx"], lay.k_bits), "k_aux": e["n32"],
+                "near_idx": e["near_idx"], "enc": e}
     if lay.k_kind == "affine8":
         e = enc.encode_k_affine8(k)
         aux = np.stack([e["a16"].view(np.uint16), e["m16"].view(np.uint16)], axis=-1)
@@ -51,6 +56,9 @@ def read_k(lay, planes: dict, state: dict) -> dict:
                 "sigma": np.where(L.unpack_signs(planes["k_signs"], d), 1.0, -1.0),
                 "n": aux[..., 0].view(np.float16).astype(np.float64),
                 "gamma": aux[..., 1].view(np.float16).astype(np.float64)}
+    if lay.k_kind == "lm_mse":
+        return {"idx": L.unpack_codes(planes["k_codes"], lay.k_bits, d),
+                "n": np.asarray(planes["k_aux"], dtype=np.float32).astype(np.float64)}
     aux = np.asarray(planes["k_aux"], dtype=np.uint16)
     return {"q8": L.unpack_codes(planes["k_codes"], 8, d),
             "a": aux[..., 0].view(np.float16).astype(np.float64),
@@ -69,7 +77,7 @@ def make_state(lay, signs_k, signs_v, S) -> dict:
     """Oracle state: its own codebooks plus the drawn random numbers (signs, QJL matrix)."""
     from .codebook import codebook_f32
     st = {"signs_k": np.asarray(signs_k), "signs_v": np.asarray(signs_v), "S": np.asarray(S)}
-    if lay.k_kind == "lm_qjl":
+    if lay.k_kind in ("lm_qjl", "lm_mse"):
         st["cb_k"] = codebook_f32(lay.head_dim, lay.k_bits)
     if lay.v_kind == "lm_rot":
         st["cb_v"] = codebook_f32(lay.head_dim, lay.v_bits)

@@ -46,6 +46,11 @@ def _scores_compressed(lay, q: np.ndarray, kd: dict, state: dict) -> np.ndarray:
         lm = c[kd["idx"]] @ q_r
         qjl = kd["sigma"] @ q_s
         return kd["n"] / math.sqrt(d) * (lm + kd["gamma"] * math.sqrt(math.pi / 2.0) / d * qjl)
+    if lay.k_kind == "lm_mse":
+        # MSE-only keys: the codebook term alone, n / sqrt(d) <Pi q, c[idx]>
+        c = state["cb_k"][0].astype(np.float64)
+        q_r = rotation_matrix(state["signs_k"]) @ q
+        return kd["n"] / math.sqrt(d) * (c[kd["idx"]] @ q_r)
     # affine 8-bit keys: k_hat = m + a * q8 per 32-block
     k_hat = _affine_k_hat(kd, d)
     return k_hat @ q / math.sqrt(d)
@@ -113,6 +118,8 @@ def reconstruct_k(lay, kd: dict, state: dict) -> np.ndarray:
     if lay.k_kind == "affine8":
         return _affine_k_hat(kd, d)
     c = state["cb_k"][0].astype(np.float64)
+    if lay.k_kind == "lm_mse":
+        return kd["n"][:, None] * (c[kd["idx"]] @ rotation_matrix(state["signs_k"]))
     S = state["S"].astype(np.float64)
     rot = c[kd["idx"]] + kd["gamma"][:, None] * math.sqrt(math.pi / 2.0) / d * (kd["sigma"] @ S)
     return kd["n"][:, None] * (rot @ rotation_matrix(state["signs_k"]))

@@ -133,6 +133,14 @@ def encode_k_affine8(k: np.ndarray) -> dict:
     return {"q8": q.reshape(k.shape), "a16": a16, "m16": m16, "near_idx": near.reshape(k.shape)}
 
 
+def encode_k_lm_mse(k: np.ndarray, signs: np.ndarray,
+                    centroids32: np.ndarray, thresholds32: np.ndarray) -> dict:
+    """MSE-only keys (vLLM guide section 2, steps 1-2 without the QJL residual step): the
+    norm, the rotation and the Lloyd-Max decision, exactly the steps of the rotated values
+    below, with the key rotation and codebook."""
+    return encode_v_lm_rot(k, signs, centroids32, thresholds32)
+
+
 def encode_v_lm_rot(v: np.ndarray, signs: np.ndarray,
                     centroids32: np.ndarray, thresholds32: np.ndarray) -> dict:
     n = np.sqrt(np.sum(v * v, axis=-1))

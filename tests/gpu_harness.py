@@ -47,6 +47,8 @@ def plane_shapes(wl, batch, cap):
     if wl.k_kind == "lm_qjl":
         s["k_signs"] = (np.uint32, (batch, wl.n_kv_heads, cap, d // 32))
         s["k_aux"] = (np.uint16, (batch, wl.n_kv_heads, cap, 2))
+    elif wl.k_kind == "lm_mse":
+        s["k_aux"] = (np.float32, (batch, wl.n_kv_heads, cap))
     else:
         s["k_aux"] = (np.uint16, (batch, wl.n_kv_heads, cap, d // 32, 2))
     if wl.v_kind == "group_sym":
@@ -189,6 +191,14 @@ def compare_encode(wl, gpu: dict, ek: dict, ev: dict, rows=slice(None)) -> dict:
         st["k_aux_mismatch"] = int(aux_bad.sum())
         # whole rows with no excluded element must be identical words (padding bits included)
         st["k_word_mismatch"] = int(((g["k_codes"] != ek["k_codes"]).any(axis=-1) & row_ok).sum())
+    elif wl.k_kind == "lm_mse":
+        idx = OL.unpack_codes(g["k_codes"], wl.k_bits, d)
+        near = ek["near_idx"]
+        diff = idx != ek["enc"]["idx"]
+        st["k_idx_mismatch"] = int((diff & ~near).sum())
+        st["k_idx_excluded"] = int(near.sum())
+        st["k_idx_excluded_differ"] = int((diff & near).sum())
+        st["k_aux_mismatch"] = int((g["k_aux"].view(np.uint32) != ek["k_aux"].view(np.uint32)).sum())
     else:
         q8 = OL.unpack_codes(g["k_codes"], 8, d)
         near = ek["near_idx"]

@@ -181,6 +181,21 @@ def test_materialize_rejects_bad_arguments():
     assert e.value.status == tq.TQ_ERR_UNSUPPORTED
 
 
+def test_mse_only_keys_arguments():
+    """MSE-only LM keys: k_bits 2..4, no QJL matrix or sign plane needed, key rotation needed."""
+    L = _layout(k_kind="lm_mse", k_bits=5)
+    with pytest.raises(tq.TQError) as e:
+        tq.tq_encode(L, _state(), FAKE, None, 1, 16, 0, _cache())
+    assert e.value.status == tq.TQ_ERR_UNSUPPORTED
+    L = _layout(k_kind="lm_mse", k_bits=3)
+    sizes = tq.tq_cache_plane_bytes(L, 1, 100)
+    assert sizes[1] == 0 and sizes[2] == 4 * 100 * L.n_kv_heads      # no sign plane; fp32 n per row
+    with pytest.raises(tq.TQError) as e:                               # no key rotation signs
+        tq.tq_encode(L, tq.tq_state(FAKE, FAKE, None, None, None, None, None), FAKE, None, 1, 16, 0,
+                     tq.tq_cache(FAKE, None, FAKE, FAKE, FAKE, 1, 256))
+    assert e.value.status == tq.TQ_ERR_INVALID
+
+
 def test_workspace_bound_covers_every_length():
     L = _layout(head_dim=64, n_q_heads=32, n_kv_heads=8)
     import ctypes

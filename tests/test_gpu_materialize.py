@@ -154,6 +154,9 @@ VARIANTS = [
     (64, "affine8", 8, "lm_rot", 4, 2, 2, "bf16"),
     (256, "affine8", 8, "lm_rot", 4, 4, 2, "f16"),
     (256, "affine8", 8, "lm_rot", 2, 2, 1, "f16"),
+    (64, "lm_mse", 3, "lm_rot", 3, 4, 2, "f16"),
+    (128, "lm_mse", 4, "group_sym", 4, 4, 2, "bf16"),
+    (256, "lm_mse", 2, "lm_rot", 4, 2, 1, "f16"),
 ]
 
 

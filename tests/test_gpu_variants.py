@@ -1,7 +1,7 @@
 """GPU parity over the compiled variants the benchmark workloads do not reach.
 
-Every kernel family (2/3/4-bit Lloyd-Max + QJL keys, per-block affine keys, group-32
-and rotated Lloyd-Max values, head_dim 64/128/256, n_rep 1..8, fp16/bf16 inputs) is
+Every kernel family (2/3/4-bit Lloyd-Max + QJL keys, MSE-only Lloyd-Max keys, per-block
+affine keys, group-32 and rotated Lloyd-Max values, head_dim 64/128/256, n_rep 1..8, fp16/bf16 inputs) is
 encoded and decoded at a small, ragged size against the CPU oracle, and degenerate
 vectors (all zero, constant, a single non-zero element, signed zeros, subnormals) go
 through both sides.
@@ -41,6 +41,13 @@ VARIANTS = [
     (64, "affine8", 8, "lm_rot", 4, 2, 2, "bf16", 200, 20),
     (128, "affine8", 8, "lm_rot", 2, 14, 2, "f16", 222, 100),
     (256, "affine8", 8, "lm_rot", 4, 6, 3, "bf16", 170, 9),
+    # MSE-only keys (no QJL term) with rotated LM and group values
+    (64, "lm_mse", 3, "lm_rot", 3, 4, 2, "f16", 300, 17),
+    (64, "lm_mse", 2, "group_sym", 2, 16, 2, "bf16", 260, 0),
+    (128, "lm_mse", 4, "lm_rot", 4, 8, 1, "f16", 333, 64),
+    (128, "lm_mse", 3, "group_sym", 4, 6, 2, "bf16", 222, 5),
+    (256, "lm_mse", 4, "lm_rot", 2, 10, 2, "f16", 190, 31),
+    (256, "lm_mse", 2, "group_sym", 2, 3, 3, "f16", 150, 0),
 ]
 
 

@@ -257,6 +257,37 @@ def test_qjl_sign_identity_and_unbiased_score():
     assert abs(lm_only.mean() - shrink * truth) < 4.5 * se0 + 1e-3 * truth
 
 
+def test_mse_only_keys_score_is_the_shrunk_inner_product():
+    """MSE-only keys (no QJL residual): over independent rotations the score of the whole
+    oracle chain (encode, pack, read back, score) averages (1 - d D) <q, k>/sqrt(d), D the
+    per-coordinate distortion of the Lloyd-Max codebook: E[<y, c[idx]>] = 1 - d D for a
+    unit vector, and the rotation makes the error isotropic."""
+    d = 64
+    lay = Lay(d, 1, 1, "lm_mse", 3, "group_sym", 2)
+    rng = np.random.default_rng(11)
+    k = rng.standard_normal(d)
+    q = 0.8 * k + 0.6 * rng.standard_normal(d)
+    truth = float(q @ k) / math.sqrt(d)
+    c32, t32 = cb.codebook_f32(d, 3)
+    M = 4096
+    got = []
+    for m in range(M):
+        s = np.where(rng.integers(0, 2, d) == 1, -1, 1).astype(np.int8)
+        st = {"signs_k": s, "cb_k": (c32, t32)}
+        planes = C.encode_k(lay, k[None], st)
+        kd = C.read_k(lay, {"k_codes": planes["k_codes"], "k_aux": planes["k_aux"]}, st)
+        got.append(D._scores_compressed(lay, q, kd, st)[0])
+    got = np.array(got)
+    se = got.std() / math.sqrt(M)
+    shrink = 1.0 - d * cb.distortion(cb.lloyd_max(d, 3)[0], d)
+    assert truth - got.mean() > 4.5 * se                       # biased toward zero
+    assert abs(got.mean() - shrink * truth) < 4.5 * se + 1e-3 * truth
+    # and the decoded key is n Pi^T c[idx]: rotating it back gives n c[idx] exactly
+    khat = D.reconstruct_k(lay, kd, st)[0]
+    y = R.rotation_matrix(s) @ khat
+    assert np.max(np.abs(y - kd["n"][0] * c32[kd["idx"][0]])) < 1e-12
+
+
 # --------------------------------------------------------------------------- encoders: special cases
 def test_group_sym_grid_and_ties_by_hand():
     # 2-bit, amax 0.375 -> Delta = 0.25 exactly; levels Delta*(idx-1.5) reconstruct exactly
@@ -330,7 +361,8 @@ def test_zero_residual_when_unit_vector_lands_on_centroids():
 
 # --------------------------------------------------------------------------- decode
 KINDS = [("lm_qjl", 3, "group_sym", 2), ("lm_qjl", 4, "group_sym", 4), ("lm_qjl", 2, "group_sym", 2),
-         ("affine8", 8, "lm_rot", 3), ("affine8", 8, "lm_rot", 2)]
+         ("affine8", 8, "lm_rot", 3), ("affine8", 8, "lm_rot", 2),
+         ("lm_mse", 3, "lm_rot", 3), ("lm_mse", 4, "group_sym", 4), ("lm_mse", 2, "lm_rot", 2)]
 
 
 @pytest.mark.parametrize("kind", KINDS)
