@@ -133,8 +133,9 @@ def bench_materialize(tq, lay, state, caches, wl, stream, steps: int, warmup: in
     ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
     gb = alg / (ms * 1e-3) / 1e9
     res = {"us": ms * 1e3, "gbps": gb, "algorithmic_bytes": alg, "steps": steps,
-           "kernels": ("materialize_lm_kernel (keys, QJL term on fp16 matrix cores)" if wl.k_kind == "lm_qjl"
-                       else "materialize_elem_kernel (keys)") + " + " +
+           "kernels": {"lm_qjl": "materialize_lm_kernel (keys, QJL term on fp16 matrix cores)",
+                       "lm_mse": "materialize_lm_kernel (keys)",
+                       "affine8": "materialize_elem_kernel (keys)"}[wl.k_kind] + " + " +
                       ("materialize_elem_kernel (values)" if wl.v_kind == "group_sym"
                        else "materialize_lm_kernel (values)"),
            "roofline": {"bound": "hbm", "achieved": gb, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -319,7 +320,7 @@ def main():
 
     digest = source_digest()
     groups = {
-        "encode_k": {"kernel": "encode_lm_kernel (keys)" if wl.k_kind == "lm_qjl" else "encode_affine8_kernel",
+        "encode_k": {"kernel": "encode_lm_kernel (keys)" if wl.k_kind != "affine8" else "encode_affine8_kernel",
                      "ms": t_ek},
         "encode_v": {"kernel": "encode_group_kernel" if wl.v_kind == "group_sym" else "encode_lm_kernel (values)",
                      "ms": t_ev},

@@ -84,6 +84,15 @@ WORKLOADS = {
     "qwen32b_h40x8_d256_b4_t128k": Workload(
         "qwen32b_h40x8_d256_b4_t128k", 106, 4, 40, 8, 256, 131072, 0,
         "lm_qjl", 4, "group_sym", 4, "bf16", "f16"),
+    # the pages' other modes on the same geometries: MSE-only 3-bit keys (no QJL sketch) on
+    # the Llama-like layer, and K8+V4 (per-block affine 8-bit keys, rotated 4-bit Lloyd-Max
+    # values; the MLX page's mixed mode, quoted on a Qwen2.5-7B at 32K)
+    "llama1b_mse3_h32x8_d64_t32k": Workload(
+        "llama1b_mse3_h32x8_d64_t32k", 107, 1, 32, 8, 64, 32768, 128,
+        "lm_mse", 3, "group_sym", 2, "f16", "f16", "const10", 4),
+    "qwen7b_k8v4_h28x4_d128_b16_t32k": Workload(
+        "qwen7b_k8v4_h28x4_d128_b16_t32k", 108, 16, 28, 4, 128, 32768, 128,
+        "affine8", 8, "lm_rot", 4, "bf16", "f16", "studentt3x10", 4, flush_tokens=128),
 }
 
 # The workload the benchmark line is quoted on (Llama-3.2-1B-like layer, 32K context).
