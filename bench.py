@@ -135,7 +135,8 @@ def bench_materialize(tq, lay, state, caches, wl, stream, steps: int, warmup: in
     res = {"us": ms * 1e3, "gbps": gb, "algorithmic_bytes": alg, "steps": steps,
            "kernels": {"lm_qjl": "materialize_lm_kernel (keys, QJL term on fp16 matrix cores)",
                        "lm_mse": "materialize_lm_kernel (keys)",
-                       "affine8": "materialize_elem_kernel (keys)"}[wl.k_kind] + " + " +
+                       "affine8": "materialize_elem_kernel (keys)",
+                       "f16": "materialize_elem_kernel (16-bit keys, copy)"}[wl.k_kind] + " + " +
                       ("materialize_elem_kernel (values)" if wl.v_kind == "group_sym"
                        else "materialize_lm_kernel (values)"),
            "roofline": {"bound": "hbm", "achieved": gb, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -320,7 +321,8 @@ def main():
 
     digest = source_digest()
     groups = {
-        "encode_k": {"kernel": "encode_lm_kernel (keys)" if wl.k_kind != "affine8" else "encode_affine8_kernel",
+        "encode_k": {"kernel": {"lm_qjl": "encode_lm_kernel (keys)", "lm_mse": "encode_lm_kernel (keys)",
+                                "affine8": "encode_affine8_kernel", "f16": "encode_copy16_kernel"}[wl.k_kind],
                      "ms": t_ek},
         "encode_v": {"kernel": "encode_group_kernel" if wl.v_kind == "group_sym" else "encode_lm_kernel (values)",
                      "ms": t_ev},

@@ -27,9 +27,16 @@ int lm_words(int d, int bits) {
   const int per = (bits == 3) ? 10 : 32 / bits;
   return (d + per - 1) / per;
 }
-int k_code_words(const tq_layout& L) { return L.k_kind == TQ_K_AFFINE8 ? L.head_dim / 4 : lm_words(L.head_dim, L.k_bits); }
+int k_code_words(const tq_layout& L) {
+  if (L.k_kind == TQ_K_AFFINE8) return L.head_dim / 4;
+  if (L.k_kind == TQ_K_F16) return L.head_dim / 2;
+  return lm_words(L.head_dim, L.k_bits);
+}
 int k_sign_words(const tq_layout& L) { return L.k_kind == TQ_K_LM_QJL ? L.head_dim / 32 : 0; }
-int k_aux_words(const tq_layout& L) { return L.k_kind == TQ_K_AFFINE8 ? L.head_dim / 32 : 1; }
+int k_aux_words(const tq_layout& L) {
+  if (L.k_kind == TQ_K_AFFINE8) return L.head_dim / 32;
+  return L.k_kind == TQ_K_F16 ? 0 : 1;
+}
 int v_code_words(const tq_layout& L) { return lm_words(L.head_dim, L.v_bits); }
 int v_aux_bytes(const tq_layout& L) { return L.v_kind == TQ_V_GROUP_SYM ? (L.head_dim / 32) * 2 : 4; }
 
@@ -67,6 +74,8 @@ int check_layout(const tq_layout* L) {
     if (L->k_bits < 2 || L->k_bits > 4) return fail(TQ_ERR_UNSUPPORTED, "LM keys need k_bits 2..4, got %d", L->k_bits);
   } else if (L->k_kind == TQ_K_AFFINE8) {
     if (L->k_bits != 8) return fail(TQ_ERR_UNSUPPORTED, "affine keys need k_bits 8, got %d", L->k_bits);
+  } else if (L->k_kind == TQ_K_F16) {
+    if (L->k_bits != 16) return fail(TQ_ERR_UNSUPPORTED, "16-bit keys need k_bits 16, got %d", L->k_bits);
   } else {
     return fail(TQ_ERR_UNSUPPORTED, "unknown k_kind %d", L->k_kind);
   }
@@ -88,7 +97,8 @@ int check_cache(const tq_cache* C, bool need_k, bool need_v, const tq_layout* L)
   if (C->batch <= 0 || C->capacity <= 0)
     return fail(TQ_ERR_INVALID, "cache batch %d / capacity %d must be positive", C->batch, C->capacity);
   if (need_k) {
-    if (!C->k_codes || !C->k_aux || !aligned16(C->k_codes) || !aligned16(C->k_aux))
+    const bool aux = L->k_kind != TQ_K_F16;   // 16-bit keys have no aux plane
+    if (!C->k_codes || !aligned16(C->k_codes) || (aux && (!C->k_aux || !aligned16(C->k_aux))))
       return fail(TQ_ERR_INVALID, "key planes must be non-NULL and 16-byte aligned");
     if (L->k_kind == TQ_K_LM_QJL && (!C->k_signs || !aligned16(C->k_signs)))
       return fail(TQ_ERR_INVALID, "k_signs plane must be non-NULL and 16-byte aligned");

@@ -224,6 +224,12 @@ MainKernel find_main(const tq_layout& L) {
     }
   }
   if (L.k_kind == TQ_K_AFFINE8 && L.k_bits == 8) { TQ_BY_D(find_main_aff8) }
+  // 16-bit keys: d = 64 and 128 (a d = 256 row tile, 512 B per token, exceeds the LDS of a group)
+  if (L.k_kind == TQ_K_F16 && L.k_bits == 16) {
+    if (d == 64) return find_main_f16_d64(nrep, vk, vb);
+    if (d == 128) return find_main_f16_d128(nrep, vk, vb);
+    return MainKernel{nullptr, nullptr};
+  }
 #undef TQ_BY_D
   return MainKernel{nullptr, nullptr};
 }

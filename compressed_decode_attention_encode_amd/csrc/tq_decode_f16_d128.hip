@@ -1,0 +1,33 @@
+// Compiled instantiations of the decode main kernel: 16-bit keys (V-only mode), head_dim
+// 128, n_rep 1..8, group-32 symmetric 2/4-bit values and rotated Lloyd-Max 2/3/4-bit values.
+#include "tq_decode_main.h"
+
+namespace tq {
+
+namespace {
+template <int KK, int KB, int VK, int VB>
+MainKernel pick(int nrep) {
+  switch (nrep) {
+    case 1: return main_kernel<128, 1, KK, KB, VK, VB>();
+    case 2: return main_kernel<128, 2, KK, KB, VK, VB>();
+    case 3: return main_kernel<128, 3, KK, KB, VK, VB>();
+    case 4: return main_kernel<128, 4, KK, KB, VK, VB>();
+    case 5: return main_kernel<128, 5, KK, KB, VK, VB>();
+    case 6: return main_kernel<128, 6, KK, KB, VK, VB>();
+    case 7: return main_kernel<128, 7, KK, KB, VK, VB>();
+    case 8: return main_kernel<128, 8, KK, KB, VK, VB>();
+    default: return MainKernel{nullptr, nullptr};
+  }
+}
+}  // namespace
+
+MainKernel find_main_f16_d128(int nrep, int vk, int vb) {
+  if (vk == TQ_V_GROUP_SYM && vb == 2) return pick<TQ_K_F16, 16, TQ_V_GROUP_SYM, 2>(nrep);
+  if (vk == TQ_V_GROUP_SYM && vb == 4) return pick<TQ_K_F16, 16, TQ_V_GROUP_SYM, 4>(nrep);
+  if (vk == TQ_V_LM_ROT && vb == 2) return pick<TQ_K_F16, 16, TQ_V_LM_ROT, 2>(nrep);
+  if (vk == TQ_V_LM_ROT && vb == 3) return pick<TQ_K_F16, 16, TQ_V_LM_ROT, 3>(nrep);
+  if (vk == TQ_V_LM_ROT && vb == 4) return pick<TQ_K_F16, 16, TQ_V_LM_ROT, 4>(nrep);
+  return MainKernel{nullptr, nullptr};
+}
+
+}  // namespace tq

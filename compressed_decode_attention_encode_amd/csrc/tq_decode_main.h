@@ -34,6 +34,8 @@
 // without device-wide cache flushes.
 #pragma once
 
+#include <type_traits>
+
 #include "tq_device.h"
 #include "tq_internal.h"
 
@@ -47,7 +49,7 @@ struct DecodeGeom {
   static constexpr int KPER = (KB == 3) ? 10 : (KK == TQ_K_AFFINE8 ? 4 : 32 / KB);
   static constexpr int WK = (KK == TQ_K_AFFINE8) ? D / 4 : (D + KPER - 1) / KPER;
   static constexpr int WS = (KK == TQ_K_LM_QJL) ? D / 32 : 0;
-  static constexpr int WAK = (KK == TQ_K_AFFINE8) ? D / 32 : 1;
+  static constexpr int WAK = (KK == TQ_K_AFFINE8) ? D / 32 : (KK == TQ_K_F16 ? 0 : 1);
   static constexpr int VPER = (VB == 3) ? 10 : 32 / VB;
   static constexpr int WV = (D + VPER - 1) / VPER;
   static constexpr int WAV = (VK == TQ_V_GROUP_SYM) ? D / 64 : 1;
@@ -60,7 +62,7 @@ struct DecodeGeom {
   static constexpr int PS = D + 4;                                  // partial stride (floats)
   // lookup tables
   static constexpr int NE = NREP == 1 ? 1 : (NREP == 2 ? 2 : (NREP <= 4 ? 4 : 8));   // floats per entry
-  static constexpr int LK = (KK == TQ_K_AFFINE8) ? 1 : (1 << KB);
+  static constexpr int LK = (KK == TQ_K_AFFINE8 || KK == TQ_K_F16) ? 1 : (1 << KB);
   static constexpr int TQ_FLOATS = (KK == TQ_K_LM_QJL) ? (D / 4) * 16 * NE : 0;
   // LDS carve-out (floats): queries, second query block (QJL projection / affine block
   // sums), QJL table, staging, softmax weights, codebooks, merge scalars
@@ -181,7 +183,7 @@ __device__ void prepare_queries(const DecodeArgs& A, int b, int g, float* sm) {
   float* qb = sm + G::OFF_QB;
   const float scale = kLog2e * rsqrtf((float)D);
   const uint16_t* qsrc = A.q + (size_t)(b * A.Hq + g * NREP) * D;
-  if constexpr (KK != TQ_K_AFFINE8) {
+  if constexpr (KK == TQ_K_LM_QJL || KK == TQ_K_LM_MSE) {
     constexpr bool QJL = KK == TQ_K_LM_QJL;
     // this thread's slice of S (row i, columns part*KL ..): its first reads go out first
     constexpr int KS = (256 / D) > 0 ? 256 / D : 1;
@@ -295,7 +297,7 @@ __device__ void prepare_queries(const DecodeArgs& A, int b, int g, float* sm) {
   } else {
     for (int i = tid; i < NREP * D; i += 256) qa[i] = bits16_to_f32(qsrc[i], A.q_bf16) * scale;
     __syncthreads();
-    for (int i = tid; i < NREP * (D / 32); i += 256) {
+    for (int i = tid; KK == TQ_K_AFFINE8 && i < NREP * (D / 32); i += 256) {
       const int h = i / (D / 32), blk = i % (D / 32);
       float s = 0.f;
       for (int k = 0; k < 32; ++k) s += qa[h * D + 32 * blk + k];
@@ -450,7 +452,8 @@ decode_main_kernel(const DecodeArgs A) {
   float* s_kcent = sm + G::OFF_CENT;
   float* s_vcent = s_kcent + 16;
   if (threadIdx.x < 16) {
-    if constexpr (KK != TQ_K_AFFINE8) s_kcent[threadIdx.x] = (threadIdx.x < LK) ? A.kcent[threadIdx.x] : 0.f;
+    if constexpr (KK == TQ_K_LM_QJL || KK == TQ_K_LM_MSE)
+      s_kcent[threadIdx.x] = (threadIdx.x < LK) ? A.kcent[threadIdx.x] : 0.f;
     if constexpr (VK == TQ_V_LM_ROT) s_vcent[threadIdx.x] = (threadIdx.x < LV) ? A.vcent[threadIdx.x] : 0.f;
   }
   const float* qa = sm + G::OFF_QA;
@@ -523,7 +526,40 @@ decode_main_kernel(const DecodeArgs A) {
     float s2[NREP];
     {
       const uint32_t* krow = st_k + lane * G::SK;
-      if constexpr (KK != TQ_K_AFFINE8) {
+      if constexpr (KK == TQ_K_F16) {
+        // 16-bit keys (V-only mode): <q, k> over the stored row, 8 dimensions (4 words)
+        // per trip, keys in the query's storage type
+#pragma unroll
+        for (int h = 0; h < NREP; ++h) s2[h] = 0.f;
+        auto score_rows = [&](auto bf) {
+#pragma unroll 1
+          for (int j0 = 0; j0 < D; j0 += 8) {
+            const uint32_t w[4] = {krow[j0 / 2], krow[j0 / 2 + 1], krow[j0 / 2 + 2], krow[j0 / 2 + 3]};
+            float kv[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              if constexpr (decltype(bf)::value) {
+                kv[2 * i] = __uint_as_float(w[i] << 16);
+                kv[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+              } else {
+                kv[2 * i] = f16_to_f32(w[i] & 0xFFFFu);
+                kv[2 * i + 1] = f16_to_f32(w[i] >> 16);
+              }
+            }
+#pragma unroll
+            for (int h = 0; h < NREP; ++h) {
+              const float4 q0 = *reinterpret_cast<const float4*>(qa + h * D + j0);
+              const float4 q1 = *reinterpret_cast<const float4*>(qa + h * D + j0 + 4);
+              float a = s2[h];
+              a = fmaf(q0.x, kv[0], a); a = fmaf(q0.y, kv[1], a); a = fmaf(q0.z, kv[2], a); a = fmaf(q0.w, kv[3], a);
+              a = fmaf(q1.x, kv[4], a); a = fmaf(q1.y, kv[5], a); a = fmaf(q1.z, kv[6], a); a = fmaf(q1.w, kv[7], a);
+              s2[h] = a;
+            }
+          }
+        };
+        if (A.q_bf16) score_rows(std::true_type{});
+        else score_rows(std::false_type{});
+      } else if constexpr (KK != TQ_K_AFFINE8) {
         constexpr bool QJL = KK == TQ_K_LM_QJL;   // MSE-only keys: the codebook term alone
         const uint32_t aux = st_ak[lane * G::SAK];
         float alm[NREP], aqj[NREP];
@@ -909,5 +945,7 @@ MainKernel find_main_lmm4_d128(int nrep, int vk, int vb);
 MainKernel find_main_lmm2_d256(int nrep, int vk, int vb);
 MainKernel find_main_lmm3_d256(int nrep, int vk, int vb);
 MainKernel find_main_lmm4_d256(int nrep, int vk, int vb);
+MainKernel find_main_f16_d64(int nrep, int vk, int vb);
+MainKernel find_main_f16_d128(int nrep, int vk, int vb);
 
 }  // namespace tq

@@ -588,6 +588,19 @@ hipError_t run_lm(const tq_layout& Lay, const tq_state& S, const void* x, int ba
   return hipGetLastError();
 }
 
+// 16-bit keys (MLX page, V-only mode): the rows are stored as given, one 16-byte chunk per
+// thread, from the contiguous input into slots [dst, dst + T) of each slice.
+__global__ void __launch_bounds__(256) encode_copy16_kernel(const uint4* __restrict__ x, int T, long slices, int dst,
+                                                           int cap, int row16, uint4* __restrict__ out) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= slices * T * row16) return;
+  const int c = (int)(i % row16);
+  const long rt = i / row16;
+  const int t = (int)(rt % T);
+  const long s = rt / T;
+  out[((s * cap) + dst + t) * row16 + c] = x[i];
+}
+
 // Grid of the group kernels: x covers one slice's parts, y the slices (looped past 65535).
 inline dim3 group_grid(int slices, int T, int D) {
   const long parts = (long)T * (D / 8);
@@ -642,6 +655,7 @@ bool encode_k_compiled(const tq_layout& L) {
   const bool dt_ok = L.in_dtype == TQ_F16 || L.in_dtype == TQ_BF16;
   if (L.k_kind == TQ_K_LM_QJL || L.k_kind == TQ_K_LM_MSE) return d_ok && dt_ok && L.k_bits >= 2 && L.k_bits <= 4;
   if (L.k_kind == TQ_K_AFFINE8) return d_ok && dt_ok && L.k_bits == 8;
+  if (L.k_kind == TQ_K_F16) return d_ok && dt_ok && L.k_bits == 16;
   return false;
 }
 
@@ -659,6 +673,13 @@ hipError_t launch_encode_k(const tq_layout& L, const tq_state& S, const void* k,
   if (L.k_kind == TQ_K_LM_QJL) {
     TQ_D_SWITCH(L.head_dim, TQ_B_SWITCH(L.k_bits, TQ_DT_SWITCH(L.in_dtype,
         err = (run_lm<DD, BB, DTT, true>(L, S, k, batch, n_tokens, dst_offset, C, st, false));)))
+  } else if (L.k_kind == TQ_K_F16) {
+    const long slices = (long)batch * L.n_kv_heads;
+    const int row16 = L.head_dim / 8;
+    const long chunks = slices * n_tokens * row16;
+    hipLaunchKernelGGL(encode_copy16_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, st,
+                       (const uint4*)k, n_tokens, slices, dst_offset, C.capacity, row16, (uint4*)C.k_codes);
+    err = hipGetLastError();
   } else if (L.k_kind == TQ_K_LM_MSE) {
     // the rotated-LM kernel without the QJL stage (fp32 n in the aux plane), key state
     TQ_D_SWITCH(L.head_dim, TQ_B_SWITCH(L.k_bits, TQ_DT_SWITCH(L.in_dtype,

@@ -52,6 +52,7 @@ __device__ __forceinline__ uint32_t to_out(float x) {
 // Elementwise kinds: thread = (row, 8-dimension octet).
 //   KIND 0: affine-8 keys (codes: bytes; aux: fp16 (a, m) per 32-block)
 //   KIND 1: group values  (codes: VB-bit; aux: fp16 Delta per 32-group)
+//   KIND 2: 16-bit keys   (codes: the stored row, dtype VB = TQ_F16 / TQ_BF16; no aux)
 // ---------------------------------------------------------------------------------
 template <int D, int KIND, int VB, int OUT>
 __global__ void __launch_bounds__(256) materialize_elem_kernel(const uint32_t* __restrict__ codes,
@@ -67,7 +68,15 @@ __global__ void __launch_bounds__(256) materialize_elem_kernel(const uint32_t* _
   const long row = slice * cap + t0 + t;
   const int g = o / 4;                       // 32-block / 32-group of the octet
   float v[8];
-  if constexpr (KIND == 0) {
+  if constexpr (KIND == 2) {
+    const uint4 w = *reinterpret_cast<const uint4*>(codes + row * (D / 2) + 4 * o);
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[2 * e] = in_to_f32<VB>(ww[e] & 0xFFFFu);
+      v[2 * e + 1] = in_to_f32<VB>(ww[e] >> 16);
+    }
+  } else if constexpr (KIND == 0) {
     const uint2 w = *reinterpret_cast<const uint2*>(codes + row * (D / 4) + 2 * o);
     const uint32_t am = aux[row * (D / 32) + g];
     const float a = f16_to_f32(am & 0xFFFFu), m = f16_to_f32(am >> 16);
@@ -373,6 +382,14 @@ hipError_t launch_materialize_k(const tq_layout& L, const tq_state& S, const tq_
                                 void* out, int out_dtype, hipStream_t st) {
   const int slices = C.batch * L.n_kv_heads;
   uint16_t* o = static_cast<uint16_t*>(out);
+  if (L.k_kind == TQ_K_F16) {
+    const uint32_t* codes = static_cast<const uint32_t*>(C.k_codes);
+    if (L.in_dtype == TQ_BF16)
+      return (out_dtype == TQ_BF16) ? run_elem_d<2, TQ_BF16, TQ_BF16>(L.head_dim, codes, nullptr, slices, C.capacity, t0, n, o, st)
+                                    : run_elem_d<2, TQ_BF16, TQ_F16>(L.head_dim, codes, nullptr, slices, C.capacity, t0, n, o, st);
+    return (out_dtype == TQ_BF16) ? run_elem_d<2, TQ_F16, TQ_BF16>(L.head_dim, codes, nullptr, slices, C.capacity, t0, n, o, st)
+                                  : run_elem_d<2, TQ_F16, TQ_F16>(L.head_dim, codes, nullptr, slices, C.capacity, t0, n, o, st);
+  }
   if (L.k_kind == TQ_K_AFFINE8) {
     const uint32_t* codes = static_cast<const uint32_t*>(C.k_codes);
     const uint32_t* aux = static_cast<const uint32_t*>(C.k_aux);

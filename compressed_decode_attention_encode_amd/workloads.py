@@ -38,7 +38,7 @@ class Workload:
     head_dim: int
     n_ctx: int            # total cached tokens (compressed + recent buffer)
     n_recent: int         # last n_recent tokens stay exact in the recent buffer
-    k_kind: str           # "lm_qjl" | "affine8" | "lm_mse"
+    k_kind: str           # "lm_qjl" | "affine8" | "lm_mse" | "f16" (keys kept 16-bit, k_bits 16)
     k_bits: int
     v_kind: str           # "group_sym" | "lm_rot"
     v_bits: int
@@ -90,6 +90,10 @@ WORKLOADS = {
     "llama1b_mse3_h32x8_d64_t32k": Workload(
         "llama1b_mse3_h32x8_d64_t32k", 107, 1, 32, 8, 64, 32768, 128,
         "lm_mse", 3, "group_sym", 2, "f16", "f16", "const10", 4),
+    # V-only mode (MLX page): keys kept 16-bit, values rotated 3-bit Lloyd-Max
+    "llama1b_vonly_h32x8_d64_t32k": Workload(
+        "llama1b_vonly_h32x8_d64_t32k", 109, 1, 32, 8, 64, 32768, 128,
+        "f16", 16, "lm_rot", 3, "f16", "f16", "const10", 4),
     "qwen7b_k8v4_h28x4_d128_b16_t32k": Workload(
         "qwen7b_k8v4_h28x4_d128_b16_t32k", 108, 16, 28, 4, 128, 32768, 128,
         "affine8", 8, "lm_rot", 4, "bf16", "f16", "studentt3x10", 4, flush_tokens=128),

@@ -53,6 +53,9 @@ typedef enum {
 typedef enum { TQ_F16 = 0, TQ_BF16 = 1 } tq_dtype;
 
 /* Key encodings.
+ * TQ_K_F16     (MLX page, V-only mode: keys stay 16-bit, only the values are compressed):
+ *   the key row is stored as given (layout->in_dtype bits); k_bits must be 16; decode
+ *   is compiled for head_dim 64 and 128 (TQ_ERR_UNSUPPORTED for 256).
  * TQ_K_LM_MSE  (vLLM guide section 2 steps 1-2 only: the MSE-optimal codes without the
  *   QJL residual sketch; vLLM guide, MSE score kernel): n = |k| stored fp32, y = Pi k/n,
  *   idx_j = #{i : t_i < y_j} (k_bits in {2,3,4}); decoded key n Pi^T c[idx].  Its
@@ -64,7 +67,7 @@ typedef enum { TQ_F16 = 0, TQ_BF16 = 1 } tq_dtype;
  * TQ_K_AFFINE8 (vllm-metal guide, quantisation principle table: per-block affine,
  *   no rotation): per 32-block a = fp16((max-min)/255), m = fp16(min),
  *   q = clamp(rne((k - m)/a), 0, 255)  (q = 0 where a = 0). k_bits must be 8.      */
-typedef enum { TQ_K_LM_QJL = 0, TQ_K_AFFINE8 = 1, TQ_K_LM_MSE = 2 } tq_kkind;
+typedef enum { TQ_K_LM_QJL = 0, TQ_K_AFFINE8 = 1, TQ_K_LM_MSE = 2, TQ_K_F16 = 3 } tq_kkind;
 
 /* Value encodings.
  * TQ_V_GROUP_SYM (vLLM guide section 2 step 4, symmetric group-of-32 scaling):
@@ -119,6 +122,7 @@ typedef struct {
  *   k_signs  LM_QJL: uint32[d/32], bit j%32 of word j/32 = QJL bit j   (else unused)
  *   k_aux    LM_QJL: fp16[2] = (n, gamma);  AFFINE8: fp16[d/32][2] = (a, m) per block;
  *            LM_MSE: fp32 n  (LM_MSE codes are packed like LM_QJL codes)
+ *            F16: k_codes holds the d 16-bit key values (in_dtype bits); no k_aux plane
  *   v_codes  uint32[W], same packing as LM codes (GROUP_SYM v_bits 2/4, LM_ROT 2/3/4)
  *   v_aux    GROUP_SYM: fp16[d/32] scales Delta;  LM_ROT: fp32 n
  * tq_cache_plane_bytes gives each plane's size.                                        */
@@ -182,7 +186,7 @@ size_t tq_decode_workspace_bytes(const tq_layout* layout, int batch, int max_com
  * domain then one inverse butterfly, GQA n_rep without replicating KV; vLLM guide
  * section 5: exact recent buffer).  For q-head h of batch b, kv-head g = h / n_rep:
  *   LM_QJL keys:  s_t = n_t/sqrt(d) (<Pi q, c[idx_t]> + gamma_t sqrt(pi/2)/d <S Pi q, sigma_t>)
- *   LM_MSE keys:  s_t = n_t/sqrt(d) <Pi q, c[idx_t]>
+ *   LM_MSE keys:  s_t = n_t/sqrt(d) <Pi q, c[idx_t]>;  F16 keys: s_t = <q, k_t>/sqrt(d)
  *   AFFINE8 keys: s_t = <q, m + a q8_t>/sqrt(d);  recent keys: s_r = <q, k_r>/sqrt(d)
  *   out = softmax-weighted sum of decoded values over all n_compressed + n_recent
  *   tokens (GROUP_SYM: Delta (idx-(L-1)/2); LM_ROT: n Pi_v^T c[idx]; recent: v_r).
@@ -207,7 +211,7 @@ int tq_decode_attn(const tq_layout* layout, const tq_state* state, const void* q
  * guide, section 7: the hybrid path dequantises the whole history).  Row t of slice
  * (b, g) is exactly the decoded vector the decode attention uses:
  *   LM_QJL keys:    k = n Pi^T (c[idx] + gamma sqrt(pi/2)/d S^T sigma)
- *   LM_MSE keys:    k = n Pi^T c[idx]
+ *   LM_MSE keys:    k = n Pi^T c[idx];   F16 keys: the stored row (converted to out_dtype)
  *   AFFINE8 keys:   k_j = m + a q8_j
  *   GROUP_SYM vals: v_j = Delta (idx_j - (L-1)/2)
  *   LM_ROT values:  v = n Pi_v^T c[idx]

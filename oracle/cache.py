@@ -21,6 +21,17 @@ def encode_k(lay, k: np.ndarray, state: dict) -> dict:
         aux = np.stack([e["n16"].view(np.uint16), e["g16"].view(np.uint16)], axis=-1)
         return {"k_codes": L.pack_codes(e["idx"], lay.k_bits), "k_signs": L.pack_signs(e["qjl"]),
                 "k_aux": aux, "near_idx": e["near_idx"], "near_qjl": e["near_qjl"], "enc": e}
+    if lay.k_kind == "f16":
+        # V-only mode (MLX page): the key row kept as its 16-bit storage value; k holds
+        # values of that type exactly, so the conversion back to bits is exact
+        dt = getattr(lay, "in_dtype", "f16")
+        if dt == "f16":
+            bits = np.asarray(k).astype(np.float16).view(np.uint16)
+        else:
+            bits = (np.asarray(k).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        assert np.array_equal(_bits_to_f64(bits, dt), np.asarray(k)), "keys not representable in the storage type"
+        return {"k_codes": np.ascontiguousarray(bits).view(np.uint32), "near_idx": np.zeros(np.shape(k), bool),
+                "enc": {"bits": bits}}
     if lay.k_kind == "lm_mse":
         c, t = state["cb_k"]
         e = enc.encode_k_lm_mse(k, state["signs_k"], c, t)
@@ -47,9 +58,19 @@ def encode_v(lay, v: np.ndarray, state: dict) -> dict:
     raise ValueError(lay.v_kind)
 
 
+def _bits_to_f64(bits: np.ndarray, dt: str) -> np.ndarray:
+    bits = np.asarray(bits, dtype=np.uint16)
+    if dt == "f16":
+        return bits.view(np.float16).astype(np.float64)
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
 def read_k(lay, planes: dict, state: dict) -> dict:
     """Unpack K planes of shape [..., W] to codes and float64 side values."""
     d = lay.head_dim
+    if lay.k_kind == "f16":
+        bits = np.ascontiguousarray(planes["k_codes"], dtype=np.uint32).view(np.uint16)
+        return {"k": _bits_to_f64(bits, getattr(lay, "in_dtype", "f16"))}
     if lay.k_kind == "lm_qjl":
         aux = np.asarray(planes["k_aux"], dtype=np.uint16)
         return {"idx": L.unpack_codes(planes["k_codes"], lay.k_bits, d),

@@ -46,6 +46,9 @@ def _scores_compressed(lay, q: np.ndarray, kd: dict, state: dict) -> np.ndarray:
         lm = c[kd["idx"]] @ q_r
         qjl = kd["sigma"] @ q_s
         return kd["n"] / math.sqrt(d) * (lm + kd["gamma"] * math.sqrt(math.pi / 2.0) / d * qjl)
+    if lay.k_kind == "f16":
+        # 16-bit keys (V-only mode): the plain scaled dot product
+        return kd["k"] @ q / math.sqrt(d)
     if lay.k_kind == "lm_mse":
         # MSE-only keys: the codebook term alone, n / sqrt(d) <Pi q, c[idx]>
         c = state["cb_k"][0].astype(np.float64)
@@ -117,6 +120,8 @@ def reconstruct_k(lay, kd: dict, state: dict) -> np.ndarray:
     d = lay.head_dim
     if lay.k_kind == "affine8":
         return _affine_k_hat(kd, d)
+    if lay.k_kind == "f16":
+        return kd["k"]
     c = state["cb_k"][0].astype(np.float64)
     if lay.k_kind == "lm_mse":
         return kd["n"][:, None] * (c[kd["idx"]] @ rotation_matrix(state["signs_k"]))

@@ -80,6 +80,8 @@ def bytes_per_token_head(d: int, k_kind: str, k_bits: int, v_kind: str, v_bits: 
     """Bytes of each plane for one token of one kv-head."""
     if k_kind == "lm_qjl":
         k = {"k_codes": 4 * words_for(d, k_bits), "k_signs": d // 8, "k_aux": 4}
+    elif k_kind == "f16":
+        k = {"k_codes": 2 * d, "k_signs": 0, "k_aux": 0}
     elif k_kind == "lm_mse":
         k = {"k_codes": 4 * words_for(d, k_bits), "k_signs": 0, "k_aux": 4}
     elif k_kind == "affine8":

@@ -40,7 +40,7 @@ def dev_u16(bits: np.ndarray):
 
 def plane_shapes(wl, batch, cap):
     d = wl.head_dim
-    wk = OL.words_for(d, wl.k_bits)
+    wk = d // 2 if wl.k_kind == "f16" else OL.words_for(d, wl.k_bits)   # 16-bit keys: the row itself
     wv = OL.words_for(d, wl.v_bits)
     s = {"k_codes": (np.uint32, (batch, wl.n_kv_heads, cap, wk)),
          "v_codes": (np.uint32, (batch, wl.n_kv_heads, cap, wv))}
@@ -49,6 +49,8 @@ def plane_shapes(wl, batch, cap):
         s["k_aux"] = (np.uint16, (batch, wl.n_kv_heads, cap, 2))
     elif wl.k_kind == "lm_mse":
         s["k_aux"] = (np.float32, (batch, wl.n_kv_heads, cap))
+    elif wl.k_kind == "f16":
+        pass
     else:
         s["k_aux"] = (np.uint16, (batch, wl.n_kv_heads, cap, d // 32, 2))
     if wl.v_kind == "group_sym":
@@ -191,6 +193,8 @@ def compare_encode(wl, gpu: dict, ek: dict, ev: dict, rows=slice(None)) -> dict:
         st["k_aux_mismatch"] = int(aux_bad.sum())
         # whole rows with no excluded element must be identical words (padding bits included)
         st["k_word_mismatch"] = int(((g["k_codes"] != ek["k_codes"]).any(axis=-1) & row_ok).sum())
+    elif wl.k_kind == "f16":
+        st["k_word_mismatch"] = int((g["k_codes"] != ek["k_codes"]).sum())
     elif wl.k_kind == "lm_mse":
         idx = OL.unpack_codes(g["k_codes"], wl.k_bits, d)
         near = ek["near_idx"]

@@ -196,6 +196,23 @@ def test_mse_only_keys_arguments():
     assert e.value.status == tq.TQ_ERR_INVALID
 
 
+def test_sixteen_bit_keys_arguments():
+    """16-bit keys (V-only mode): k_bits 16, no aux plane; decode compiled for d 64/128."""
+    with pytest.raises(tq.TQError) as e:
+        tq.tq_encode(_layout(k_kind="f16", k_bits=8), _state(), FAKE, None, 1, 16, 0, _cache())
+    assert e.value.status == tq.TQ_ERR_UNSUPPORTED
+    L = _layout(k_kind="f16", k_bits=16, v_kind="lm_rot", v_bits=3)
+    sizes = tq.tq_cache_plane_bytes(L, 1, 10)
+    assert sizes[:3] == [2 * 128 * 10 * L.n_kv_heads, 0, 0]
+    ws = tq.tq_decode_workspace_bytes(L, 1, 100)
+    cache = tq.tq_cache(FAKE, None, None, FAKE, FAKE, 1, 256)
+    with pytest.raises(tq.TQError) as e:          # d = 256 16-bit-key decode is not compiled
+        tq.tq_decode_attn(_layout(head_dim=256, k_kind="f16", k_bits=16, v_kind="lm_rot", v_bits=3), _state(),
+                          FAKE, cache, 100, None, None, 0, 0, FAKE, FAKE, 1 << 30)
+    assert e.value.status == tq.TQ_ERR_UNSUPPORTED
+    assert ws > 0
+
+
 def test_workspace_bound_covers_every_length():
     L = _layout(head_dim=64, n_q_heads=32, n_kv_heads=8)
     import ctypes

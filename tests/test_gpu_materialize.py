@@ -157,6 +157,8 @@ VARIANTS = [
     (64, "lm_mse", 3, "lm_rot", 3, 4, 2, "f16"),
     (128, "lm_mse", 4, "group_sym", 4, 4, 2, "bf16"),
     (256, "lm_mse", 2, "lm_rot", 4, 2, 1, "f16"),
+    (128, "f16", 16, "lm_rot", 3, 4, 2, "bf16"),
+    (256, "f16", 16, "group_sym", 2, 2, 2, "f16"),
 ]
 
 

@@ -48,6 +48,11 @@ VARIANTS = [
     (128, "lm_mse", 3, "group_sym", 4, 6, 2, "bf16", 222, 5),
     (256, "lm_mse", 4, "lm_rot", 2, 10, 2, "f16", 190, 31),
     (256, "lm_mse", 2, "group_sym", 2, 3, 3, "f16", 150, 0),
+    # 16-bit keys (V-only mode)
+    (64, "f16", 16, "lm_rot", 3, 4, 2, "f16", 300, 17),
+    (64, "f16", 16, "group_sym", 4, 8, 1, "bf16", 250, 0),
+    (128, "f16", 16, "lm_rot", 2, 14, 2, "bf16", 222, 40),
+    (128, "f16", 16, "group_sym", 2, 2, 2, "f16", 180, 3),
 ]
 
 

@@ -362,7 +362,13 @@ def test_zero_residual_when_unit_vector_lands_on_centroids():
 # --------------------------------------------------------------------------- decode
 KINDS = [("lm_qjl", 3, "group_sym", 2), ("lm_qjl", 4, "group_sym", 4), ("lm_qjl", 2, "group_sym", 2),
          ("affine8", 8, "lm_rot", 3), ("affine8", 8, "lm_rot", 2),
-         ("lm_mse", 3, "lm_rot", 3), ("lm_mse", 4, "group_sym", 4), ("lm_mse", 2, "lm_rot", 2)]
+         ("lm_mse", 3, "lm_rot", 3), ("lm_mse", 4, "group_sym", 4), ("lm_mse", 2, "lm_rot", 2),
+         ("f16", 16, "lm_rot", 3), ("f16", 16, "group_sym", 2)]
+
+
+def _keys(kind, k):
+    """16-bit keys are stored as given: feed values of that type."""
+    return k.astype(np.float16).astype(np.float64) if kind[0] == "f16" else k
 
 
 @pytest.mark.parametrize("kind", KINDS)
@@ -372,7 +378,7 @@ def test_fast_decode_equals_bruteforce(kind, d):
     st = _rand_state(lay, d)
     rng = np.random.default_rng(5)
     B, T, Rn = 2, 40, 6
-    k = rng.standard_normal((B, 2, T, d))
+    k = _keys(kind, rng.standard_normal((B, 2, T, d)))
     v = rng.standard_normal((B, 2, T, d))
     pk, pv = C.encode_k(lay, k, st), C.encode_v(lay, v, st)
     planes = {n: a for n, a in {**pk, **pv}.items() if n in ("k_codes", "k_signs", "k_aux", "v_codes", "v_aux")}
@@ -410,7 +416,7 @@ def test_one_token_and_identical_keys(kind):
     lay = Lay(d, 2, 1, *kind)
     st = _rand_state(lay, 2)
     rng = np.random.default_rng(4)
-    k1 = rng.standard_normal((1, 1, 1, d))
+    k1 = _keys(kind, rng.standard_normal((1, 1, 1, d)))
     v = rng.standard_normal((1, 1, 5, d))
     q = rng.standard_normal((1, 2, d))
     pk = C.encode_k(lay, np.repeat(k1, 5, axis=2), st)
