@@ -115,6 +115,27 @@ struct RowLoader {
       }
     }
   }
+  // Word w of row t goes to lds[w * LS + t] instead (token-major columns: the same word
+  // of consecutive rows is contiguous).
+  __device__ __forceinline__ void store_transposed(uint32_t* __restrict__ lds, int lane) const {
+    if constexpr (W == 0) return;
+    if (vec) {
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int q = 4 * (i * kWave + lane) + k;
+          if (q < N) lds[(q % W) * LS + (q / W)] = r[4 * i + k];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        const int q = i * kWave + lane;
+        if (q < N) lds[(q % W) * LS + (q / W)] = r[i];
+      }
+    }
+  }
   __device__ __forceinline__ void store(uint32_t* __restrict__ lds, int lane) const {
     if constexpr (W == 0) return;
     if (vec) {
@@ -174,7 +195,7 @@ __device__ __forceinline__ void read_entry(const float* p, float (&e)[NE]) {
 //   LM + QJL keys: qa = Pi q * log2(e)/sqrt(d), qb = S Pi q * log2(e)/sqrt(d) * sqrt(pi/2)/d,
 //                  then the QJL table;
 //   affine keys:   qa = q * log2(e)/sqrt(d), qb[h][blk] = sum of qa over the 32-block.
-template <int D, int NREP, int KK, int KB, int VK, int VB>
+template <int D, int NREP, int KK, int KB, int VK, int VB, bool TABLE = true>
 __device__ void prepare_queries(const DecodeArgs& A, int b, int g, float* sm) {
   using G = DecodeGeom<D, NREP, KK, KB, VK, VB>;
   constexpr int NE = G::NE;
@@ -283,7 +304,7 @@ __device__ void prepare_queries(const DecodeArgs& A, int b, int g, float* sm) {
     __syncthreads();
     // QJL table: entry (nib, v), head h = sum_t (bit t of v ? +1 : -1) qb[h][4 nib + t]
     float* tq = sm + G::OFF_TQ;
-    for (int i = tid; QJL && i < (D / 4) * 16; i += 256) {
+    for (int i = tid; QJL && TABLE && i < (D / 4) * 16; i += 256) {
       const int nib = i / 16, v = i % 16;
 #pragma unroll
       for (int h = 0; h < NREP; ++h) {

@@ -1,0 +1,462 @@
+// Split-K decode attention on the fp16 matrix cores, for Lloyd-Max + QJL keys and
+// group-32 symmetric values (gfx950, v_mfma_f32_16x16x32_f16).
+//
+// Same method, split plan, partial format and recent-buffer split as tq_decode_main.h
+// (news page "vLLM, llama.cpp, MLX all follow up", oMLX section: attention straight from
+// the packed indices; TurboQuant-MLX page, GPU kernel optimisation section: pre-rotated
+// query, GQA without repeating KV; TurboQuant vLLM guide, section 2: the LM + QJL inner
+// product <q, k> = n (<Pi q, c[idx]> + gamma sqrt(pi/2)/d <S Pi q, sigma>)).  What changes
+// is how a 64-token tile is reduced.  With n_rep query heads per kv-head, both products of
+// a tile are dense contractions once a code is replaced by its value:
+//
+//   scores  S^T[token, head] = A[token, k] B[k, head], the contraction index k running
+//           over five blocks of d dimensions:
+//             A = c_hi[idx]  B = q_hi        A = c_lo[idx]  B = q_hi
+//             A = c_hi[idx]  B = q_lo        A = gamma*sigma  B = qb_hi,  A = gamma*sigma  B = qb_lo
+//           where c_hi/c_lo are the fp16 halves of 8 c (a 21-bit centroid), q_hi/q_lo those
+//           of the scaled rotated query and qb_hi/qb_lo those of the scaled projected query;
+//           gamma*sigma is the key's fp16 gamma with the sign of its QJL bit, exact in fp16.
+//           Every product is exact in fp32; the dropped c_lo q_lo term is ~2^-22 relative.
+//           The token's norm n (and a power-of-two unscale) multiplies the sum afterwards.
+//   values O[head, dim] = P'[head, token] V[token, dim] per 32-dimension group, with
+//           P' = fp16(p * Delta) (the softmax weight times the token's group scale, rounded
+//           once as in the vector-ALU kernel) and V the fp16 value 1 + c/2^m of the code
+//           (exact); sum_t P' (the offset term) comes from fp16 dot instructions on the same
+//           rounded weights, and F*O - (F + (L-1)/2) * sum P' is the group-dequantised sum.
+//
+// Operand layouts (16x16x32 f16): A lane l holds row l%16, k = 8(l/16)..+7; B lane l holds
+// column l%16, the same k; C lane l holds column l%16, rows 4(l/16)..+3.  The k order inside a
+// 32-wide block is free as long as A and B agree: the value product takes the 8 tokens
+// {4q..4q+3, 16+4q..16+4q+3} (q = l/16) of a 32-token block, which are exactly the rows a
+// lane holds in the score accumulators of two 16-token blocks, so softmax weights go from the
+// score accumulators to the value operands without leaving the lane.
+//
+// Codes become operands through LDS tables: one 8-byte entry (hi pair, lo pair) per pair of
+// codes (2 KB for 4-bit codes), and one 16-byte xor-mask entry per 8 sign bits.  Tiles are
+// staged as in the vector-ALU kernel (coalesced 16-byte loads, next tile in flight), value
+// codes and scales transposed (word-major) so that 4 consecutive tokens of one word are one
+// 16-byte LDS read.
+#pragma once
+
+#include "tq_decode_main.h"
+
+namespace tq {
+
+typedef _Float16 mma_h8_t __attribute__((ext_vector_type(8)));
+typedef float mma_f4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t mma_u4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ mma_f4_t mma16(mma_u4_t a, mma_u4_t b, mma_f4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(mma_h8_t, a), __builtin_bit_cast(mma_h8_t, b),
+                                                c, 0, 0, 0);
+}
+
+// Operand scales: centroids x 8 (O(1) values, fp16 halves both normal); the query operands
+// carry 2^8 / 8 (codebook) and 2^8 (QJL) so that the sum is 2^8 times the log2-domain score.
+constexpr float kMmaCentScale = 8.f;
+constexpr float kMmaQScale = 256.f;
+constexpr float kMmaUnscale = 1.f / 256.f;
+
+template <int D, int NREP, int KB, int VB>
+struct MmaGeom {
+  using G = DecodeGeom<D, NREP, TQ_K_LM_QJL, KB, TQ_V_GROUP_SYM, VB>;
+  static constexpr int KPER = G::KPER, WK = G::WK, SK = G::SK;
+  static constexpr int WS = D / 32, SS = G::SS;
+  static constexpr int WV = G::WV, WAV = G::WAV;
+  static constexpr int TS = kTile + 4;        // token stride of the transposed value planes
+  static constexpr int NKB = D / 32;          // 32-dimension blocks of the score contraction
+  static constexpr int NNB = D / 16;          // 16-dimension blocks of the value product
+  static constexpr int NG = D / 32;           // value groups
+  // one wave's staging area (words): key rows, sign rows, key aux (n, gamma) per token,
+  // value codes and value scales word-major
+  static constexpr int OFF_SK = 0;
+  static constexpr int OFF_SS = OFF_SK + kTile * SK;
+  static constexpr int OFF_SAK = OFF_SS + kTile * SS;
+  static constexpr int OFF_SV = OFF_SAK + kTile;
+  static constexpr int OFF_SAV = OFF_SV + WV * TS;
+  static constexpr int STAGE = OFF_SAV + WAV * TS;
+  static_assert(OFF_SAK % 4 == 0 && OFF_SV % 4 == 0 && OFF_SAV % 4 == 0 && STAGE % 4 == 0, "16-byte LDS reads");
+  // group LDS (words): qa, qb as prepare_queries leaves them, the fp16 query operands
+  // [4][NREP + 1][D] halves (q_hi, q_lo, qb_hi, qb_lo; row NREP is zero, the operand of
+  // the columns beyond n_rep), the code-pair table, the sign table,
+  // four staging areas, merge scalars
+  static constexpr int NPT = 1 << (2 * KB);
+  static constexpr int OFF_BQ = (G::OFF_QB + NREP * D + 3) & ~3;
+  static constexpr int NRB = NREP + 1;         // query operand rows: the heads, then a zero row
+  static constexpr int OFF_PT = OFF_BQ + 2 * NRB * D;
+  static constexpr int OFF_SGT = OFF_PT + 2 * NPT;
+  static constexpr int OFF_ST = OFF_SGT + 4 * 256;
+  static constexpr int OFF_MRG = OFF_ST + 4 * STAGE;
+  static constexpr int OWN = OFF_MRG + 8 * NREP + 16;
+  static constexpr int FLOATS = OWN > G::FLOATS ? OWN : G::FLOATS;   // the recent split shares it
+  static_assert(4 * STAGE >= 4 * NREP * D, "merge buffer does not fit in the staging area");
+  static_assert(NREP <= 16, "one 16-column operand holds the heads");
+};
+
+template <int D, int NREP, int KB, int VB>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+decode_mma_kernel(const DecodeArgs A) {
+  using M = MmaGeom<D, NREP, KB, VB>;
+  constexpr int LK = 1 << KB;
+  constexpr int LV = 1 << VB;
+  constexpr int NKB = M::NKB, NNB = M::NNB, NG = M::NG;
+  static_assert(VB == 2 || VB == 4, "group-scaled values are 2 or 4 bits");
+
+  __shared__ __attribute__((aligned(16))) float sm[M::FLOATS];
+  uint32_t* smw = reinterpret_cast<uint32_t*>(sm);
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, q4 = lane >> 4;
+
+  // grid: the compressed splits first, then one recent-buffer group per (batch, kv-head)
+  const int n_comp = A.nsplit * A.Hkv * A.batch;
+  if ((int)blockIdx.x >= n_comp) {
+    const int u = blockIdx.x - n_comp;
+    recent_split<D, NREP, TQ_K_LM_QJL, KB, TQ_V_GROUP_SYM, VB>(A, u / A.Hkv, u % A.Hkv, sm);
+    return;
+  }
+  const int split = blockIdx.x % A.nsplit;
+  const int g = (blockIdx.x / A.nsplit) % A.Hkv;
+  const int b = blockIdx.x / (A.nsplit * A.Hkv);
+  const size_t slice = (size_t)b * A.Hkv + g;
+  const int tb = split * A.chunk;
+  const int te = min(A.n_c, tb + A.chunk);
+  const int cap = A.cap;
+
+  uint32_t* st = smw + M::OFF_ST + wave * M::STAGE;
+  const uint32_t* stk = st + M::OFF_SK;
+  const uint32_t* sts = st + M::OFF_SS;
+  const uint32_t* stak = st + M::OFF_SAK;
+  const uint32_t* stv = st + M::OFF_SV;
+  const uint32_t* stav = st + M::OFF_SAV;
+
+  RowLoader<M::WK, M::SK> ld_k;
+  RowLoader<M::WS, M::SS> ld_s;
+  RowLoader<1, 1> ld_ak;
+  RowLoader<M::WV, M::TS> ld_v;
+  RowLoader<M::WAV, M::TS> ld_av;
+  auto issue = [&](int t0) {
+    const int nv = min(kTile, te - t0);
+    const size_t row0 = slice * cap + t0;
+    ld_k.load(A.kc + row0 * M::WK, nv, lane);
+    ld_s.load(A.ks + row0 * M::WS, nv, lane);
+    ld_ak.load(A.ka + row0, nv, lane);
+    ld_v.load(A.vc + row0 * M::WV, nv, lane);
+    ld_av.load(A.va + row0 * M::WAV, nv, lane);
+  };
+  if (tb + wave * kTile < te) issue(tb + wave * kTile);
+
+  // code-pair table: entry pc = (code a = low KB bits, code b), words (hi pair, lo pair)
+  for (int i = threadIdx.x; i < M::NPT; i += 256) {
+    const float ca = A.kcent[i & (LK - 1)] * kMmaCentScale;
+    const float cb = A.kcent[i >> KB] * kMmaCentScale;
+    const _Float16 ha = (_Float16)ca, hb = (_Float16)cb;
+    smw[M::OFF_PT + 2 * i] = pack_f16x2((float)ha, (float)hb);
+    smw[M::OFF_PT + 2 * i + 1] = pack_f16x2(ca - (float)ha, cb - (float)hb);
+  }
+  // sign table: 8 stored bits (bit 1 <=> sigma = +1) -> xor masks of 4 fp16 pairs
+  {
+    const int i = threadIdx.x;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      smw[M::OFF_SGT + 4 * i + k] = (((i >> (2 * k)) & 1) ? 0u : 0x8000u) | (((i >> (2 * k + 1)) & 1) ? 0u : 0x80000000u);
+  }
+  prepare_queries<D, NREP, TQ_K_LM_QJL, KB, TQ_V_GROUP_SYM, VB, false>(A, b, g, sm);
+  {
+    // fp16 query operands (hi, lo) from the prepared fp32 queries
+    const float* qa = sm + M::G::OFF_QA;
+    const float* qb = sm + M::G::OFF_QB;
+    _Float16* bq = reinterpret_cast<_Float16*>(smw + M::OFF_BQ);
+    constexpr int RS = M::NRB * D;               // halves per operand region
+    for (int i = threadIdx.x; i < RS; i += 256) {
+      const bool on = i < NREP * D;
+      const float a = on ? qa[i] * (kMmaQScale / kMmaCentScale) : 0.f;
+      const float s = on ? qb[i] * kMmaQScale : 0.f;
+      const _Float16 ah = (_Float16)a, sh = (_Float16)s;
+      bq[i] = ah;
+      bq[RS + i] = (_Float16)(a - (float)ah);
+      bq[2 * RS + i] = sh;
+      bq[3 * RS + i] = (_Float16)(s - (float)sh);
+    }
+  }
+  __syncthreads();
+
+  const uint32_t* bqw = smw + M::OFF_BQ;
+  const uint32_t* ptab = smw + M::OFF_PT;
+  const uint32_t* sgt = smw + M::OFF_SGT;
+  const int hq = (l16 < NREP) ? l16 : NREP;    // operand column (head); the zero row beyond n_rep
+
+  float m_run = -INFINITY, l_part = 0.f;        // head l16 (per lane: its tokens)
+  float off[NG];                                // sum of P' per group, head l16
+  mma_f4_t acc[NNB];                            // head 4 q4 + r, dimension 16 nb + l16
+#pragma unroll
+  for (int k = 0; k < NG; ++k) off[k] = 0.f;
+#pragma unroll
+  for (int nb = 0; nb < NNB; ++nb) acc[nb] = mma_f4_t{0.f, 0.f, 0.f, 0.f};
+
+  for (int t0 = tb + wave * kTile; t0 < te; t0 += 4 * kTile) {
+    const int nv = min(kTile, te - t0);
+    ld_k.store(st + M::OFF_SK, lane);
+    ld_s.store(st + M::OFF_SS, lane);
+    ld_ak.store(st + M::OFF_SAK, lane);
+    ld_v.store_transposed(st + M::OFF_SV, lane);
+    ld_av.store_transposed(st + M::OFF_SAV, lane);
+    if (t0 + 4 * kTile < te) issue(t0 + 4 * kTile);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // ---- scores: four 16-token blocks ------------------------------------------------------
+    mma_f4_t sacc[4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) sacc[mb] = mma_f4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const int kw = 16 * kb + 4 * q4;           // word offset of this lane's 8 dimensions
+      mma_u4_t bq0, bq1, bq2, bq3;
+      {
+        constexpr int RW = M::NRB * D / 2;         // words per operand region
+        const uint32_t* src = bqw + hq * (D / 2) + kw;
+        const uint4 r0 = *reinterpret_cast<const uint4*>(src);
+        const uint4 r1 = *reinterpret_cast<const uint4*>(src + RW);
+        const uint4 r2 = *reinterpret_cast<const uint4*>(src + 2 * RW);
+        const uint4 r3 = *reinterpret_cast<const uint4*>(src + 3 * RW);
+        bq0 = mma_u4_t{r0.x, r0.y, r0.z, r0.w};
+        bq1 = mma_u4_t{r1.x, r1.y, r1.z, r1.w};
+        bq2 = mma_u4_t{r2.x, r2.y, r2.z, r2.w};
+        bq3 = mma_u4_t{r3.x, r3.y, r3.z, r3.w};
+      }
+      mma_u4_t ahi[4], alo[4], asg[4];
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const int tok = 16 * mb + l16;
+        const uint32_t* row = stk + tok * M::SK;
+        // the lane's 8 codes (dimensions 32 kb + 8 q4 ..) as the low 8 KB bits of y
+        uint32_t y;
+        if constexpr (KB == 3) {
+          const int a0 = 32 * kb + 8 * q4;
+          const int w0 = a0 / 10, b0 = 3 * (a0 - 10 * w0);
+          const uint32_t x0 = row[w0], x1 = row[w0 + 1];
+          y = __builtin_amdgcn_alignbit(x1 >> 2, x0 | (x1 << 30), (uint32_t)b0);
+        } else if constexpr (KB == 4) {
+          y = row[4 * kb + q4];
+        } else {
+          y = row[2 * kb + (q4 >> 1)] >> (16 * (q4 & 1));
+        }
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const uint32_t pc = (y >> (2 * KB * p)) & (M::NPT - 1);
+          const uint2 e = *reinterpret_cast<const uint2*>(ptab + 2 * pc);
+          ahi[mb][p] = e.x;
+          alo[mb][p] = e.y;
+        }
+        const uint32_t sb = (sts[tok * M::SS + kb] >> (8 * q4)) & 0xFFu;
+        const uint4 mk = *reinterpret_cast<const uint4*>(sgt + 4 * sb);
+        const uint32_t aux = stak[tok];
+        const uint32_t g2 = __builtin_amdgcn_perm(aux, aux, 0x03020302u);   // (gamma, gamma)
+        asg[mb] = mma_u4_t{g2 ^ mk.x, g2 ^ mk.y, g2 ^ mk.z, g2 ^ mk.w};
+      }
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) sacc[mb] = mma16(ahi[mb], bq0, sacc[mb]);
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) sacc[mb] = mma16(alo[mb], bq0, sacc[mb]);
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) sacc[mb] = mma16(ahi[mb], bq1, sacc[mb]);
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) sacc[mb] = mma16(asg[mb], bq2, sacc[mb]);
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) sacc[mb] = mma16(asg[mb], bq3, sacc[mb]);
+    }
+    // sacc[mb][r]: head l16, token 16 mb + 4 q4 + r; times n (and the operand unscale)
+    float p[4][4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const uint4 nw = *reinterpret_cast<const uint4*>(stak + 16 * mb + 4 * q4);
+      const uint32_t nn[4] = {nw.x, nw.y, nw.z, nw.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) p[mb][r] = sacc[mb][r] * (f16_to_f32(nn[r] & 0xFFFFu) * kMmaUnscale);
+    }
+    if (nv < kTile) {   // the last tile of a split: tokens past its end score -inf
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (16 * mb + 4 * q4 + r >= nv) p[mb][r] = -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, p[mb][r]);
+    // ---- online softmax (log2 domain): head l16 spans lanes l16 + 16 q ------------------
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mn = fmaxf(m_run, mx);
+    // v_exp_f32 directly: arguments are <= 0, results in [0, 1] (a result below 2^-126 is
+    // flushed to zero, far below the fp32 sums it joins)
+    const float alpha = (mn == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - mn);
+    float ps = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        p[mb][r] = __builtin_amdgcn_exp2f(p[mb][r] - mn);
+        ps += p[mb][r];
+      }
+    }
+    l_part = fmaf(l_part, alpha, ps);
+    m_run = mn;
+#pragma unroll
+    for (int k = 0; k < NG; ++k) off[k] *= alpha;
+    {
+      float al[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) al[r] = __shfl(alpha, 4 * q4 + r);
+#pragma unroll
+      for (int nb = 0; nb < NNB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[nb][r] *= al[r];
+    }
+
+    // ---- weighted values: two 32-token blocks ------------------------------------------
+    constexpr uint32_t kOne = 0x3C003C00u;       // fp16 pair (1, 1)
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      // k slot i of this lane: token 32 kb2 + 4 q4 + i (i < 4), 32 kb2 + 16 + 4 q4 + i - 4
+      const int tk = 32 * kb2 + 4 * q4;
+      mma_u4_t apv[NG];
+#pragma unroll
+      for (int w = 0; w < M::WAV; ++w) {
+        const uint4 d0 = *reinterpret_cast<const uint4*>(stav + w * M::TS + tk);
+        const uint4 d1 = *reinterpret_cast<const uint4*>(stav + w * M::TS + tk + 16);
+        const uint32_t dw[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const int gi = 2 * w + hf;
+          if (gi < NG) {
+            float wt[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+              wt[i] = p[2 * kb2 + (i >> 2)][i & 3] * f16_to_f32((dw[i] >> (16 * hf)) & 0xFFFFu);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              apv[gi][k] = pack_f16x2(wt[2 * k], wt[2 * k + 1]);
+              off[gi] = dot2_f16(apv[gi][k], kOne, off[gi]);
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int nb = 0; nb < NNB; ++nb) {
+        uint32_t x[8];
+        int bit;
+        if constexpr (VB == 2) {
+          const uint32_t* src = stv + nb * M::TS + tk;
+          const uint4 x0 = *reinterpret_cast<const uint4*>(src);
+          const uint4 x1 = *reinterpret_cast<const uint4*>(src + 16);
+          x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w; x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
+          bit = 2 * l16;
+        } else {
+          const uint32_t* src = stv + (2 * nb + (l16 >> 3)) * M::TS + tk;
+          const uint4 x0 = *reinterpret_cast<const uint4*>(src);
+          const uint4 x1 = *reinterpret_cast<const uint4*>(src + 16);
+          x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w; x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
+          bit = 4 * (l16 & 7);
+        }
+        // code c -> fp16 1 + c / 2^MV: the code dropped into the mantissa under 1.0's exponent
+        constexpr int MV = (VB == 2) ? 8 : 6;
+        mma_u4_t bv;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t c0 = __builtin_amdgcn_ubfe(x[2 * k], (uint32_t)bit, VB);
+          const uint32_t c1 = __builtin_amdgcn_ubfe(x[2 * k + 1], (uint32_t)bit, VB);
+          bv[k] = (c0 << MV) | (c1 << (16 + MV)) | kOne;
+        }
+        acc[nb] = mma16(apv[nb / 2], bv, acc[nb]);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+
+  // ---- wave totals -------------------------------------------------------------------------
+  l_part += __shfl_xor(l_part, 16);
+  l_part += __shfl_xor(l_part, 32);
+#pragma unroll
+  for (int k = 0; k < NG; ++k) {
+    off[k] += __shfl_xor(off[k], 16);
+    off[k] += __shfl_xor(off[k], 32);
+  }
+  // acc = sum P' (1 + c / F), off = sum P'  ->  sum P' (c - (L-1)/2) = F acc - (F + (L-1)/2) off
+  constexpr float F = (VB == 2) ? 4.f : 16.f;
+  constexpr float FO = F + 0.5f * (float)(LV - 1);
+  __syncthreads();   // every wave is done with its staging area
+  float(*s_mrg_acc)[NREP * D] = reinterpret_cast<float(*)[NREP * D]>(smw + M::OFF_ST);
+  float* s_mrg_m = sm + M::OFF_MRG;            // [4][NREP]
+  float* s_mrg_l = s_mrg_m + 4 * NREP;         // [4][NREP]
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int h = 4 * q4 + r;
+    float o[NG];
+#pragma unroll
+    for (int k = 0; k < NG; ++k) o[k] = __shfl(off[k], h);
+    if (h < NREP) {
+#pragma unroll
+      for (int nb = 0; nb < NNB; ++nb)
+        s_mrg_acc[wave][h * D + 16 * nb + l16] = fmaf(F, acc[nb][r], -FO * o[nb / 2]);
+    }
+  }
+  if (lane < NREP) {
+    s_mrg_m[wave * NREP + lane] = m_run;
+    s_mrg_l[wave * NREP + lane] = l_part;
+  }
+  __syncthreads();
+
+  // ---- merge the four waves, write one partial per head ----------------------------------
+  for (int i = threadIdx.x; i < NREP * D; i += blockDim.x) {
+    const int h = i / D, j = i % D;
+    float mxw = s_mrg_m[h];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) mxw = fmaxf(mxw, s_mrg_m[w * NREP + h]);
+    float a = 0.f, l = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float mw = s_mrg_m[w * NREP + h];
+      const float sc = (mw == -INFINITY) ? 0.f : exp2f(mw - mxw);
+      a = fmaf(s_mrg_acc[w][h * D + j], sc, a);
+      l = fmaf(s_mrg_l[w * NREP + h], sc, l);
+    }
+    float* dst = partial_ptr<D>(A, b, g * NREP + h, split);
+    dst[4 + j] = a;
+    if (j == 0) {
+      dst[0] = mxw;
+      dst[1] = l;
+    }
+  }
+}
+
+template <int D, int NREP, int KB, int VB>
+hipError_t mma_launch(dim3 grid, hipStream_t st, const DecodeArgs& A) {
+  hipLaunchKernelGGL((decode_mma_kernel<D, NREP, KB, VB>), grid, dim3(256), 0, st, A);
+  return hipGetLastError();
+}
+
+template <int D, int NREP, int KB, int VB>
+int mma_blocks_per_cu() {
+  static const int n = [] {
+    int b = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, decode_mma_kernel<D, NREP, KB, VB>, 256, 0) != hipSuccess ||
+        b <= 0)
+      b = 1;
+    return b;
+  }();
+  return n;
+}
+
+template <int D, int NREP, int KB, int VB>
+constexpr MainKernel mma_kernel() {
+  return MainKernel{&mma_launch<D, NREP, KB, VB>, &mma_blocks_per_cu<D, NREP, KB, VB>};
+}
+
+}  // namespace tq
