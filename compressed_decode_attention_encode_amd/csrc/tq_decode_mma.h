@@ -94,7 +94,7 @@ struct MmaGeom {
 };
 
 template <int D, int NREP, int KB, int VB>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 2)))
 decode_mma_kernel(const DecodeArgs A) {
   using M = MmaGeom<D, NREP, KB, VB>;
   constexpr int LK = 1 << KB;
@@ -226,7 +226,8 @@ decode_mma_kernel(const DecodeArgs A) {
         bq2 = mma_u4_t{r2.x, r2.y, r2.z, r2.w};
         bq3 = mma_u4_t{r3.x, r3.y, r3.z, r3.w};
       }
-      mma_u4_t ahi[4], alo[4], asg[4];
+      // one 16-token block at a time: its three operands, then its five products (the
+      // accumulator chains through the matrix unit; few registers stay live)
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
         const int tok = 16 * mb + l16;
@@ -243,29 +244,25 @@ decode_mma_kernel(const DecodeArgs A) {
         } else {
           y = row[2 * kb + (q4 >> 1)] >> (16 * (q4 & 1));
         }
+        mma_u4_t ahi, alo;
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
           const uint32_t pc = (y >> (2 * KB * p)) & (M::NPT - 1);
           const uint2 e = *reinterpret_cast<const uint2*>(ptab + 2 * pc);
-          ahi[mb][p] = e.x;
-          alo[mb][p] = e.y;
+          ahi[p] = e.x;
+          alo[p] = e.y;
         }
         const uint32_t sb = (sts[tok * M::SS + kb] >> (8 * q4)) & 0xFFu;
         const uint4 mk = *reinterpret_cast<const uint4*>(sgt + 4 * sb);
         const uint32_t aux = stak[tok];
         const uint32_t g2 = __builtin_amdgcn_perm(aux, aux, 0x03020302u);   // (gamma, gamma)
-        asg[mb] = mma_u4_t{g2 ^ mk.x, g2 ^ mk.y, g2 ^ mk.z, g2 ^ mk.w};
+        const mma_u4_t asg = mma_u4_t{g2 ^ mk.x, g2 ^ mk.y, g2 ^ mk.z, g2 ^ mk.w};
+        sacc[mb] = mma16(ahi, bq0, sacc[mb]);
+        sacc[mb] = mma16(alo, bq0, sacc[mb]);
+        sacc[mb] = mma16(ahi, bq1, sacc[mb]);
+        sacc[mb] = mma16(asg, bq2, sacc[mb]);
+        sacc[mb] = mma16(asg, bq3, sacc[mb]);
       }
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) sacc[mb] = mma16(ahi[mb], bq0, sacc[mb]);
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) sacc[mb] = mma16(alo[mb], bq0, sacc[mb]);
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) sacc[mb] = mma16(ahi[mb], bq1, sacc[mb]);
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) sacc[mb] = mma16(asg[mb], bq2, sacc[mb]);
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) sacc[mb] = mma16(asg[mb], bq3, sacc[mb]);
     }
     // sacc[mb][r]: head l16, token 16 mb + 4 q4 + r; times n (and the operand unscale)
     float p[4][4];
@@ -324,7 +321,6 @@ decode_mma_kernel(const DecodeArgs A) {
     for (int kb2 = 0; kb2 < 2; ++kb2) {
       // k slot i of this lane: token 32 kb2 + 4 q4 + i (i < 4), 32 kb2 + 16 + 4 q4 + i - 4
       const int tk = 32 * kb2 + 4 * q4;
-      mma_u4_t apv[NG];
 #pragma unroll
       for (int w = 0; w < M::WAV; ++w) {
         const uint4 d0 = *reinterpret_cast<const uint4*>(stav + w * M::TS + tk);
@@ -334,45 +330,43 @@ decode_mma_kernel(const DecodeArgs A) {
         for (int hf = 0; hf < 2; ++hf) {
           const int gi = 2 * w + hf;
           if (gi < NG) {
-            float wt[8];
+            mma_u4_t apv;
+            {
+              float wt[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-              wt[i] = p[2 * kb2 + (i >> 2)][i & 3] * f16_to_f32((dw[i] >> (16 * hf)) & 0xFFFFu);
+              for (int i = 0; i < 8; ++i)
+                wt[i] = p[2 * kb2 + (i >> 2)][i & 3] * f16_to_f32((dw[i] >> (16 * hf)) & 0xFFFFu);
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              apv[gi][k] = pack_f16x2(wt[2 * k], wt[2 * k + 1]);
-              off[gi] = dot2_f16(apv[gi][k], kOne, off[gi]);
+              for (int k = 0; k < 4; ++k) {
+                apv[k] = pack_f16x2(wt[2 * k], wt[2 * k + 1]);
+                off[gi] = dot2_f16(apv[k], kOne, off[gi]);
+              }
+            }
+            // the group's two 16-dimension blocks
+#pragma unroll
+            for (int nb = 2 * gi; nb < 2 * gi + 2; ++nb) {
+              uint32_t x[8];
+              int bit;
+              {
+                const uint32_t* src = (VB == 2) ? stv + nb * M::TS + tk : stv + (2 * nb + (l16 >> 3)) * M::TS + tk;
+                const uint4 x0 = *reinterpret_cast<const uint4*>(src);
+                const uint4 x1 = *reinterpret_cast<const uint4*>(src + 16);
+                x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w; x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
+                bit = (VB == 2) ? 2 * l16 : 4 * (l16 & 7);
+              }
+              // code c -> fp16 1 + c / 2^MV: the code dropped into the mantissa under 1.0's exponent
+              constexpr int MV = (VB == 2) ? 8 : 6;
+              mma_u4_t bv;
+#pragma unroll
+              for (int k = 0; k < 4; ++k) {
+                const uint32_t c0 = __builtin_amdgcn_ubfe(x[2 * k], (uint32_t)bit, VB);
+                const uint32_t c1 = __builtin_amdgcn_ubfe(x[2 * k + 1], (uint32_t)bit, VB);
+                bv[k] = (c0 << MV) | (c1 << (16 + MV)) | kOne;
+              }
+              acc[nb] = mma16(apv, bv, acc[nb]);
             }
           }
         }
-      }
-#pragma unroll
-      for (int nb = 0; nb < NNB; ++nb) {
-        uint32_t x[8];
-        int bit;
-        if constexpr (VB == 2) {
-          const uint32_t* src = stv + nb * M::TS + tk;
-          const uint4 x0 = *reinterpret_cast<const uint4*>(src);
-          const uint4 x1 = *reinterpret_cast<const uint4*>(src + 16);
-          x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w; x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
-          bit = 2 * l16;
-        } else {
-          const uint32_t* src = stv + (2 * nb + (l16 >> 3)) * M::TS + tk;
-          const uint4 x0 = *reinterpret_cast<const uint4*>(src);
-          const uint4 x1 = *reinterpret_cast<const uint4*>(src + 16);
-          x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w; x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
-          bit = 4 * (l16 & 7);
-        }
-        // code c -> fp16 1 + c / 2^MV: the code dropped into the mantissa under 1.0's exponent
-        constexpr int MV = (VB == 2) ? 8 : 6;
-        mma_u4_t bv;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const uint32_t c0 = __builtin_amdgcn_ubfe(x[2 * k], (uint32_t)bit, VB);
-          const uint32_t c1 = __builtin_amdgcn_ubfe(x[2 * k + 1], (uint32_t)bit, VB);
-          bv[k] = (c0 << MV) | (c1 << (16 + MV)) | kOne;
-        }
-        acc[nb] = mma16(apv[nb / 2], bv, acc[nb]);
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
