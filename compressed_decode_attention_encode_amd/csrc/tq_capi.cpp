@@ -427,4 +427,47 @@ int tq_decode_attn(const tq_layout* L, const tq_state* S, const void* q, const t
   return TQ_OK;
 }
 
+size_t tq_decode_multi_workspace_bytes(const tq_layout* L, int batch, int n_query, int max_compressed) {
+  if (check_layout(L) || batch <= 0 || n_query <= 0 || n_query > kMaxQueries || max_compressed < 0) return 0;
+  return decode_multi_ws_bound(*L, batch, n_query, max_compressed);
+}
+
+int tq_decode_attn_multi(const tq_layout* L, const tq_state* S, const void* q, int n_query, const tq_cache* C,
+                         int n_compressed, const void* recent_k, const void* recent_v, int n_recent,
+                         int recent_capacity, float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_layout(L);
+  if (rc) return rc;
+  if (n_query < 1 || n_query > kMaxQueries) return fail(TQ_ERR_INVALID, "n_query %d outside 1..%d", n_query, kMaxQueries);
+  if (n_recent < n_query)
+    return fail(TQ_ERR_INVALID, "n_recent %d < n_query %d: the queries' own keys/values must be the last recent tokens",
+                n_recent, n_query);
+  if (n_query == 1)
+    return tq_decode_attn(L, S, q, C, n_compressed, recent_k, recent_v, n_recent, recent_capacity, out, workspace,
+                          workspace_bytes, stream);
+  if (!q || !out || !workspace) return fail(TQ_ERR_INVALID, "q, out and workspace must be non-NULL");
+  if (!aligned16(q) || !aligned16(out) || !aligned16(workspace))
+    return fail(TQ_ERR_INVALID, "q, out and workspace must be 16-byte aligned");
+  if (n_compressed < 0) return fail(TQ_ERR_INVALID, "negative token count");
+  if (n_recent > kMaxRecent) return fail(TQ_ERR_INVALID, "n_recent %d > %d", n_recent, kMaxRecent);
+  if (!recent_k || !recent_v) return fail(TQ_ERR_INVALID, "recent_k/recent_v are NULL with n_recent %d", n_recent);
+  if (!aligned16(recent_k) || !aligned16(recent_v)) return fail(TQ_ERR_INVALID, "recent buffers must be 16-byte aligned");
+  if (recent_capacity < n_recent) return fail(TQ_ERR_INVALID, "recent_capacity %d < n_recent %d", recent_capacity, n_recent);
+  if ((rc = check_cache(C, n_compressed > 0, n_compressed > 0, L))) return rc;
+  if ((rc = check_state(S, L, true, true))) return rc;
+  if (L->k_kind == TQ_K_LM_QJL && (!S->k_signs || !S->qjl)) return fail(TQ_ERR_INVALID, "k_signs and qjl are needed");
+  if (n_compressed > C->capacity)
+    return fail(TQ_ERR_CAPACITY, "n_compressed %d > capacity %d", n_compressed, C->capacity);
+  if (!decode_multi_compiled(*L, n_query))
+    return fail(TQ_ERR_UNSUPPORTED,
+                "no multi-query decode kernel for head_dim %d, n_rep %d, n_query %d, key/value kinds %d/%d bits %d/%d",
+                L->head_dim, L->n_q_heads / L->n_kv_heads, n_query, L->k_kind, L->k_bits, L->v_kind, L->v_bits);
+  DecodePlan plan = plan_decode(*L, C->batch, n_compressed);
+  const size_t need = decode_multi_ws_bound(*L, C->batch, n_query, n_compressed);
+  if (workspace_bytes < need) return fail(TQ_ERR_INVALID, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  hipError_t e = launch_decode_multi(*L, *S, q, n_query, *C, n_compressed, recent_k, recent_v, n_recent,
+                                     recent_capacity, out, workspace, plan, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(TQ_ERR_HIP, "multi-query decode launch: %s", hipGetErrorString(e));
+  return TQ_OK;
+}
+
 }  // extern "C"

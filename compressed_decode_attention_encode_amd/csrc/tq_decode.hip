@@ -184,6 +184,12 @@ size_t decode_ws_bound(const tq_layout& L, int batch, int max_c) {
   return ws_layout_bytes(L, batch, max_splits(L, batch, std::max(max_c, 0)));
 }
 
+// Multi-query decode: the splits are planned over the (batch, kv-head) units as for one
+// query; the partials hold one row per (batch, query, q-head).
+size_t decode_multi_ws_bound(const tq_layout& L, int batch, int n_query, int max_c) {
+  return ws_layout_bytes(L, batch * n_query, max_splits(L, batch, std::max(max_c, 0)));
+}
+
 namespace {
 
 int device_cus() {
@@ -240,12 +246,24 @@ hipError_t run_finish(const DecodeArgs& A, int batch, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Multi-query instantiations (LM + QJL keys, group values): n_rep query heads, nq queries.
+MainKernel find_multi(const tq_layout& L, int nq) {
+  const int nrep = L.n_q_heads / L.n_kv_heads;
+  if (L.k_kind != TQ_K_LM_QJL || L.v_kind != TQ_V_GROUP_SYM) return MainKernel{nullptr, nullptr};
+  if (L.head_dim == 64 && L.k_bits == 3) return find_multi_lm3_d64(nrep, nq, L.v_bits);
+  if (L.head_dim == 64 && L.k_bits == 4) return find_multi_lm4_d64(nrep, nq, L.v_bits);
+  if (L.head_dim == 128 && L.k_bits == 3) return find_multi_lm3_d128(nrep, nq, L.v_bits);
+  if (L.head_dim == 128 && L.k_bits == 4) return find_multi_lm4_d128(nrep, nq, L.v_bits);
+  return MainKernel{nullptr, nullptr};
+}
+
+// One decode launch sequence: the split kernel `mk` over (split, kv-head, batch) groups, then
+// the merge over (q-head, batch x nq) rows.
 template <int D>
 hipError_t run_decode_d(const tq_layout& L, const tq_state& S, const void* q, const tq_cache& C, int n_c,
                         const void* rk, const void* rv, int n_recent, int rcap, float* out, void* ws,
-                        const DecodePlan& plan, hipStream_t st) {
+                        const DecodePlan& plan, hipStream_t st, const MainKernel& mk, int nq) {
   const int batch = C.batch;
-  const MainKernel mk = find_main(L);
   if (!mk.launch) return hipErrorInvalidDeviceFunction;
   // splits: one round of resident work-groups over all (batch, kv-head) units, within the
   // planned maximum; every split a whole number of tiles
@@ -294,8 +312,8 @@ hipError_t run_decode_d(const tq_layout& L, const tq_state& S, const void* q, co
     const hipError_t e = mk.launch(dim3((unsigned)groups), st, A);
     if (e != hipSuccess) return e;
   }
-  return (L.v_kind == TQ_V_GROUP_SYM) ? run_finish<D, TQ_V_GROUP_SYM>(A, batch, st)
-                                      : run_finish<D, TQ_V_LM_ROT>(A, batch, st);
+  return (L.v_kind == TQ_V_GROUP_SYM) ? run_finish<D, TQ_V_GROUP_SYM>(A, batch * nq, st)
+                                      : run_finish<D, TQ_V_LM_ROT>(A, batch * nq, st);
 }
 
 }  // namespace
@@ -309,10 +327,27 @@ bool decode_compiled(const tq_layout& L) {
 hipError_t launch_decode(const tq_layout& L, const tq_state& S, const void* q, const tq_cache& C, int n_c,
                          const void* rk, const void* rv, int n_recent, int rcap, float* out, void* ws,
                          const DecodePlan& plan, hipStream_t st) {
+  const MainKernel mk = find_main(L);
   switch (L.head_dim) {
-    case 64: return run_decode_d<64>(L, S, q, C, n_c, rk, rv, n_recent, rcap, out, ws, plan, st);
-    case 128: return run_decode_d<128>(L, S, q, C, n_c, rk, rv, n_recent, rcap, out, ws, plan, st);
-    case 256: return run_decode_d<256>(L, S, q, C, n_c, rk, rv, n_recent, rcap, out, ws, plan, st);
+    case 64: return run_decode_d<64>(L, S, q, C, n_c, rk, rv, n_recent, rcap, out, ws, plan, st, mk, 1);
+    case 128: return run_decode_d<128>(L, S, q, C, n_c, rk, rv, n_recent, rcap, out, ws, plan, st, mk, 1);
+    case 256: return run_decode_d<256>(L, S, q, C, n_c, rk, rv, n_recent, rcap, out, ws, plan, st, mk, 1);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+bool decode_multi_compiled(const tq_layout& L, int n_query) {
+  if (L.n_kv_heads <= 0 || L.n_q_heads % L.n_kv_heads) return false;
+  return find_multi(L, n_query).launch != nullptr;
+}
+
+hipError_t launch_decode_multi(const tq_layout& L, const tq_state& S, const void* q, int n_query, const tq_cache& C,
+                               int n_c, const void* rk, const void* rv, int n_recent, int rcap, float* out, void* ws,
+                               const DecodePlan& plan, hipStream_t st) {
+  const MainKernel mk = find_multi(L, n_query);
+  switch (L.head_dim) {
+    case 64: return run_decode_d<64>(L, S, q, C, n_c, rk, rv, n_recent, rcap, out, ws, plan, st, mk, n_query);
+    case 128: return run_decode_d<128>(L, S, q, C, n_c, rk, rv, n_recent, rcap, out, ws, plan, st, mk, n_query);
     default: return hipErrorInvalidValue;
   }
 }

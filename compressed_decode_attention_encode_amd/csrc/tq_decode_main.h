@@ -174,6 +174,15 @@ __device__ __forceinline__ float bits16_to_f32(uint32_t bits, int bf16) {
   return bf16 ? __uint_as_float(bits << 16) : f16_to_f32(bits);
 }
 
+// Query rows of one (batch, kv-head) group: NR = NQ x n_rep rows, row r = query j = r / n_rep of
+// the step's NQ consecutive queries, head g n_rep + r % n_rep.  Queries are [B][NQ][Hq][d]; with
+// NQ = 1 this is [B][Hq][d].  Partials are indexed by (b NQ + j, head).
+template <int D, int NR, int NQ>
+__device__ __forceinline__ const uint16_t* query_row(const DecodeArgs& A, int b, int g, int r) {
+  constexpr int NK = NR / NQ;
+  return A.q + ((size_t)(b * NQ + r / NK) * A.Hq + g * NK + r % NK) * D;
+}
+
 // NE consecutive floats of a table entry (16-byte aligned for NE >= 4).
 template <int NE>
 __device__ __forceinline__ void read_entry(const float* p, float (&e)[NE]) {
@@ -195,7 +204,7 @@ __device__ __forceinline__ void read_entry(const float* p, float (&e)[NE]) {
 //   LM + QJL keys: qa = Pi q * log2(e)/sqrt(d), qb = S Pi q * log2(e)/sqrt(d) * sqrt(pi/2)/d,
 //                  then the QJL table;
 //   affine keys:   qa = q * log2(e)/sqrt(d), qb[h][blk] = sum of qa over the 32-block.
-template <int D, int NREP, int KK, int KB, int VK, int VB, bool TABLE = true>
+template <int D, int NREP, int KK, int KB, int VK, int VB, bool TABLE = true, int NQ = 1>
 __device__ void prepare_queries(const DecodeArgs& A, int b, int g, float* sm) {
   using G = DecodeGeom<D, NREP, KK, KB, VK, VB>;
   constexpr int NE = G::NE;
@@ -203,7 +212,6 @@ __device__ void prepare_queries(const DecodeArgs& A, int b, int g, float* sm) {
   float* qa = sm + G::OFF_QA;
   float* qb = sm + G::OFF_QB;
   const float scale = kLog2e * rsqrtf((float)D);
-  const uint16_t* qsrc = A.q + (size_t)(b * A.Hq + g * NREP) * D;
   if constexpr (KK == TQ_K_LM_QJL || KK == TQ_K_LM_MSE) {
     constexpr bool QJL = KK == TQ_K_LM_QJL;
     // this thread's slice of S (row i, columns part*KL ..): its first reads go out first
@@ -227,7 +235,7 @@ __device__ void prepare_queries(const DecodeArgs& A, int b, int g, float* sm) {
 #pragma unroll
         for (int e = 0; e < E; ++e) {
           const int j = lane * E + e;
-          const float v = bits16_to_f32(qsrc[h * D + j], A.q_bf16);
+          const float v = bits16_to_f32(query_row<D, NREP, NQ>(A, b, g, h)[j], A.q_bf16);
           x[e] = ((A.ksign[j >> 5] >> (j & 31)) & 1u) ? -v : v;
         }
 #pragma unroll
@@ -316,7 +324,8 @@ __device__ void prepare_queries(const DecodeArgs& A, int b, int g, float* sm) {
       }
     }
   } else {
-    for (int i = tid; i < NREP * D; i += 256) qa[i] = bits16_to_f32(qsrc[i], A.q_bf16) * scale;
+    for (int i = tid; i < NREP * D; i += 256)
+      qa[i] = bits16_to_f32(query_row<D, NREP, NQ>(A, b, g, i / D)[i % D], A.q_bf16) * scale;
     __syncthreads();
     for (int i = tid; KK == TQ_K_AFFINE8 && i < NREP * (D / 32); i += 256) {
       const int h = i / (D / 32), blk = i % (D / 32);
@@ -339,7 +348,11 @@ __device__ __forceinline__ float* partial_ptr(const DecodeArgs& A, int b, int he
 // global read is issued on entry, before any is used: two threads per token row (half a
 // row each) for the scores, and value columns as thread = (dimension, token subset), 32
 // rows at a time.
-template <int D, int NREP, int KK, int KB, int VK, int VB>
+//
+// With NQ > 1 (multi-query groups, NREP = NQ x n_rep rows) the last NQ recent tokens are the
+// queries' own, in order, and query j sees recent tokens 0 .. R - NQ + j (causal inside the
+// suffix); R >= NQ is checked on the host, so every row sees at least one token.
+template <int D, int NREP, int KK, int KB, int VK, int VB, int NQ = 1>
 __device__ void recent_split(const DecodeArgs& A, int b, int g, float* sm) {
   using G = DecodeGeom<D, NREP, KK, KB, VK, VB>;
   static_assert(kMaxRecent * 2 <= 256, "two threads per recent token");
@@ -373,8 +386,8 @@ __device__ void recent_split(const DecodeArgs& A, int b, int g, float* sm) {
 #pragma unroll
   for (int i = 0; i < VCH; ++i) vv[i] = A.rv[(rbase + min(grp + NG * i, R - 1)) * D + j];
   const float scale = kLog2e * rsqrtf((float)D);
-  const uint16_t* qsrc = A.q + (size_t)(b * A.Hq + g * NREP) * D;
-  for (int i = tid; i < NREP * D; i += 256) qn[i] = bits16_to_f32(qsrc[i], A.q_bf16) * scale;
+  for (int i = tid; i < NREP * D; i += 256)
+    qn[i] = bits16_to_f32(query_row<D, NREP, NQ>(A, b, g, i / D)[i % D], A.q_bf16) * scale;
   __syncthreads();
   // scores: each thread dots its half row with every head, the pair adds its halves
 #pragma unroll 1
@@ -391,7 +404,7 @@ __device__ void recent_split(const DecodeArgs& A, int b, int g, float* sm) {
       }
     }
     a += xor_lanes<1>(a);
-    if (half == 0 && r_k < R) sr[h * kMaxRecent + r_k] = a;
+    if (half == 0 && r_k < R) sr[h * kMaxRecent + r_k] = (r_k <= R - NQ + h / (NREP / NQ)) ? a : -INFINITY;
   }
   __syncthreads();
   for (int h = wave; h < NREP; h += 4) {
@@ -435,7 +448,8 @@ __device__ void recent_split(const DecodeArgs& A, int b, int g, float* sm) {
     float a = 0.f;
 #pragma unroll
     for (int q = 0; q < NG; ++q) a += sacc[(q * NREP + h) * D + jj];
-    float* dst = partial_ptr<D>(A, b, g * NREP + h, A.nsplit);
+    constexpr int NK = NREP / NQ;
+    float* dst = partial_ptr<D>(A, b * NQ + h / NK, g * NK + h % NK, A.nsplit);
     dst[4 + jj] = a;
     if (jj == 0) { dst[0] = sML[h]; dst[1] = sML[NREP + h]; }
   }
@@ -968,5 +982,10 @@ MainKernel find_main_lmm3_d256(int nrep, int vk, int vb);
 MainKernel find_main_lmm4_d256(int nrep, int vk, int vb);
 MainKernel find_main_f16_d64(int nrep, int vk, int vb);
 MainKernel find_main_f16_d128(int nrep, int vk, int vb);
+// multi-query groups (LM + QJL keys, group values): n_rep heads x nq queries, vb value bits
+MainKernel find_multi_lm3_d64(int nrep, int nq, int vb);
+MainKernel find_multi_lm4_d64(int nrep, int nq, int vb);
+MainKernel find_multi_lm3_d128(int nrep, int nq, int vb);
+MainKernel find_multi_lm4_d128(int nrep, int nq, int vb);
 
 }  // namespace tq

@@ -86,16 +86,21 @@ struct MmaGeom {
   static constexpr int OFF_PT = OFF_BQ + 2 * NRB * D;
   static constexpr int OFF_SGT = OFF_PT + 2 * NPT;
   static constexpr int OFF_ST = OFF_SGT + 4 * 256;
-  static constexpr int OFF_MRG = OFF_ST + 4 * STAGE;
+  // the four staging areas also hold the waves' value sums for the merge
+  static constexpr int STAGE_ALL = (4 * STAGE > 4 * NREP * D) ? 4 * STAGE : 4 * NREP * D;
+  static constexpr int OFF_MRG = OFF_ST + STAGE_ALL;
   static constexpr int OWN = OFF_MRG + 8 * NREP + 16;
   static constexpr int FLOATS = OWN > G::FLOATS ? OWN : G::FLOATS;   // the recent split shares it
-  static_assert(4 * STAGE >= 4 * NREP * D, "merge buffer does not fit in the staging area");
   static_assert(NREP <= 16, "one 16-column operand holds the heads");
 };
 
-template <int D, int NREP, int KB, int VB>
+// NQ > 1: a multi-query group.  The NQ x n_rep rows (query j, head h at row j n_rep + h) take
+// the operand columns of the heads, so the score and value products cost the same per tile;
+// only the softmax and the output rows grow.  Below, NREP counts rows.
+template <int D, int NREP_KV, int KB, int VB, int NQ = 1>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 2)))
 decode_mma_kernel(const DecodeArgs A) {
+  constexpr int NREP = NQ * NREP_KV;
   using M = MmaGeom<D, NREP, KB, VB>;
   constexpr int LK = 1 << KB;
   constexpr int LV = 1 << VB;
@@ -112,7 +117,7 @@ decode_mma_kernel(const DecodeArgs A) {
   const int n_comp = A.nsplit * A.Hkv * A.batch;
   if ((int)blockIdx.x >= n_comp) {
     const int u = blockIdx.x - n_comp;
-    recent_split<D, NREP, TQ_K_LM_QJL, KB, TQ_V_GROUP_SYM, VB>(A, u / A.Hkv, u % A.Hkv, sm);
+    recent_split<D, NREP, TQ_K_LM_QJL, KB, TQ_V_GROUP_SYM, VB, NQ>(A, u / A.Hkv, u % A.Hkv, sm);
     return;
   }
   const int split = blockIdx.x % A.nsplit;
@@ -161,7 +166,7 @@ decode_mma_kernel(const DecodeArgs A) {
     for (int k = 0; k < 4; ++k)
       smw[M::OFF_SGT + 4 * i + k] = (((i >> (2 * k)) & 1) ? 0u : 0x8000u) | (((i >> (2 * k + 1)) & 1) ? 0u : 0x80000000u);
   }
-  prepare_queries<D, NREP, TQ_K_LM_QJL, KB, TQ_V_GROUP_SYM, VB, false>(A, b, g, sm);
+  prepare_queries<D, NREP, TQ_K_LM_QJL, KB, TQ_V_GROUP_SYM, VB, false, NQ>(A, b, g, sm);
   {
     // fp16 query operands (hi, lo) from the prepared fp32 queries
     const float* qa = sm + M::G::OFF_QA;
@@ -421,7 +426,7 @@ decode_mma_kernel(const DecodeArgs A) {
       a = fmaf(s_mrg_acc[w][h * D + j], sc, a);
       l = fmaf(s_mrg_l[w * NREP + h], sc, l);
     }
-    float* dst = partial_ptr<D>(A, b, g * NREP + h, split);
+    float* dst = partial_ptr<D>(A, b * NQ + h / NREP_KV, g * NREP_KV + h % NREP_KV, split);
     dst[4 + j] = a;
     if (j == 0) {
       dst[0] = mxw;
@@ -430,17 +435,18 @@ decode_mma_kernel(const DecodeArgs A) {
   }
 }
 
-template <int D, int NREP, int KB, int VB>
+template <int D, int NREP, int KB, int VB, int NQ>
 hipError_t mma_launch(dim3 grid, hipStream_t st, const DecodeArgs& A) {
-  hipLaunchKernelGGL((decode_mma_kernel<D, NREP, KB, VB>), grid, dim3(256), 0, st, A);
+  hipLaunchKernelGGL((decode_mma_kernel<D, NREP, KB, VB, NQ>), grid, dim3(256), 0, st, A);
   return hipGetLastError();
 }
 
-template <int D, int NREP, int KB, int VB>
+template <int D, int NREP, int KB, int VB, int NQ>
 int mma_blocks_per_cu() {
   static const int n = [] {
     int b = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, decode_mma_kernel<D, NREP, KB, VB>, 256, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, decode_mma_kernel<D, NREP, KB, VB, NQ>, 256, 0) !=
+            hipSuccess ||
         b <= 0)
       b = 1;
     return b;
@@ -448,9 +454,10 @@ int mma_blocks_per_cu() {
   return n;
 }
 
-template <int D, int NREP, int KB, int VB>
+// n_rep query heads per kv-head, NQ queries per step
+template <int D, int NREP, int KB, int VB, int NQ = 1>
 constexpr MainKernel mma_kernel() {
-  return MainKernel{&mma_launch<D, NREP, KB, VB>, &mma_blocks_per_cu<D, NREP, KB, VB>};
+  return MainKernel{&mma_launch<D, NREP, KB, VB, NQ>, &mma_blocks_per_cu<D, NREP, KB, VB, NQ>};
 }
 
 }  // namespace tq

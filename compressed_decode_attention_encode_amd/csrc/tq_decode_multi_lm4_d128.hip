@@ -1,0 +1,33 @@
+// Compiled instantiations of the multi-query decode kernel (several consecutive queries per
+// step against one pass over the packed cache) for 4-bit Lloyd-Max + QJL keys, head_dim 128,
+// group-32 symmetric 2/4-bit values: n_rep 1, 2, 4 with 2, 4 or 8 queries, n_query x n_rep <= 16.
+#include "tq_decode_mma.h"
+
+namespace tq {
+
+namespace {
+template <int VB>
+MainKernel pick(int nrep, int nq) {
+  if (nq == 2) {
+    if (nrep == 1) return mma_kernel<128, 1, 4, VB, 2>();
+    if (nrep == 2) return mma_kernel<128, 2, 4, VB, 2>();
+    if (nrep == 4) return mma_kernel<128, 4, 4, VB, 2>();
+  } else if (nq == 4) {
+    if (nrep == 1) return mma_kernel<128, 1, 4, VB, 4>();
+    if (nrep == 2) return mma_kernel<128, 2, 4, VB, 4>();
+    if (nrep == 4) return mma_kernel<128, 4, 4, VB, 4>();
+  } else if (nq == 8) {
+    if (nrep == 1) return mma_kernel<128, 1, 4, VB, 8>();
+    if (nrep == 2) return mma_kernel<128, 2, 4, VB, 8>();
+  }
+  return MainKernel{nullptr, nullptr};
+}
+}  // namespace
+
+MainKernel find_multi_lm4_d128(int nrep, int nq, int vb) {
+  if (vb == 2) return pick<2>(nrep, nq);
+  if (vb == 4) return pick<4>(nrep, nq);
+  return MainKernel{nullptr, nullptr};
+}
+
+}  // namespace tq

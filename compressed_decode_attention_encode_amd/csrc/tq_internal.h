@@ -14,6 +14,9 @@ namespace tq {
 constexpr int kTile = 64;
 // Largest recent buffer accepted by the decode (vLLM guide, section 5: 128-token buffer).
 constexpr int kMaxRecent = 128;
+// Most queries of one multi-query decode step (vllm-metal guide, prefill section: short
+// suffixes and speculative verification stay on the compressed kernels).
+constexpr int kMaxQueries = 8;
 // Decode work-group count the split bound is sized for (4 per CU on 256 CUs), and the
 // fewest 64-token tiles a split gets (two per wave: the query preparation is amortised
 // over eight tiles).
@@ -40,6 +43,7 @@ struct DecodePlan {
 };
 DecodePlan plan_decode(const tq_layout& L, int batch, int n_compressed);
 size_t decode_ws_bound(const tq_layout& L, int batch, int max_compressed);
+size_t decode_multi_ws_bound(const tq_layout& L, int batch, int n_query, int max_compressed);
 
 // Launchers (enqueue only; argument checks are done by the caller).
 hipError_t launch_encode_k(const tq_layout& L, const tq_state& S, const void* k, int batch, int n_tokens,
@@ -50,6 +54,9 @@ hipError_t launch_decode(const tq_layout& L, const tq_state& S, const void* q, c
                          int n_compressed, const void* rk, const void* rv, int n_recent, int recent_cap,
                          float* out, void* ws, const DecodePlan& plan, hipStream_t st);
 
+hipError_t launch_decode_multi(const tq_layout& L, const tq_state& S, const void* q, int n_query, const tq_cache& C,
+                               int n_compressed, const void* rk, const void* rv, int n_recent, int recent_cap,
+                               float* out, void* ws, const DecodePlan& plan, hipStream_t st);
 hipError_t launch_materialize_k(const tq_layout& L, const tq_state& S, const tq_cache& C, int t0, int n_tokens,
                                 void* out, int out_dtype, hipStream_t st);
 hipError_t launch_materialize_v(const tq_layout& L, const tq_state& S, const tq_cache& C, int t0, int n_tokens,
@@ -59,6 +66,7 @@ hipError_t launch_materialize_v(const tq_layout& L, const tq_state& S, const tq_
 bool encode_k_compiled(const tq_layout& L);
 bool encode_v_compiled(const tq_layout& L);
 bool decode_compiled(const tq_layout& L);
+bool decode_multi_compiled(const tq_layout& L, int n_query);
 bool materialize_compiled(const tq_layout& L);
 
 // Per-thread error message (set by the C-ABI entry points and launchers).

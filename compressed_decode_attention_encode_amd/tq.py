@@ -46,7 +46,8 @@ TQ_K_LM_QJL, TQ_K_AFFINE8, TQ_K_LM_MSE, TQ_K_F16 = 0, 1, 2, 3
 TQ_V_GROUP_SYM, TQ_V_LM_ROT = 0, 1
 
 EXPORTED = ("tq_make_codebook", "tq_make_rotation", "tq_cache_plane_bytes", "tq_encode",
-            "tq_decode_workspace_bytes", "tq_decode_attn", "tq_materialize", "tq_strerror", "tq_last_error")
+            "tq_decode_workspace_bytes", "tq_decode_attn", "tq_decode_multi_workspace_bytes", "tq_decode_attn_multi",
+            "tq_materialize", "tq_strerror", "tq_last_error")
 
 
 class tq_layout(ctypes.Structure):
@@ -77,6 +78,11 @@ _lib.tq_decode_workspace_bytes.argtypes = [ctypes.POINTER(tq_layout), ctypes.c_i
 _lib.tq_decode_workspace_bytes.restype = ctypes.c_size_t
 _lib.tq_decode_attn.argtypes = [ctypes.POINTER(tq_layout), ctypes.POINTER(tq_state), _P, ctypes.POINTER(tq_cache),
                                 ctypes.c_int, _P, _P, ctypes.c_int, ctypes.c_int, _P, _P, ctypes.c_size_t, _P]
+_lib.tq_decode_multi_workspace_bytes.argtypes = [ctypes.POINTER(tq_layout), ctypes.c_int, ctypes.c_int, ctypes.c_int]
+_lib.tq_decode_multi_workspace_bytes.restype = ctypes.c_size_t
+_lib.tq_decode_attn_multi.argtypes = [ctypes.POINTER(tq_layout), ctypes.POINTER(tq_state), _P, ctypes.c_int,
+                                      ctypes.POINTER(tq_cache), ctypes.c_int, _P, _P, ctypes.c_int, ctypes.c_int, _P, _P,
+                                      ctypes.c_size_t, _P]
 _lib.tq_materialize.argtypes = [ctypes.POINTER(tq_layout), ctypes.POINTER(tq_state), ctypes.POINTER(tq_cache),
                                 ctypes.c_int, ctypes.c_int, _P, _P, ctypes.c_int, _P]
 _lib.tq_strerror.argtypes = [ctypes.c_int]
@@ -165,6 +171,18 @@ def tq_decode_attn(layout: tq_layout, state: tq_state, q, cache: tq_cache, n_com
     _check(_lib.tq_decode_attn(ctypes.byref(layout), ctypes.byref(state), _ptr(q), ctypes.byref(cache), n_compressed,
                                _ptr(recent_k), _ptr(recent_v), n_recent, recent_capacity, _ptr(out), _ptr(workspace),
                                workspace_bytes, _stream(stream)))
+
+
+def tq_decode_multi_workspace_bytes(layout: tq_layout, batch: int, n_query: int, max_compressed: int) -> int:
+    return int(_lib.tq_decode_multi_workspace_bytes(ctypes.byref(layout), batch, n_query, max_compressed))
+
+
+def tq_decode_attn_multi(layout: tq_layout, state: tq_state, q, n_query: int, cache: tq_cache, n_compressed: int,
+                         recent_k, recent_v, n_recent: int, recent_capacity: int, out, workspace, workspace_bytes: int,
+                         stream=None) -> None:
+    _check(_lib.tq_decode_attn_multi(ctypes.byref(layout), ctypes.byref(state), _ptr(q), n_query, ctypes.byref(cache),
+                                     n_compressed, _ptr(recent_k), _ptr(recent_v), n_recent, recent_capacity, _ptr(out),
+                                     _ptr(workspace), workspace_bytes, _stream(stream)))
 
 
 def tq_materialize(layout: tq_layout, state: tq_state, cache: tq_cache, t0: int, n_tokens: int, out_k, out_v,

@@ -211,6 +211,13 @@ def q_bits(wl: Workload, variant: str = "normal") -> np.ndarray:
     return to_storage(q, wl.in_dtype)
 
 
+def q_bits_multi(wl: Workload, n_query: int) -> np.ndarray:
+    """Queries of a multi-query decode step [B, n_query, Hq, d] as storage bits, N(0,1)."""
+    rng = _rng(wl, ROLE_Q, 1 + n_query)
+    q = rng.standard_normal((wl.batch, n_query, wl.n_q_heads, wl.head_dim), dtype=np.float32)
+    return to_storage(q, wl.in_dtype)
+
+
 def rotation_signs(wl: Workload, which: str) -> np.ndarray:
     """Random sign vector s in {+1,-1}^d of one rotation (shared by all heads and tokens).
 

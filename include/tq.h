@@ -205,6 +205,34 @@ int tq_decode_attn(const tq_layout* layout, const tq_state* state, const void* q
                    const void* recent_k, const void* recent_v, int n_recent, int recent_capacity,
                    float* out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Workspace bytes tq_decode_attn_multi needs for n_query queries and any
+ * n_compressed <= max_compressed (0 for an invalid layout or n_query outside 1..8). */
+size_t tq_decode_multi_workspace_bytes(const tq_layout* layout, int batch, int n_query, int max_compressed);
+
+/* Multi-query decode attention: n_query consecutive query tokens per sequence (a short
+ * suffix, or the draft tokens of a speculative step) scored against the same cache in
+ * one pass over the packed planes (vllm-metal guide, prefill section: short suffixes,
+ * decode steps and speculative verification stay on the compressed kernels; the scores
+ * and values are those of tq_decode_attn).  The caller appends the queries' own keys
+ * and values to the recent buffer first: its last n_query tokens are the queries', in
+ * order, and query j (0-based) attends to every compressed token and to recent tokens
+ * 0 .. n_recent - n_query + j (causal inside the suffix).  With n_query == 1 this is
+ * exactly tq_decode_attn.
+ *   q          device [batch][n_query][n_q_heads][head_dim], layout->in_dtype
+ *   out        device float [batch][n_query][n_q_heads][head_dim]
+ *   n_recent   n_query..128, <= recent_capacity; recent_k/v as for tq_decode_attn
+ *   workspace  device, >= tq_decode_multi_workspace_bytes(layout, batch, n_query, n_compressed)
+ * Compiled for LM_QJL keys (3 or 4 bits) with GROUP_SYM values (2 or 4 bits), head_dim 64
+ * and 128, n_rep 1, 2, 4 with n_query 2, 4, 8 and n_query * n_rep <= 16 (the query
+ * rows share one 16-column matrix-core operand); other combinations with n_query > 1
+ * return TQ_ERR_UNSUPPORTED.  Errors: TQ_ERR_INVALID when n_query is outside 1..8,
+ * n_recent < n_query or > 128, a needed pointer is null/misaligned or the workspace is
+ * too small; TQ_ERR_CAPACITY; TQ_ERR_UNSUPPORTED; TQ_ERR_HIP. */
+int tq_decode_attn_multi(const tq_layout* layout, const tq_state* state, const void* q, int n_query,
+                         const tq_cache* cache, int n_compressed,
+                         const void* recent_k, const void* recent_v, int n_recent, int recent_capacity,
+                         float* out, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Materialisation: dequantise cache slots [t0, t0 + n_tokens) of every (batch,
  * kv-head) slice into natural-domain rows (vllm-metal guide, prefill section: long
  * prefills materialise the compressed history and run ordinary attention on it; vLLM

@@ -115,6 +115,26 @@ def decode_attention(lay, q: np.ndarray, planes: dict, n_compressed: int, state:
     return out
 
 
+def decode_attention_multi(lay, q: np.ndarray, planes: dict, n_compressed: int, state: dict,
+                           recent_k: np.ndarray, recent_v: np.ndarray) -> np.ndarray:
+    """Several consecutive queries per step (vllm-metal guide, prefill section: a short suffix
+    or the draft tokens of speculative verification read the compressed cache directly).
+
+    q: float64 [B, NQ, Hq, d]; recent_*: float64 [B, Hkv, R, d] whose last NQ tokens are the
+    queries' own keys/values, in order.  Query j attends to every compressed token and to
+    recent tokens 0 .. R - NQ + j (causal inside the suffix): it is the single-query decode
+    with the recent buffer cut after its own token.  Returns float64 [B, NQ, Hq, d].
+    """
+    B, NQ, Hq, d = q.shape
+    R = recent_k.shape[2]
+    assert R >= NQ, "the queries' own tokens are the last NQ recent tokens"
+    out = np.empty((B, NQ, Hq, d))
+    for j in range(NQ):
+        lim = R - NQ + j + 1
+        out[:, j] = decode_attention(lay, q[:, j], planes, n_compressed, state, recent_k[:, :, :lim], recent_v[:, :, :lim])
+    return out
+
+
 def reconstruct_k(lay, kd: dict, state: dict) -> np.ndarray:
     """Explicit natural-domain key estimate n Pi^T (c[idx] + gamma sqrt(pi/2)/d S^T sigma)."""
     d = lay.head_dim

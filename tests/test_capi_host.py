@@ -156,6 +156,38 @@ def test_decode_rejects_bad_arguments():
     assert e.value.status == tq.TQ_ERR_UNSUPPORTED
 
 
+def test_multi_query_decode_rejects_bad_arguments():
+    """Host-side checks of tq_decode_attn_multi: every rejection happens before any HIP call."""
+    L = _layout(head_dim=64, n_q_heads=8, n_kv_heads=2)       # n_rep 4
+    ws = tq.tq_decode_multi_workspace_bytes(L, 1, 4, 256)
+    assert ws > tq.tq_decode_multi_workspace_bytes(L, 1, 2, 256) > 0
+    assert tq.tq_decode_multi_workspace_bytes(L, 1, 2, 256) == 2 * tq.tq_decode_workspace_bytes(L, 1, 256)
+    assert tq.tq_decode_multi_workspace_bytes(L, 1, 0, 256) == 0
+    assert tq.tq_decode_multi_workspace_bytes(L, 1, 9, 256) == 0
+    base = dict(L=L, nq=4, q=FAKE, n_c=100, rk=FAKE, rv=FAKE, n_r=8, rcap=128, out=FAKE, ws=FAKE, wsb=ws, cache=_cache())
+    cases = [
+        (dict(nq=0), tq.TQ_ERR_INVALID),
+        (dict(nq=9), tq.TQ_ERR_INVALID),
+        (dict(n_r=3), tq.TQ_ERR_INVALID),                # fewer recent tokens than queries
+        (dict(n_r=129, rcap=256), tq.TQ_ERR_INVALID),
+        (dict(rk=None), tq.TQ_ERR_INVALID),
+        (dict(wsb=ws - 1), tq.TQ_ERR_INVALID),
+        (dict(n_c=300), tq.TQ_ERR_CAPACITY),
+        (dict(q=FAKE + 4), tq.TQ_ERR_INVALID),
+        (dict(nq=8), tq.TQ_ERR_UNSUPPORTED),             # 8 x 4 rows > 16
+        (dict(nq=3), tq.TQ_ERR_UNSUPPORTED),
+        (dict(L=_layout(head_dim=256, n_q_heads=4, n_kv_heads=2)), tq.TQ_ERR_UNSUPPORTED),
+        (dict(L=_layout(head_dim=64, k_kind="affine8", k_bits=8, v_kind="lm_rot", v_bits=3)), tq.TQ_ERR_UNSUPPORTED),
+    ]
+    for over, code in cases:
+        a = dict(base)
+        a.update(over)
+        with pytest.raises(tq.TQError) as e:
+            tq.tq_decode_attn_multi(a["L"], _state(), a["q"], a["nq"], a["cache"], a["n_c"], a["rk"], a["rv"], a["n_r"],
+                                    a["rcap"], a["out"], a["ws"], a["wsb"])
+        assert e.value.status == code, (over, e.value)
+
+
 def test_materialize_rejects_bad_arguments():
     """Host-side checks of tq_materialize: every rejection happens before any HIP call."""
     L = _layout()

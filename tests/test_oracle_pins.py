@@ -394,6 +394,51 @@ def test_fast_decode_equals_bruteforce(kind, d):
     assert np.mean(cos) > 0.75 and np.min(cos) > 0.5
 
 
+@pytest.mark.parametrize("kind", [("lm_qjl", 3, "group_sym", 2), ("lm_qjl", 4, "group_sym", 4)])
+@pytest.mark.parametrize("nq", [2, 4])
+def test_multi_query_decode_is_causal_masked_attention(kind, nq):
+    """Several queries per step: one masked attention matrix over the reconstructed cache
+    (every query sees all compressed tokens; recent token r is visible to query j when
+    r <= R - NQ + j) equals the oracle, which cuts the recent buffer per query."""
+    d, T, Rn = 64, 37, 7
+    lay = Lay(d, 4, 2, *kind)
+    st = _rand_state(lay, 11)
+    rng = np.random.default_rng(12)
+    B = 2
+    k = rng.standard_normal((B, 2, T, d))
+    v = rng.standard_normal((B, 2, T, d))
+    pk, pv = C.encode_k(lay, k, st), C.encode_v(lay, v, st)
+    planes = {n: a for n, a in {**pk, **pv}.items() if n in ("k_codes", "k_signs", "k_aux", "v_codes", "v_aux")}
+    q = rng.standard_normal((B, nq, 4, d)) * 2
+    rk = rng.standard_normal((B, 2, Rn, d))
+    rv = rng.standard_normal((B, 2, Rn, d))
+    got = D.decode_attention_multi(lay, q, planes, T, st, rk, rv)
+    allowed = np.ones((nq, T + Rn), dtype=bool)
+    for j in range(nq):
+        allowed[j, T + (Rn - nq + j) + 1:] = False
+    for b in range(B):
+        for g in range(2):
+            sl = {n: planes[n][b, g, :T] for n in planes}
+            K = np.concatenate([D.reconstruct_k(lay, C.read_k(lay, sl, st), st), rk[b, g]])
+            V = np.concatenate([D.reconstruct_v(lay, C.read_v(lay, sl, st), st), rv[b, g]])
+            for h in range(2 * g, 2 * g + 2):
+                S = q[b, :, h] @ K.T / math.sqrt(d)                 # [nq, T + R]
+                S = np.where(allowed, S, -np.inf)
+                P = np.exp(S - S.max(axis=1, keepdims=True))
+                P /= P.sum(axis=1, keepdims=True)
+                assert np.max(np.abs(P @ V - got[b, :, h])) < 1e-12
+    # causality: tokens after a query's own position do not move it; the last query is the
+    # single-query decode over the whole buffer
+    rk2, rv2 = rk.copy(), rv.copy()
+    rk2[:, :, Rn - 1] += 5.0
+    rv2[:, :, Rn - 1] -= 3.0
+    got2 = D.decode_attention_multi(lay, q, planes, T, st, rk2, rv2)
+    assert np.array_equal(got2[:, :nq - 1], got[:, :nq - 1])
+    assert not np.allclose(got2[:, nq - 1], got[:, nq - 1])
+    one = D.decode_attention(lay, q[:, nq - 1], planes, T, st, rk, rv)
+    assert np.max(np.abs(one - got[:, nq - 1])) == 0.0
+
+
 def test_no_compressed_tokens_is_exact_sdpa():
     torch = pytest.importorskip("torch")
     lay = Lay(64, 4, 2, "lm_qjl", 3, "group_sym", 2)
