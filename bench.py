@@ -19,6 +19,8 @@ Prints one JSON line on stdout:
   roofline    the dominant kernel against its MI355X peak
   materialize tq_materialize of the whole history to fp16 rows (timed apart from the
               step: the dequantise path ahead of a dense prefill)
+  multi_query tq_decode_attn_multi with 4 queries (a speculative step) against 4
+              single-query decodes of the same cache (timed apart from the step)
   cpu_baseline  the CPU oracle timed on a bounded sample of the same workload
 """
 from __future__ import annotations
@@ -145,6 +147,59 @@ def bench_materialize(tq, lay, state, caches, wl, stream, steps: int, warmup: in
         res["qjl_tflops_fp16"] = 2.0 * d * d * rows / (ms * 1e-3) / 1e12
     del outs
     return res
+
+
+def bench_multi(tq, lay, state, caches, wl, stream, rk, rv, steps: int, warmup: int, n_query: int = 4) -> dict | None:
+    """tq_decode_attn_multi with n_query queries (a speculative step: the last n_query recent
+    tokens are the drafts' own) against n_query single-query decodes of the same cache, timed
+    apart from the step; None where the layout has no multi-query kernel."""
+    import torch
+    B, n, R = wl.batch, wl.n_compressed, wl.n_recent
+    if R < n_query:
+        return None
+    qm = torch.from_numpy(np.ascontiguousarray(W.q_bits_multi(wl, n_query)).view(np.int16)).cuda()
+    ws_m = tq.tq_decode_multi_workspace_bytes(lay, B, n_query, n)
+    if ws_m == 0:
+        return None
+    wsm = torch.empty(ws_m, dtype=torch.uint8, device="cuda")
+    outm = torch.empty((B, n_query, wl.n_q_heads, wl.head_dim), dtype=torch.float32, device="cuda")
+    ws_s = tq.tq_decode_workspace_bytes(lay, B, n)
+    wss = torch.empty(ws_s, dtype=torch.uint8, device="cuda")
+    outs = torch.empty((B, wl.n_q_heads, wl.head_dim), dtype=torch.float32, device="cuda")
+    q1 = [qm[:, j].contiguous() for j in range(n_query)]
+
+    def multi(i):
+        c = caches[(5 * i + 2) % len(caches)]
+        tq.tq_decode_attn_multi(lay, state.struct, qm, n_query, c.struct, n, rk, rv, R, R, outm, wsm, ws_m, stream)
+
+    def singles(i):
+        c = caches[(5 * i + 2) % len(caches)]
+        for j in range(n_query):
+            tq.tq_decode_attn(lay, state.struct, q1[j], c.struct, n, rk, rv, R - n_query + j + 1, R, outs, wss, ws_s,
+                              stream)
+
+    try:
+        multi(0)
+    except tq.TQError:
+        return None
+    res = {}
+    for name, fn in (("multi", multi), ("singles", singles)):
+        for i in range(warmup):
+            fn(i)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        torch.cuda.synchronize()
+        for i in range(steps):
+            evs[i][0].record(stream)
+            fn(i)
+            evs[i][1].record(stream)
+        torch.cuda.synchronize()
+        res[name] = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs])) * 1e3
+    per = plane_bytes_per_token_head(wl)
+    kv_bytes = B * wl.n_kv_heads * n * sum(per.values()) + 2 * B * wl.n_kv_heads * R * wl.head_dim * 2
+    return {"n_query": n_query, "us": res["multi"], "single_query_decodes_us": res["singles"],
+            "speedup_vs_single_decodes": res["singles"] / res["multi"],
+            "kv_gbps": kv_bytes / (res["multi"] * 1e-6) / 1e9,
+            "kernels": "decode_mma_kernel (n_query x n_rep query rows) + decode_finish_kernel"}
 
 
 def cpu_baseline(wl, budget_s: float = 15.0):
@@ -370,6 +425,10 @@ def main():
     if not a.no_materialize:
         line["materialize"] = bench_materialize(tq, lay, state, caches, wl, stream, max(10, a.steps // 4),
                                                 max(2, a.warmup // 4))
+    if not a.no_materialize:
+        mq = bench_multi(tq, lay, state, caches, wl, stream, rk, rv, max(10, a.steps // 4), max(2, a.warmup // 4))
+        if mq is not None:
+            line["multi_query"] = mq
     if not a.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample ...")
         line["cpu_baseline"] = cpu_baseline(wl)
