@@ -1,21 +1,23 @@
-// Compiled instantiations of the decode main kernel: per-block affine 8-bit keys, head_dim 64,
-// n_rep 1..8, rotated Lloyd-Max 2/3/4-bit values.
-#include "tq_decode_main.h"
+// Compiled instantiations of the decode kernel: per-block affine 8-bit keys, head_dim 64,
+// n_rep 1..8, rotated Lloyd-Max 2/3/4-bit values: n_rep 1 and 2 on the vector ALUs, n_rep
+// 3..8 on the matrix cores.
+#include "tq_decode_mma.h"
 
 namespace tq {
 
 namespace {
-template <int KK, int KB, int VK, int VB>
+template <int VB>
 MainKernel pick(int nrep) {
+  constexpr int KK = TQ_K_AFFINE8, VK = TQ_V_LM_ROT;
   switch (nrep) {
-    case 1: return main_kernel<64, 1, KK, KB, VK, VB>();
-    case 2: return main_kernel<64, 2, KK, KB, VK, VB>();
-    case 3: return main_kernel<64, 3, KK, KB, VK, VB>();
-    case 4: return main_kernel<64, 4, KK, KB, VK, VB>();
-    case 5: return main_kernel<64, 5, KK, KB, VK, VB>();
-    case 6: return main_kernel<64, 6, KK, KB, VK, VB>();
-    case 7: return main_kernel<64, 7, KK, KB, VK, VB>();
-    case 8: return main_kernel<64, 8, KK, KB, VK, VB>();
+    case 1: return main_kernel<64, 1, KK, 8, VK, VB>();
+    case 2: return main_kernel<64, 2, KK, 8, VK, VB>();
+    case 3: return mma_kernel_kv<64, 3, KK, 8, VK, VB>();
+    case 4: return mma_kernel_kv<64, 4, KK, 8, VK, VB>();
+    case 5: return mma_kernel_kv<64, 5, KK, 8, VK, VB>();
+    case 6: return mma_kernel_kv<64, 6, KK, 8, VK, VB>();
+    case 7: return mma_kernel_kv<64, 7, KK, 8, VK, VB>();
+    case 8: return mma_kernel_kv<64, 8, KK, 8, VK, VB>();
     default: return MainKernel{nullptr, nullptr};
   }
 }
@@ -24,9 +26,9 @@ MainKernel pick(int nrep) {
 MainKernel find_main_aff8_d64(int nrep, int vk, int vb) {
   if (vk != TQ_V_LM_ROT) return MainKernel{nullptr, nullptr};
   switch (vb) {
-    case 2: return pick<TQ_K_AFFINE8, 8, TQ_V_LM_ROT, 2>(nrep);
-    case 3: return pick<TQ_K_AFFINE8, 8, TQ_V_LM_ROT, 3>(nrep);
-    case 4: return pick<TQ_K_AFFINE8, 8, TQ_V_LM_ROT, 4>(nrep);
+    case 2: return pick<2>(nrep);
+    case 3: return pick<3>(nrep);
+    case 4: return pick<4>(nrep);
     default: return MainKernel{nullptr, nullptr};
   }
 }

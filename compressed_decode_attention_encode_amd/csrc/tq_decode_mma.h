@@ -31,6 +31,14 @@
 // lane holds in the score accumulators of two 16-token blocks, so softmax weights go from the
 // score accumulators to the value operands without leaving the lane.
 //
+// Per-block affine 8-bit keys (vllm-metal guide, quantisation principle) take the same path with
+// the codes themselves as exact fp16 operands (c - 128, from a byte permute and one packed fp16
+// add) and the block's scale and offset applied to each 32-dimension partial sum:
+//   s = sum_blk a (sum_j (c_j - 128) q_j) + (m + 128 a) sum_j q_j.
+// Rotated Lloyd-Max values (vllm-metal guide; TurboQuant-MLX page: 3-bit codes ten per word) use
+// P'' = p n (hi/lo fp16) against the centroid values (hi/lo, through a value code-pair table);
+// their sum stays in the rotated domain for the merge kernel's single inverse butterfly.
+//
 // Codes become operands through LDS tables: one 8-byte entry (hi pair, lo pair) per pair of
 // codes (2 KB for 4-bit codes), and one 16-byte xor-mask entry per 8 sign bits.  Tiles are
 // staged as in the vector-ALU kernel (coalesced 16-byte loads, next tile in flight), value
@@ -56,23 +64,38 @@ __device__ __forceinline__ mma_f4_t mma16(mma_u4_t a, mma_u4_t b, mma_f4_t c) {
 constexpr float kMmaCentScale = 8.f;
 constexpr float kMmaQScale = 256.f;
 constexpr float kMmaUnscale = 1.f / 256.f;
+constexpr float kMmaAffQScale = 16.f;        // affine keys: query operands carry 16
 
-template <int D, int NREP, int KB, int VB>
+// (a, b) -> fp16 hi pair and the pair of their fp16 remainders (a - hi_a, b - hi_b)
+__device__ __forceinline__ void split_f16x2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  f16x2_t h, l;
+  h.x = (_Float16)a;
+  h.y = (_Float16)b;
+  l.x = (_Float16)(a - (float)h.x);
+  l.y = (_Float16)(b - (float)h.y);
+  hi = __builtin_bit_cast(uint32_t, h);
+  lo = __builtin_bit_cast(uint32_t, l);
+}
+
+template <int D, int NREP, int KK, int KB, int VK, int VB>
 struct MmaGeom {
-  using G = DecodeGeom<D, NREP, TQ_K_LM_QJL, KB, TQ_V_GROUP_SYM, VB>;
+  using G = DecodeGeom<D, NREP, KK, KB, VK, VB>;
+  static constexpr bool QJL = KK == TQ_K_LM_QJL;
+  static constexpr bool AFF = KK == TQ_K_AFFINE8;
   static constexpr int KPER = G::KPER, WK = G::WK, SK = G::SK;
-  static constexpr int WS = D / 32, SS = G::SS;
+  static constexpr int WS = G::WS, SS = G::SS;
+  static constexpr int WAK = G::WAK;            // key aux words per token: (n, gamma) / fp32 n / (a, m) per block
   static constexpr int WV = G::WV, WAV = G::WAV;
   static constexpr int TS = kTile + 4;        // token stride of the transposed value planes
   static constexpr int NKB = D / 32;          // 32-dimension blocks of the score contraction
   static constexpr int NNB = D / 16;          // 16-dimension blocks of the value product
   static constexpr int NG = D / 32;           // value groups
-  // one wave's staging area (words): key rows, sign rows, key aux (n, gamma) per token,
-  // value codes and value scales word-major
+  // one wave's staging area (words): key rows, sign rows, key aux (one word per token for the
+  // LM kinds; word-major [block][token] for affine keys), value codes and value aux word-major
   static constexpr int OFF_SK = 0;
   static constexpr int OFF_SS = OFF_SK + kTile * SK;
   static constexpr int OFF_SAK = OFF_SS + kTile * SS;
-  static constexpr int OFF_SV = OFF_SAK + kTile;
+  static constexpr int OFF_SV = OFF_SAK + (AFF ? WAK * TS : kTile);
   static constexpr int OFF_SAV = OFF_SV + WV * TS;
   static constexpr int STAGE = OFF_SAV + WAV * TS;
   static_assert(OFF_SAK % 4 == 0 && OFF_SV % 4 == 0 && OFF_SAV % 4 == 0 && STAGE % 4 == 0, "16-byte LDS reads");
@@ -80,12 +103,18 @@ struct MmaGeom {
   // [4][NREP + 1][D] halves (q_hi, q_lo, qb_hi, qb_lo; row NREP is zero, the operand of
   // the columns beyond n_rep), the code-pair table, the sign table,
   // four staging areas, merge scalars
-  static constexpr int NPT = 1 << (2 * KB);
+  static constexpr int NPT = AFF ? 0 : 1 << (2 * KB);                  // key code pairs
+  static constexpr int NVT = (VK == TQ_V_LM_ROT) ? 1 << (2 * VB) : 0;  // value code pairs
   static constexpr int OFF_BQ = (G::OFF_QB + NREP * D + 3) & ~3;
   static constexpr int NRB = NREP + 1;         // query operand rows: the heads, then a zero row
   static constexpr int OFF_PT = OFF_BQ + 2 * NRB * D;
-  static constexpr int OFF_SGT = OFF_PT + 2 * NPT;
-  static constexpr int OFF_ST = OFF_SGT + 4 * 256;
+  static constexpr int OFF_VT = OFF_PT + 2 * NPT;
+  // 3-bit rotated values (ten codes per word): per 16-dimension block and column l16 of it, the
+  // word offset of dimension 16 nb + l16 in the transposed staging and its bit, (TS w) | bit << 16
+  static constexpr int NVW = (VK == TQ_V_LM_ROT && VB == 3) ? D : 0;
+  static constexpr int OFF_VW = OFF_VT + 2 * NVT;
+  static constexpr int OFF_SGT = OFF_VW + NVW;
+  static constexpr int OFF_ST = OFF_SGT + (QJL ? 4 * 256 : 0);
   // the four staging areas also hold the waves' value sums for the merge
   static constexpr int STAGE_ALL = (4 * STAGE > 4 * NREP * D) ? 4 * STAGE : 4 * NREP * D;
   static constexpr int OFF_MRG = OFF_ST + STAGE_ALL;
@@ -97,15 +126,17 @@ struct MmaGeom {
 // NQ > 1: a multi-query group.  The NQ x n_rep rows (query j, head h at row j n_rep + h) take
 // the operand columns of the heads, so the score and value products cost the same per tile;
 // only the softmax and the output rows grow.  Below, NREP counts rows.
-template <int D, int NREP_KV, int KB, int VB, int NQ = 1>
+template <int D, int NREP_KV, int KK, int KB, int VK, int VB, int NQ = 1>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 2)))
 decode_mma_kernel(const DecodeArgs A) {
   constexpr int NREP = NQ * NREP_KV;
-  using M = MmaGeom<D, NREP, KB, VB>;
+  using M = MmaGeom<D, NREP, KK, KB, VK, VB>;
+  constexpr bool QJL = M::QJL, AFF = M::AFF, ROT = VK == TQ_V_LM_ROT;
   constexpr int LK = 1 << KB;
   constexpr int LV = 1 << VB;
   constexpr int NKB = M::NKB, NNB = M::NNB, NG = M::NG;
-  static_assert(VB == 2 || VB == 4, "group-scaled values are 2 or 4 bits");
+  static_assert(KK == TQ_K_LM_QJL || KK == TQ_K_LM_MSE || KK == TQ_K_AFFINE8, "key kind");
+  static_assert(ROT ? (VB >= 2 && VB <= 4) : (VB == 2 || VB == 4), "value bits");
 
   __shared__ __attribute__((aligned(16))) float sm[M::FLOATS];
   uint32_t* smw = reinterpret_cast<uint32_t*>(sm);
@@ -117,7 +148,7 @@ decode_mma_kernel(const DecodeArgs A) {
   const int n_comp = A.nsplit * A.Hkv * A.batch;
   if ((int)blockIdx.x >= n_comp) {
     const int u = blockIdx.x - n_comp;
-    recent_split<D, NREP, TQ_K_LM_QJL, KB, TQ_V_GROUP_SYM, VB, NQ>(A, u / A.Hkv, u % A.Hkv, sm);
+    recent_split<D, NREP, KK, KB, VK, VB, NQ>(A, u / A.Hkv, u % A.Hkv, sm);
     return;
   }
   const int split = blockIdx.x % A.nsplit;
@@ -137,7 +168,7 @@ decode_mma_kernel(const DecodeArgs A) {
 
   RowLoader<M::WK, M::SK> ld_k;
   RowLoader<M::WS, M::SS> ld_s;
-  RowLoader<1, 1> ld_ak;
+  RowLoader<M::WAK, AFF ? M::TS : 1> ld_ak;
   RowLoader<M::WV, M::TS> ld_v;
   RowLoader<M::WAV, M::TS> ld_av;
   auto issue = [&](int t0) {
@@ -145,38 +176,45 @@ decode_mma_kernel(const DecodeArgs A) {
     const size_t row0 = slice * cap + t0;
     ld_k.load(A.kc + row0 * M::WK, nv, lane);
     ld_s.load(A.ks + row0 * M::WS, nv, lane);
-    ld_ak.load(A.ka + row0, nv, lane);
+    ld_ak.load(A.ka + row0 * M::WAK, nv, lane);
     ld_v.load(A.vc + row0 * M::WV, nv, lane);
     ld_av.load(A.va + row0 * M::WAV, nv, lane);
   };
   if (tb + wave * kTile < te) issue(tb + wave * kTile);
 
-  // code-pair table: entry pc = (code a = low KB bits, code b), words (hi pair, lo pair)
+  // code-pair tables: entry pc = (code a = low bits, code b), words (hi pair, lo pair) of 8 c
   for (int i = threadIdx.x; i < M::NPT; i += 256) {
-    const float ca = A.kcent[i & (LK - 1)] * kMmaCentScale;
-    const float cb = A.kcent[i >> KB] * kMmaCentScale;
-    const _Float16 ha = (_Float16)ca, hb = (_Float16)cb;
-    smw[M::OFF_PT + 2 * i] = pack_f16x2((float)ha, (float)hb);
-    smw[M::OFF_PT + 2 * i + 1] = pack_f16x2(ca - (float)ha, cb - (float)hb);
+    uint32_t hi, lo;
+    split_f16x2(A.kcent[i & (LK - 1)] * kMmaCentScale, A.kcent[i >> KB] * kMmaCentScale, hi, lo);
+    smw[M::OFF_PT + 2 * i] = hi;
+    smw[M::OFF_PT + 2 * i + 1] = lo;
   }
+  for (int i = threadIdx.x; i < M::NVT; i += 256) {
+    uint32_t hi, lo;
+    split_f16x2(A.vcent[i & (LV - 1)] * kMmaCentScale, A.vcent[i >> VB] * kMmaCentScale, hi, lo);
+    smw[M::OFF_VT + 2 * i] = hi;
+    smw[M::OFF_VT + 2 * i + 1] = lo;
+  }
+  for (int j = threadIdx.x; j < M::NVW; j += 256) smw[M::OFF_VW + j] = (j / 10) * M::TS | (3 * (j % 10)) << 16;
   // sign table: 8 stored bits (bit 1 <=> sigma = +1) -> xor masks of 4 fp16 pairs
-  {
+  if constexpr (QJL) {
     const int i = threadIdx.x;
 #pragma unroll
     for (int k = 0; k < 4; ++k)
       smw[M::OFF_SGT + 4 * i + k] = (((i >> (2 * k)) & 1) ? 0u : 0x8000u) | (((i >> (2 * k + 1)) & 1) ? 0u : 0x80000000u);
   }
-  prepare_queries<D, NREP, TQ_K_LM_QJL, KB, TQ_V_GROUP_SYM, VB, false, NQ>(A, b, g, sm);
+  prepare_queries<D, NREP, KK, KB, VK, VB, false, NQ>(A, b, g, sm);
   {
     // fp16 query operands (hi, lo) from the prepared fp32 queries
     const float* qa = sm + M::G::OFF_QA;
     const float* qb = sm + M::G::OFF_QB;
     _Float16* bq = reinterpret_cast<_Float16*>(smw + M::OFF_BQ);
     constexpr int RS = M::NRB * D;               // halves per operand region
+    constexpr float QA = AFF ? kMmaAffQScale : kMmaQScale / kMmaCentScale;
     for (int i = threadIdx.x; i < RS; i += 256) {
       const bool on = i < NREP * D;
-      const float a = on ? qa[i] * (kMmaQScale / kMmaCentScale) : 0.f;
-      const float s = on ? qb[i] * kMmaQScale : 0.f;
+      const float a = on ? qa[i] * QA : 0.f;
+      const float s = (on && QJL) ? qb[i] * kMmaQScale : 0.f;
       const _Float16 ah = (_Float16)a, sh = (_Float16)s;
       bq[i] = ah;
       bq[RS + i] = (_Float16)(a - (float)ah);
@@ -190,6 +228,14 @@ decode_mma_kernel(const DecodeArgs A) {
   const uint32_t* ptab = smw + M::OFF_PT;
   const uint32_t* sgt = smw + M::OFF_SGT;
   const int hq = (l16 < NREP) ? l16 : NREP;    // operand column (head); the zero row beyond n_rep
+  const uint32_t* vtab = smw + M::OFF_VT;
+  // affine keys: per 32-dimension block, the sum of the lane's head's query operand
+  float qsum[AFF ? NKB : 1];
+  if constexpr (AFF) {
+    const float* qb = sm + M::G::OFF_QB;      // prepare_queries: block sums of qa
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) qsum[kb] = (l16 < NREP) ? qb[l16 * NKB + kb] * kMmaAffQScale : 0.f;
+  }
 
   float m_run = -INFINITY, l_part = 0.f;        // head l16 (per lane: its tokens)
   float off[NG];                                // sum of P' per group, head l16
@@ -203,7 +249,8 @@ decode_mma_kernel(const DecodeArgs A) {
     const int nv = min(kTile, te - t0);
     ld_k.store(st + M::OFF_SK, lane);
     ld_s.store(st + M::OFF_SS, lane);
-    ld_ak.store(st + M::OFF_SAK, lane);
+    if constexpr (AFF) ld_ak.store_transposed(st + M::OFF_SAK, lane);
+    else ld_ak.store(st + M::OFF_SAK, lane);
     ld_v.store_transposed(st + M::OFF_SV, lane);
     ld_av.store_transposed(st + M::OFF_SAV, lane);
     if (t0 + 4 * kTile < te) issue(t0 + 4 * kTile);
@@ -212,71 +259,123 @@ decode_mma_kernel(const DecodeArgs A) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
     // ---- scores: four 16-token blocks ------------------------------------------------------
-    mma_f4_t sacc[4];
+    // p[mb][r]: head l16, token 16 mb + 4 q4 + r (log2-domain score, then its weight)
+    float p[4][4];
+    if constexpr (!AFF) {
+      mma_f4_t sacc[4];
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) sacc[mb] = mma_f4_t{0.f, 0.f, 0.f, 0.f};
+      for (int mb = 0; mb < 4; ++mb) sacc[mb] = mma_f4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      const int kw = 16 * kb + 4 * q4;           // word offset of this lane's 8 dimensions
-      mma_u4_t bq0, bq1, bq2, bq3;
-      {
-        constexpr int RW = M::NRB * D / 2;         // words per operand region
+      for (int kb = 0; kb < NKB; ++kb) {
+        const int kw = 16 * kb + 4 * q4;           // word offset of this lane's 8 dimensions
+        mma_u4_t bq0, bq1, bq2, bq3;
+        {
+          constexpr int RW = M::NRB * D / 2;         // words per operand region
+          const uint32_t* src = bqw + hq * (D / 2) + kw;
+          const uint4 r0 = *reinterpret_cast<const uint4*>(src);
+          const uint4 r1 = *reinterpret_cast<const uint4*>(src + RW);
+          bq0 = mma_u4_t{r0.x, r0.y, r0.z, r0.w};
+          bq1 = mma_u4_t{r1.x, r1.y, r1.z, r1.w};
+          if constexpr (QJL) {
+            const uint4 r2 = *reinterpret_cast<const uint4*>(src + 2 * RW);
+            const uint4 r3 = *reinterpret_cast<const uint4*>(src + 3 * RW);
+            bq2 = mma_u4_t{r2.x, r2.y, r2.z, r2.w};
+            bq3 = mma_u4_t{r3.x, r3.y, r3.z, r3.w};
+          }
+        }
+        // one 16-token block at a time: its operands, then its products (the accumulator
+        // chains through the matrix unit; few registers stay live)
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+          const int tok = 16 * mb + l16;
+          const uint32_t* row = stk + tok * M::SK;
+          // the lane's 8 codes (dimensions 32 kb + 8 q4 ..) as the low 8 KB bits of y
+          uint32_t y;
+          if constexpr (KB == 3) {
+            const int a0 = 32 * kb + 8 * q4;
+            const int w0 = a0 / 10, b0 = 3 * (a0 - 10 * w0);
+            const uint32_t x0 = row[w0], x1 = row[w0 + 1];
+            y = __builtin_amdgcn_alignbit(x1 >> 2, x0 | (x1 << 30), (uint32_t)b0);
+          } else if constexpr (KB == 4) {
+            y = row[4 * kb + q4];
+          } else {
+            y = row[2 * kb + (q4 >> 1)] >> (16 * (q4 & 1));
+          }
+          mma_u4_t ahi, alo;
+#pragma unroll
+          for (int pp = 0; pp < 4; ++pp) {
+            const uint32_t pc = (y >> (2 * KB * pp)) & (M::NPT - 1);
+            const uint2 e = *reinterpret_cast<const uint2*>(ptab + 2 * pc);
+            ahi[pp] = e.x;
+            alo[pp] = e.y;
+          }
+          sacc[mb] = mma16(ahi, bq0, sacc[mb]);
+          sacc[mb] = mma16(alo, bq0, sacc[mb]);
+          sacc[mb] = mma16(ahi, bq1, sacc[mb]);
+          if constexpr (QJL) {
+            const uint32_t sb = (sts[tok * M::SS + kb] >> (8 * q4)) & 0xFFu;
+            const uint4 mk = *reinterpret_cast<const uint4*>(sgt + 4 * sb);
+            const uint32_t aux = stak[tok];
+            const uint32_t g2 = __builtin_amdgcn_perm(aux, aux, 0x03020302u);   // (gamma, gamma)
+            const mma_u4_t asg = mma_u4_t{g2 ^ mk.x, g2 ^ mk.y, g2 ^ mk.z, g2 ^ mk.w};
+            sacc[mb] = mma16(asg, bq2, sacc[mb]);
+            sacc[mb] = mma16(asg, bq3, sacc[mb]);
+          }
+        }
+      }
+      // times n (fp16 with gamma for LM + QJL keys, fp32 for MSE-only keys) and the unscale
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const uint4 nw = *reinterpret_cast<const uint4*>(stak + 16 * mb + 4 * q4);
+        const uint32_t nn[4] = {nw.x, nw.y, nw.z, nw.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float n = QJL ? f16_to_f32(nn[r] & 0xFFFFu) : __uint_as_float(nn[r]);
+          p[mb][r] = sacc[mb][r] * (n * kMmaUnscale);
+        }
+      }
+    } else {
+      // affine keys: per 32-dimension block, sum_j (c_j - 128) q_j on the matrix cores, then
+      // a times it plus (m + 128 a) times the block's query sum
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) p[mb][r] = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const int kw = 16 * kb + 4 * q4;
+        constexpr int RW = M::NRB * D / 2;
         const uint32_t* src = bqw + hq * (D / 2) + kw;
         const uint4 r0 = *reinterpret_cast<const uint4*>(src);
         const uint4 r1 = *reinterpret_cast<const uint4*>(src + RW);
-        const uint4 r2 = *reinterpret_cast<const uint4*>(src + 2 * RW);
-        const uint4 r3 = *reinterpret_cast<const uint4*>(src + 3 * RW);
-        bq0 = mma_u4_t{r0.x, r0.y, r0.z, r0.w};
-        bq1 = mma_u4_t{r1.x, r1.y, r1.z, r1.w};
-        bq2 = mma_u4_t{r2.x, r2.y, r2.z, r2.w};
-        bq3 = mma_u4_t{r3.x, r3.y, r3.z, r3.w};
-      }
-      // one 16-token block at a time: its three operands, then its five products (the
-      // accumulator chains through the matrix unit; few registers stay live)
+        const mma_u4_t bq0 = mma_u4_t{r0.x, r0.y, r0.z, r0.w};
+        const mma_u4_t bq1 = mma_u4_t{r1.x, r1.y, r1.z, r1.w};
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        const int tok = 16 * mb + l16;
-        const uint32_t* row = stk + tok * M::SK;
-        // the lane's 8 codes (dimensions 32 kb + 8 q4 ..) as the low 8 KB bits of y
-        uint32_t y;
-        if constexpr (KB == 3) {
-          const int a0 = 32 * kb + 8 * q4;
-          const int w0 = a0 / 10, b0 = 3 * (a0 - 10 * w0);
-          const uint32_t x0 = row[w0], x1 = row[w0 + 1];
-          y = __builtin_amdgcn_alignbit(x1 >> 2, x0 | (x1 << 30), (uint32_t)b0);
-        } else if constexpr (KB == 4) {
-          y = row[4 * kb + q4];
-        } else {
-          y = row[2 * kb + (q4 >> 1)] >> (16 * (q4 & 1));
+        for (int mb = 0; mb < 4; ++mb) {
+          const uint32_t* row = stk + (16 * mb + l16) * M::SK + 8 * kb + 2 * q4;
+          const uint32_t w0 = row[0], w1 = row[1];
+          // bytes c -> fp16 1024 + c (0x64 over the byte) -> c - 128, exact
+          const f16x2_t off = {(_Float16)-1152.f, (_Float16)-1152.f};
+          mma_u4_t ac;
+          ac[0] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0x64646464u, w0, 0x04010400u)) + off);
+          ac[1] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0x64646464u, w0, 0x04030402u)) + off);
+          ac[2] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0x64646464u, w1, 0x04010400u)) + off);
+          ac[3] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0x64646464u, w1, 0x04030402u)) + off);
+          mma_f4_t t = mma16(ac, bq0, mma_f4_t{0.f, 0.f, 0.f, 0.f});
+          t = mma16(ac, bq1, t);
+          const uint4 aw = *reinterpret_cast<const uint4*>(stak + kb * M::TS + 16 * mb + 4 * q4);
+          const uint32_t am[4] = {aw.x, aw.y, aw.z, aw.w};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float a = f16_to_f32(am[r] & 0xFFFFu), m = f16_to_f32(am[r] >> 16);
+            p[mb][r] = fmaf(a, t[r], fmaf(fmaf(128.f, a, m), qsum[kb], p[mb][r]));
+          }
         }
-        mma_u4_t ahi, alo;
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const uint32_t pc = (y >> (2 * KB * p)) & (M::NPT - 1);
-          const uint2 e = *reinterpret_cast<const uint2*>(ptab + 2 * pc);
-          ahi[p] = e.x;
-          alo[p] = e.y;
-        }
-        const uint32_t sb = (sts[tok * M::SS + kb] >> (8 * q4)) & 0xFFu;
-        const uint4 mk = *reinterpret_cast<const uint4*>(sgt + 4 * sb);
-        const uint32_t aux = stak[tok];
-        const uint32_t g2 = __builtin_amdgcn_perm(aux, aux, 0x03020302u);   // (gamma, gamma)
-        const mma_u4_t asg = mma_u4_t{g2 ^ mk.x, g2 ^ mk.y, g2 ^ mk.z, g2 ^ mk.w};
-        sacc[mb] = mma16(ahi, bq0, sacc[mb]);
-        sacc[mb] = mma16(alo, bq0, sacc[mb]);
-        sacc[mb] = mma16(ahi, bq1, sacc[mb]);
-        sacc[mb] = mma16(asg, bq2, sacc[mb]);
-        sacc[mb] = mma16(asg, bq3, sacc[mb]);
       }
-    }
-    // sacc[mb][r]: head l16, token 16 mb + 4 q4 + r; times n (and the operand unscale)
-    float p[4][4];
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      const uint4 nw = *reinterpret_cast<const uint4*>(stak + 16 * mb + 4 * q4);
-      const uint32_t nn[4] = {nw.x, nw.y, nw.z, nw.w};
+      for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) p[mb][r] = sacc[mb][r] * (f16_to_f32(nn[r] & 0xFFFFu) * kMmaUnscale);
+        for (int r = 0; r < 4; ++r) p[mb][r] *= 1.f / kMmaAffQScale;
     }
     if (nv < kTile) {   // the last tile of a split: tokens past its end score -inf
 #pragma unroll
@@ -321,56 +420,112 @@ decode_mma_kernel(const DecodeArgs A) {
     }
 
     // ---- weighted values: two 32-token blocks ------------------------------------------
-    constexpr uint32_t kOne = 0x3C003C00u;       // fp16 pair (1, 1)
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-      // k slot i of this lane: token 32 kb2 + 4 q4 + i (i < 4), 32 kb2 + 16 + 4 q4 + i - 4
-      const int tk = 32 * kb2 + 4 * q4;
-#pragma unroll
-      for (int w = 0; w < M::WAV; ++w) {
-        const uint4 d0 = *reinterpret_cast<const uint4*>(stav + w * M::TS + tk);
-        const uint4 d1 = *reinterpret_cast<const uint4*>(stav + w * M::TS + tk + 16);
-        const uint32_t dw[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const int gi = 2 * w + hf;
-          if (gi < NG) {
-            mma_u4_t apv;
-            {
-              float wt[8];
-#pragma unroll
-              for (int i = 0; i < 8; ++i)
-                wt[i] = p[2 * kb2 + (i >> 2)][i & 3] * f16_to_f32((dw[i] >> (16 * hf)) & 0xFFFFu);
-#pragma unroll
-              for (int k = 0; k < 4; ++k) {
-                apv[k] = pack_f16x2(wt[2 * k], wt[2 * k + 1]);
-                off[gi] = dot2_f16(apv[k], kOne, off[gi]);
-              }
-            }
-            // the group's two 16-dimension blocks
-#pragma unroll
-            for (int nb = 2 * gi; nb < 2 * gi + 2; ++nb) {
-              uint32_t x[8];
-              int bit;
+    if constexpr (!ROT) {
+      constexpr uint32_t kOne = 0x3C003C00u;       // fp16 pair (1, 1)
+  #pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        // k slot i of this lane: token 32 kb2 + 4 q4 + i (i < 4), 32 kb2 + 16 + 4 q4 + i - 4
+        const int tk = 32 * kb2 + 4 * q4;
+  #pragma unroll
+        for (int w = 0; w < M::WAV; ++w) {
+          const uint4 d0 = *reinterpret_cast<const uint4*>(stav + w * M::TS + tk);
+          const uint4 d1 = *reinterpret_cast<const uint4*>(stav + w * M::TS + tk + 16);
+          const uint32_t dw[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+  #pragma unroll
+          for (int hf = 0; hf < 2; ++hf) {
+            const int gi = 2 * w + hf;
+            if (gi < NG) {
+              mma_u4_t apv;
               {
-                const uint32_t* src = (VB == 2) ? stv + nb * M::TS + tk : stv + (2 * nb + (l16 >> 3)) * M::TS + tk;
-                const uint4 x0 = *reinterpret_cast<const uint4*>(src);
-                const uint4 x1 = *reinterpret_cast<const uint4*>(src + 16);
-                x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w; x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
-                bit = (VB == 2) ? 2 * l16 : 4 * (l16 & 7);
+                float wt[8];
+  #pragma unroll
+                for (int i = 0; i < 8; ++i)
+                  wt[i] = p[2 * kb2 + (i >> 2)][i & 3] * f16_to_f32((dw[i] >> (16 * hf)) & 0xFFFFu);
+  #pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                  apv[k] = pack_f16x2(wt[2 * k], wt[2 * k + 1]);
+                  off[gi] = dot2_f16(apv[k], kOne, off[gi]);
+                }
               }
-              // code c -> fp16 1 + c / 2^MV: the code dropped into the mantissa under 1.0's exponent
-              constexpr int MV = (VB == 2) ? 8 : 6;
-              mma_u4_t bv;
-#pragma unroll
-              for (int k = 0; k < 4; ++k) {
-                const uint32_t c0 = __builtin_amdgcn_ubfe(x[2 * k], (uint32_t)bit, VB);
-                const uint32_t c1 = __builtin_amdgcn_ubfe(x[2 * k + 1], (uint32_t)bit, VB);
-                bv[k] = (c0 << MV) | (c1 << (16 + MV)) | kOne;
+              // the group's two 16-dimension blocks
+  #pragma unroll
+              for (int nb = 2 * gi; nb < 2 * gi + 2; ++nb) {
+                uint32_t x[8];
+                int bit;
+                {
+                  const uint32_t* src = (VB == 2) ? stv + nb * M::TS + tk : stv + (2 * nb + (l16 >> 3)) * M::TS + tk;
+                  const uint4 x0 = *reinterpret_cast<const uint4*>(src);
+                  const uint4 x1 = *reinterpret_cast<const uint4*>(src + 16);
+                  x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w; x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
+                  bit = (VB == 2) ? 2 * l16 : 4 * (l16 & 7);
+                }
+                // code c -> fp16 1 + c / 2^MV: the code dropped into the mantissa under 1.0's exponent
+                constexpr int MV = (VB == 2) ? 8 : 6;
+                mma_u4_t bv;
+  #pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                  const uint32_t c0 = __builtin_amdgcn_ubfe(x[2 * k], (uint32_t)bit, VB);
+                  const uint32_t c1 = __builtin_amdgcn_ubfe(x[2 * k + 1], (uint32_t)bit, VB);
+                  bv[k] = (c0 << MV) | (c1 << (16 + MV)) | kOne;
+                }
+                acc[nb] = mma16(apv, bv, acc[nb]);
               }
-              acc[nb] = mma16(apv, bv, acc[nb]);
             }
           }
+        }
+      }
+    } else {
+      // rotated Lloyd-Max values: P'' = p n (hi/lo) against 8 c (hi/lo) per 16 dimensions
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        const int tk = 32 * kb2 + 4 * q4;            // k slots as for the group values
+        mma_u4_t aph, apl;
+        {
+          const uint4 n0 = *reinterpret_cast<const uint4*>(stav + tk);
+          const uint4 n1 = *reinterpret_cast<const uint4*>(stav + tk + 16);
+          const uint32_t nw[8] = {n0.x, n0.y, n0.z, n0.w, n1.x, n1.y, n1.z, n1.w};
+          float wt[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) wt[i] = p[2 * kb2 + (i >> 2)][i & 3] * __uint_as_float(nw[i]);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            uint32_t hi, lo;
+            split_f16x2(wt[2 * k], wt[2 * k + 1], hi, lo);
+            aph[k] = hi;
+            apl[k] = lo;
+          }
+        }
+#pragma unroll
+        for (int nb = 0; nb < NNB; ++nb) {
+          // dimension 16 nb + l16: its code in word j / VPER of each of the lane's 8 tokens
+          constexpr int VPER = M::G::VPER;
+          const int j = 16 * nb + l16;
+          int wo, bit;
+          if constexpr (VB == 3) {
+            // read per block (LDS) rather than kept live across the tile loop for every block
+            const uint32_t e = smw[M::OFF_VW + j];
+            wo = (int)(e & 0xFFFFu);
+            bit = (int)(e >> 16);
+          } else {
+            wo = (j / VPER) * M::TS;
+            bit = VB * (j % VPER);
+          }
+          const uint32_t* src = stv + wo + tk;
+          const uint4 x0 = *reinterpret_cast<const uint4*>(src);
+          const uint4 x1 = *reinterpret_cast<const uint4*>(src + 16);
+          const uint32_t x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+          mma_u4_t bvh, bvl;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const uint32_t c0 = __builtin_amdgcn_ubfe(x[2 * k], (uint32_t)bit, VB);
+            const uint32_t c1 = __builtin_amdgcn_ubfe(x[2 * k + 1], (uint32_t)bit, VB);
+            const uint2 e = *reinterpret_cast<const uint2*>(vtab + 2 * (c0 | (c1 << VB)));
+            bvh[k] = e.x;
+            bvl[k] = e.y;
+          }
+          acc[nb] = mma16(aph, bvh, acc[nb]);
+          acc[nb] = mma16(apl, bvh, acc[nb]);
+          acc[nb] = mma16(aph, bvl, acc[nb]);
         }
       }
     }
@@ -387,9 +542,10 @@ decode_mma_kernel(const DecodeArgs A) {
     off[k] += __shfl_xor(off[k], 16);
     off[k] += __shfl_xor(off[k], 32);
   }
-  // acc = sum P' (1 + c / F), off = sum P'  ->  sum P' (c - (L-1)/2) = F acc - (F + (L-1)/2) off
-  constexpr float F = (VB == 2) ? 4.f : 16.f;
-  constexpr float FO = F + 0.5f * (float)(LV - 1);
+  // group values: acc = sum P' (1 + c / F), off = sum P'  ->  sum P' (c - (L-1)/2) = F acc - (F + (L-1)/2) off;
+  // rotated values: acc = sum P'' 8 c  ->  acc / 8 (still in the rotated domain)
+  constexpr float F = ROT ? 1.f / kMmaCentScale : ((VB == 2) ? 4.f : 16.f);
+  constexpr float FO = ROT ? 0.f : F + 0.5f * (float)(LV - 1);
   __syncthreads();   // every wave is done with its staging area
   float(*s_mrg_acc)[NREP * D] = reinterpret_cast<float(*)[NREP * D]>(smw + M::OFF_ST);
   float* s_mrg_m = sm + M::OFF_MRG;            // [4][NREP]
@@ -403,7 +559,7 @@ decode_mma_kernel(const DecodeArgs A) {
     if (h < NREP) {
 #pragma unroll
       for (int nb = 0; nb < NNB; ++nb)
-        s_mrg_acc[wave][h * D + 16 * nb + l16] = fmaf(F, acc[nb][r], -FO * o[nb / 2]);
+        s_mrg_acc[wave][h * D + 16 * nb + l16] = ROT ? F * acc[nb][r] : fmaf(F, acc[nb][r], -FO * o[nb / 2]);
     }
   }
   if (lane < NREP) {
@@ -435,17 +591,17 @@ decode_mma_kernel(const DecodeArgs A) {
   }
 }
 
-template <int D, int NREP, int KB, int VB, int NQ>
+template <int D, int NREP, int KK, int KB, int VK, int VB, int NQ>
 hipError_t mma_launch(dim3 grid, hipStream_t st, const DecodeArgs& A) {
-  hipLaunchKernelGGL((decode_mma_kernel<D, NREP, KB, VB, NQ>), grid, dim3(256), 0, st, A);
+  hipLaunchKernelGGL((decode_mma_kernel<D, NREP, KK, KB, VK, VB, NQ>), grid, dim3(256), 0, st, A);
   return hipGetLastError();
 }
 
-template <int D, int NREP, int KB, int VB, int NQ>
+template <int D, int NREP, int KK, int KB, int VK, int VB, int NQ>
 int mma_blocks_per_cu() {
   static const int n = [] {
     int b = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, decode_mma_kernel<D, NREP, KB, VB, NQ>, 256, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, decode_mma_kernel<D, NREP, KK, KB, VK, VB, NQ>, 256, 0) !=
             hipSuccess ||
         b <= 0)
       b = 1;
@@ -454,10 +610,17 @@ int mma_blocks_per_cu() {
   return n;
 }
 
-// n_rep query heads per kv-head, NQ queries per step
+// n_rep query heads per kv-head, NQ queries per step; LM + QJL keys with group values
 template <int D, int NREP, int KB, int VB, int NQ = 1>
 constexpr MainKernel mma_kernel() {
-  return MainKernel{&mma_launch<D, NREP, KB, VB, NQ>, &mma_blocks_per_cu<D, NREP, KB, VB, NQ>};
+  return MainKernel{&mma_launch<D, NREP, TQ_K_LM_QJL, KB, TQ_V_GROUP_SYM, VB, NQ>,
+                    &mma_blocks_per_cu<D, NREP, TQ_K_LM_QJL, KB, TQ_V_GROUP_SYM, VB, NQ>};
+}
+
+// any compiled key / value kind
+template <int D, int NREP, int KK, int KB, int VK, int VB>
+constexpr MainKernel mma_kernel_kv() {
+  return MainKernel{&mma_launch<D, NREP, KK, KB, VK, VB, 1>, &mma_blocks_per_cu<D, NREP, KK, KB, VK, VB, 1>};
 }
 
 }  // namespace tq
