@@ -50,6 +50,11 @@ def encode_v(lay, v: np.ndarray, state: dict) -> dict:
         e = enc.encode_v_group_sym(v, lay.v_bits)
         return {"v_codes": L.pack_codes(e["idx"], lay.v_bits), "v_aux": e["scale16"].view(np.uint16),
                 "near_idx": e["near_idx"], "enc": e}
+    if lay.v_kind == "group_asym":
+        e = enc.encode_v_group_asym(v, lay.v_bits)
+        aux = np.stack([e["a16"].view(np.uint16), e["m16"].view(np.uint16)], axis=-1)
+        return {"v_codes": L.pack_codes(e["idx"], lay.v_bits), "v_aux": aux,
+                "near_idx": e["near_idx"], "enc": e}
     if lay.v_kind == "lm_rot":
         c, t = state["cb_v"]
         e = enc.encode_v_lm_rot(v, state["signs_v"], c, t)
@@ -91,6 +96,10 @@ def read_v(lay, planes: dict, state: dict) -> dict:
     idx = L.unpack_codes(planes["v_codes"], lay.v_bits, d)
     if lay.v_kind == "group_sym":
         return {"idx": idx, "scale": np.asarray(planes["v_aux"], dtype=np.uint16).view(np.float16).astype(np.float64)}
+    if lay.v_kind == "group_asym":
+        aux = np.asarray(planes["v_aux"], dtype=np.uint16)
+        return {"idx": idx, "a": aux[..., 0].view(np.float16).astype(np.float64),
+                "m": aux[..., 1].view(np.float16).astype(np.float64)}
     return {"idx": idx, "n": np.asarray(planes["v_aux"], dtype=np.float32).astype(np.float64)}
 
 

@@ -14,6 +14,7 @@ page, GPU kernel optimisation section, n_rep item):
   buffering strategy):             s_r = <q, k_r> / sqrt(d)
   p = softmax over all N_c + R scores;
   group values:        out = sum_t p_t Delta_t (idx_t - (L-1)/2) + sum_r p_r v_r
+  min/max values:      out = sum_t p_t (m_t + a_t idx_t) + sum_r p_r v_r  (per 32-group a, m)
   rotated-LM values:   out = Pi_v^T ( sum_t p_t n_t c[idx_t] ) + sum_r p_r v_r
   (the weighted sum is formed in the rotated domain and rotated back once:
   TurboQuant-MLX page, GPU kernel optimisation section, butterfly item).
@@ -66,6 +67,8 @@ def _affine_k_hat(kd: dict, d: int) -> np.ndarray:
 
 
 def _v_hat_group(lay, vd: dict) -> np.ndarray:
+    if lay.v_kind == "group_asym":
+        return np.repeat(vd["m"], 32, axis=-1) + np.repeat(vd["a"], 32, axis=-1) * vd["idx"]
     Lv = 1 << lay.v_bits
     scale = np.repeat(vd["scale"], 32, axis=-1)
     return scale * (vd["idx"] - (Lv - 1) / 2.0)
@@ -103,7 +106,7 @@ def decode_attention(lay, q: np.ndarray, planes: dict, n_compressed: int, state:
                 pc, pr = p[:n_compressed], p[n_compressed:]
                 o = np.zeros(d)
                 if n_compressed:
-                    if lay.v_kind == "group_sym":
+                    if lay.v_kind in ("group_sym", "group_asym"):
                         o += pc @ _v_hat_group(lay, vd)
                     else:
                         c = state["cb_v"][0].astype(np.float64)
@@ -151,7 +154,7 @@ def reconstruct_k(lay, kd: dict, state: dict) -> np.ndarray:
 
 
 def reconstruct_v(lay, vd: dict, state: dict) -> np.ndarray:
-    if lay.v_kind == "group_sym":
+    if lay.v_kind in ("group_sym", "group_asym"):
         return _v_hat_group(lay, vd)
     c = state["cb_v"][0].astype(np.float64)
     return vd["n"][:, None] * (c[vd["idx"]] @ rotation_matrix(state["signs_v"]))

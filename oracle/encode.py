@@ -13,6 +13,11 @@ of the quantisation residual so that the inner-product estimate is unbiased.
 Values, group-32 symmetric (TurboQuant vLLM guide, section 2 step 4): each group
 of 32 consecutive channels gets one scale and symmetric 2- or 4-bit levels.
 
+Values, group-32 min/max (TurboQuant benchmark page, compression algorithm details:
+values keep a per-group minimum and maximum): each group of 32 channels gets an
+fp16 step a = (max - min)/(L-1) and offset m = min, and codes 0 .. L-1 -- the same
+quantiser as the per-block affine keys below, at 2 or 4 bits.
+
 Keys, per-block affine 8-bit and values, rotated Lloyd-Max 3-bit (vllm-metal
 TurboQuant guide, quantisation principle table): keys keep their own scale and
 offset per block with no rotation; values are rotated, then mapped to the
@@ -29,7 +34,7 @@ Readings where the pages are silent (each also listed in the design notes):
   * group scale Delta = fp16(2 amax / (L-1)), idx = clamp(rne(v/Delta + (L-1)/2), 0, L-1)
     with the stored Delta; Delta = 0 gives idx = L-1, 0, L/2 for v > 0, v < 0, v = 0;
   * affine scale a = fp16((max-min)/255), offset m = fp16(min), q = clamp(rne((k-m)/a), 0, 255);
-    a = 0 gives q = 0;
+    a = 0 gives q = 0; min/max values alike with L - 1 = 3 or 15 in place of 255;
   * a quotient lying exactly on a half-integer is an exact tie, decided by round-half-
     to-even and compared like any other element; only inexact values within BAND of a
     boundary are marked near.  Exact ties are common with fp16 inputs (a value that is
@@ -116,21 +121,34 @@ def encode_v_group_sym(v: np.ndarray, bits: int) -> dict:
             "near_idx": near.reshape(v.shape)}
 
 
-def encode_k_affine8(k: np.ndarray) -> dict:
-    d = k.shape[-1]
-    kg = k.reshape(k.shape[:-1] + (d // 32, 32))
-    lo = np.min(kg, axis=-1)
-    hi = np.max(kg, axis=-1)
-    a16 = ((hi - lo) / 255.0).astype(np.float16)
+def _group_minmax(x: np.ndarray, top: int):
+    """Per group of 32: a = fp16((max-min)/top), m = fp16(min), q = clamp(rne((x-m)/a), 0, top)
+    with the stored a and m (a = 0: q = 0)."""
+    d = x.shape[-1]
+    xg = x.reshape(x.shape[:-1] + (d // 32, 32))
+    lo = np.min(xg, axis=-1)
+    hi = np.max(xg, axis=-1)
+    a16 = ((hi - lo) / float(top)).astype(np.float16)
     m16 = lo.astype(np.float16)
     a = a16.astype(np.float64)[..., None]
     m = m16.astype(np.float64)[..., None]
     with np.errstate(divide="ignore", invalid="ignore"):
-        x = (kg - m) / a
-    q = np.where(a == 0, 0, np.clip(np.rint(x), 0, 255)).astype(np.int64)
-    frac = x - np.floor(x)
-    near = (a != 0) & (np.abs(frac - 0.5) < BAND) & ~_exact_half(kg - m, a, 0.0)
-    return {"q8": q.reshape(k.shape), "a16": a16, "m16": m16, "near_idx": near.reshape(k.shape)}
+        xq = (xg - m) / a
+    q = np.where(a == 0, 0, np.clip(np.rint(xq), 0, top)).astype(np.int64)
+    frac = xq - np.floor(xq)
+    near = (a != 0) & (np.abs(frac - 0.5) < BAND) & ~_exact_half(xg - m, a, 0.0)
+    return q.reshape(x.shape), a16, m16, near.reshape(x.shape)
+
+
+def encode_k_affine8(k: np.ndarray) -> dict:
+    q, a16, m16, near = _group_minmax(k, 255)
+    return {"q8": q, "a16": a16, "m16": m16, "near_idx": near}
+
+
+def encode_v_group_asym(v: np.ndarray, bits: int) -> dict:
+    """Group-32 min/max values (benchmark page): v_hat = m + a idx."""
+    idx, a16, m16, near = _group_minmax(v, (1 << bits) - 1)
+    return {"idx": idx, "a16": a16, "m16": m16, "near_idx": near}
 
 
 def encode_k_lm_mse(k: np.ndarray, signs: np.ndarray,

@@ -90,6 +90,8 @@ def bytes_per_token_head(d: int, k_kind: str, k_bits: int, v_kind: str, v_bits: 
         raise ValueError(k_kind)
     if v_kind == "group_sym":
         v = {"v_codes": 4 * words_for(d, v_bits), "v_aux": (d // 32) * 2}
+    elif v_kind == "group_asym":
+        v = {"v_codes": 4 * words_for(d, v_bits), "v_aux": (d // 32) * 4}
     elif v_kind == "lm_rot":
         v = {"v_codes": 4 * words_for(d, v_bits), "v_aux": 4}
     else:

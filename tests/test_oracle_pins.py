@@ -327,6 +327,58 @@ def test_affine8_grid_by_hand():
     assert np.array_equal(-1.0 + 2.0 ** -4 * e3["q8"][0], k3)
 
 
+@pytest.mark.parametrize("bits", [2, 4])
+def test_group_minmax_values_grid_and_ties_by_hand(bits):
+    """Min/max values (benchmark page): min -> code 0, max -> code L-1, values on the grid
+    m + a k reconstruct exactly, a value exactly half-way goes to the even code, a flat
+    group has a = 0 and codes 0."""
+    top = (1 << bits) - 1
+    a = 2.0 ** -3
+    m = -0.75
+    k = np.arange(32) % (top + 1)
+    v = m + a * k.astype(np.float64)
+    v[0], v[1] = m, m + a * top                  # the group's min and max
+    e = E.encode_v_group_asym(v[None], bits)
+    assert float(e["a16"][0, 0]) == a and float(e["m16"][0, 0]) == m
+    assert e["idx"][0, 0] == 0 and e["idx"][0, 1] == top
+    assert np.array_equal(m + a * e["idx"][0], v)
+    assert not e["near_idx"].any()
+    # exact half-way points: ties to the even code
+    w = v.copy()
+    w[2:2 + top] = m + a * (np.arange(top) + 0.5)
+    e2 = E.encode_v_group_asym(w[None], bits)
+    half = e2["idx"][0, 2:2 + top]
+    lo = np.arange(top)
+    assert np.array_equal(half, np.where(lo % 2 == 0, lo, lo + 1))
+    assert not e2["near_idx"].any()
+    e3 = E.encode_v_group_asym(np.full((1, 32), 0.3), bits)
+    assert float(e3["a16"][0, 0]) == 0 and np.all(e3["idx"] == 0)
+    # reconstruction error of N(0,1) groups stays within half a step plus the fp16 rounding of m
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((50, 64)).astype(np.float16).astype(np.float64)
+    e4 = E.encode_v_group_asym(x, bits)
+    ah = np.repeat(e4["a16"].astype(np.float64), 32, -1)
+    mh = np.repeat(e4["m16"].astype(np.float64), 32, -1)
+    lo32 = np.repeat(x.reshape(50, 2, 32).min(-1), 32, -1)
+    assert np.all(np.abs(mh + ah * e4["idx"] - x) <= ah / 2 + np.abs(mh - lo32) + ah * 2.0 ** -10 * top + 1e-12)
+
+
+def test_benchmark_memory_table_reproduced_by_the_layout():
+    """The benchmark page's 4096-token cache, 512 MB fp16 -> 113 MB, with its last 128 tokens
+    in fp16: keys read as 2 Lloyd-Max bits + the 1-bit QJL sketch ("3-bit keys", R1 reading)
+    and values as 2-bit group-32 min/max give 100 bytes per token and kv-head at d = 128,
+    6.25 bits per K/V element pair, and the printed total to the megabyte."""
+    g = json.load(open(os.path.join(GOLDEN, "compression_ratios.json")))["memory_table"]
+    per = sum(L.bytes_per_token_head(128, "lm_qjl", 2, "group_asym", 2).values())
+    assert per == 100
+    fp16_per_token = g["fp16_mb"] * 2 ** 20 / g["tokens"]            # bytes per token, all layers
+    heads_x_layers = fp16_per_token / (4 * 128)                         # (kv-head, layer) pairs
+    buf = g["fp16_buffer_tokens"]
+    total = buf * fp16_per_token + (g["tokens"] - buf) * heads_x_layers * per
+    assert round(total / 2 ** 20) == g["compressed_mb"]
+    assert L.compression_ratio(128, "lm_qjl", 2, "group_asym", 2) == 5.12
+
+
 def test_key_on_centroids_has_zero_residual():
     d = 128
     rng = np.random.default_rng(3)
@@ -363,7 +415,8 @@ def test_zero_residual_when_unit_vector_lands_on_centroids():
 KINDS = [("lm_qjl", 3, "group_sym", 2), ("lm_qjl", 4, "group_sym", 4), ("lm_qjl", 2, "group_sym", 2),
          ("affine8", 8, "lm_rot", 3), ("affine8", 8, "lm_rot", 2),
          ("lm_mse", 3, "lm_rot", 3), ("lm_mse", 4, "group_sym", 4), ("lm_mse", 2, "lm_rot", 2),
-         ("f16", 16, "lm_rot", 3), ("f16", 16, "group_sym", 2)]
+         ("f16", 16, "lm_rot", 3), ("f16", 16, "group_sym", 2),
+         ("lm_qjl", 2, "group_asym", 2), ("lm_qjl", 3, "group_asym", 4)]
 
 
 def _keys(kind, k):
