@@ -139,7 +139,7 @@ def bench_materialize(tq, lay, state, caches, wl, stream, steps: int, warmup: in
                        "lm_mse": "materialize_lm_kernel (keys)",
                        "affine8": "materialize_elem_kernel (keys)",
                        "f16": "materialize_elem_kernel (16-bit keys, copy)"}[wl.k_kind] + " + " +
-                      ("materialize_elem_kernel (values)" if wl.v_kind == "group_sym"
+                      ("materialize_elem_kernel (values)" if wl.v_kind in ("group_sym", "group_asym")
                        else "materialize_lm_kernel (values)"),
            "roofline": {"bound": "hbm", "achieved": gb, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": gb / HBM_PEAK_GBS, "traffic": None}}
@@ -379,7 +379,8 @@ def main():
         "encode_k": {"kernel": {"lm_qjl": "encode_lm_kernel (keys)", "lm_mse": "encode_lm_kernel (keys)",
                                 "affine8": "encode_affine8_kernel", "f16": "encode_copy16_kernel"}[wl.k_kind],
                      "ms": t_ek},
-        "encode_v": {"kernel": "encode_group_kernel" if wl.v_kind == "group_sym" else "encode_lm_kernel (values)",
+        "encode_v": {"kernel": {"group_sym": "encode_group_kernel", "group_asym": "encode_affine8_kernel (min/max values)",
+                                "lm_rot": "encode_lm_kernel (values)"}[wl.v_kind],
                      "ms": t_ev},
         "decode": {"kernel": "decode_main_kernel + decode_finish_kernel", "ms": t_dec},
     }

@@ -38,7 +38,11 @@ int k_aux_words(const tq_layout& L) {
   return L.k_kind == TQ_K_F16 ? 0 : 1;
 }
 int v_code_words(const tq_layout& L) { return lm_words(L.head_dim, L.v_bits); }
-int v_aux_bytes(const tq_layout& L) { return L.v_kind == TQ_V_GROUP_SYM ? (L.head_dim / 32) * 2 : 4; }
+int v_aux_bytes(const tq_layout& L) {
+  if (L.v_kind == TQ_V_GROUP_SYM) return (L.head_dim / 32) * 2;
+  if (L.v_kind == TQ_V_GROUP_ASYM) return (L.head_dim / 32) * 4;   // (a, m) fp16 per group
+  return 4;
+}
 
 }  // namespace tq
 
@@ -79,7 +83,7 @@ int check_layout(const tq_layout* L) {
   } else {
     return fail(TQ_ERR_UNSUPPORTED, "unknown k_kind %d", L->k_kind);
   }
-  if (L->v_kind == TQ_V_GROUP_SYM) {
+  if (L->v_kind == TQ_V_GROUP_SYM || L->v_kind == TQ_V_GROUP_ASYM) {
     if (L->v_bits != 2 && L->v_bits != 4) return fail(TQ_ERR_UNSUPPORTED, "group values need v_bits 2 or 4, got %d", L->v_bits);
   } else if (L->v_kind == TQ_V_LM_ROT) {
     if (L->v_bits < 2 || L->v_bits > 4) return fail(TQ_ERR_UNSUPPORTED, "rotated LM values need v_bits 2..4, got %d", L->v_bits);

@@ -312,8 +312,10 @@ hipError_t run_decode_d(const tq_layout& L, const tq_state& S, const void* q, co
     const hipError_t e = mk.launch(dim3((unsigned)groups), st, A);
     if (e != hipSuccess) return e;
   }
-  return (L.v_kind == TQ_V_GROUP_SYM) ? run_finish<D, TQ_V_GROUP_SYM>(A, batch * nq, st)
-                                      : run_finish<D, TQ_V_LM_ROT>(A, batch * nq, st);
+  // natural-domain value sums (symmetric and min/max groups) merge alike; rotated ones are
+  // rotated back once after the merge
+  return (L.v_kind == TQ_V_LM_ROT) ? run_finish<D, TQ_V_LM_ROT>(A, batch * nq, st)
+                                   : run_finish<D, TQ_V_GROUP_SYM>(A, batch * nq, st);
 }
 
 }  // namespace

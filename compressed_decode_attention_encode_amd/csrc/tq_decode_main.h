@@ -52,7 +52,7 @@ struct DecodeGeom {
   static constexpr int WAK = (KK == TQ_K_AFFINE8) ? D / 32 : (KK == TQ_K_F16 ? 0 : 1);
   static constexpr int VPER = (VB == 3) ? 10 : 32 / VB;
   static constexpr int WV = (D + VPER - 1) / VPER;
-  static constexpr int WAV = (VK == TQ_V_GROUP_SYM) ? D / 64 : 1;
+  static constexpr int WAV = (VK == TQ_V_GROUP_SYM) ? D / 64 : (VK == TQ_V_GROUP_ASYM ? D / 32 : 1);
   // odd LDS strides
   static constexpr int odd(int w) { return w == 0 ? 0 : (w | 1); }
   static constexpr int SK = odd(WK), SS = odd(WS), SAK = odd(WAK), SV = odd(WV), SAV = odd(WAV);

@@ -35,6 +35,8 @@
 // the codes themselves as exact fp16 operands (c - 128, from a byte permute and one packed fp16
 // add) and the block's scale and offset applied to each 32-dimension partial sum:
 //   s = sum_blk a (sum_j (c_j - 128) q_j) + (m + 128 a) sum_j q_j.
+// Group-32 min/max values (benchmark page, compression details) reuse the group path with
+// a = the group's step and an extra fp32 sum of p m per group (the offset term).
 // Rotated Lloyd-Max values (vllm-metal guide; TurboQuant-MLX page: 3-bit codes ten per word) use
 // P'' = p n (hi/lo fp16) against the centroid values (hi/lo, through a value code-pair table);
 // their sum stays in the rotated domain for the merge kernel's single inverse butterfly.
@@ -131,12 +133,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 6
 decode_mma_kernel(const DecodeArgs A) {
   constexpr int NREP = NQ * NREP_KV;
   using M = MmaGeom<D, NREP, KK, KB, VK, VB>;
-  constexpr bool QJL = M::QJL, AFF = M::AFF, ROT = VK == TQ_V_LM_ROT;
+  constexpr bool QJL = M::QJL, AFF = M::AFF, ROT = VK == TQ_V_LM_ROT, ASYM = VK == TQ_V_GROUP_ASYM;
   constexpr int LK = 1 << KB;
   constexpr int LV = 1 << VB;
   constexpr int NKB = M::NKB, NNB = M::NNB, NG = M::NG;
   static_assert(KK == TQ_K_LM_QJL || KK == TQ_K_LM_MSE || KK == TQ_K_AFFINE8, "key kind");
   static_assert(ROT ? (VB >= 2 && VB <= 4) : (VB == 2 || VB == 4), "value bits");
+  static_assert(VK == TQ_V_GROUP_SYM || VK == TQ_V_GROUP_ASYM || VK == TQ_V_LM_ROT, "value kind");
 
   __shared__ __attribute__((aligned(16))) float sm[M::FLOATS];
   uint32_t* smw = reinterpret_cast<uint32_t*>(sm);
@@ -239,9 +242,12 @@ decode_mma_kernel(const DecodeArgs A) {
 
   float m_run = -INFINITY, l_part = 0.f;        // head l16 (per lane: its tokens)
   float off[NG];                                // sum of P' per group, head l16
+  float moff[ASYM ? NG : 1];                    // min/max values: sum of p m per group, head l16
   mma_f4_t acc[NNB];                            // head 4 q4 + r, dimension 16 nb + l16
 #pragma unroll
   for (int k = 0; k < NG; ++k) off[k] = 0.f;
+#pragma unroll
+  for (int k = 0; k < (ASYM ? NG : 1); ++k) moff[k] = 0.f;
 #pragma unroll
   for (int nb = 0; nb < NNB; ++nb) acc[nb] = mma_f4_t{0.f, 0.f, 0.f, 0.f};
 
@@ -409,6 +415,10 @@ decode_mma_kernel(const DecodeArgs A) {
     m_run = mn;
 #pragma unroll
     for (int k = 0; k < NG; ++k) off[k] *= alpha;
+    if constexpr (ASYM) {
+#pragma unroll
+      for (int k = 0; k < NG; ++k) moff[k] *= alpha;
+    }
     {
       float al[4];
 #pragma unroll
@@ -421,56 +431,59 @@ decode_mma_kernel(const DecodeArgs A) {
 
     // ---- weighted values: two 32-token blocks ------------------------------------------
     if constexpr (!ROT) {
+      // group values: P' = fp16(p Delta) against the exact fp16 1 + c/2^m; min/max values
+      // also sum p m per group in fp32 (their offset term)
       constexpr uint32_t kOne = 0x3C003C00u;       // fp16 pair (1, 1)
-  #pragma unroll
+#pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
         // k slot i of this lane: token 32 kb2 + 4 q4 + i (i < 4), 32 kb2 + 16 + 4 q4 + i - 4
         const int tk = 32 * kb2 + 4 * q4;
-  #pragma unroll
-        for (int w = 0; w < M::WAV; ++w) {
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+          // the group's scale (two fp16 per word for symmetric groups; one (a, m) word per
+          // group for min/max values) for the lane's 8 tokens
+          const int w = ASYM ? gi : gi / 2, hf = ASYM ? 0 : gi % 2;
           const uint4 d0 = *reinterpret_cast<const uint4*>(stav + w * M::TS + tk);
           const uint4 d1 = *reinterpret_cast<const uint4*>(stav + w * M::TS + tk + 16);
           const uint32_t dw[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
-  #pragma unroll
-          for (int hf = 0; hf < 2; ++hf) {
-            const int gi = 2 * w + hf;
-            if (gi < NG) {
-              mma_u4_t apv;
-              {
-                float wt[8];
-  #pragma unroll
-                for (int i = 0; i < 8; ++i)
-                  wt[i] = p[2 * kb2 + (i >> 2)][i & 3] * f16_to_f32((dw[i] >> (16 * hf)) & 0xFFFFu);
-  #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                  apv[k] = pack_f16x2(wt[2 * k], wt[2 * k + 1]);
-                  off[gi] = dot2_f16(apv[k], kOne, off[gi]);
-                }
-              }
-              // the group's two 16-dimension blocks
-  #pragma unroll
-              for (int nb = 2 * gi; nb < 2 * gi + 2; ++nb) {
-                uint32_t x[8];
-                int bit;
-                {
-                  const uint32_t* src = (VB == 2) ? stv + nb * M::TS + tk : stv + (2 * nb + (l16 >> 3)) * M::TS + tk;
-                  const uint4 x0 = *reinterpret_cast<const uint4*>(src);
-                  const uint4 x1 = *reinterpret_cast<const uint4*>(src + 16);
-                  x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w; x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
-                  bit = (VB == 2) ? 2 * l16 : 4 * (l16 & 7);
-                }
-                // code c -> fp16 1 + c / 2^MV: the code dropped into the mantissa under 1.0's exponent
-                constexpr int MV = (VB == 2) ? 8 : 6;
-                mma_u4_t bv;
-  #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                  const uint32_t c0 = __builtin_amdgcn_ubfe(x[2 * k], (uint32_t)bit, VB);
-                  const uint32_t c1 = __builtin_amdgcn_ubfe(x[2 * k + 1], (uint32_t)bit, VB);
-                  bv[k] = (c0 << MV) | (c1 << (16 + MV)) | kOne;
-                }
-                acc[nb] = mma16(apv, bv, acc[nb]);
-              }
+          mma_u4_t apv;
+          {
+            float wt[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+              wt[i] = p[2 * kb2 + (i >> 2)][i & 3] * f16_to_f32((dw[i] >> (16 * hf)) & 0xFFFFu);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              apv[k] = pack_f16x2(wt[2 * k], wt[2 * k + 1]);
+              off[gi] = dot2_f16(apv[k], kOne, off[gi]);
             }
+            if constexpr (ASYM) {
+#pragma unroll
+              for (int i = 0; i < 8; ++i) moff[gi] = fmaf(p[2 * kb2 + (i >> 2)][i & 3], f16_to_f32(dw[i] >> 16), moff[gi]);
+            }
+          }
+          // the group's two 16-dimension blocks
+#pragma unroll
+          for (int nb = 2 * gi; nb < 2 * gi + 2; ++nb) {
+            uint32_t x[8];
+            int bit;
+            {
+              const uint32_t* src = (VB == 2) ? stv + nb * M::TS + tk : stv + (2 * nb + (l16 >> 3)) * M::TS + tk;
+              const uint4 x0 = *reinterpret_cast<const uint4*>(src);
+              const uint4 x1 = *reinterpret_cast<const uint4*>(src + 16);
+              x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w; x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
+              bit = (VB == 2) ? 2 * l16 : 4 * (l16 & 7);
+            }
+            // code c -> fp16 1 + c / 2^MV: the code dropped into the mantissa under 1.0's exponent
+            constexpr int MV = (VB == 2) ? 8 : 6;
+            mma_u4_t bv;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const uint32_t c0 = __builtin_amdgcn_ubfe(x[2 * k], (uint32_t)bit, VB);
+              const uint32_t c1 = __builtin_amdgcn_ubfe(x[2 * k + 1], (uint32_t)bit, VB);
+              bv[k] = (c0 << MV) | (c1 << (16 + MV)) | kOne;
+            }
+            acc[nb] = mma16(apv, bv, acc[nb]);
           }
         }
       }
@@ -542,10 +555,18 @@ decode_mma_kernel(const DecodeArgs A) {
     off[k] += __shfl_xor(off[k], 16);
     off[k] += __shfl_xor(off[k], 32);
   }
+  if constexpr (ASYM) {
+#pragma unroll
+    for (int k = 0; k < NG; ++k) {
+      moff[k] += __shfl_xor(moff[k], 16);
+      moff[k] += __shfl_xor(moff[k], 32);
+    }
+  }
   // group values: acc = sum P' (1 + c / F), off = sum P'  ->  sum P' (c - (L-1)/2) = F acc - (F + (L-1)/2) off;
   // rotated values: acc = sum P'' 8 c  ->  acc / 8 (still in the rotated domain)
   constexpr float F = ROT ? 1.f / kMmaCentScale : ((VB == 2) ? 4.f : 16.f);
-  constexpr float FO = ROT ? 0.f : F + 0.5f * (float)(LV - 1);
+  // min/max values: sum p (m + a c) = F acc - F off + sum p m
+  constexpr float FO = ROT ? 0.f : (ASYM ? F : F + 0.5f * (float)(LV - 1));
   __syncthreads();   // every wave is done with its staging area
   float(*s_mrg_acc)[NREP * D] = reinterpret_cast<float(*)[NREP * D]>(smw + M::OFF_ST);
   float* s_mrg_m = sm + M::OFF_MRG;            // [4][NREP]
@@ -553,13 +574,16 @@ decode_mma_kernel(const DecodeArgs A) {
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int h = 4 * q4 + r;
-    float o[NG];
+    float o[NG], mo[NG];
 #pragma unroll
-    for (int k = 0; k < NG; ++k) o[k] = __shfl(off[k], h);
+    for (int k = 0; k < NG; ++k) {
+      o[k] = __shfl(off[k], h);
+      mo[k] = ASYM ? __shfl(moff[k], h) : 0.f;
+    }
     if (h < NREP) {
 #pragma unroll
       for (int nb = 0; nb < NNB; ++nb)
-        s_mrg_acc[wave][h * D + 16 * nb + l16] = ROT ? F * acc[nb][r] : fmaf(F, acc[nb][r], -FO * o[nb / 2]);
+        s_mrg_acc[wave][h * D + 16 * nb + l16] = ROT ? F * acc[nb][r] : fmaf(F, acc[nb][r], fmaf(-FO, o[nb / 2], mo[nb / 2]));
     }
   }
   if (lane < NREP) {

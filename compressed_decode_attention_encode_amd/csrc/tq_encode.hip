@@ -464,18 +464,21 @@ encode_group_kernel(const uint16_t* __restrict__ x, int T, int slices, int dst_o
   }
 }
 
-// Per-block affine 8-bit keys.  Boundaries m + a (q -+ 1/2) are exact in float64 for fp16
-// a and m, so a float32 estimate of rne((k - m)/a) is corrected by two exact float64
-// comparisons (ties to even).
+// Per-block affine 8-bit keys, and group-32 min/max values at 2 or 4 bits (benchmark page,
+// compression details): the same quantiser with L - 1 = 255, 3 or 15.  Boundaries
+// m + a (q -+ 1/2) are exact in float64 for fp16 a and m, so a float32 estimate of
+// rne((k - m)/a) is corrected by two exact float64 comparisons (ties to even).
 __device__ __forceinline__ bool passes64(double v, double tau, int k) {
   return (k & 1) ? (v > tau) : (v >= tau);
 }
 
-template <int D, int DT>
+template <int D, int DT, int QB = 8>
 __global__ void __launch_bounds__(256)
 encode_affine8_kernel(const uint16_t* __restrict__ x, int T, int slices, int dst_offset, int cap,
                       uint32_t* __restrict__ codes_out, uint32_t* __restrict__ aux_out) {
+  static_assert(QB == 8 || QB == 4 || QB == 2, "8-bit keys, 2/4-bit values");
   constexpr int G = D / 32;
+  constexpr int TOP = (1 << QB) - 1;
   const int parts = T * (D / 8);
   for (int slice = blockIdx.y; slice < slices; slice += gridDim.y) {
     const uint16_t* xs = x + (size_t)slice * T * D;
@@ -503,8 +506,12 @@ encode_affine8_kernel(const uint16_t* __restrict__ x, int T, int slices, int dst
       // a = fp16((hi - lo)/255): the difference is exact in float64; the quotient's binary
       // fraction repeats with period 8 (1/255), far from an fp16 rounding tie, so rounding
       // the float64 product to float32 and then to fp16 gives the exactly rounded result.
-      const uint32_t abits =
-          __builtin_bit_cast(uint16_t, (_Float16)(float)(((double)hi - (double)lo) * (1.0 / 255.0)));
+      // (for 3 and 15 the float64 quotient rounds straight to fp16: its exact value is a
+      // terminating binary fraction (then exact in float64) or at least 2^-53 relatively away
+      // from an fp16 tie)
+      const uint32_t abits = (QB == 8)
+          ? (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(float)(((double)hi - (double)lo) * (1.0 / 255.0)))
+          : f64_to_f16_rne(((double)hi - (double)lo) / (double)TOP);
       const uint32_t mbits = __builtin_bit_cast(uint16_t, (_Float16)lo);
       const double a = (double)f16_to_f32(abits);
       const double m = (double)f16_to_f32(mbits);
@@ -518,18 +525,25 @@ encode_affine8_kernel(const uint16_t* __restrict__ x, int T, int slices, int dst
         // a half-integer (a level boundary, exact ties included) needs the exact test
         const float x = (ve - mf) * inva;
         const float qr = rintf(x);
-        float qf = fminf(fmaxf(qr, 0.f), 255.f);
+        float qf = fminf(fmaxf(qr, 0.f), (float)TOP);
         if (fabsf(fabsf(x - qr) - 0.5f) < 0x1p-11f && a > 0.0) {
           // boundary b between levels b-1 and b at m + a (b - 1/2), exact in float64
           const float bf = rintf(x + 0.5f);
           qf = passes64((double)ve, fma(a, (double)bf - 0.5, m), (int)bf) ? bf : bf - 1.f;
-          qf = fminf(fmaxf(qf, 0.f), 255.f);
+          qf = fminf(fmaxf(qf, 0.f), (float)TOP);
         }
-        words[e >> 2] |= (uint32_t)qf << (8 * (e & 3));
+        if constexpr (QB == 8) words[e >> 2] |= (uint32_t)qf << (8 * (e & 3));
+        else words[0] |= (uint32_t)qf << (QB * e);
       }
       if (p < parts) {
         const size_t row = row_s + t;
-        *reinterpret_cast<uint2*>(codes_out + row * (D / 4) + 8 * g + 2 * sub) = make_uint2(words[0], words[1]);
+        if constexpr (QB == 8) {
+          *reinterpret_cast<uint2*>(codes_out + row * (D / 4) + 8 * g + 2 * sub) = make_uint2(words[0], words[1]);
+        } else if constexpr (QB == 4) {
+          codes_out[row * (D / 8) + g * 4 + sub] = words[0];                                  // 8 codes = one word
+        } else {
+          reinterpret_cast<uint16_t*>(codes_out + row * (D / 16) + g * 2)[sub] = (uint16_t)words[0];   // half a word
+        }
         if (sub == 0) aux_out[row * G + g] = abits | (mbits << 16);
       }
     }
@@ -617,6 +631,16 @@ hipError_t run_group(const tq_layout& Lay, const void* x, int batch, int T, int 
   return hipGetLastError();
 }
 
+// group-32 min/max values: the affine quantiser at v_bits
+template <int D, int QB, int DT>
+hipError_t run_minmax_v(const tq_layout& Lay, const void* x, int batch, int T, int dst, const tq_cache& C,
+                        hipStream_t st) {
+  const int slices = batch * Lay.n_kv_heads;
+  hipLaunchKernelGGL((encode_affine8_kernel<D, DT, QB>), group_grid(slices, T, D), dim3(256), 0, st,
+                     (const uint16_t*)x, T, slices, dst, C.capacity, (uint32_t*)C.v_codes, (uint32_t*)C.v_aux);
+  return hipGetLastError();
+}
+
 template <int D, int DT>
 hipError_t run_affine(const tq_layout& Lay, const void* x, int batch, int T, int dst, const tq_cache& C,
                       hipStream_t st) {
@@ -662,7 +686,7 @@ bool encode_k_compiled(const tq_layout& L) {
 bool encode_v_compiled(const tq_layout& L) {
   const bool d_ok = L.head_dim == 64 || L.head_dim == 128 || L.head_dim == 256;
   const bool dt_ok = L.in_dtype == TQ_F16 || L.in_dtype == TQ_BF16;
-  if (L.v_kind == TQ_V_GROUP_SYM) return d_ok && dt_ok && (L.v_bits == 2 || L.v_bits == 4);
+  if (L.v_kind == TQ_V_GROUP_SYM || L.v_kind == TQ_V_GROUP_ASYM) return d_ok && dt_ok && (L.v_bits == 2 || L.v_bits == 4);
   if (L.v_kind == TQ_V_LM_ROT) return d_ok && dt_ok && L.v_bits >= 2 && L.v_bits <= 4;
   return false;
 }
@@ -698,6 +722,10 @@ hipError_t launch_encode_v(const tq_layout& L, const tq_state& S, const void* v,
     TQ_D_SWITCH(L.head_dim, TQ_DT_SWITCH(L.in_dtype,
         if (L.v_bits == 2) err = (run_group<DD, 2, DTT>(L, v, batch, n_tokens, dst_offset, C, st));
         else err = (run_group<DD, 4, DTT>(L, v, batch, n_tokens, dst_offset, C, st));))
+  } else if (L.v_kind == TQ_V_GROUP_ASYM) {
+    TQ_D_SWITCH(L.head_dim, TQ_DT_SWITCH(L.in_dtype,
+        if (L.v_bits == 2) err = (run_minmax_v<DD, 2, DTT>(L, v, batch, n_tokens, dst_offset, C, st));
+        else err = (run_minmax_v<DD, 4, DTT>(L, v, batch, n_tokens, dst_offset, C, st));))
   } else {
     TQ_D_SWITCH(L.head_dim, TQ_B_SWITCH(L.v_bits, TQ_DT_SWITCH(L.in_dtype,
         err = (run_lm<DD, BB, DTT, false>(L, S, v, batch, n_tokens, dst_offset, C, st, true));)))

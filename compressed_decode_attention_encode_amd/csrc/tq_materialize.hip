@@ -53,6 +53,7 @@ __device__ __forceinline__ uint32_t to_out(float x) {
 //   KIND 0: affine-8 keys (codes: bytes; aux: fp16 (a, m) per 32-block)
 //   KIND 1: group values  (codes: VB-bit; aux: fp16 Delta per 32-group)
 //   KIND 2: 16-bit keys   (codes: the stored row, dtype VB = TQ_F16 / TQ_BF16; no aux)
+//   KIND 3: min/max values (codes: VB-bit; aux: fp16 (a, m) per 32-group; v = m + a c)
 // ---------------------------------------------------------------------------------
 template <int D, int KIND, int VB, int OUT>
 __global__ void __launch_bounds__(256) materialize_elem_kernel(const uint32_t* __restrict__ codes,
@@ -85,6 +86,15 @@ __global__ void __launch_bounds__(256) materialize_elem_kernel(const uint32_t* _
       v[e] = fmaf(a, (float)((w.x >> (8 * e)) & 0xFFu), m);
       v[4 + e] = fmaf(a, (float)((w.y >> (8 * e)) & 0xFFu), m);
     }
+  } else if constexpr (KIND == 3) {
+    constexpr int L = 1 << VB;
+    constexpr int WR = D * VB / 32;
+    const int bit0 = 8 * VB * o;
+    const uint32_t w = codes[row * WR + (bit0 >> 5)] >> (bit0 & 31);
+    const uint32_t am = aux[row * (D / 32) + g];
+    const float a = f16_to_f32(am & 0xFFFFu), m = f16_to_f32(am >> 16);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = fmaf(a, (float)((w >> (VB * e)) & (L - 1)), m);
   } else {
     constexpr int L = 1 << VB;
     constexpr int WR = D * VB / 32;          // code words per row
@@ -420,6 +430,13 @@ hipError_t launch_materialize_v(const tq_layout& L, const tq_state& S, const tq_
   uint16_t* o = static_cast<uint16_t*>(out);
   const uint32_t* codes = static_cast<const uint32_t*>(C.v_codes);
   const uint32_t* aux = static_cast<const uint32_t*>(C.v_aux);
+  if (L.v_kind == TQ_V_GROUP_ASYM) {
+    if (L.v_bits == 2)
+      return (out_dtype == TQ_BF16) ? run_elem_d<3, 2, TQ_BF16>(L.head_dim, codes, aux, slices, C.capacity, t0, n, o, st)
+                                    : run_elem_d<3, 2, TQ_F16>(L.head_dim, codes, aux, slices, C.capacity, t0, n, o, st);
+    return (out_dtype == TQ_BF16) ? run_elem_d<3, 4, TQ_BF16>(L.head_dim, codes, aux, slices, C.capacity, t0, n, o, st)
+                                  : run_elem_d<3, 4, TQ_F16>(L.head_dim, codes, aux, slices, C.capacity, t0, n, o, st);
+  }
   if (L.v_kind == TQ_V_GROUP_SYM) {
     if (L.v_bits == 2)
       return (out_dtype == TQ_BF16) ? run_elem_d<1, 2, TQ_BF16>(L.head_dim, codes, aux, slices, C.capacity, t0, n, o, st)

@@ -43,7 +43,7 @@ if len(_hip_runtimes_loaded()) > 1:
 TQ_OK, TQ_ERR_INVALID, TQ_ERR_UNSUPPORTED, TQ_ERR_CAPACITY, TQ_ERR_HIP = 0, -1, -2, -3, -4
 TQ_F16, TQ_BF16 = 0, 1
 TQ_K_LM_QJL, TQ_K_AFFINE8, TQ_K_LM_MSE, TQ_K_F16 = 0, 1, 2, 3
-TQ_V_GROUP_SYM, TQ_V_LM_ROT = 0, 1
+TQ_V_GROUP_SYM, TQ_V_LM_ROT, TQ_V_GROUP_ASYM = 0, 1, 2
 
 EXPORTED = ("tq_make_codebook", "tq_make_rotation", "tq_cache_plane_bytes", "tq_encode",
             "tq_decode_workspace_bytes", "tq_decode_attn", "tq_decode_multi_workspace_bytes", "tq_decode_attn_multi",
@@ -193,7 +193,7 @@ def tq_materialize(layout: tq_layout, state: tq_state, cache: tq_cache, t0: int,
 
 # ---------------------------------------------------------------------------- marshalling helpers
 _KIND_K = {"lm_qjl": TQ_K_LM_QJL, "affine8": TQ_K_AFFINE8, "lm_mse": TQ_K_LM_MSE, "f16": TQ_K_F16}
-_KIND_V = {"group_sym": TQ_V_GROUP_SYM, "lm_rot": TQ_V_LM_ROT}
+_KIND_V = {"group_sym": TQ_V_GROUP_SYM, "lm_rot": TQ_V_LM_ROT, "group_asym": TQ_V_GROUP_ASYM}
 _DT = {"f16": TQ_F16, "bf16": TQ_BF16}
 
 

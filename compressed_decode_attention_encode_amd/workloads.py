@@ -40,7 +40,7 @@ class Workload:
     n_recent: int         # last n_recent tokens stay exact in the recent buffer
     k_kind: str           # "lm_qjl" | "affine8" | "lm_mse" | "f16" (keys kept 16-bit, k_bits 16)
     k_bits: int
-    v_kind: str           # "group_sym" | "lm_rot"
+    v_kind: str           # "group_sym" | "lm_rot" | "group_asym" (group-32 min/max)
     v_bits: int
     in_dtype: str         # "f16" | "bf16"   (K/V/Q as produced by the model)
     recent_dtype: str     # "f16"
@@ -94,6 +94,12 @@ WORKLOADS = {
     "llama1b_vonly_h32x8_d64_t32k": Workload(
         "llama1b_vonly_h32x8_d64_t32k", 109, 1, 32, 8, 64, 32768, 128,
         "f16", 16, "lm_rot", 3, "f16", "f16", "const10", 4),
+    # the benchmark page's layout under the 2 + 1 bit reading of "3-bit keys" (2 Lloyd-Max
+    # bits + the QJL sign) with group-32 min/max 2-bit values, on the Qwen2.5-32B-like geometry
+    # (its memory table comes out of this layout: 100 bytes per token and kv-head)
+    "qwen32b_r1_h40x8_d128_b4_t32k": Workload(
+        "qwen32b_r1_h40x8_d128_b4_t32k", 110, 4, 40, 8, 128, 32768, 128,
+        "lm_qjl", 2, "group_asym", 2, "bf16", "f16"),
     "qwen7b_k8v4_h28x4_d128_b16_t32k": Workload(
         "qwen7b_k8v4_h28x4_d128_b16_t32k", 108, 16, 28, 4, 128, 32768, 128,
         "affine8", 8, "lm_rot", 4, "bf16", "f16", "studentt3x10", 4, flush_tokens=128),

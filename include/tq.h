@@ -76,8 +76,12 @@ typedef enum { TQ_K_LM_QJL = 0, TQ_K_AFFINE8 = 1, TQ_K_LM_MSE = 2, TQ_K_F16 = 3 
  *   Delta = 0 gives idx = L-1 / 0 / L/2 for v > 0 / v < 0 / v = 0.
  * TQ_V_LM_ROT (vllm-metal guide principle table; MLX page core technique): n = |v|
  *   stored fp32, y = Pi v/n with the value rotation, idx by the value codebook
- *   (v_bits in {2,3,4}); decoded value n Pi^T c[idx].                              */
-typedef enum { TQ_V_GROUP_SYM = 0, TQ_V_LM_ROT = 1 } tq_vkind;
+ *   (v_bits in {2,3,4}); decoded value n Pi^T c[idx].
+ * TQ_V_GROUP_ASYM (benchmark page, compression details: values keep a per-group minimum
+ *   and maximum): per 32-group a = fp16((max - min)/(L-1)), m = fp16(min), v_bits in
+ *   {2,4}; idx = clamp(rne((v - m)/a), 0, L-1) with the stored a, m (ties to even; a = 0
+ *   gives idx = 0); decoded value m + a idx; aux plane one (a, m) fp16 pair per group.  */
+typedef enum { TQ_V_GROUP_SYM = 0, TQ_V_LM_ROT = 1, TQ_V_GROUP_ASYM = 2 } tq_vkind;
 
 typedef struct {
   int32_t head_dim;      /* d in {64, 128, 256}                                          */

@@ -55,6 +55,8 @@ def plane_shapes(wl, batch, cap):
         s["k_aux"] = (np.uint16, (batch, wl.n_kv_heads, cap, d // 32, 2))
     if wl.v_kind == "group_sym":
         s["v_aux"] = (np.uint16, (batch, wl.n_kv_heads, cap, d // 32))
+    elif wl.v_kind == "group_asym":
+        s["v_aux"] = (np.uint16, (batch, wl.n_kv_heads, cap, d // 32, 2))
     else:
         s["v_aux"] = (np.float32, (batch, wl.n_kv_heads, cap))
     return s
@@ -75,6 +77,20 @@ def upload_planes(cache, planes: dict):
             src = torch.from_numpy(np.ascontiguousarray(arr).view(np.uint8).reshape(-1))
             assert src.numel() == cache.planes[name].numel(), name
             cache.planes[name].copy_(src.cuda())
+
+
+def upload_slice(cache, wl, planes: dict, b: int, g: int, cap: int):
+    """Overwrite slice (b, g) of every plane of a device cache [B][Hkv][cap][row] with the
+    given planes of shape [1, 1, cap, ...] (the oracle's encoding of that slice)."""
+    torch = torch_mod()
+    for name, (dt, shape) in plane_shapes(wl, cache.struct.batch, cap).items():
+        if name not in planes or name not in cache.planes:
+            continue
+        row = int(np.prod(shape[3:], dtype=np.int64)) * np.dtype(dt).itemsize
+        src = np.ascontiguousarray(planes[name]).view(np.uint8).reshape(-1)
+        assert src.size == cap * row, (name, src.size, cap * row)
+        off = ((b * wl.n_kv_heads + g) * cap) * row
+        cache.planes[name][off:off + cap * row].copy_(torch.from_numpy(src).cuda())
 
 
 class Setup:
@@ -211,7 +227,7 @@ def compare_encode(wl, gpu: dict, ek: dict, ev: dict, rows=slice(None)) -> dict:
         st["k_idx_excluded"] = int(near.sum())
         st["k_idx_excluded_differ"] = int((diff & near).sum())
         st["k_aux_mismatch"] = int((g["k_aux"] != ek["k_aux"]).sum())
-    if wl.v_kind == "group_sym":
+    if wl.v_kind in ("group_sym", "group_asym"):
         vi = OL.unpack_codes(g["v_codes"], wl.v_bits, d)
         near = ev["near_idx"]
         diff = vi != ev["enc"]["idx"]

@@ -51,7 +51,8 @@ def test_rotation_state_matches_reference_generator(d):
 
 
 CONFIGS = [(64, "lm_qjl", 3, "group_sym", 2), (128, "lm_qjl", 4, "group_sym", 4), (128, "affine8", 8, "lm_rot", 3),
-           (256, "lm_qjl", 4, "group_sym", 4), (128, "lm_qjl", 2, "lm_rot", 2)]
+           (256, "lm_qjl", 4, "group_sym", 4), (128, "lm_qjl", 2, "lm_rot", 2), (128, "lm_qjl", 2, "group_asym", 2),
+           (64, "lm_qjl", 3, "group_asym", 4)]
 
 
 @pytest.mark.parametrize("cfg", CONFIGS)
