@@ -83,9 +83,9 @@ struct DecodeGeom {
 // reads of the next tile (they stay in flight while the current tile is computed),
 // store() later writes them into the wave's LDS area with row stride LS.  Reads never
 // go past the last valid row; rows beyond it are zero-filled.
-template <int W, int LS>
+template <int W, int LS, int TR = kTile>
 struct RowLoader {
-  static constexpr int N = kTile * W;               // words per tile
+  static constexpr int N = TR * W;                  // words per tile (TR rows)
   static constexpr int NV = (N + 4 * kWave - 1) / (4 * kWave);
   static constexpr int NR = (W == 0) ? 1 : 4 * NV;  // registers per lane
   uint32_t r[NR];
@@ -352,7 +352,9 @@ __device__ __forceinline__ float* partial_ptr(const DecodeArgs& A, int b, int he
 // With NQ > 1 (multi-query groups, NREP = NQ x n_rep rows) the last NQ recent tokens are the
 // queries' own, in order, and query j sees recent tokens 0 .. R - NQ + j (causal inside the
 // suffix); R >= NQ is checked on the host, so every row sees at least one token.
-template <int D, int NREP, int KK, int KB, int VK, int VB, int NQ = 1>
+// SCR: float offset of its scratch in the work-group's LDS (by default the staging area of
+// the vector-ALU kernel; the matrix-core kernel places it right after the queries).
+template <int D, int NREP, int KK, int KB, int VK, int VB, int NQ = 1, int SCR = -1>
 __device__ void recent_split(const DecodeArgs& A, int b, int g, float* sm) {
   using G = DecodeGeom<D, NREP, KK, KB, VK, VB>;
   static_assert(kMaxRecent * 2 <= 256, "two threads per recent token");
@@ -363,10 +365,10 @@ __device__ void recent_split(const DecodeArgs& A, int b, int g, float* sm) {
   const int R = A.n_recent;
   const int bf = A.recent_bf16;
   float* qn = sm + G::OFF_QA;
-  float* sr = sm + G::OFF_ST;                 // [NREP][kMaxRecent] scores -> weights
+  float* sr = sm + (SCR >= 0 ? SCR : G::OFF_ST);   // [NREP][kMaxRecent] scores -> weights
   float* sML = sr + NREP * kMaxRecent;        // [NREP] max, [NREP] normaliser
   float* sacc = sML + 2 * NREP;               // [NG][NREP][D] partial value sums
-  static_assert(G::STAGE_ALL >= NREP * kMaxRecent + 2 * NREP + NG * NREP * D,
+  static_assert(SCR >= 0 || G::STAGE_ALL >= NREP * kMaxRecent + 2 * NREP + NG * NREP * D,
                 "recent scratch does not fit the staging area");
   const size_t rbase = ((size_t)b * A.Hkv + g) * A.recent_cap;
   // Reads past the last row are clamped to it (never out of bounds, never a branch

@@ -79,7 +79,7 @@ __device__ __forceinline__ void split_f16x2(float a, float b, uint32_t& hi, uint
   lo = __builtin_bit_cast(uint32_t, l);
 }
 
-template <int D, int NREP, int KK, int KB, int VK, int VB>
+template <int D, int NREP, int KK, int KB, int VK, int VB, int TT = kTile>
 struct MmaGeom {
   using G = DecodeGeom<D, NREP, KK, KB, VK, VB>;
   static constexpr bool QJL = KK == TQ_K_LM_QJL;
@@ -88,16 +88,16 @@ struct MmaGeom {
   static constexpr int WS = G::WS, SS = G::SS;
   static constexpr int WAK = G::WAK;            // key aux words per token: (n, gamma) / fp32 n / (a, m) per block
   static constexpr int WV = G::WV, WAV = G::WAV;
-  static constexpr int TS = kTile + 4;        // token stride of the transposed value planes
+  static constexpr int TS = TT + 4;           // token stride of the transposed value planes
   static constexpr int NKB = D / 32;          // 32-dimension blocks of the score contraction
   static constexpr int NNB = D / 16;          // 16-dimension blocks of the value product
   static constexpr int NG = D / 32;           // value groups
   // one wave's staging area (words): key rows, sign rows, key aux (one word per token for the
   // LM kinds; word-major [block][token] for affine keys), value codes and value aux word-major
   static constexpr int OFF_SK = 0;
-  static constexpr int OFF_SS = OFF_SK + kTile * SK;
-  static constexpr int OFF_SAK = OFF_SS + kTile * SS;
-  static constexpr int OFF_SV = OFF_SAK + (AFF ? WAK * TS : kTile);
+  static constexpr int OFF_SS = OFF_SK + TT * SK;
+  static constexpr int OFF_SAK = OFF_SS + TT * SS;
+  static constexpr int OFF_SV = OFF_SAK + (AFF ? WAK * TS : TT);
   static constexpr int OFF_SAV = OFF_SV + WV * TS;
   static constexpr int STAGE = OFF_SAV + WAV * TS;
   static_assert(OFF_SAK % 4 == 0 && OFF_SV % 4 == 0 && OFF_SAV % 4 == 0 && STAGE % 4 == 0, "16-byte LDS reads");
@@ -121,18 +121,25 @@ struct MmaGeom {
   static constexpr int STAGE_ALL = (4 * STAGE > 4 * NREP * D) ? 4 * STAGE : 4 * NREP * D;
   static constexpr int OFF_MRG = OFF_ST + STAGE_ALL;
   static constexpr int OWN = OFF_MRG + 8 * NREP + 16;
-  static constexpr int FLOATS = OWN > G::FLOATS ? OWN : G::FLOATS;   // the recent split shares it
+  // the recent-buffer split: the queries (G::OFF_QA) and its scratch right after qa, qb
+  static constexpr int OFF_RSCR = G::OFF_TQ;
+  static constexpr int RECENT_NEED = OFF_RSCR + G::RECENT_SCRATCH;
+  static constexpr int FLOATS = OWN > RECENT_NEED ? OWN : RECENT_NEED;
   static_assert(NREP <= 16, "one 16-column operand holds the heads");
 };
 
 // NQ > 1: a multi-query group.  The NQ x n_rep rows (query j, head h at row j n_rep + h) take
 // the operand columns of the heads, so the score and value products cost the same per tile;
 // only the softmax and the output rows grow.  Below, NREP counts rows.
-template <int D, int NREP_KV, int KK, int KB, int VK, int VB, int NQ = 1>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 2)))
+// TT: tokens per wave tile (64; 32 at head_dim 256, where a 64-token tile's staging and
+// registers would leave one wave per SIMD).
+template <int D, int NREP_KV, int KK, int KB, int VK, int VB, int NQ = 1, int TT = kTile>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : (D == 256 ? 1 : 2))))
 decode_mma_kernel(const DecodeArgs A) {
   constexpr int NREP = NQ * NREP_KV;
-  using M = MmaGeom<D, NREP, KK, KB, VK, VB>;
+  using M = MmaGeom<D, NREP, KK, KB, VK, VB, TT>;
+  constexpr int MB = TT / 16;                    // 16-token blocks per tile
+  static_assert(TT == 64 || TT == 32, "tile of 32 or 64 tokens");
   constexpr bool QJL = M::QJL, AFF = M::AFF, ROT = VK == TQ_V_LM_ROT, ASYM = VK == TQ_V_GROUP_ASYM;
   constexpr int LK = 1 << KB;
   constexpr int LV = 1 << VB;
@@ -151,7 +158,7 @@ decode_mma_kernel(const DecodeArgs A) {
   const int n_comp = A.nsplit * A.Hkv * A.batch;
   if ((int)blockIdx.x >= n_comp) {
     const int u = blockIdx.x - n_comp;
-    recent_split<D, NREP, KK, KB, VK, VB, NQ>(A, u / A.Hkv, u % A.Hkv, sm);
+    recent_split<D, NREP, KK, KB, VK, VB, NQ, M::OFF_RSCR>(A, u / A.Hkv, u % A.Hkv, sm);
     return;
   }
   const int split = blockIdx.x % A.nsplit;
@@ -169,13 +176,13 @@ decode_mma_kernel(const DecodeArgs A) {
   const uint32_t* stv = st + M::OFF_SV;
   const uint32_t* stav = st + M::OFF_SAV;
 
-  RowLoader<M::WK, M::SK> ld_k;
-  RowLoader<M::WS, M::SS> ld_s;
-  RowLoader<M::WAK, AFF ? M::TS : 1> ld_ak;
-  RowLoader<M::WV, M::TS> ld_v;
-  RowLoader<M::WAV, M::TS> ld_av;
+  RowLoader<M::WK, M::SK, TT> ld_k;
+  RowLoader<M::WS, M::SS, TT> ld_s;
+  RowLoader<M::WAK, AFF ? M::TS : 1, TT> ld_ak;
+  RowLoader<M::WV, M::TS, TT> ld_v;
+  RowLoader<M::WAV, M::TS, TT> ld_av;
   auto issue = [&](int t0) {
-    const int nv = min(kTile, te - t0);
+    const int nv = min(TT, te - t0);
     const size_t row0 = slice * cap + t0;
     ld_k.load(A.kc + row0 * M::WK, nv, lane);
     ld_s.load(A.ks + row0 * M::WS, nv, lane);
@@ -183,7 +190,7 @@ decode_mma_kernel(const DecodeArgs A) {
     ld_v.load(A.vc + row0 * M::WV, nv, lane);
     ld_av.load(A.va + row0 * M::WAV, nv, lane);
   };
-  if (tb + wave * kTile < te) issue(tb + wave * kTile);
+  if (tb + wave * TT < te) issue(tb + wave * TT);
 
   // code-pair tables: entry pc = (code a = low bits, code b), words (hi pair, lo pair) of 8 c
   for (int i = threadIdx.x; i < M::NPT; i += 256) {
@@ -251,26 +258,26 @@ decode_mma_kernel(const DecodeArgs A) {
 #pragma unroll
   for (int nb = 0; nb < NNB; ++nb) acc[nb] = mma_f4_t{0.f, 0.f, 0.f, 0.f};
 
-  for (int t0 = tb + wave * kTile; t0 < te; t0 += 4 * kTile) {
-    const int nv = min(kTile, te - t0);
+  for (int t0 = tb + wave * TT; t0 < te; t0 += 4 * TT) {
+    const int nv = min(TT, te - t0);
     ld_k.store(st + M::OFF_SK, lane);
     ld_s.store(st + M::OFF_SS, lane);
     if constexpr (AFF) ld_ak.store_transposed(st + M::OFF_SAK, lane);
     else ld_ak.store(st + M::OFF_SAK, lane);
     ld_v.store_transposed(st + M::OFF_SV, lane);
     ld_av.store_transposed(st + M::OFF_SAV, lane);
-    if (t0 + 4 * kTile < te) issue(t0 + 4 * kTile);
+    if (t0 + 4 * TT < te) issue(t0 + 4 * TT);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
     // ---- scores: four 16-token blocks ------------------------------------------------------
     // p[mb][r]: head l16, token 16 mb + 4 q4 + r (log2-domain score, then its weight)
-    float p[4][4];
+    float p[MB][4];
     if constexpr (!AFF) {
-      mma_f4_t sacc[4];
+      mma_f4_t sacc[MB];
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) sacc[mb] = mma_f4_t{0.f, 0.f, 0.f, 0.f};
+      for (int mb = 0; mb < MB; ++mb) sacc[mb] = mma_f4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         const int kw = 16 * kb + 4 * q4;           // word offset of this lane's 8 dimensions
@@ -292,7 +299,7 @@ decode_mma_kernel(const DecodeArgs A) {
         // one 16-token block at a time: its operands, then its products (the accumulator
         // chains through the matrix unit; few registers stay live)
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
+        for (int mb = 0; mb < MB; ++mb) {
           const int tok = 16 * mb + l16;
           const uint32_t* row = stk + tok * M::SK;
           // the lane's 8 codes (dimensions 32 kb + 8 q4 ..) as the low 8 KB bits of y
@@ -331,7 +338,7 @@ decode_mma_kernel(const DecodeArgs A) {
       }
       // times n (fp16 with gamma for LM + QJL keys, fp32 for MSE-only keys) and the unscale
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
+      for (int mb = 0; mb < MB; ++mb) {
         const uint4 nw = *reinterpret_cast<const uint4*>(stak + 16 * mb + 4 * q4);
         const uint32_t nn[4] = {nw.x, nw.y, nw.z, nw.w};
 #pragma unroll
@@ -344,7 +351,7 @@ decode_mma_kernel(const DecodeArgs A) {
       // affine keys: per 32-dimension block, sum_j (c_j - 128) q_j on the matrix cores, then
       // a times it plus (m + 128 a) times the block's query sum
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
+      for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) p[mb][r] = 0.f;
 #pragma unroll
@@ -357,7 +364,7 @@ decode_mma_kernel(const DecodeArgs A) {
         const mma_u4_t bq0 = mma_u4_t{r0.x, r0.y, r0.z, r0.w};
         const mma_u4_t bq1 = mma_u4_t{r1.x, r1.y, r1.z, r1.w};
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
+        for (int mb = 0; mb < MB; ++mb) {
           const uint32_t* row = stk + (16 * mb + l16) * M::SK + 8 * kb + 2 * q4;
           const uint32_t w0 = row[0], w1 = row[1];
           // bytes c -> fp16 1024 + c (0x64 over the byte) -> c - 128, exact
@@ -379,20 +386,20 @@ decode_mma_kernel(const DecodeArgs A) {
         }
       }
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
+      for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) p[mb][r] *= 1.f / kMmaAffQScale;
     }
-    if (nv < kTile) {   // the last tile of a split: tokens past its end score -inf
+    if (nv < TT) {      // the last tile of a split: tokens past its end score -inf
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
+      for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           if (16 * mb + 4 * q4 + r >= nv) p[mb][r] = -INFINITY;
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) mx = fmaxf(mx, p[mb][r]);
     // ---- online softmax (log2 domain): head l16 spans lanes l16 + 16 q ------------------
@@ -404,7 +411,7 @@ decode_mma_kernel(const DecodeArgs A) {
     const float alpha = (mn == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - mn);
     float ps = 0.f;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
+    for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         p[mb][r] = __builtin_amdgcn_exp2f(p[mb][r] - mn);
@@ -435,7 +442,7 @@ decode_mma_kernel(const DecodeArgs A) {
       // also sum p m per group in fp32 (their offset term)
       constexpr uint32_t kOne = 0x3C003C00u;       // fp16 pair (1, 1)
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) {
+      for (int kb2 = 0; kb2 < TT / 32; ++kb2) {
         // k slot i of this lane: token 32 kb2 + 4 q4 + i (i < 4), 32 kb2 + 16 + 4 q4 + i - 4
         const int tk = 32 * kb2 + 4 * q4;
 #pragma unroll
@@ -490,7 +497,7 @@ decode_mma_kernel(const DecodeArgs A) {
     } else {
       // rotated Lloyd-Max values: P'' = p n (hi/lo) against 8 c (hi/lo) per 16 dimensions
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) {
+      for (int kb2 = 0; kb2 < TT / 32; ++kb2) {
         const int tk = 32 * kb2 + 4 * q4;            // k slots as for the group values
         mma_u4_t aph, apl;
         {
@@ -615,17 +622,17 @@ decode_mma_kernel(const DecodeArgs A) {
   }
 }
 
-template <int D, int NREP, int KK, int KB, int VK, int VB, int NQ>
+template <int D, int NREP, int KK, int KB, int VK, int VB, int NQ, int TT = kTile>
 hipError_t mma_launch(dim3 grid, hipStream_t st, const DecodeArgs& A) {
-  hipLaunchKernelGGL((decode_mma_kernel<D, NREP, KK, KB, VK, VB, NQ>), grid, dim3(256), 0, st, A);
+  hipLaunchKernelGGL((decode_mma_kernel<D, NREP, KK, KB, VK, VB, NQ, TT>), grid, dim3(256), 0, st, A);
   return hipGetLastError();
 }
 
-template <int D, int NREP, int KK, int KB, int VK, int VB, int NQ>
+template <int D, int NREP, int KK, int KB, int VK, int VB, int NQ, int TT = kTile>
 int mma_blocks_per_cu() {
   static const int n = [] {
     int b = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, decode_mma_kernel<D, NREP, KK, KB, VK, VB, NQ>, 256, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, decode_mma_kernel<D, NREP, KK, KB, VK, VB, NQ, TT>, 256, 0) !=
             hipSuccess ||
         b <= 0)
       b = 1;
@@ -641,10 +648,10 @@ constexpr MainKernel mma_kernel() {
                     &mma_blocks_per_cu<D, NREP, TQ_K_LM_QJL, KB, TQ_V_GROUP_SYM, VB, NQ>};
 }
 
-// any compiled key / value kind
-template <int D, int NREP, int KK, int KB, int VK, int VB>
+// any compiled key / value kind, TT tokens per wave tile
+template <int D, int NREP, int KK, int KB, int VK, int VB, int TT = kTile>
 constexpr MainKernel mma_kernel_kv() {
-  return MainKernel{&mma_launch<D, NREP, KK, KB, VK, VB, 1>, &mma_blocks_per_cu<D, NREP, KK, KB, VK, VB, 1>};
+  return MainKernel{&mma_launch<D, NREP, KK, KB, VK, VB, 1, TT>, &mma_blocks_per_cu<D, NREP, KK, KB, VK, VB, 1, TT>};
 }
 
 }  // namespace tq
