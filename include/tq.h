@@ -201,7 +201,10 @@ size_t tq_decode_workspace_bytes(const tq_layout* layout, int batch, int max_com
  *   n_recent   0..128, <= recent_capacity
  *   out        device float [batch][n_q_heads][head_dim]
  *   workspace  device, >= tq_decode_workspace_bytes(layout, batch, n_compressed)
- * Accumulation is float32.  Errors: TQ_ERR_INVALID when n_compressed + n_recent == 0,
+ * Accumulation is float32.  Where the query heads of a kv-head share a tile on the matrix
+ * cores, scores use fp16 hi/lo halves of the centroids (x8) and of the scaled queries, so
+ * every product is exact and only the dropped lo x lo term (~2^-22 relative) is lost; value
+ * weights are rounded once to fp16 as in the vector path.  Errors: TQ_ERR_INVALID when n_compressed + n_recent == 0,
  * n_recent > 128, a needed pointer is null/misaligned or the workspace is too small;
  * TQ_ERR_CAPACITY when n_compressed > cache->capacity; TQ_ERR_UNSUPPORTED; TQ_ERR_HIP. */
 int tq_decode_attn(const tq_layout* layout, const tq_state* state, const void* q,
