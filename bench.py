@@ -19,8 +19,9 @@ Prints one JSON line on stdout:
   roofline    the dominant kernel against its MI355X peak
   materialize tq_materialize of the whole history to fp16 rows (timed apart from the
               step: the dequantise path ahead of a dense prefill)
-  multi_query tq_decode_attn_multi with 4 queries (a speculative step) against 4
-              single-query decodes of the same cache (timed apart from the step)
+  multi_query tq_decode_attn_multi with 4 queries (2 where 4 x n_rep rows are not compiled;
+              a speculative step) against as many single-query decodes of the same cache
+              (timed apart from the step)
   cpu_baseline  the CPU oracle timed on a bounded sample of the same workload
 """
 from __future__ import annotations
@@ -149,10 +150,19 @@ def bench_materialize(tq, lay, state, caches, wl, stream, steps: int, warmup: in
     return res
 
 
-def bench_multi(tq, lay, state, caches, wl, stream, rk, rv, steps: int, warmup: int, n_query: int = 4) -> dict | None:
-    """tq_decode_attn_multi with n_query queries (a speculative step: the last n_query recent
-    tokens are the drafts' own) against n_query single-query decodes of the same cache, timed
-    apart from the step; None where the layout has no multi-query kernel."""
+def bench_multi(tq, lay, state, caches, wl, stream, rk, rv, steps: int, warmup: int) -> dict | None:
+    """tq_decode_attn_multi with 4 queries (a speculative step: the last n_query recent tokens
+    are the drafts' own; 2 where 4 x n_rep query rows exceed the compiled set) against
+    n_query single-query decodes of the same cache, timed apart from the step; None where the
+    layout has no multi-query kernel."""
+    for nq in (4, 2):
+        r = _bench_multi(tq, lay, state, caches, wl, stream, rk, rv, steps, warmup, nq)
+        if r is not None:
+            return r
+    return None
+
+
+def _bench_multi(tq, lay, state, caches, wl, stream, rk, rv, steps: int, warmup: int, n_query: int) -> dict | None:
     import torch
     B, n, R = wl.batch, wl.n_compressed, wl.n_recent
     if R < n_query:

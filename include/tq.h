@@ -230,9 +230,9 @@ size_t tq_decode_multi_workspace_bytes(const tq_layout* layout, int batch, int n
  *   n_recent   n_query..128, <= recent_capacity; recent_k/v as for tq_decode_attn
  *   workspace  device, >= tq_decode_multi_workspace_bytes(layout, batch, n_query, n_compressed)
  * Compiled for LM_QJL keys (3 or 4 bits) with GROUP_SYM values (2 or 4 bits), head_dim 64
- * and 128, n_rep 1, 2, 4 with n_query 2, 4, 8 and n_query * n_rep <= 16 (the query
- * rows share one 16-column matrix-core operand); other combinations with n_query > 1
- * return TQ_ERR_UNSUPPORTED.  Errors: TQ_ERR_INVALID when n_query is outside 1..8,
+ * and 128: n_query 2 with n_rep 1..8, n_query 4 with n_rep 1, 2, 4, n_query 8 with n_rep
+ * 1, 2 (n_query * n_rep <= 16: the query rows share one 16-column matrix-core operand);
+ * other combinations with n_query > 1 return TQ_ERR_UNSUPPORTED.  Errors: TQ_ERR_INVALID when n_query is outside 1..8,
  * n_recent < n_query or > 128, a needed pointer is null/misaligned or the workspace is
  * too small; TQ_ERR_CAPACITY; TQ_ERR_UNSUPPORTED; TQ_ERR_HIP. */
 int tq_decode_attn_multi(const tq_layout* layout, const tq_state* state, const void* q, int n_query,

@@ -177,6 +177,7 @@ def test_multi_query_decode_rejects_bad_arguments():
         (dict(q=FAKE + 4), tq.TQ_ERR_INVALID),
         (dict(nq=8), tq.TQ_ERR_UNSUPPORTED),             # 8 x 4 rows > 16
         (dict(nq=3), tq.TQ_ERR_UNSUPPORTED),
+        (dict(nq=4, L=_layout(head_dim=64, n_q_heads=6, n_kv_heads=2)), tq.TQ_ERR_UNSUPPORTED),   # 4 x 3 rows: not compiled
         (dict(L=_layout(head_dim=256, n_q_heads=4, n_kv_heads=2)), tq.TQ_ERR_UNSUPPORTED),
         (dict(L=_layout(head_dim=64, k_kind="affine8", k_bits=8, v_kind="lm_rot", v_bits=3)), tq.TQ_ERR_UNSUPPORTED),
     ]

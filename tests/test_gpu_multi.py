@@ -33,6 +33,8 @@ CASES = [
     ("qwen7b_h28x4_d128_b16_t32k", 2, 4, 357 + 128, 2),     # d 128, bf16 inputs, LM3 + sym2
     ("qwen32b_h40x8_d128_b4_t128k", 4, 2, 421, 2),          # d 128, LM4 + sym4, recent = own tokens only
     ("qwen32b_h40x8_d128_b4_t128k", 2, 8, 300, 1),
+    ("qwen7b_h28x4_d128_b16_t32k", None, 2, 357 + 128, 2),   # n_rep 7: 14 query rows
+    ("qwen32b_h40x8_d128_b4_t128k", None, 2, 300, 1),        # n_rep 5
 ]
 
 
