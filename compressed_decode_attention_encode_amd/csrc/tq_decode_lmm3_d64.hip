@@ -1,11 +1,26 @@
 // Compiled instantiations of the decode main kernel: MSE-only 3-bit Lloyd-Max keys (no QJL
 // term), head_dim 64, n_rep 1..8, group-32 symmetric 2/4-bit values and rotated Lloyd-Max
-// 2/3/4-bit values.
-#include "tq_decode_main.h"
+// 2/3/4-bit values (group values at n_rep 3..8 on the matrix cores).
+#include "tq_decode_mma.h"
 
 namespace tq {
 
 namespace {
+// group values at n_rep 3..8: the matrix-core kernel (codebook term only)
+template <int VB>
+MainKernel pick_mma(int nrep) {
+  constexpr int KK = TQ_K_LM_MSE, VK = TQ_V_GROUP_SYM;
+  switch (nrep) {
+    case 3: return mma_kernel_kv<64, 3, KK, 3, VK, VB>();
+    case 4: return mma_kernel_kv<64, 4, KK, 3, VK, VB>();
+    case 5: return mma_kernel_kv<64, 5, KK, 3, VK, VB>();
+    case 6: return mma_kernel_kv<64, 6, KK, 3, VK, VB>();
+    case 7: return mma_kernel_kv<64, 7, KK, 3, VK, VB>();
+    case 8: return mma_kernel_kv<64, 8, KK, 3, VK, VB>();
+    default: return MainKernel{nullptr, nullptr};
+  }
+}
+
 template <int KK, int KB, int VK, int VB>
 MainKernel pick(int nrep) {
   switch (nrep) {
@@ -23,8 +38,8 @@ MainKernel pick(int nrep) {
 }  // namespace
 
 MainKernel find_main_lmm3_d64(int nrep, int vk, int vb) {
-  if (vk == TQ_V_GROUP_SYM && vb == 2) return pick<TQ_K_LM_MSE, 3, TQ_V_GROUP_SYM, 2>(nrep);
-  if (vk == TQ_V_GROUP_SYM && vb == 4) return pick<TQ_K_LM_MSE, 3, TQ_V_GROUP_SYM, 4>(nrep);
+  if (vk == TQ_V_GROUP_SYM && vb == 2) return nrep >= 3 ? pick_mma<2>(nrep) : pick<TQ_K_LM_MSE, 3, TQ_V_GROUP_SYM, 2>(nrep);
+  if (vk == TQ_V_GROUP_SYM && vb == 4) return nrep >= 3 ? pick_mma<4>(nrep) : pick<TQ_K_LM_MSE, 3, TQ_V_GROUP_SYM, 4>(nrep);
   if (vk == TQ_V_LM_ROT && vb == 2) return pick<TQ_K_LM_MSE, 3, TQ_V_LM_ROT, 2>(nrep);
   if (vk == TQ_V_LM_ROT && vb == 3) return pick<TQ_K_LM_MSE, 3, TQ_V_LM_ROT, 3>(nrep);
   if (vk == TQ_V_LM_ROT && vb == 4) return pick<TQ_K_LM_MSE, 3, TQ_V_LM_ROT, 4>(nrep);

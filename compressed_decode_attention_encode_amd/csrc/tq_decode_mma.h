@@ -84,7 +84,9 @@ struct MmaGeom {
   using G = DecodeGeom<D, NREP, KK, KB, VK, VB>;
   static constexpr bool QJL = KK == TQ_K_LM_QJL;
   static constexpr bool AFF = KK == TQ_K_AFFINE8;
-  static constexpr int KPER = G::KPER, WK = G::WK, SK = G::SK;
+  static constexpr bool F16K = KK == TQ_K_F16;  // 16-bit keys, used as stored (fp16 storage only)
+  static constexpr int KPER = G::KPER, WK = G::WK;
+  static constexpr int SK = F16K ? WK + 4 : G::SK;   // 16-bit rows: 16-byte aligned row stride
   static constexpr int WS = G::WS, SS = G::SS;
   static constexpr int WAK = G::WAK;            // key aux words per token: (n, gamma) / fp32 n / (a, m) per block
   static constexpr int WV = G::WV, WAV = G::WAV;
@@ -100,12 +102,13 @@ struct MmaGeom {
   static constexpr int OFF_SV = OFF_SAK + (AFF ? WAK * TS : TT);
   static constexpr int OFF_SAV = OFF_SV + WV * TS;
   static constexpr int STAGE = OFF_SAV + WAV * TS;
-  static_assert(OFF_SAK % 4 == 0 && OFF_SV % 4 == 0 && OFF_SAV % 4 == 0 && STAGE % 4 == 0, "16-byte LDS reads");
+  static_assert(OFF_SS % 4 == 0 && OFF_SAK % 4 == 0 && OFF_SV % 4 == 0 && OFF_SAV % 4 == 0 && STAGE % 4 == 0,
+                "16-byte LDS reads");
   // group LDS (words): qa, qb as prepare_queries leaves them, the fp16 query operands
   // [4][NREP + 1][D] halves (q_hi, q_lo, qb_hi, qb_lo; row NREP is zero, the operand of
   // the columns beyond n_rep), the code-pair table, the sign table,
   // four staging areas, merge scalars
-  static constexpr int NPT = AFF ? 0 : 1 << (2 * KB);                  // key code pairs
+  static constexpr int NPT = (AFF || F16K) ? 0 : 1 << (2 * KB);       // key code pairs
   static constexpr int NVT = (VK == TQ_V_LM_ROT) ? 1 << (2 * VB) : 0;  // value code pairs
   static constexpr int OFF_BQ = (G::OFF_QB + NREP * D + 3) & ~3;
   static constexpr int NRB = NREP + 1;         // query operand rows: the heads, then a zero row
@@ -134,17 +137,17 @@ struct MmaGeom {
 // TT: tokens per wave tile (64; 32 at head_dim 256, where a 64-token tile's staging and
 // registers would leave one wave per SIMD).
 template <int D, int NREP_KV, int KK, int KB, int VK, int VB, int NQ = 1, int TT = kTile>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : (D == 256 ? 1 : 2))))
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((D == 64 && KK != TQ_K_F16) ? 3 : (D == 256 ? 1 : 2))))
 decode_mma_kernel(const DecodeArgs A) {
   constexpr int NREP = NQ * NREP_KV;
   using M = MmaGeom<D, NREP, KK, KB, VK, VB, TT>;
   constexpr int MB = TT / 16;                    // 16-token blocks per tile
   static_assert(TT == 64 || TT == 32, "tile of 32 or 64 tokens");
-  constexpr bool QJL = M::QJL, AFF = M::AFF, ROT = VK == TQ_V_LM_ROT, ASYM = VK == TQ_V_GROUP_ASYM;
+  constexpr bool QJL = M::QJL, AFF = M::AFF, F16K = M::F16K, ROT = VK == TQ_V_LM_ROT, ASYM = VK == TQ_V_GROUP_ASYM;
   constexpr int LK = 1 << KB;
   constexpr int LV = 1 << VB;
   constexpr int NKB = M::NKB, NNB = M::NNB, NG = M::NG;
-  static_assert(KK == TQ_K_LM_QJL || KK == TQ_K_LM_MSE || KK == TQ_K_AFFINE8, "key kind");
+  static_assert(KK == TQ_K_LM_QJL || KK == TQ_K_LM_MSE || KK == TQ_K_AFFINE8 || KK == TQ_K_F16, "key kind");
   static_assert(ROT ? (VB >= 2 && VB <= 4) : (VB == 2 || VB == 4), "value bits");
   static_assert(VK == TQ_V_GROUP_SYM || VK == TQ_V_GROUP_ASYM || VK == TQ_V_LM_ROT, "value kind");
 
@@ -220,7 +223,7 @@ decode_mma_kernel(const DecodeArgs A) {
     const float* qb = sm + M::G::OFF_QB;
     _Float16* bq = reinterpret_cast<_Float16*>(smw + M::OFF_BQ);
     constexpr int RS = M::NRB * D;               // halves per operand region
-    constexpr float QA = AFF ? kMmaAffQScale : kMmaQScale / kMmaCentScale;
+    constexpr float QA = (AFF || F16K) ? kMmaAffQScale : kMmaQScale / kMmaCentScale;
     for (int i = threadIdx.x; i < RS; i += 256) {
       const bool on = i < NREP * D;
       const float a = on ? qa[i] * QA : 0.f;
@@ -274,7 +277,34 @@ decode_mma_kernel(const DecodeArgs A) {
     // ---- scores: four 16-token blocks ------------------------------------------------------
     // p[mb][r]: head l16, token 16 mb + 4 q4 + r (log2-domain score, then its weight)
     float p[MB][4];
-    if constexpr (!AFF) {
+    if constexpr (F16K) {
+      // 16-bit keys (fp16 storage): the stored rows are the A operand as they are, against the
+      // hi/lo query operands (x16); every product exact
+      mma_f4_t sacc[MB];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) sacc[mb] = mma_f4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const int kw = 16 * kb + 4 * q4;
+        constexpr int RW = M::NRB * D / 2;
+        const uint32_t* src = bqw + hq * (D / 2) + kw;
+        const uint4 r0 = *reinterpret_cast<const uint4*>(src);
+        const uint4 r1 = *reinterpret_cast<const uint4*>(src + RW);
+        const mma_u4_t bq0 = mma_u4_t{r0.x, r0.y, r0.z, r0.w};
+        const mma_u4_t bq1 = mma_u4_t{r1.x, r1.y, r1.z, r1.w};
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const uint4 w = *reinterpret_cast<const uint4*>(stk + (16 * mb + l16) * M::SK + kw);
+          const mma_u4_t ak = mma_u4_t{w.x, w.y, w.z, w.w};
+          sacc[mb] = mma16(ak, bq0, sacc[mb]);
+          sacc[mb] = mma16(ak, bq1, sacc[mb]);
+        }
+      }
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) p[mb][r] = sacc[mb][r] * (1.f / kMmaAffQScale);
+    } else if constexpr (!AFF) {
       mma_f4_t sacc[MB];
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) sacc[mb] = mma_f4_t{0.f, 0.f, 0.f, 0.f};

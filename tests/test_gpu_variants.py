@@ -53,6 +53,8 @@ VARIANTS = [
     (64, "f16", 16, "group_sym", 4, 8, 1, "bf16", 250, 0),
     (128, "f16", 16, "lm_rot", 2, 14, 2, "bf16", 222, 40),
     (128, "f16", 16, "group_sym", 2, 2, 2, "f16", 180, 3),
+    (64, "f16", 16, "group_sym", 2, 12, 2, "f16", 230, 9),       # fp16 keys, n_rep 6: matrix cores
+    (64, "f16", 16, "lm_rot", 4, 10, 2, "f16", 190, 0),
     # group-32 min/max values (matrix cores at every n_rep)
     (64, "lm_qjl", 2, "group_asym", 2, 4, 2, "f16", 300, 17),
     (64, "lm_qjl", 3, "group_asym", 2, 2, 2, "f16", 200, 5),
