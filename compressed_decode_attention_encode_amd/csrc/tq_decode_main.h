@@ -83,15 +83,29 @@ struct DecodeGeom {
 // reads of the next tile (they stay in flight while the current tile is computed),
 // store() later writes them into the wave's LDS area with row stride LS.  Reads never
 // go past the last valid row; rows beyond it are zero-filled.
-template <int W, int LS, int TR = kTile>
+//
+// DW = true: one 4-byte read per register, the index clamped to the last valid word and the
+// value selected away past it -- no branch and no alignment case, so no load ever waits for an
+// earlier one (the two-path form makes the compiler wait on every load in flight where the
+// paths join, which serialises the prefetch behind the tile in flight).
+template <int W, int LS, int TR = kTile, bool DW = false>
 struct RowLoader {
   static constexpr int N = TR * W;                  // words per tile (TR rows)
   static constexpr int NV = (N + 4 * kWave - 1) / (4 * kWave);
-  static constexpr int NR = (W == 0) ? 1 : 4 * NV;  // registers per lane
+  static constexpr int NR = (W == 0) ? 1 : (DW ? (N + kWave - 1) / kWave : 4 * NV);  // registers per lane
   uint32_t r[NR];
   bool vec;
+  int nvalid_dw;                                    // DW: words past it are zero-filled at store
   __device__ __forceinline__ void load(const uint32_t* __restrict__ g, int rows, int lane) {
     if constexpr (W == 0) return;
+    if constexpr (DW) {
+      const int nvalid = rows * W;                  // >= 1: a tile has at least one row
+      vec = false;
+      nvalid_dw = nvalid;
+#pragma unroll
+      for (int i = 0; i < NR; ++i) r[i] = g[min(i * kWave + lane, nvalid - 1)];
+      return;
+    }
     const int nvalid = rows * W;
     vec = (reinterpret_cast<uintptr_t>(g) & 15) == 0;
     if (vec) {
@@ -119,6 +133,14 @@ struct RowLoader {
   // of consecutive rows is contiguous).
   __device__ __forceinline__ void store_transposed(uint32_t* __restrict__ lds, int lane) const {
     if constexpr (W == 0) return;
+    if constexpr (DW) {
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        const int q = i * kWave + lane;
+        if (q < N) lds[(q % W) * LS + (q / W)] = (q < nvalid_dw) ? r[i] : 0u;
+      }
+      return;
+    }
     if (vec) {
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
@@ -138,6 +160,14 @@ struct RowLoader {
   }
   __device__ __forceinline__ void store(uint32_t* __restrict__ lds, int lane) const {
     if constexpr (W == 0) return;
+    if constexpr (DW) {
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        const int q = i * kWave + lane;
+        if (q < N) lds[(q / W) * LS + (q % W)] = (q < nvalid_dw) ? r[i] : 0u;
+      }
+      return;
+    }
     if (vec) {
 #pragma unroll
       for (int i = 0; i < NV; ++i) {

@@ -179,11 +179,16 @@ decode_mma_kernel(const DecodeArgs A) {
   const uint32_t* stv = st + M::OFF_SV;
   const uint32_t* stav = st + M::OFF_SAV;
 
-  RowLoader<M::WK, M::SK, TT> ld_k;
-  RowLoader<M::WS, M::SS, TT> ld_s;
-  RowLoader<M::WAK, AFF ? M::TS : 1, TT> ld_ak;
-  RowLoader<M::WV, M::TS, TT> ld_v;
-  RowLoader<M::WAV, M::TS, TT> ld_av;
+  // Branch-free dword loads keep the next tile's loads in flight through the score and PV
+  // work (a vector/scalar split per chunk made the compiler wait for every outstanding load
+  // at its join).  The affine-key kernels are the exception: their extra per-lane state
+  // (block scales and offsets) plus the dword registers spill, so they keep the 16-byte path.
+  static constexpr bool DWL = !AFF;
+  RowLoader<M::WK, M::SK, TT, DWL> ld_k;
+  RowLoader<M::WS, M::SS, TT, DWL> ld_s;
+  RowLoader<M::WAK, AFF ? M::TS : 1, TT, DWL> ld_ak;
+  RowLoader<M::WV, M::TS, TT, DWL> ld_v;
+  RowLoader<M::WAV, M::TS, TT, DWL> ld_av;
   auto issue = [&](int t0) {
     const int nv = min(TT, te - t0);
     const size_t row0 = slice * cap + t0;
