@@ -137,7 +137,7 @@ struct MmaGeom {
 // TT: tokens per wave tile (64; 32 at head_dim 256, where a 64-token tile's staging and
 // registers would leave one wave per SIMD).
 template <int D, int NREP_KV, int KK, int KB, int VK, int VB, int NQ = 1, int TT = kTile>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((D == 64 && KK != TQ_K_F16) ? 3 : (D == 256 ? 1 : 2))))
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((D == 64 && KK != TQ_K_F16) ? 3 : ((D == 256 || (D == 128 && KK == TQ_K_AFFINE8 && VK == TQ_V_LM_ROT && VB == 4)) ? 1 : 2))))
 decode_mma_kernel(const DecodeArgs A) {
   constexpr int NREP = NQ * NREP_KV;
   using M = MmaGeom<D, NREP, KK, KB, VK, VB, TT>;
@@ -182,8 +182,10 @@ decode_mma_kernel(const DecodeArgs A) {
   // Branch-free dword loads keep the next tile's loads in flight through the score and PV
   // work (a vector/scalar split per chunk made the compiler wait for every outstanding load
   // at its join).  The affine-key kernels are the exception: their extra per-lane state
-  // (block scales and offsets) plus the dword registers spill, so they keep the 16-byte path.
-  static constexpr bool DWL = !AFF;
+  // (block scales and offsets) plus the dword registers spill at two waves per SIMD, so they
+  // keep the 16-byte path, except at head_dim 128 with 4-bit rotated values, which run one
+  // wave per SIMD (no spill; measured faster there, slower with 3-bit values).
+  static constexpr bool DWL = !AFF || (D == 128 && ROT && VB == 4);
   RowLoader<M::WK, M::SK, TT, DWL> ld_k;
   RowLoader<M::WS, M::SS, TT, DWL> ld_s;
   RowLoader<M::WAK, AFF ? M::TS : 1, TT, DWL> ld_ak;
