@@ -82,6 +82,21 @@ def algorithmic(wl):
             "encode_k_qjl_flops": qjl_flops, "vectors": rows}
 
 
+def decode_kernel_name(wl) -> str:
+    """The split kernel the library picks for this layout: the matrix-core kernel from 3 query
+    heads per kv-head (LM, MSE-only and affine keys; min/max values at every n_rep), for
+    fp16-stored 16-bit keys at head_dim 64 from 3 heads and at head_dim 256 always; otherwise
+    (bf16 16-bit keys, MSE-only keys with rotated values, n_rep 1-2) the vector-ALU kernel."""
+    n_rep = wl.n_q_heads // wl.n_kv_heads
+    if wl.k_kind == "f16":
+        mma = wl.in_dtype == "f16" and (wl.head_dim == 256 or (wl.head_dim == 64 and n_rep >= 3))
+    elif wl.k_kind == "lm_mse":
+        mma = wl.v_kind != "lm_rot" and (n_rep >= 3 or wl.v_kind == "group_asym")
+    else:
+        mma = n_rep >= 3 or wl.v_kind == "group_asym"
+    return "decode_mma_kernel" if mma else "decode_main_kernel"
+
+
 def read_traffic(workload: str, digest: str):
     """HBM bytes per launch of each kernel group (key encode, value encode, decode) from
     the committed counter summary, or {} when it is absent or was taken on different
@@ -392,7 +407,7 @@ def main():
         "encode_v": {"kernel": {"group_sym": "encode_group_kernel", "group_asym": "encode_affine8_kernel (min/max values)",
                                 "lm_rot": "encode_lm_kernel (values)"}[wl.v_kind],
                      "ms": t_ev},
-        "decode": {"kernel": "decode_main_kernel + decode_finish_kernel", "ms": t_dec},
+        "decode": {"kernel": decode_kernel_name(wl) + " + decode_finish_kernel", "ms": t_dec},
     }
     rl = {}
     # key encode: the QJL contraction runs on the fp16 matrix cores (fp16 S times the fp16
