@@ -103,7 +103,11 @@ struct RowLoader {
       vec = false;
       nvalid_dw = nvalid;
 #pragma unroll
-      for (int i = 0; i < NR; ++i) r[i] = g[min(i * kWave + lane, nvalid - 1)];
+      for (int i = 0; i < NR; ++i) {
+        // a 32-bit unsigned byte offset from a wave-uniform base: one VGPR per address
+        const uint32_t off = 4u * (uint32_t)min(i * kWave + lane, nvalid - 1);
+        r[i] = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(g) + off);
+      }
       return;
     }
     const int nvalid = rows * W;

@@ -154,7 +154,7 @@ decode_mma_kernel(const DecodeArgs A) {
   __shared__ __attribute__((aligned(16))) float sm[M::FLOATS];
   uint32_t* smw = reinterpret_cast<uint32_t*>(sm);
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: scalar tile bases
   const int l16 = lane & 15, q4 = lane >> 4;
 
   // grid: the compressed splits first, then one recent-buffer group per (batch, kv-head)
