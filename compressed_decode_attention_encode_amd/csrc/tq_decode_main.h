@@ -88,6 +88,9 @@ struct DecodeGeom {
 // value selected away past it -- no branch and no alignment case, so no load ever waits for an
 // earlier one (the two-path form makes the compiler wait on every load in flight where the
 // paths join, which serialises the prefetch behind the tile in flight).
+// Fourth word of a raw buffer resource on CDNA (gfx9 family): 32-bit data format, no swizzle.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+
 template <int W, int LS, int TR = kTile, bool DW = false>
 struct RowLoader {
   static constexpr int N = TR * W;                  // words per tile (TR rows)
@@ -95,19 +98,18 @@ struct RowLoader {
   static constexpr int NR = (W == 0) ? 1 : (DW ? (N + kWave - 1) / kWave : 4 * NV);  // registers per lane
   uint32_t r[NR];
   bool vec;
-  int nvalid_dw;                                    // DW: words past it are zero-filled at store
   __device__ __forceinline__ void load(const uint32_t* __restrict__ g, int rows, int lane) {
     if constexpr (W == 0) return;
     if constexpr (DW) {
       const int nvalid = rows * W;                  // >= 1: a tile has at least one row
       vec = false;
-      nvalid_dw = nvalid;
+      // Raw buffer loads over exactly the tile's words: the base and range live in scalar
+      // registers, each lane supplies a 32-bit byte offset, and words past the range read as
+      // zero (the hardware's range check), so no clamp and no select.
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(g), (short)0, 4 * nvalid, kBufferRsrcWord3);
 #pragma unroll
-      for (int i = 0; i < NR; ++i) {
-        // a 32-bit unsigned byte offset from a wave-uniform base: one VGPR per address
-        const uint32_t off = 4u * (uint32_t)min(i * kWave + lane, nvalid - 1);
-        r[i] = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(g) + off);
-      }
+      for (int i = 0; i < NR; ++i) r[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * (i * kWave + lane), 0, 0);
       return;
     }
     const int nvalid = rows * W;
@@ -141,7 +143,7 @@ struct RowLoader {
 #pragma unroll
       for (int i = 0; i < NR; ++i) {
         const int q = i * kWave + lane;
-        if (q < N) lds[(q % W) * LS + (q / W)] = (q < nvalid_dw) ? r[i] : 0u;
+        if (q < N) lds[(q % W) * LS + (q / W)] = r[i];   // past the tile's words: zero
       }
       return;
     }
@@ -168,7 +170,7 @@ struct RowLoader {
 #pragma unroll
       for (int i = 0; i < NR; ++i) {
         const int q = i * kWave + lane;
-        if (q < N) lds[(q / W) * LS + (q % W)] = (q < nvalid_dw) ? r[i] : 0u;
+        if (q < N) lds[(q / W) * LS + (q % W)] = r[i];   // past the tile's words: zero
       }
       return;
     }
