@@ -181,11 +181,9 @@ decode_mma_kernel(const DecodeArgs A) {
 
   // Branch-free dword loads keep the next tile's loads in flight through the score and PV
   // work (a vector/scalar split per chunk made the compiler wait for every outstanding load
-  // at its join).  The affine-key kernels are the exception: their extra per-lane state
-  // (block scales and offsets) plus the dword registers spill at two waves per SIMD, so they
-  // keep the 16-byte path, except at head_dim 128 with 4-bit rotated values, which run one
-  // wave per SIMD (no spill; measured faster there, slower with 3-bit values).
-  static constexpr bool DWL = !AFF || (D == 128 && ROT && VB == 4);
+  // at its join); as raw buffer loads they also cost no per-lane address arithmetic, which
+  // leaves the affine-key kernels room to hold them without a spill.
+  static constexpr bool DWL = true;
   RowLoader<M::WK, M::SK, TT, DWL> ld_k;
   RowLoader<M::WS, M::SS, TT, DWL> ld_s;
   RowLoader<M::WAK, AFF ? M::TS : 1, TT, DWL> ld_ak;
