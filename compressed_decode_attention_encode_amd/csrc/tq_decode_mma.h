@@ -137,7 +137,7 @@ struct MmaGeom {
 // TT: tokens per wave tile (64; 32 at head_dim 256, where a 64-token tile's staging and
 // registers would leave one wave per SIMD).
 template <int D, int NREP_KV, int KK, int KB, int VK, int VB, int NQ = 1, int TT = kTile>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((D == 64 && KK != TQ_K_F16) ? 3 : ((D == 256 || (D == 128 && KK == TQ_K_AFFINE8 && VK == TQ_V_LM_ROT && VB == 4)) ? 1 : 2))))
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((D == 64 && KK != TQ_K_F16) ? 3 : (D == 256 ? 1 : 2))))
 decode_mma_kernel(const DecodeArgs A) {
   constexpr int NREP = NQ * NREP_KV;
   using M = MmaGeom<D, NREP, KK, KB, VK, VB, TT>;
