@@ -28,9 +28,8 @@ Readings where the pages are silent (each also listed in the design notes):
     gamma) are kept as fp16, rounded to nearest-even; the rotated-LM value norm is fp32;
   * LM decision: idx_j = #{i : t_i < y_j} with float32 thresholds t_i (ties go low);
   * the QJL projection acts on the rotated-domain residual r = y - c[idx];
-    S is d x d i.i.d. N(0,1), held at fp16 resolution (any S passed in is used exactly
-    as given); stored bit = (z_j >= 0), z = S r.  The sign is decided in float32,
-    z = S . fl32(r) accumulated in float32 -- the kernel's precision;
+    S is d x d i.i.d. N(0,1) (any S passed in is used exactly as given); stored
+    bit = (z_j >= 0), z = S r, with z evaluated in float64 on the float64 residual;
   * group scale Delta = fp16(2 amax / (L-1)), idx = clamp(rne(v/Delta + (L-1)/2), 0, L-1)
     with the stored Delta; Delta = 0 gives idx = L-1, 0, L/2 for v > 0, v < 0, v = 0;
   * affine scale a = fp16((max-min)/255), offset m = fp16(min), q = clamp(rne((k-m)/a), 0, 255);
@@ -87,10 +86,9 @@ def encode_k_lm_qjl(k: np.ndarray, signs: np.ndarray, S: np.ndarray,
     # step 3: residual and its sign sketch
     r = y - centroids32.astype(np.float64)[idx]
     gamma = np.sqrt(np.sum(r * r, axis=-1))
-    z32 = r.astype(np.float32) @ np.asarray(S, dtype=np.float32).T   # float32 decision
-    z64 = r @ np.asarray(S, dtype=np.float64).T                      # exact reference, for the band only
-    bits = z32 >= 0
-    near_qjl = (np.abs(z64) < BAND) | (np.abs(z32) < BAND)
+    z = r @ np.asarray(S, dtype=np.float64).T
+    bits = z >= 0
+    near_qjl = np.abs(z) < BAND
     # a vector with a near-threshold LM index may legitimately differ in its residual,
     # so all of its sign bits are excluded too
     near_qjl |= np.any(near_lm, axis=-1, keepdims=True)
@@ -98,7 +96,7 @@ def encode_k_lm_qjl(k: np.ndarray, signs: np.ndarray, S: np.ndarray,
         "idx": idx, "qjl": bits,
         "n16": n.astype(np.float16), "g16": gamma.astype(np.float16),
         "near_idx": near_lm, "near_qjl": near_qjl,
-        "y": y, "z": z64,
+        "y": y, "z": z,
     }
 
 

@@ -257,6 +257,40 @@ def test_qjl_sign_identity_and_unbiased_score():
     assert abs(lm_only.mean() - shrink * truth) < 4.5 * se0 + 1e-3 * truth
 
 
+@pytest.mark.parametrize("s_dtype", ["float64", "float16"])
+@pytest.mark.parametrize("bits", [2, 3])
+def test_qjl_unbiased_through_the_stored_planes(bits, s_dtype):
+    """The whole LM+QJL chain as it is stored -- encode, pack into the k_codes / k_signs /
+    k_aux planes, read back the fp16 n and gamma and the sign bits, score -- is an unbiased
+    estimate of <q, k>/sqrt(d) over independent (Pi, S) draws (vLLM guide section 2, steps
+    2-3: the residual's sign sketch makes the expected inner-product estimate equal to the
+    true one).  A norm, residual norm or sign stored wrongly (gamma^2, the residual's norm
+    before the codebook subtraction, an inverted bit) biases the mean by several standard
+    errors.  With S rounded to fp16 the estimate stays unbiased: only S's distribution
+    enters the expectation, and every rounded row is still a symmetric random direction."""
+    d = 64
+    lay = Lay(d, 1, 1, "lm_qjl", bits, "group_sym", 2)
+    rng = np.random.default_rng(100 + bits)
+    k = rng.standard_normal(d)
+    q = 0.8 * k + 0.6 * rng.standard_normal(d)
+    truth = float(q @ k) / math.sqrt(d)
+    c32, t32 = cb.codebook_f32(d, bits)
+    M = 4096
+    got, lm_only = np.empty(M), np.empty(M)
+    for m in range(M):
+        s = np.where(rng.integers(0, 2, d) == 1, -1, 1).astype(np.int8)
+        S = rng.standard_normal((d, d)).astype(s_dtype)
+        st = {"signs_k": s, "S": S, "cb_k": (c32, t32)}
+        planes = C.encode_k(lay, k[None], st)
+        kd = C.read_k(lay, {n: planes[n] for n in ("k_codes", "k_signs", "k_aux")}, st)
+        got[m] = D._scores_compressed(lay, q, kd, st)[0]
+        lm_only[m] = D._scores_compressed(lay, q, dict(kd, gamma=np.zeros(1)), st)[0]
+    se = got.std() / math.sqrt(M)
+    assert abs(got.mean() - truth) < 4.5 * se, (got.mean(), truth, se)
+    # the correction is not vacuous: without it the same stored codes are biased
+    assert truth - lm_only.mean() > 8 * se
+
+
 def test_mse_only_keys_score_is_the_shrunk_inner_product():
     """MSE-only keys (no QJL residual): over independent rotations the score of the whole
     oracle chain (encode, pack, read back, score) averages (1 - d D) <q, k>/sqrt(d), D the
