@@ -47,7 +47,7 @@ TQ_V_GROUP_SYM, TQ_V_LM_ROT, TQ_V_GROUP_ASYM = 0, 1, 2
 
 EXPORTED = ("tq_make_codebook", "tq_make_rotation", "tq_cache_plane_bytes", "tq_encode",
             "tq_decode_workspace_bytes", "tq_decode_attn", "tq_decode_multi_workspace_bytes", "tq_decode_attn_multi",
-            "tq_materialize", "tq_strerror", "tq_last_error")
+            "tq_materialize", "tq_strerror", "tq_last_error", "tq_probe_stream_read")
 
 
 class tq_layout(ctypes.Structure):
@@ -85,6 +85,7 @@ _lib.tq_decode_attn_multi.argtypes = [ctypes.POINTER(tq_layout), ctypes.POINTER(
                                       ctypes.c_size_t, _P]
 _lib.tq_materialize.argtypes = [ctypes.POINTER(tq_layout), ctypes.POINTER(tq_state), ctypes.POINTER(tq_cache),
                                 ctypes.c_int, ctypes.c_int, _P, _P, ctypes.c_int, _P]
+_lib.tq_probe_stream_read.argtypes = [_P, ctypes.c_size_t, _P, _P]
 _lib.tq_strerror.argtypes = [ctypes.c_int]
 _lib.tq_strerror.restype = ctypes.c_char_p
 _lib.tq_last_error.argtypes = []
@@ -189,6 +190,13 @@ def tq_materialize(layout: tq_layout, state: tq_state, cache: tq_cache, t0: int,
                    out_dtype: int = TQ_F16, stream=None) -> None:
     _check(_lib.tq_materialize(ctypes.byref(layout), ctypes.byref(state), ctypes.byref(cache), t0, n_tokens,
                                _ptr(out_k), _ptr(out_v), out_dtype, _stream(stream)))
+
+
+def tq_probe_stream_read(src, nbytes: int, sink, stream=None) -> None:
+    """Measurement helper (include/tq_probe.h): one streaming read of `nbytes` device bytes."""
+    rc = _lib.tq_probe_stream_read(_ptr(src), nbytes, _ptr(sink), _stream(stream))
+    if rc != TQ_OK:
+        raise TQError(rc, "tq_probe_stream_read failed")
 
 
 # ---------------------------------------------------------------------------- marshalling helpers

@@ -17,7 +17,9 @@ tq = pytest.importorskip("compressed_decode_attention_encode_amd.tq",
 
 
 def declared_symbols():
-    text = open(os.path.join(ROOT, "include", "tq.h")).read()
+    """Every entry point declared in include/*.h."""
+    inc = os.path.join(ROOT, "include")
+    text = "".join(open(os.path.join(inc, f)).read() for f in sorted(os.listdir(inc)) if f.endswith(".h"))
     return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(tq_\w+)\s*\(", text, re.M)))
 
 
