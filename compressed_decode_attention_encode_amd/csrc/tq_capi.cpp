@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "tq_internal.h"
@@ -132,6 +133,34 @@ int check_state(const tq_state* S, const tq_layout* L, bool need_k, bool need_v)
     if (!aligned4(S->v_centroids) || !aligned4(S->v_thresholds) || !aligned4(S->v_signs))
       return fail(TQ_ERR_INVALID, "state arrays must be 4-byte aligned");
   }
+  return TQ_OK;
+}
+
+// Every host check of a single-query decode except the workspace; fills the split plan.
+int check_decode(const tq_layout* L, const tq_state* S, const void* q, const tq_cache* C, int n_compressed,
+                 const void* recent_k, const void* recent_v, int n_recent, int recent_capacity, float* out,
+                 DecodePlan* plan) {
+  int rc = check_layout(L);
+  if (rc) return rc;
+  if (!q || !out) return fail(TQ_ERR_INVALID, "q and out must be non-NULL");
+  if (!aligned16(q) || !aligned16(out)) return fail(TQ_ERR_INVALID, "q and out must be 16-byte aligned");
+  if (n_compressed < 0 || n_recent < 0) return fail(TQ_ERR_INVALID, "negative token count");
+  if (n_recent > kMaxRecent) return fail(TQ_ERR_INVALID, "n_recent %d > %d", n_recent, kMaxRecent);
+  if (n_compressed + n_recent == 0) return fail(TQ_ERR_INVALID, "nothing to attend to (no compressed and no recent tokens)");
+  if (n_recent > 0) {
+    if (!recent_k || !recent_v) return fail(TQ_ERR_INVALID, "recent_k/recent_v are NULL with n_recent %d", n_recent);
+    if (!aligned16(recent_k) || !aligned16(recent_v)) return fail(TQ_ERR_INVALID, "recent buffers must be 16-byte aligned");
+    if (recent_capacity < n_recent) return fail(TQ_ERR_INVALID, "recent_capacity %d < n_recent %d", recent_capacity, n_recent);
+  }
+  if ((rc = check_cache(C, n_compressed > 0, n_compressed > 0, L))) return rc;
+  if ((rc = check_state(S, L, true, true))) return rc;
+  if (L->k_kind == TQ_K_LM_QJL && (!S->k_signs || !S->qjl)) return fail(TQ_ERR_INVALID, "k_signs and qjl are needed");
+  if (n_compressed > C->capacity)
+    return fail(TQ_ERR_CAPACITY, "n_compressed %d > capacity %d", n_compressed, C->capacity);
+  if (!decode_compiled(*L))
+    return fail(TQ_ERR_UNSUPPORTED, "no decode kernel compiled for head_dim %d, n_rep %d, key/value kinds %d/%d bits %d/%d",
+                L->head_dim, L->n_q_heads / L->n_kv_heads, L->k_kind, L->k_bits, L->v_kind, L->v_bits);
+  *plan = plan_decode(*L, C->batch, n_compressed);
   return TQ_OK;
 }
 
@@ -401,32 +430,76 @@ size_t tq_decode_workspace_bytes(const tq_layout* L, int batch, int max_compress
 int tq_decode_attn(const tq_layout* L, const tq_state* S, const void* q, const tq_cache* C, int n_compressed,
                    const void* recent_k, const void* recent_v, int n_recent, int recent_capacity, float* out,
                    void* workspace, size_t workspace_bytes, void* stream) {
-  int rc = check_layout(L);
+  if (!workspace) return fail(TQ_ERR_INVALID, "workspace must be non-NULL");
+  if (!aligned16(workspace)) return fail(TQ_ERR_INVALID, "workspace must be 16-byte aligned");
+  DecodePlan plan{};
+  int rc = check_decode(L, S, q, C, n_compressed, recent_k, recent_v, n_recent, recent_capacity, out, &plan);
   if (rc) return rc;
-  if (!q || !out || !workspace) return fail(TQ_ERR_INVALID, "q, out and workspace must be non-NULL");
-  if (!aligned16(q) || !aligned16(out) || !aligned16(workspace))
-    return fail(TQ_ERR_INVALID, "q, out and workspace must be 16-byte aligned");
-  if (n_compressed < 0 || n_recent < 0) return fail(TQ_ERR_INVALID, "negative token count");
-  if (n_recent > kMaxRecent) return fail(TQ_ERR_INVALID, "n_recent %d > %d", n_recent, kMaxRecent);
-  if (n_compressed + n_recent == 0) return fail(TQ_ERR_INVALID, "nothing to attend to (no compressed and no recent tokens)");
-  if (n_recent > 0) {
-    if (!recent_k || !recent_v) return fail(TQ_ERR_INVALID, "recent_k/recent_v are NULL with n_recent %d", n_recent);
-    if (!aligned16(recent_k) || !aligned16(recent_v)) return fail(TQ_ERR_INVALID, "recent buffers must be 16-byte aligned");
-    if (recent_capacity < n_recent) return fail(TQ_ERR_INVALID, "recent_capacity %d < n_recent %d", recent_capacity, n_recent);
-  }
-  if ((rc = check_cache(C, n_compressed > 0, n_compressed > 0, L))) return rc;
-  if ((rc = check_state(S, L, true, true))) return rc;
-  if (L->k_kind == TQ_K_LM_QJL && (!S->k_signs || !S->qjl)) return fail(TQ_ERR_INVALID, "k_signs and qjl are needed");
-  if (n_compressed > C->capacity)
-    return fail(TQ_ERR_CAPACITY, "n_compressed %d > capacity %d", n_compressed, C->capacity);
-  if (!decode_compiled(*L))
-    return fail(TQ_ERR_UNSUPPORTED, "no decode kernel compiled for head_dim %d, n_rep %d, key/value kinds %d/%d bits %d/%d",
-                L->head_dim, L->n_q_heads / L->n_kv_heads, L->k_kind, L->k_bits, L->v_kind, L->v_bits);
-  const DecodePlan plan = plan_decode(*L, C->batch, n_compressed);
   if (workspace_bytes < plan.ws_bytes)
     return fail(TQ_ERR_INVALID, "workspace %zu bytes < %zu needed", workspace_bytes, plan.ws_bytes);
   hipError_t e = launch_decode(*L, *S, q, *C, n_compressed, recent_k, recent_v, n_recent,
                                n_recent > 0 ? recent_capacity : 1, out, workspace, plan, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(TQ_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+  return TQ_OK;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------------------
+// Decode without a caller workspace: the split partials live in a fixed device array of
+// this library (one copy per GPU, held until the process ends).  The host never touches the
+// array through its name: the device address comes from hipGetSymbolAddress, once per
+// device, with that device current.  The partials are written in full before the merge
+// reads them, so nothing has to be cleared between calls; calls that overlap on one GPU
+// share the array and race.
+// ---------------------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kScratchBytes = size_t(16) << 20;
+constexpr int kMaxDevices = 64;
+
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this GPU's scratch array (looked up on the first call on the device).
+int scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(TQ_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(TQ_ERR_UNSUPPORTED, "device index %d >= %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(TQ_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return TQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t tq_decode_noalloc_max_scratch_bytes(void) { return kScratchBytes; }
+
+int tq_decode_attn_noalloc(const tq_layout* L, const tq_state* S, const void* q, const tq_cache* C, int n_compressed,
+                           const void* recent_k, const void* recent_v, int n_recent, int recent_capacity, float* out,
+                           void* stream) {
+  DecodePlan plan{};
+  int rc = check_decode(L, S, q, C, n_compressed, recent_k, recent_v, n_recent, recent_capacity, out, &plan);
+  if (rc) return rc;
+  if (plan.ws_bytes > kScratchBytes)
+    return fail(TQ_ERR_CAPACITY, "this decode needs %zu bytes of split partials, above the %zu-byte static scratch of "
+                "tq_decode_attn_noalloc (use tq_decode_attn with a workspace)", plan.ws_bytes, kScratchBytes);
+  void* ws = nullptr;
+  if ((rc = scratch_of_current_device(&ws))) return rc;
+  hipError_t e = launch_decode(*L, *S, q, *C, n_compressed, recent_k, recent_v, n_recent,
+                               n_recent > 0 ? recent_capacity : 1, out, ws, plan, (hipStream_t)stream);
   if (e != hipSuccess) return fail(TQ_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
   return TQ_OK;
 }

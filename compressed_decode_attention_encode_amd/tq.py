@@ -47,7 +47,8 @@ TQ_V_GROUP_SYM, TQ_V_LM_ROT, TQ_V_GROUP_ASYM = 0, 1, 2
 
 EXPORTED = ("tq_make_codebook", "tq_make_rotation", "tq_cache_plane_bytes", "tq_encode",
             "tq_decode_workspace_bytes", "tq_decode_attn", "tq_decode_multi_workspace_bytes", "tq_decode_attn_multi",
-            "tq_materialize", "tq_strerror", "tq_last_error", "tq_probe_stream_read")
+            "tq_materialize", "tq_strerror", "tq_last_error", "tq_probe_stream_read", "tq_decode_attn_noalloc",
+            "tq_decode_noalloc_max_scratch_bytes")
 
 
 class tq_layout(ctypes.Structure):
@@ -86,6 +87,11 @@ _lib.tq_decode_attn_multi.argtypes = [ctypes.POINTER(tq_layout), ctypes.POINTER(
 _lib.tq_materialize.argtypes = [ctypes.POINTER(tq_layout), ctypes.POINTER(tq_state), ctypes.POINTER(tq_cache),
                                 ctypes.c_int, ctypes.c_int, _P, _P, ctypes.c_int, _P]
 _lib.tq_probe_stream_read.argtypes = [_P, ctypes.c_size_t, _P, _P]
+_lib.tq_decode_attn_noalloc.argtypes = [ctypes.POINTER(tq_layout), ctypes.POINTER(tq_state), _P,
+                                        ctypes.POINTER(tq_cache), ctypes.c_int, _P, _P, ctypes.c_int, ctypes.c_int, _P,
+                                        _P]
+_lib.tq_decode_noalloc_max_scratch_bytes.argtypes = []
+_lib.tq_decode_noalloc_max_scratch_bytes.restype = ctypes.c_size_t
 _lib.tq_strerror.argtypes = [ctypes.c_int]
 _lib.tq_strerror.restype = ctypes.c_char_p
 _lib.tq_last_error.argtypes = []
@@ -172,6 +178,17 @@ def tq_decode_attn(layout: tq_layout, state: tq_state, q, cache: tq_cache, n_com
     _check(_lib.tq_decode_attn(ctypes.byref(layout), ctypes.byref(state), _ptr(q), ctypes.byref(cache), n_compressed,
                                _ptr(recent_k), _ptr(recent_v), n_recent, recent_capacity, _ptr(out), _ptr(workspace),
                                workspace_bytes, _stream(stream)))
+
+
+def tq_decode_attn_noalloc(layout: tq_layout, state: tq_state, q, cache: tq_cache, n_compressed: int, recent_k,
+                           recent_v, n_recent: int, recent_capacity: int, out, stream=None) -> None:
+    _check(_lib.tq_decode_attn_noalloc(ctypes.byref(layout), ctypes.byref(state), _ptr(q), ctypes.byref(cache),
+                                       n_compressed, _ptr(recent_k), _ptr(recent_v), n_recent, recent_capacity,
+                                       _ptr(out), _stream(stream)))
+
+
+def tq_decode_noalloc_max_scratch_bytes() -> int:
+    return int(_lib.tq_decode_noalloc_max_scratch_bytes())
 
 
 def tq_decode_multi_workspace_bytes(layout: tq_layout, batch: int, n_query: int, max_compressed: int) -> int:

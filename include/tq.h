@@ -22,7 +22,8 @@
  * Conventions for every entry point:
  *   - Pointers marked "device" are HIP device memory; "host" pointers are CPU memory.
  *     The caller owns all memory.  The library allocates nothing and keeps no state
- *     between calls; it is reentrant.
+ *     between calls; it is reentrant.  The one exception is tq_decode_attn_noalloc,
+ *     whose split partials live in a static device array of the library (one per GPU).
  *   - `stream` is a hipStream_t (NULL = the default stream).  tq_encode,
  *     tq_decode_attn and tq_materialize validate their arguments on the host, then
  *     enqueue kernels on `stream` and return without synchronising.
@@ -211,6 +212,25 @@ int tq_decode_attn(const tq_layout* layout, const tq_state* state, const void* q
                    const tq_cache* cache, int n_compressed,
                    const void* recent_k, const void* recent_v, int n_recent, int recent_capacity,
                    float* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Single-query decode without a caller workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  Same arguments, results and errors as tq_decode_attn minus the
+ * workspace: the split partials live in a static device array of the library, 16 MiB
+ * (tq_decode_noalloc_max_scratch_bytes()), one per GPU the library runs on, held until
+ * the process ends.  A decode whose partials need more (tq_decode_workspace_bytes above
+ * the maximum) fails with TQ_ERR_CAPACITY before any launch.  The call allocates nothing;
+ * its first call on a device looks up that device's copy of the array.  The array keeps
+ * the last call's contents; nothing in it needs clearing (every partial is written before
+ * it is read).  Calls that overlap on one GPU share the array and race: serialise them
+ * (one stream, or events) per device.                                                    */
+int tq_decode_attn_noalloc(const tq_layout* layout, const tq_state* state, const void* q,
+                           const tq_cache* cache, int n_compressed,
+                           const void* recent_k, const void* recent_v, int n_recent, int recent_capacity,
+                           float* out, void* stream);
+
+/* Size of tq_decode_attn_noalloc's static scratch array in bytes. */
+size_t tq_decode_noalloc_max_scratch_bytes(void);
 
 /* Workspace bytes tq_decode_attn_multi needs for n_query queries and any
  * n_compressed <= max_compressed (0 for an invalid layout or n_query outside 1..8). */
