@@ -1,28 +1,27 @@
 // TurboQuant encode kernels for gfx950.
 //
-// Rotated Lloyd-Max encode (keys with the QJL sketch; rotated-LM values):
+// Rotated Lloyd-Max encode (keys with the QJL sketch; rotated-LM values; MSE-only keys):
 //   TurboQuant vLLM guide (kwkr.cn), section 2, steps 1-3 and 5; TurboQuant-MLX page
 //   (pomoai.com), core technique items 1-3.
 // Group-32 symmetric values: TurboQuant vLLM guide, section 2, step 4.
 // Per-block affine 8-bit keys: vllm-metal TurboQuant guide (wmrh.cn), quantisation
 //   principle table (per-block scale, no rotation).
 //
-// Work decomposition (rotated-LM kernel): a persistent work-group walks 64-token tiles
-// of the (batch, kv-head) slices, prefetching the next tile's inputs into registers while
-// it computes the current one.  Each vector is handled by P = d/32 consecutive lanes,
-// each holding 32 coordinates: the first five butterfly stages of the Walsh-Hadamard
-// transform stay inside a lane, the remaining log2(P) stages go across lanes with DPP
-// exchanges.  Keys rotate in float64, so n, gamma and every decision match a float64
-// evaluation; values rotate in float32 (only their decisions depend on it, and those
-// move only within a float32 ulp of a threshold) with a float64 norm.  Codes are packed
-// in registers and stored straight from the lanes.
-// The QJL projection Z = R S^T (64 x d times d x d) is a dense contraction and runs on
-// the fp16 matrix cores (v_mfma_f32_32x32x16_f16): S is stored at fp16 resolution, the
-// float32 residual is split into fp16 hi + lo halves, and Z accumulates S*hi + S*lo in
-// float32 -- every product exact, the residual carried to ~21 significant bits -- at two
-// fp16 MFMAs instead of sixteen float32 ones per k-block of 16.  Each of the d/32 waves
-// keeps its 32 rows of S in VGPRs for the whole kernel and reads the residual tile from
-// LDS; each lane packs the sign bits of its accumulators.
+// Rotated Lloyd-Max encode, work decomposition: every wave of a persistent work-group walks
+// 32-token blocks of the (batch, kv-head) slices on its own.  The rotation y = H diag(s) x
+// runs on the matrix cores: with H_d = H_{d/32} (x) H_32 (Sylvester order, high index bits
+// outer), each 32-feature input block goes through one 32 x 32 Hadamard product
+// (v_mfma_f32_32x32x16_{f16,bf16}; the +-1 entries, with the rotation's sign flips folded
+// in, and the fp16/bf16 inputs are exact operands, so only the float32 sums round), and the
+// H_{d/32} stage combines the blocks' outputs inside each lane.  The Hadamard rows are fed
+// in a permuted order so that lane l ends up holding the 16 contiguous coordinates
+// 32 b + 16 (l / 32) + r (r = 0..15) of token l % 32 for every block b: the Lloyd-Max
+// decision, the code packing and the residual all work on contiguous coordinates.
+// The QJL projection z = S r (keys) is a second matrix-core product: the residual, split
+// into fp16 hi + lo halves (every product with the fp16 S exact, ~21 significant bits
+// carried), is already in the B-operand layout in the lanes' registers, and S is read from
+// LDS as the A operand in the matching order, with its rows permuted like H's so that each
+// lane's accumulators are 16 contiguous projection outputs (16 sign bits).
 #include <type_traits>
 
 #include "tq_internal.h"
@@ -31,18 +30,20 @@
 namespace tq {
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------------------------
 // Rotated Lloyd-Max encode.  QJL = true: keys (codes + QJL signs + fp16 (n, gamma));
-// QJL = false: rotated values (codes + fp32 n).
+// QJL = false: rotated values or MSE-only keys (codes + fp32 n).
 // ---------------------------------------------------------------------------------
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 
 // Keys work on y, thresholds and centroids scaled by 2^12 (exact): the residual then
-// enters the fp16 split as |r| 2^12 < 4096, where the low half of nearly every coordinate
+// enters the fp16 split as |r| 2^12 < 8192, where the low half of nearly every coordinate
 // stays a normal fp16 number; decisions are unchanged, the projection's sign needs no
-// rescaling and gamma = sqrt(sum r'^2) 2^-12 exactly.
-constexpr double kKeyScale = 4096.0;
+// rescaling and gamma = sqrt(sum r'^2) 2^-12.
+constexpr float kKeyScale = 4096.f;
 
 // Number of positive thresholds p_0 < p_1 < ... below |y| (binary search over the L/2
 // magnitude cells of the symmetric codebook).
@@ -55,297 +56,374 @@ __device__ __forceinline__ uint32_t magnitude_cell(float ay, const float (&p)[(1
     const uint32_t c2 = ay > (c1 ? p[2] : p[0]) ? 1u : 0u;
     return 2u * c1 + c2;
   } else {
-    const uint32_t c1 = ay > p[3] ? 1u : 0u;
-    const uint32_t c2 = ay > (c1 ? p[5] : p[1]) ? 1u : 0u;
-    const float t3 = c1 ? (c2 ? p[6] : p[4]) : (c2 ? p[2] : p[0]);
+    // selects written as bit masks, so that the search stays branch-free
+    auto pick = [](uint32_t m, float a, float b) { return __uint_as_float((__float_as_uint(a) & m) | (__float_as_uint(b) & ~m)); };
+    const uint32_t m1 = ay > p[3] ? ~0u : 0u;
+    const uint32_t m2 = ay > pick(m1, p[5], p[1]) ? ~0u : 0u;
+    const float t3 = pick(m2, pick(m1, p[6], p[2]), pick(m1, p[4], p[0]));
     const uint32_t c3 = ay > t3 ? 1u : 0u;
-    return 4u * c1 + 2u * c2 + c3;
+    return (m1 & 4u) | (m2 & 2u) | c3;
   }
 }
 
-// Coordinates per lane (a vector spans d / coordinates lanes).  32: five butterfly stages
-// inside a lane and a 64-VGPR float64 rotation state.  (16 per lane fits a third wave per
-// SIMD but adds a cross-lane stage; measured no faster at d = 64 and slower at d = 128.)
+// Row of H_32 (or of S within a 32-row block) fed to matrix row m: the accumulator of
+// register r in lane l (matrix row 8 (r / 4) + 4 (l / 32) + r % 4) then holds output
+// 16 (l / 32) + r.
+__host__ __device__ constexpr int rot_row(int m) { return 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3); }
+
+// 32 x 32 x 16 matrix-core product with 16-bit operands of the input type.
+template <int DT>
+__device__ __forceinline__ floatx16 mfma_in(uint4 a, uint4 b, floatx16 c) {
+  if constexpr (DT == TQ_F16) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, a), __builtin_bit_cast(half8, b), c, 0, 0,
+                                                  0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                   0, 0);
+  }
+}
+
+__device__ __forceinline__ floatx16 mfma_f16(uint4 a, uint4 b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, a), __builtin_bit_cast(half8, b), c, 0, 0, 0);
+}
+
+// c + lo^2 + hi^2 of a pair of 16-bit inputs (exact products, float32 sum).
+template <int DT>
+__device__ __forceinline__ float sq2(uint32_t x, float c) {
+  if constexpr (DT == TQ_F16) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, x), __builtin_bit_cast(f16x2_t, x), c, false);
+  } else {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, x), __builtin_bit_cast(bf16x2_t, x), c, false);
+  }
+}
+
+// Values of lanes l and l ^ 32 for every lane: .lo = the lane-half-0 value (lanes 0..31),
+// .hi = the lane-half-1 value (lanes 32..63), in both halves (one permlane32 swap).
+struct HalfPair {
+  uint32_t lo, hi;
+};
+__device__ __forceinline__ HalfPair half_pair(uint32_t v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return {(uint32_t)p[0], (uint32_t)p[1]};
+}
+
+// Waves per work-group, and waves per SIMD the registers are budgeted for: keys at d = 256
+// hold 128 residual registers through the projection and their S fills most of a CU's LDS,
+// so they run one wave per SIMD (one group per CU) without spilling.
 template <int D>
-constexpr int lm_coords() { return 32; }
+constexpr int rot_waves() { return 4; }
+template <int D, bool QJL>
+constexpr int rot_waves_per_simd() { return D <= 64 ? (QJL ? 3 : 4) : ((D >= 256 && QJL) ? 1 : 2); }
 
 template <int D, int KB, int DT, bool QJL>
-__global__ void __launch_bounds__(64 * D / lm_coords<D>()) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1)))
-encode_lm_kernel(const uint16_t* __restrict__ x, int T, int tiles_per_slice, int n_tiles,
-                 int dst_offset, int cap,
+__global__ void __launch_bounds__(64 * rot_waves<D>()) __attribute__((amdgpu_waves_per_eu(rot_waves_per_simd<D, QJL>())))
+encode_lm_kernel(const uint16_t* __restrict__ x, int T, int mb_per_slice, int n_mb, int dst_offset, int cap,
                  const float* __restrict__ cent, const float* __restrict__ thr,
                  const uint32_t* __restrict__ sign_mask, const uint16_t* __restrict__ S,
                  uint32_t* __restrict__ codes_out, uint32_t* __restrict__ signs_out,
                  uint32_t* __restrict__ aux_out) {
-  // keys: float64 rotation and residual, so n, gamma and every decision agree with a
-  // float64 evaluation; values: float32 rotation (only the decisions depend on it) and a
-  // float64 norm
-  using W = typename std::conditional<QJL, double, float>::type;
-  constexpr int C = lm_coords<D>();        // coordinates per lane
-  constexpr int P = D / C;                 // lanes per vector (= waves per group)
-  constexpr int NT = 64 * P;               // threads: one 64-token tile
+  constexpr int NB = D / 32;                       // 32-feature blocks
+  constexpr int NK = D / 16;                       // 16-feature input operand blocks
+  constexpr int NW = rot_waves<D>();
   constexpr int L = 1 << KB;
   constexpr int PER = (KB == 3) ? 10 : 32 / KB;   // codes per word
   constexpr int WK = (D + PER - 1) / PER;          // words per row
-  constexpr int SW = D / 32;                       // sign words per row (= MFMA n-blocks)
-  constexpr int RH = D + 8;                        // LDS row stride of the residual halves
-  constexpr int NKB = D / 16;                      // MFMA k-blocks
-  constexpr int LW = C * KB / 32;                  // whole stream words of a lane's codes
-  constexpr int LSH = (C * KB) % 32;               // bits of a partial last stream word
-  constexpr int MPW = 2 * SW / P;                  // projection m-blocks per wave
-  static_assert(P >= 2 && P <= 16 && NT <= 1024, "lane split");
-  static_assert(MPW == 1 || MPW == 2, "each wave takes one n-block and one or both m-blocks");
+  constexpr int CW = (16 * KB + 31) / 32;          // words of a lane's 16-code chunk
+  constexpr int SP = D + 8;                        // LDS row stride of S (halves)
+  constexpr bool kPrefetch = D <= 128 || QJL;       // next block's inputs held in registers
+  constexpr float kPre = QJL ? kKeyScale : 1.f;
+  static_assert(NB >= 2 && NB <= 8, "head_dim 64..256");
 
-  __shared__ double s_cent[16];
-  __shared__ __attribute__((aligned(16))) uint32_t s_xm[P * (C / 2)];
-  __shared__ __attribute__((aligned(16))) _Float16 s_rhi[QJL ? kTile * RH : 8];
-  __shared__ __attribute__((aligned(16))) _Float16 s_rlo[QJL ? kTile * RH : 8];
+  __shared__ uint4 s_h[NB * 2 * kWave];            // rotation A operands, per (block, k-half, lane)
+  __shared__ float s_cent[16];
+  __shared__ __attribute__((aligned(16))) uint16_t s_S[QJL ? D * SP : 8];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int vec = tid / P;     // vector within the tile
-  const int part = tid % P;    // which C coordinates
+  const int h = lane >> 5;                         // lane half
+  const int col = lane & 31;                       // token within the 32-token block
 
-  constexpr double kPre = QJL ? kKeyScale : 1.0;
-  if (tid < L) s_cent[tid] = (double)cent[tid] * kPre;
-  if (tid < P * (C / 2)) {
-    // sign flips as xor masks on pairs of packed 16-bit inputs: coordinate C p + 2 i at
-    // bit 15, C p + 2 i + 1 at bit 31
-    const int pp = tid / (C / 2), i = tid % (C / 2);
-    const int j = C * pp + 2 * i;
-    const uint32_t sm = sign_mask[j >> 5] >> (j & 31);
-    s_xm[tid] = ((sm & 1u) << 15) | (((sm >> 1) & 1u) << 31);
+  // A operands of the rotation: lane l, k-half kb of block b holds
+  // H_32[rot_row(l % 32)][16 kb + 8 (l / 32) + i] * s[32 b + 16 kb + 8 (l / 32) + i], i = 0..7
+  for (int e = tid; e < NB * 2 * kWave; e += kWave * NW) {
+    const int l = e & 63, kb = (e >> 6) & 1, b = e >> 7;
+    const int row = rot_row(l & 31);
+    const uint32_t one = (DT == TQ_F16) ? 0x3C00u : 0x3F80u;
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint32_t pair = 0u;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int c = 16 * kb + 8 * (l >> 5) + 2 * q + u;
+        const int j = 32 * b + c;
+        const uint32_t neg = (uint32_t)(__popc(row & c) & 1) ^ ((sign_mask[j >> 5] >> (j & 31)) & 1u);
+        pair |= (one | (neg << 15)) << (16 * u);
+      }
+      w[q] = pair;
+    }
+    s_h[e] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  if (tid < L) s_cent[tid] = cent[tid] * kPre;
+  if constexpr (QJL) {
+    for (int e = tid; e < D * D / 8; e += kWave * NW) {
+      const int r = e / (D / 8), c8 = e % (D / 8);
+      *reinterpret_cast<uint4*>(&s_S[r * SP + 8 * c8]) = reinterpret_cast<const uint4*>(S)[e];
+    }
   }
   // symmetric codebook: t[L/2-1] = 0 and t[L/2-1+i] = -t[L/2-1-i]; only the positive
   // thresholds are compared, against |y|
   float thp[L / 2 - 1];
 #pragma unroll
-  for (int i = 0; i < L / 2 - 1; ++i) thp[i] = thr[L / 2 + i] * (float)kPre;
-
-  // QJL: wave w computes projection outputs 32 nb .. 32 nb + 31 (nb = w % SW) for the
-  // 32-token m-blocks mb0 .. mb0 + MPW - 1 (mb0 = w / SW).  Its rows of S, fp16, as MFMA A
-  // operands: lane l holds S[32 nb + l % 32][16 kb + 8 (l / 32) + i], i = 0..7.
-  const int nb = wave % SW, mb0 = wave / SW;
-  half8 sop[QJL ? NKB : 1];
-  if constexpr (QJL) {
-    const uint16_t* srow = S + (size_t)(32 * nb + (lane & 31)) * D + 8 * (lane >> 5);
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) sop[kb] = __builtin_bit_cast(half8, *reinterpret_cast<const uint4*>(srow + 16 * kb));
-  }
-
-  // 3-bit codes: word kw holds codes 10 kw .. 10 kw + 9, so words straddle the lanes'
-  // C-code ranges.  A lane writes the words that start in its range, kw0 .. kw1, taking
-  // the first bits of the next lane's stream where a word runs past its own.
-  const int kw0 = (C * part + PER - 1) / PER;
-  const int kw1 = min((C * part + C - 1) / PER, WK - 1);
-  const int b0 = KB * (PER * kw0 - C * part);     // bit offset of word kw0 in the lane's stream
-
-  auto load_tile = [&](int tile, uint4 (&raw)[C / 8]) {
-    const int slice = tile / tiles_per_slice;
-    const int t0 = (tile % tiles_per_slice) * kTile;
-    if (tile < n_tiles && vec < min(kTile, T - t0)) {
-      const uint4* src = reinterpret_cast<const uint4*>(x + ((size_t)slice * T + t0 + vec) * D + C * part);
-#pragma unroll
-      for (int i = 0; i < C / 8; ++i) raw[i] = src[i];
-    } else {
-#pragma unroll
-      for (int i = 0; i < C / 8; ++i) raw[i] = make_uint4(0u, 0u, 0u, 0u);
-    }
-  };
-
-  uint4 raw[C / 8];
-  load_tile(blockIdx.x, raw);
+  for (int i = 0; i < L / 2 - 1; ++i) thp[i] = thr[L / 2 + i] * kPre;
   __syncthreads();
 
-  for (int tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
-    const int slice = tile / tiles_per_slice;
-    const int t0 = (tile % tiles_per_slice) * kTile;
-    const int nv = min(kTile, T - t0);
-    const bool valid = vec < nv;
-    const size_t row0 = (size_t)slice * cap + dst_offset + t0;
+  // this lane's S row offset (QJL A operands): row rot_row(col) of each 32-row block,
+  // columns 16 h + 8 j of each 32-feature block
+  const int s_base = rot_row(col) * SP + 16 * h;
 
-    uint32_t w[C / 2];
-    {
-      const uint32_t* rw = reinterpret_cast<const uint32_t*>(raw);
-      const uint4* xm4 = reinterpret_cast<const uint4*>(&s_xm[part * (C / 2)]);
+  // input operands: xr[k] = features 16 k + 8 h .. + 7 of token col (B layout)
+  auto load = [&](int mb, uint4 (&dst)[NK]) {
+    const int slice = mb / mb_per_slice;
+    const int t = min((mb % mb_per_slice) * 32 + col, T - 1);     // rows past T repeat the last one
+    const uint4* src = reinterpret_cast<const uint4*>(x + ((size_t)slice * T + t) * D + 8 * h);
 #pragma unroll
-      for (int i = 0; i < C / 8; ++i) {
-        const uint4 m = xm4[i];
-        w[4 * i] = rw[4 * i] ^ m.x;
-        w[4 * i + 1] = rw[4 * i + 1] ^ m.y;
-        w[4 * i + 2] = rw[4 * i + 2] ^ m.z;
-        w[4 * i + 3] = rw[4 * i + 3] ^ m.w;
-      }
-    }
-    // the next tile's inputs stay in flight while this one is computed
-    load_tile(tile + gridDim.x, raw);
+    for (int k = 0; k < NK; ++k) dst[k] = src[2 * k];
+  };
 
-    // ---- phase A: sign flip, norm (float64), Walsh-Hadamard ----------------------------
-    W xv[C];
-    double ss = 0.0;
-#pragma unroll
-    for (int i = 0; i < C / 2; ++i) {
-      const float a = in_to_f32<DT>(w[i] & 0xFFFFu);
-      const float b = in_to_f32<DT>(w[i] >> 16);
-      ss = fma((double)a, (double)a, ss);
-      ss = fma((double)b, (double)b, ss);
-      xv[2 * i] = (W)a;
-      xv[2 * i + 1] = (W)b;
-    }
-#pragma unroll
-    for (int h = 1; h < C; h <<= 1) {
-#pragma unroll
-      for (int e = 0; e < C; ++e) {
-        if ((e & h) == 0) {
-          const W a = xv[e], b = xv[e + h];
-          xv[e] = a + b;
-          xv[e + h] = a - b;
-        }
-      }
-    }
-    // butterflies across the P lanes of the vector (stride C m <-> lane xor m): the upper
-    // lane of each pair keeps partner - own, the lower own + partner
-#define TQ_XSTAGE(M)                                              \
-    if constexpr (P > M) {                                        \
-      const W sg = (part & M) ? W(-1) : W(1);                     \
-      _Pragma("unroll") for (int e = 0; e < C; ++e) {             \
-        const W o = xor_lanes<M>(xv[e]);                          \
-        xv[e] = fma(xv[e], sg, o);                                \
-      }                                                           \
-    }
-    TQ_XSTAGE(1)
-    TQ_XSTAGE(2)
-    TQ_XSTAGE(4)
-    TQ_XSTAGE(8)
-#undef TQ_XSTAGE
-    ss = group_sum_dpp<P>(ss);
-    const double n = sqrt(ss);
-    const double scale64 = (n > 0.0) ? kPre / (sqrt((double)D) * n) : 0.0;
-    const W scale = (W)scale64;
+  const int first = blockIdx.x * NW + wave;
+  const int stride = gridDim.x * NW;
+  uint4 xr[NK];
+  if (first < n_mb) load(first, xr);
 
-    // ---- Lloyd-Max decision, packed codes, residual -----------------------------------
-    uint32_t cw[LW + 1];                // the lane's C codes as a KB-bit stream
+  for (int mb = first; mb < n_mb; mb += stride) {
+    const int slice = mb / mb_per_slice;
+    const int t0 = (mb % mb_per_slice) * 32;
+    const bool valid = col < T - t0;
+    const size_t row = (size_t)slice * cap + dst_offset + t0 + col;
+
+    if constexpr (!kPrefetch) load(mb, xr);
+
+    // ---- norm of the input ---------------------------------------------------------
+    // keys: float32 sums of exact squares (n stored as fp16); values / MSE keys: float64,
+    // so the stored float32 n is the correctly rounded norm
+    float n;
+    double ss64 = 0.0;
+    float ss32 = 0.f;
 #pragma unroll
-    for (int i = 0; i <= LW; ++i) cw[i] = 0u;
-    double gg = 0.0;
-    // eight coordinates at a time (keeps the centroid reads and residuals of one chunk
-    // in registers); keys write each chunk's residual halves to LDS:
-    // hi = fp16(r) and lo = fp16(r - hi), both rounded toward zero -- the pair carries 21+
-    // significant bits and every product of halves is exact in float32
+    for (int k = 0; k < NK; ++k) {
+      const uint32_t w4[4] = {xr[k].x, xr[k].y, xr[k].z, xr[k].w};
 #pragma unroll
-    for (int c = 0; c < C / 8; ++c) {
-      float rf[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int e = 8 * c + k;
-        const W y = xv[e] * scale;
-        // idx = #{i : t_i < y} = L/2 + cnt for y > 0 and L/2 - 1 - cnt otherwise, with cnt
-        // the number of positive thresholds below |y| (L/2 + cnt = cnt ^ L/2 and
-        // L/2 - 1 - cnt = cnt ^ (L/2 - 1) for cnt < L/2); float32 |y| changes a decision
-        // only where y lies within one float32 ulp of a threshold
-        const float yf = (float)y;
-        const uint32_t cnt = magnitude_cell<KB>(fabsf(yf), thp);
-        const uint32_t idx = cnt ^ ((yf > 0.f) ? (uint32_t)(L / 2) : (uint32_t)(L / 2 - 1));
-        const int bit = KB * e;
-        cw[bit >> 5] |= idx << (bit & 31);
-        if ((bit & 31) + KB > 32) cw[(bit >> 5) + 1] |= idx >> (32 - (bit & 31));
+      for (int q = 0; q < 4; ++q) {
         if constexpr (QJL) {
-          const double r = (double)y - s_cent[idx];
-          gg = fma(r, r, gg);
-          rf[k] = (float)r;
-        }
-      }
-      if constexpr (QJL) {
-        uint32_t hw[4], lw[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const auto h = __builtin_amdgcn_cvt_pkrtz(rf[2 * q], rf[2 * q + 1]);
-          const auto l = __builtin_amdgcn_cvt_pkrtz(rf[2 * q] - (float)h[0], rf[2 * q + 1] - (float)h[1]);
-          hw[q] = __builtin_bit_cast(uint32_t, h);
-          lw[q] = __builtin_bit_cast(uint32_t, l);
-        }
-        *reinterpret_cast<uint4*>(&s_rhi[vec * RH + C * part + 8 * c]) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-        *reinterpret_cast<uint4*>(&s_rlo[vec * RH + C * part + 8 * c]) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if constexpr (KB != 3) {
-      // whole words: 16 / 8 codes per word, C codes per lane
-      if (valid) {
-        uint32_t* crow = codes_out + (row0 + vec) * WK + LW * part;
-        if constexpr (LW == 1) {
-          crow[0] = cw[0];
-        } else if constexpr (LW == 2) {
-          *reinterpret_cast<uint2*>(crow) = make_uint2(cw[0], cw[1]);
+          ss32 = sq2<DT>(w4[q], ss32);
         } else {
-          *reinterpret_cast<uint4*>(crow) = make_uint4(cw[0], cw[1], cw[2], cw[3]);
+          const double a = (double)in_to_f32<DT>(w4[q] & 0xFFFFu), b = (double)in_to_f32<DT>(w4[q] >> 16);
+          ss64 = fma(a, a, ss64);
+          ss64 = fma(b, b, ss64);
         }
+      }
+    }
+
+    // bf16 inputs span the float32 exponent range: a float32 sum of squares can underflow
+    // (|x| below ~1e-19, down to the subnormals) and the rotated sums can overflow (|x|
+    // above ~1e37).  Such a token (rare; never a zero vector) is rescaled by a power of two --
+    // exact for every input, and the codes depend only on the direction -- before the
+    // rotation; its norm is divided back.  fp16 inputs never need it.
+    float inv_s = 1.f;
+    if constexpr (DT == TQ_BF16) {
+      bool odd;
+      if constexpr (QJL) {
+        const HalfPair p = half_pair(__float_as_uint(ss32));
+        const float tot = __uint_as_float(p.lo) + __uint_as_float(p.hi);
+        odd = !(tot >= 0x1p-100f && tot <= 0x1p100f);
+      } else {
+        const uint64_t u = (uint64_t)__double_as_longlong(ss64);
+        const HalfPair plo = half_pair((uint32_t)u), phi = half_pair((uint32_t)(u >> 32));
+        const double tot = __longlong_as_double((long long)(((uint64_t)phi.lo << 32) | plo.lo)) +
+                           __longlong_as_double((long long)(((uint64_t)phi.hi << 32) | plo.hi));
+        odd = !(tot >= 0x1p-100 && tot <= 0x1p100);
+      }
+      if (__builtin_amdgcn_ballot_w64(odd) != 0) {
+        float amax = 0.f;
+#pragma unroll
+        for (int k = 0; k < NK; ++k) {
+          const uint32_t w4[4] = {xr[k].x, xr[k].y, xr[k].z, xr[k].w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            amax = fmaxf(amax, fmaxf(fabsf(in_to_f32<DT>(w4[q] & 0xFFFFu)), fabsf(in_to_f32<DT>(w4[q] >> 16))));
+        }
+        const HalfPair pm = half_pair(__float_as_uint(amax));
+        amax = fmaxf(__uint_as_float(pm.lo), __uint_as_float(pm.hi));
+        const bool need = odd && amax > 0.f;
+        int e = 0;
+        (void)frexpf(need ? amax : 1.f, &e);
+        const int k2 = need ? 1 - e : 0;            // scaled maximum in [2, 4)
+        inv_s = ldexpf(1.f, -k2);                   // may be subnormal: the stored fp16 n rounds to 0 then
+        if constexpr (QJL) ss32 = 0.f;
+#pragma unroll
+        for (int k = 0; k < NK; ++k) {
+          uint32_t w4[4] = {xr[k].x, xr[k].y, xr[k].z, xr[k].w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float a = ldexpf(in_to_f32<DT>(w4[q] & 0xFFFFu), k2);
+            const float b = ldexpf(in_to_f32<DT>(w4[q] >> 16), k2);
+            w4[q] = (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xFFFF0000u);   // exact in bf16
+            if constexpr (QJL) ss32 = sq2<DT>(w4[q], ss32);
+          }
+          xr[k] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+        }
+      }
+    }
+
+    // ---- rotation: one Hadamard product per 32-feature block, then H_{d/32} in-lane ----
+    floatx16 y[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      y[b] = floatx16{};
+      y[b] = mfma_in<DT>(s_h[(2 * b) * kWave + lane], xr[2 * b], y[b]);
+      y[b] = mfma_in<DT>(s_h[(2 * b + 1) * kWave + lane], xr[2 * b + 1], y[b]);
+      if constexpr (D >= 256) __builtin_amdgcn_sched_barrier(0);   // two A operands live at a time
+    }
+    if constexpr (kPrefetch) {
+      if (mb + stride < n_mb) load(mb + stride, xr);     // in flight through the rest of the block
+    }
+#pragma unroll
+    for (int s = 1; s < NB; s <<= 1) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        if ((b & s) == 0) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float a = y[b][r], c = y[b + s][r];
+            y[b][r] = a + c;
+            y[b + s][r] = a - c;
+          }
+        }
+      }
+    }
+    float scale;
+    if constexpr (QJL) {
+      const HalfPair p = half_pair(__float_as_uint(ss32));
+      const float ns = sqrtf(__uint_as_float(p.lo) + __uint_as_float(p.hi));   // norm of the (rescaled) input
+      n = ns * inv_s;
+      scale = (ns > 0.f) ? kPre / (sqrtf((float)D) * ns) : 0.f;
+    } else {
+      const uint64_t u = (uint64_t)__double_as_longlong(ss64);
+      const HalfPair plo = half_pair((uint32_t)u), phi = half_pair((uint32_t)(u >> 32));
+      const double n64 = sqrt(__longlong_as_double((long long)(((uint64_t)phi.lo << 32) | plo.lo)) +
+                              __longlong_as_double((long long)(((uint64_t)phi.hi << 32) | plo.hi)));
+      n = (float)n64;
+      scale = (n64 > 0.0) ? (float)(1.0 / (sqrt((double)D) * n64 / (double)inv_s)) : 0.f;
+    }
+
+    // ---- Lloyd-Max decision, packed codes, residual --------------------------------
+    uint32_t cw[NB][CW];
+    uint32_t rh[QJL ? NB : 1][8], rl[QJL ? NB : 1][8];
+    float gg = 0.f;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+#pragma unroll
+      for (int i = 0; i < CW; ++i) cw[b][i] = 0u;
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        float rr[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          // idx = #{i : t_i < y} = L/2 + cnt for y > 0 and L/2 - 1 - cnt otherwise, with cnt
+          // the number of positive thresholds below |y| (L/2 + cnt = cnt ^ L/2 and
+          // L/2 - 1 - cnt = cnt ^ (L/2 - 1) for cnt < L/2); the float32 y differs from the
+          // exact one by ~1e-7, so a decision can change only next to a threshold
+          const float ys = y[b][r + u] * scale;
+          const uint32_t cnt = magnitude_cell<KB>(fabsf(ys), thp);
+          const uint32_t idx = cnt ^ ((ys > 0.f) ? (uint32_t)(L / 2) : (uint32_t)(L / 2 - 1));
+          const int bit = KB * (r + u);
+          cw[b][bit >> 5] |= idx << (bit & 31);
+          if ((bit & 31) + KB > 32) cw[b][(bit >> 5) + 1] |= idx >> (32 - (bit & 31));
+          if constexpr (QJL) {
+            rr[u] = ys - s_cent[idx];
+            gg = fmaf(rr[u], rr[u], gg);
+          }
+        }
+        if constexpr (QJL) {
+          // hi = fp16(r) and lo = fp16(r - hi), both rounded toward zero
+          const auto hi = __builtin_amdgcn_cvt_pkrtz(rr[0], rr[1]);
+          const auto lo = __builtin_amdgcn_cvt_pkrtz(rr[0] - (float)hi[0], rr[1] - (float)hi[1]);
+          rh[b][r / 2] = __builtin_bit_cast(uint32_t, hi);
+          rl[b][r / 2] = __builtin_bit_cast(uint32_t, lo);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);     // block b's rotated values die here
+    }
+
+    // ---- store the codes: a lane holds codes 32 b + 16 h .. + 15 of its token ----------
+    if constexpr (KB == 2) {
+      if (valid) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) codes_out[row * WK + 2 * b + h] = cw[b][0];
+      }
+    } else if constexpr (KB == 4) {
+      if (valid) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          *reinterpret_cast<uint2*>(codes_out + row * WK + 4 * b + 2 * h) = make_uint2(cw[b][0], cw[b][1]);
       }
     } else {
-      // the lane's stream is C * 3 bits; append the next lane's first word behind it (the
-      // last lane of a vector appends zeros), then word kw0 + j starts at bit b0 + 30 j
-      const uint32_t nx0 = next_lane_u32(cw[0]);
-      const uint32_t nx = (part == P - 1) ? 0u : nx0;
-      constexpr int NS = LW + (LSH ? 2 : 1);
+      // 3-bit codes, ten per word: both lane halves assemble the token's whole 3d-bit
+      // stream (block b: the half-0 lane's 48 bits, then the half-1 lane's), then word w =
+      // bits 30 w .. 30 w + 29; the half-0 lane stores the even words, the half-1 lane the odd
+      constexpr int NS = 3 * NB;
       uint32_t st[NS + 1];
 #pragma unroll
-      for (int i = 0; i < LW; ++i) st[i] = cw[i];
-      if constexpr (LSH) {
-        st[LW] = cw[LW] | (nx << LSH);
-        st[LW + 1] = nx >> (32 - LSH);
-      } else {
-        st[LW] = nx;
+      for (int b = 0; b < NB; ++b) {
+        const HalfPair a = half_pair(cw[b][0]);   // low 32 bits of each half's chunk
+        const HalfPair c = half_pair(cw[b][1]);   // high 16 bits
+        st[3 * b] = a.lo;
+        st[3 * b + 1] = (c.lo & 0xFFFFu) | (a.hi << 16);
+        st[3 * b + 2] = (a.hi >> 16) | (c.hi << 16);
       }
       st[NS] = 0u;
-      constexpr int NJ = (C + PER - 1) / PER + 1;   // most words starting in a lane's range
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        // bit bb of the stream lies in stream word j (j = 0 always) or j - 1
-        const int bb = b0 + 30 * j;
-        const bool up = j == 0 || (bb >> 5) == j;
-        const uint32_t lo = up ? st[j < NS ? j : NS] : st[j - 1];
-        const uint32_t hi = up ? st[j + 1 <= NS ? j + 1 : NS] : st[j < NS ? j : NS];
-        const uint32_t word = __builtin_amdgcn_alignbit(hi, lo, (uint32_t)(bb & 31)) & 0x3FFFFFFFu;
-        if (valid && kw0 + j <= kw1) codes_out[(row0 + vec) * WK + kw0 + j] = word;
+      for (int w = 0; w < WK; ++w) {
+        const int bb = 30 * w;
+        const uint32_t word = __builtin_amdgcn_alignbit(st[(bb >> 5) + 1], st[bb >> 5], (uint32_t)(bb & 31)) & 0x3FFFFFFFu;
+        if (valid && (w & 1) == h) codes_out[row * WK + w] = word;
       }
-    }
-    if constexpr (QJL) {
-      gg = group_sum_dpp<P>(gg);
-      if (valid && part == 0)
-        aux_out[row0 + vec] = f64_to_f16_rne(n) | (f64_to_f16_rne(sqrt(gg) * (1.0 / kKeyScale)) << 16);
-    } else {
-      if (valid && part == 0) aux_out[row0 + vec] = __float_as_uint((float)n);
     }
 
-    // ---- phase B: QJL projection on the matrix cores, sign bits packed per lane --------
-    // Z^T = S R^T for the wave's 32 outputs x 32 tokens: A = rows of S, B = residual rows.
     if constexpr (QJL) {
-      __syncthreads();
+      const HalfPair p = half_pair(__float_as_uint(gg));
+      const float g = sqrtf(__uint_as_float(p.lo) + __uint_as_float(p.hi)) * (1.f / kKeyScale);
+      if (valid && h == 0) {
+        const uint32_t nb16 = __builtin_bit_cast(uint16_t, (_Float16)n);
+        const uint32_t gb16 = __builtin_bit_cast(uint16_t, (_Float16)g);
+        aux_out[row] = nb16 | (gb16 << 16);
+      }
+
+      // ---- QJL projection z = S r on the matrix cores, 16 sign bits per lane and block --
 #pragma unroll
-      for (int m = 0; m < MPW; ++m) {
-        const int mb = mb0 + m;
-        floatx16 acc = {};
-        const _Float16* ah = &s_rhi[(32 * mb + (lane & 31)) * RH + 8 * (lane >> 5)];
-        const _Float16* al = &s_rlo[(32 * mb + (lane & 31)) * RH + 8 * (lane >> 5)];
+      for (int nb = 0; nb < NB; ++nb) {
+        floatx16 z = {};
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          const half8 r_h = *reinterpret_cast<const half8*>(ah + 16 * kb);
-          const half8 r_l = *reinterpret_cast<const half8*>(al + 16 * kb);
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(sop[kb], r_h, acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(sop[kb], r_l, acc, 0, 0, 0);
+        for (int b = 0; b < NB; ++b) {
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const uint4 a = *reinterpret_cast<const uint4*>(&s_S[s_base + 32 * nb * SP + 32 * b + 8 * j]);
+            z = mfma_f16(a, make_uint4(rh[b][4 * j], rh[b][4 * j + 1], rh[b][4 * j + 2], rh[b][4 * j + 3]), z);
+            z = mfma_f16(a, make_uint4(rl[b][4 * j], rl[b][4 * j + 1], rl[b][4 * j + 2], rl[b][4 * j + 3]), z);
+          }
         }
-        // acc register r of lane l: token 32 mb + l % 32, projection output
-        // 32 nb + 8 (r / 4) + 4 (l / 32) + r % 4.  Stored bit = (z >= 0), from the sign bit.
+        // register r holds output 32 nb + 16 h + r; stored bit = (z >= 0), from the sign bit
         uint32_t neg = 0u;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) neg |= (__float_as_uint(acc[r]) >> 31) << (8 * (r >> 2) + (r & 3));
-        const uint32_t half_bits = (~neg & 0x0F0F0F0Fu) << (4 * (lane >> 5));
-        const uint32_t word = half_bits | (uint32_t)__shfl_xor((int)half_bits, 32);
-        const int t = 32 * mb + lane;
-        if (lane < 32 && t < nv) signs_out[(row0 + t) * SW + nb] = word;
+        for (int r = 0; r < 16; ++r) neg |= (__float_as_uint(z[r]) >> 31) << r;
+        const HalfPair p2 = half_pair(~neg & 0xFFFFu);
+        if (valid && h == (nb & 1)) signs_out[row * NB + nb] = p2.lo | (p2.hi << 16);
+        __builtin_amdgcn_sched_barrier(0);   // one output block's operands live at a time
       }
-      __syncthreads();   // the residual tile is overwritten by the next tile
+    } else {
+      if (valid && h == 0) aux_out[row] = __float_as_uint(n);
     }
   }
 }
@@ -570,7 +648,7 @@ template <int D, int KB, int DT, bool QJL>
 int lm_blocks_per_cu() {
   static const int n = [] {
     int b = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, encode_lm_kernel<D, KB, DT, QJL>, 64 * D / lm_coords<D>(), 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, encode_lm_kernel<D, KB, DT, QJL>, 64 * rot_waves<D>(), 0) !=
             hipSuccess ||
         b <= 0)
       b = 1;
@@ -583,19 +661,22 @@ template <int D, int KB, int DT, bool QJL>
 hipError_t run_lm(const tq_layout& Lay, const tq_state& S, const void* x, int batch, int T, int dst,
                   const tq_cache& C, hipStream_t st, bool values) {
   const int slices = batch * Lay.n_kv_heads;
-  const int tps = ceil_div(T, kTile);
-  const int n_tiles = slices * tps;
-  // persistent: as many groups as fit on the device at once; each loads its rows of S
-  // (keys) once and walks the tiles with a stride of the grid size
-  const int grid = std::min(n_tiles, device_cus() * lm_blocks_per_cu<D, KB, DT, QJL>());
+  const int mbps = ceil_div(T, 32);
+  const long n_mb = (long)slices * mbps;
+  if (n_mb > 0x7FFFFFFFL) return hipErrorInvalidValue;
+  // persistent: as many groups as fit on the device at once (each stages the rotation
+  // operands, and S for keys, in LDS once); every wave walks 32-token blocks with a stride
+  // of the grid's wave count
+  constexpr int NW = rot_waves<D>();
+  const int grid = (int)std::min<long>((n_mb + NW - 1) / NW, (long)device_cus() * lm_blocks_per_cu<D, KB, DT, QJL>());
   if (values) {
-    hipLaunchKernelGGL((encode_lm_kernel<D, KB, DT, QJL>), dim3(grid), dim3(64 * D / lm_coords<D>()), 0, st,
-                       (const uint16_t*)x, T, tps, n_tiles, dst, C.capacity, S.v_centroids, S.v_thresholds,
+    hipLaunchKernelGGL((encode_lm_kernel<D, KB, DT, QJL>), dim3(grid), dim3(64 * NW), 0, st,
+                       (const uint16_t*)x, T, mbps, (int)n_mb, dst, C.capacity, S.v_centroids, S.v_thresholds,
                        S.v_signs, (const uint16_t*)nullptr, (uint32_t*)C.v_codes, (uint32_t*)nullptr,
                        (uint32_t*)C.v_aux);
   } else {
-    hipLaunchKernelGGL((encode_lm_kernel<D, KB, DT, QJL>), dim3(grid), dim3(64 * D / lm_coords<D>()), 0, st,
-                       (const uint16_t*)x, T, tps, n_tiles, dst, C.capacity, S.k_centroids, S.k_thresholds,
+    hipLaunchKernelGGL((encode_lm_kernel<D, KB, DT, QJL>), dim3(grid), dim3(64 * NW), 0, st,
+                       (const uint16_t*)x, T, mbps, (int)n_mb, dst, C.capacity, S.k_centroids, S.k_thresholds,
                        S.k_signs, QJL ? S.qjl : (const uint16_t*)nullptr, (uint32_t*)C.k_codes,
                        QJL ? (uint32_t*)C.k_signs : (uint32_t*)nullptr, (uint32_t*)C.k_aux);
   }
