@@ -94,12 +94,16 @@ struct MmaGeom {
   static constexpr int NKB = D / 32;          // 32-dimension blocks of the score contraction
   static constexpr int NNB = D / 16;          // 16-dimension blocks of the value product
   static constexpr int NG = D / 32;           // value groups
-  // one wave's staging area (words): key rows, sign rows, key aux (one word per token for the
-  // LM kinds; word-major [block][token] for affine keys), value codes and value aux word-major
+  // Lloyd-Max keys (with or without the QJL sketch) at head_dim >= 128 come straight from
+  // memory into registers in the matrix-core operand order; affine and 16-bit keys, and the
+  // head_dim-64 rows (too short to keep four lanes' loads busy), are staged in LDS
+  static constexpr bool DIRECT = !AFF && !F16K && D >= 128;
+  // one wave's staging area (words): key rows, sign rows, key aux (word-major [block][token]
+  // for affine keys), value codes and value aux word-major
   static constexpr int OFF_SK = 0;
-  static constexpr int OFF_SS = OFF_SK + TT * SK;
-  static constexpr int OFF_SAK = OFF_SS + TT * SS;
-  static constexpr int OFF_SV = OFF_SAK + (AFF ? WAK * TS : TT);
+  static constexpr int OFF_SS = OFF_SK + (DIRECT ? 0 : TT * SK);
+  static constexpr int OFF_SAK = OFF_SS + (DIRECT ? 0 : TT * SS);
+  static constexpr int OFF_SV = OFF_SAK + (DIRECT ? 0 : (AFF ? WAK * TS : TT));
   static constexpr int OFF_SAV = OFF_SV + WV * TS;
   static constexpr int STAGE = OFF_SAV + WAV * TS;
   static_assert(OFF_SS % 4 == 0 && OFF_SAK % 4 == 0 && OFF_SV % 4 == 0 && OFF_SAV % 4 == 0 && STAGE % 4 == 0,
@@ -112,7 +116,10 @@ struct MmaGeom {
   static constexpr int NVT = (VK == TQ_V_LM_ROT) ? 1 << (2 * VB) : 0;  // value code pairs
   static constexpr int OFF_BQ = (G::OFF_QB + NREP * D + 3) & ~3;
   static constexpr int NRB = NREP + 1;         // query operand rows: the heads, then a zero row
-  static constexpr int OFF_PT = OFF_BQ + 2 * NRB * D;
+  // query operand rows padded by 4 words: the n_rep rows a 16-byte read spans fall in
+  // different LDS banks
+  static constexpr int QS = D / 2 + 4;         // words per query operand row
+  static constexpr int OFF_PT = OFF_BQ + 4 * NRB * QS;
   static constexpr int OFF_VT = OFF_PT + 2 * NPT;
   // 3-bit rotated values (ten codes per word): per 16-dimension block and column l16 of it, the
   // word offset of dimension 16 nb + l16 in the transposed staging and its bit, (TS w) | bit << 16
@@ -129,6 +136,119 @@ struct MmaGeom {
   static constexpr int RECENT_NEED = OFF_RSCR + G::RECENT_SCRATCH;
   static constexpr int FLOATS = OWN > RECENT_NEED ? OWN : RECENT_NEED;
   static_assert(NREP <= 16, "one 16-column operand holds the heads");
+};
+
+// Lloyd-Max keys loaded straight into registers in the order the score product consumes
+// them.  Lane (l16, q4) of 16-token block mb holds token 16 mb + l16's dimensions
+// q4 D/4 .. q4 D/4 + D/4 - 1 (its code words and QJL sign bits) and that token's aux word
+// (n and gamma); the score product's k slots 8 q4 .. 8 q4 + 7 of k-block kb are dimensions
+// q4 D/4 + 8 kb .. + 7, and the query operand is read in the same order.  The lane also
+// loads the aux words of the four tokens its score accumulators hold (16 mb + 4 q4 + r).
+// Raw buffer loads over exactly the tile's rows: words past the tile read as zero.
+template <int D, int KB, bool QJL, int TT>
+struct DirectKeys {
+  static constexpr int MB = TT / 16;
+  static constexpr int DPL = D / 4;                         // dimensions per lane
+  static constexpr int PER = (KB == 3) ? 10 : 32 / KB;
+  static constexpr int WK = (D + PER - 1) / PER;            // code words per row
+  static constexpr int WS = QJL ? D / 32 : 0;               // sign words per row
+  static constexpr int first_word(int q) { return (DPL * q) / PER; }
+  static constexpr int span(int q) { return (DPL * q + DPL - 1) / PER - first_word(q) + 1; }
+  static constexpr int max_span() {
+    int m = 0;
+    for (int q = 0; q < 4; ++q) m = span(q) > m ? span(q) : m;
+    return m;
+  }
+  static constexpr int KWL = (KB == 3) ? max_span() : DPL * KB / 32;   // code words per lane
+  static constexpr int SWL = QJL ? (DPL >= 32 ? DPL / 32 : 1) : 1;    // sign words per lane
+  static constexpr int SAL = (KB == 3) ? (3 * DPL + 31) / 32 : 1;     // aligned 3-bit stream words
+  static_assert(KB == 3 || (DPL * KB) % 32 == 0, "a lane's codes fill whole words");
+  uint32_t kc[MB][KWL];
+  uint32_t ks[MB][SWL];
+  uint32_t ka[MB];
+
+  __device__ __forceinline__ void load(const uint32_t* kc_g, const uint32_t* ks_g, const uint32_t* ka_g, int rows,
+                                       int l16, int q4) {
+    const __amdgpu_buffer_rsrc_t rc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(kc_g), (short)0, 4 * rows * WK, kBufferRsrcWord3);
+    const __amdgpu_buffer_rsrc_t ra =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(ka_g), (short)0, 4 * rows, kBufferRsrcWord3);
+    const int w0 = (DPL * q4) / PER;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int tok = 16 * mb + l16;
+      const int cb = 4 * (tok * WK + w0);
+      if constexpr (KB != 3 && KWL % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < KWL; i += 4) {
+          const auto v = __builtin_amdgcn_raw_buffer_load_b128(rc, cb + 4 * i, 0, 0);
+          kc[mb][i] = v[0]; kc[mb][i + 1] = v[1]; kc[mb][i + 2] = v[2]; kc[mb][i + 3] = v[3];
+        }
+      } else if constexpr (KB != 3 && KWL == 2) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(rc, cb, 0, 0);
+        kc[mb][0] = v[0]; kc[mb][1] = v[1];
+      } else {
+#pragma unroll
+        for (int i = 0; i < KWL; ++i) kc[mb][i] = __builtin_amdgcn_raw_buffer_load_b32(rc, cb + 4 * i, 0, 0);
+      }
+      ka[mb] = __builtin_amdgcn_raw_buffer_load_b32(ra, 4 * tok, 0, 0);
+      if constexpr (QJL) {
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(ks_g), (short)0, 4 * rows * WS, kBufferRsrcWord3);
+        const int sw0 = (DPL * q4) / 32;
+        if constexpr (SWL == 2) {
+          const auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, 4 * (tok * WS + sw0), 0, 0);
+          ks[mb][0] = v[0]; ks[mb][1] = v[1];
+        } else {
+          ks[mb][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * (tok * WS + sw0), 0, 0);
+        }
+      }
+    }
+  }
+
+  // the lane's 8 codes of k-block kb (dimensions q4 D/4 + 8 kb ..) in the low 8 KB bits;
+  // for 3-bit codes `al` is the lane's gap-free code stream (align3 below)
+  __device__ __forceinline__ uint32_t codes(int mb, int kb, const uint32_t (&al)[SAL]) const {
+    if constexpr (KB == 4) {
+      return kc[mb][kb];
+    } else if constexpr (KB == 2) {
+      return kc[mb][kb >> 1] >> (16 * (kb & 1));
+    } else {
+      const int bit = 24 * kb;
+      const uint32_t lo = al[bit >> 5];
+      const uint32_t hi = ((bit >> 5) + 1 < SAL) ? al[(bit >> 5) + 1] : 0u;
+      return __builtin_amdgcn_alignbit(hi, lo, (uint32_t)(bit & 31));
+    }
+  }
+
+  // 3-bit codes, ten per word: the lane's words joined into one gap-free stream, shifted so
+  // that its first dimension sits at bit 0
+  __device__ __forceinline__ void align3(int mb, int q4, uint32_t (&al)[SAL]) const {
+    if constexpr (KB == 3) {
+      constexpr int NG3 = (30 * KWL + 31) / 32;
+      uint32_t g[NG3 + 1];
+#pragma unroll
+      for (int j = 0; j <= NG3; ++j) g[j] = 0u;
+#pragma unroll
+      for (int i = 0; i < KWL; ++i) {
+        const int b = 30 * i;                 // chunk i starts at stream bit 30 i
+        g[b >> 5] |= kc[mb][i] << (b & 31);
+        if ((b & 31) + 30 > 32) g[(b >> 5) + 1] |= kc[mb][i] >> (32 - (b & 31));
+      }
+      const uint32_t off = (uint32_t)(3 * (DPL * q4 - 10 * ((DPL * q4) / 10)));
+#pragma unroll
+      for (int j = 0; j < SAL; ++j) al[j] = __builtin_amdgcn_alignbit(g[j + 1], g[j], off);
+    }
+  }
+
+  // the 8 QJL sign bits of k-block kb
+  __device__ __forceinline__ uint32_t sign_byte(int mb, int kb, int q4) const {
+    if constexpr (DPL >= 32) {
+      return (ks[mb][kb >> 2] >> (8 * (kb & 3))) & 0xFFu;
+    } else {
+      return (ks[mb][0] >> (16 * (q4 & 1) + 8 * kb)) & 0xFFu;
+    }
+  }
 };
 
 // NQ > 1: a multi-query group.  The NQ x n_rep rows (query j, head h at row j n_rep + h) take
@@ -189,12 +309,18 @@ decode_mma_kernel(const DecodeArgs A) {
   RowLoader<M::WAK, AFF ? M::TS : 1, TT, DWL> ld_ak;
   RowLoader<M::WV, M::TS, TT, DWL> ld_v;
   RowLoader<M::WAV, M::TS, TT, DWL> ld_av;
+  using DK = DirectKeys<D, (M::DIRECT ? KB : 2), QJL, TT>;
+  DK dkn;                                       // the next tile's keys (Lloyd-Max kinds)
   auto issue = [&](int t0) {
     const int nv = min(TT, te - t0);
     const size_t row0 = slice * cap + t0;
-    ld_k.load(A.kc + row0 * M::WK, nv, lane);
-    ld_s.load(A.ks + row0 * M::WS, nv, lane);
-    ld_ak.load(A.ka + row0 * M::WAK, nv, lane);
+    if constexpr (M::DIRECT) {
+      dkn.load(A.kc + row0 * M::WK, A.ks + row0 * M::WS, A.ka + row0 * M::WAK, nv, l16, q4);
+    } else {
+      ld_k.load(A.kc + row0 * M::WK, nv, lane);
+      ld_s.load(A.ks + row0 * M::WS, nv, lane);
+      ld_ak.load(A.ka + row0 * M::WAK, nv, lane);
+    }
     ld_v.load(A.vc + row0 * M::WV, nv, lane);
     ld_av.load(A.va + row0 * M::WAV, nv, lane);
   };
@@ -227,17 +353,18 @@ decode_mma_kernel(const DecodeArgs A) {
     const float* qa = sm + M::G::OFF_QA;
     const float* qb = sm + M::G::OFF_QB;
     _Float16* bq = reinterpret_cast<_Float16*>(smw + M::OFF_BQ);
-    constexpr int RS = M::NRB * D;               // halves per operand region
+    constexpr int RS = M::NRB * 2 * M::QS;       // halves per operand region
     constexpr float QA = (AFF || F16K) ? kMmaAffQScale : kMmaQScale / kMmaCentScale;
-    for (int i = threadIdx.x; i < RS; i += 256) {
+    for (int i = threadIdx.x; i < M::NRB * D; i += 256) {
       const bool on = i < NREP * D;
       const float a = on ? qa[i] * QA : 0.f;
       const float s = (on && QJL) ? qb[i] * kMmaQScale : 0.f;
       const _Float16 ah = (_Float16)a, sh = (_Float16)s;
-      bq[i] = ah;
-      bq[RS + i] = (_Float16)(a - (float)ah);
-      bq[2 * RS + i] = sh;
-      bq[3 * RS + i] = (_Float16)(s - (float)sh);
+      const int o = (i / D) * 2 * M::QS + i % D;
+      bq[o] = ah;
+      bq[RS + o] = (_Float16)(a - (float)ah);
+      bq[2 * RS + o] = sh;
+      bq[3 * RS + o] = (_Float16)(s - (float)sh);
     }
   }
   __syncthreads();
@@ -268,10 +395,13 @@ decode_mma_kernel(const DecodeArgs A) {
 
   for (int t0 = tb + wave * TT; t0 < te; t0 += 4 * TT) {
     const int nv = min(TT, te - t0);
-    ld_k.store(st + M::OFF_SK, lane);
-    ld_s.store(st + M::OFF_SS, lane);
-    if constexpr (AFF) ld_ak.store_transposed(st + M::OFF_SAK, lane);
-    else ld_ak.store(st + M::OFF_SAK, lane);
+    const DK dk = dkn;
+    if constexpr (!M::DIRECT) {
+      ld_k.store(st + M::OFF_SK, lane);
+      ld_s.store(st + M::OFF_SS, lane);
+      if constexpr (AFF) ld_ak.store_transposed(st + M::OFF_SAK, lane);
+      else ld_ak.store(st + M::OFF_SAK, lane);
+    }
     ld_v.store_transposed(st + M::OFF_SV, lane);
     ld_av.store_transposed(st + M::OFF_SAV, lane);
     if (t0 + 4 * TT < te) issue(t0 + 4 * TT);
@@ -291,8 +421,8 @@ decode_mma_kernel(const DecodeArgs A) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         const int kw = 16 * kb + 4 * q4;
-        constexpr int RW = M::NRB * D / 2;
-        const uint32_t* src = bqw + hq * (D / 2) + kw;
+        constexpr int RW = M::NRB * M::QS;
+        const uint32_t* src = bqw + hq * M::QS + kw;
         const uint4 r0 = *reinterpret_cast<const uint4*>(src);
         const uint4 r1 = *reinterpret_cast<const uint4*>(src + RW);
         const mma_u4_t bq0 = mma_u4_t{r0.x, r0.y, r0.z, r0.w};
@@ -309,7 +439,7 @@ decode_mma_kernel(const DecodeArgs A) {
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) p[mb][r] = sacc[mb][r] * (1.f / kMmaAffQScale);
-    } else if constexpr (!AFF) {
+    } else if constexpr (!AFF && !M::DIRECT) {
       mma_f4_t sacc[MB];
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) sacc[mb] = mma_f4_t{0.f, 0.f, 0.f, 0.f};
@@ -318,8 +448,8 @@ decode_mma_kernel(const DecodeArgs A) {
         const int kw = 16 * kb + 4 * q4;           // word offset of this lane's 8 dimensions
         mma_u4_t bq0, bq1, bq2, bq3;
         {
-          constexpr int RW = M::NRB * D / 2;         // words per operand region
-          const uint32_t* src = bqw + hq * (D / 2) + kw;
+          constexpr int RW = M::NRB * M::QS;         // words per operand region
+          const uint32_t* src = bqw + hq * M::QS + kw;
           const uint4 r0 = *reinterpret_cast<const uint4*>(src);
           const uint4 r1 = *reinterpret_cast<const uint4*>(src + RW);
           bq0 = mma_u4_t{r0.x, r0.y, r0.z, r0.w};
@@ -382,6 +512,68 @@ decode_mma_kernel(const DecodeArgs A) {
           p[mb][r] = sacc[mb][r] * (n * kMmaUnscale);
         }
       }
+    } else if constexpr (!AFF) {
+      mma_f4_t sacc[MB];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) sacc[mb] = mma_f4_t{0.f, 0.f, 0.f, 0.f};
+      uint32_t al[MB][DK::SAL];                  // 3-bit codes: each block's aligned stream
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) dk.align3(mb, q4, al[mb]);
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const int kw = q4 * (D / 8) + 4 * kb;     // word offset of this lane's 8 query dimensions
+        mma_u4_t bq0, bq1, bq2, bq3;
+        {
+          constexpr int RW = M::NRB * M::QS;         // words per operand region
+          const uint32_t* src = bqw + hq * M::QS + kw;
+          const uint4 r0 = *reinterpret_cast<const uint4*>(src);
+          const uint4 r1 = *reinterpret_cast<const uint4*>(src + RW);
+          bq0 = mma_u4_t{r0.x, r0.y, r0.z, r0.w};
+          bq1 = mma_u4_t{r1.x, r1.y, r1.z, r1.w};
+          if constexpr (QJL) {
+            const uint4 r2 = *reinterpret_cast<const uint4*>(src + 2 * RW);
+            const uint4 r3 = *reinterpret_cast<const uint4*>(src + 3 * RW);
+            bq2 = mma_u4_t{r2.x, r2.y, r2.z, r2.w};
+            bq3 = mma_u4_t{r3.x, r3.y, r3.z, r3.w};
+          }
+        }
+        // one 16-token block at a time: its operands, then its products (the accumulator
+        // chains through the matrix unit; few registers stay live)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const uint32_t y = dk.codes(mb, kb, al[mb]);   // the lane's 8 codes, KB bits each
+          mma_u4_t ahi, alo;
+#pragma unroll
+          for (int pp = 0; pp < 4; ++pp) {
+            const uint32_t pc = (y >> (2 * KB * pp)) & (M::NPT - 1);
+            const uint2 e = *reinterpret_cast<const uint2*>(ptab + 2 * pc);
+            ahi[pp] = e.x;
+            alo[pp] = e.y;
+          }
+          sacc[mb] = mma16(ahi, bq0, sacc[mb]);
+          sacc[mb] = mma16(alo, bq0, sacc[mb]);
+          sacc[mb] = mma16(ahi, bq1, sacc[mb]);
+          if constexpr (QJL) {
+            const uint32_t sb = dk.sign_byte(mb, kb, q4);
+            const uint4 mk = *reinterpret_cast<const uint4*>(sgt + 4 * sb);
+            const uint32_t g2 = __builtin_amdgcn_perm(dk.ka[mb], dk.ka[mb], 0x03020302u);   // (gamma, gamma)
+            const mma_u4_t asg = mma_u4_t{g2 ^ mk.x, g2 ^ mk.y, g2 ^ mk.z, g2 ^ mk.w};
+            sacc[mb] = mma16(asg, bq2, sacc[mb]);
+            sacc[mb] = mma16(asg, bq3, sacc[mb]);
+          }
+        }
+      }
+      // times n (fp16 with gamma for LM + QJL keys, fp32 for MSE-only keys) and the unscale;
+      // accumulator row r of this lane is token 16 mb + 4 q4 + r, whose aux word lane 4 q4 + r holds
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const uint32_t nn = (uint32_t)__shfl((int)dk.ka[mb], 4 * q4 + r);
+          const float n = QJL ? f16_to_f32(nn & 0xFFFFu) : __uint_as_float(nn);
+          p[mb][r] = sacc[mb][r] * (n * kMmaUnscale);
+        }
+      }
     } else {
       // affine keys: per 32-dimension block, sum_j (c_j - 128) q_j on the matrix cores, then
       // a times it plus (m + 128 a) times the block's query sum
@@ -392,8 +584,8 @@ decode_mma_kernel(const DecodeArgs A) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         const int kw = 16 * kb + 4 * q4;
-        constexpr int RW = M::NRB * D / 2;
-        const uint32_t* src = bqw + hq * (D / 2) + kw;
+        constexpr int RW = M::NRB * M::QS;
+        const uint32_t* src = bqw + hq * M::QS + kw;
         const uint4 r0 = *reinterpret_cast<const uint4*>(src);
         const uint4 r1 = *reinterpret_cast<const uint4*>(src + RW);
         const mma_u4_t bq0 = mma_u4_t{r0.x, r0.y, r0.z, r0.w};
