@@ -38,9 +38,9 @@ def encode_k(lay, k: np.ndarray, state: dict) -> dict:
         return {"k_codes": L.pack_codes(e["idx"], lay.k_bits), "k_aux": e["n32"],
                 "near_idx": e["near_idx"], "enc": e}
     if lay.k_kind == "affine8":
-        e = enc.encode_k_affine8(k)
+        e = enc.encode_k_affine(k, lay.k_bits)
         aux = np.stack([e["a16"].view(np.uint16), e["m16"].view(np.uint16)], axis=-1)
-        return {"k_codes": L.pack_codes(e["q8"], 8), "k_aux": aux,
+        return {"k_codes": L.pack_codes(e["q"], lay.k_bits), "k_aux": aux,
                 "near_idx": e["near_idx"], "enc": e}
     raise ValueError(lay.k_kind)
 
@@ -86,7 +86,7 @@ def read_k(lay, planes: dict, state: dict) -> dict:
         return {"idx": L.unpack_codes(planes["k_codes"], lay.k_bits, d),
                 "n": np.asarray(planes["k_aux"], dtype=np.float32).astype(np.float64)}
     aux = np.asarray(planes["k_aux"], dtype=np.uint16)
-    return {"q8": L.unpack_codes(planes["k_codes"], 8, d),
+    return {"q": L.unpack_codes(planes["k_codes"], lay.k_bits, d),
             "a": aux[..., 0].view(np.float16).astype(np.float64),
             "m": aux[..., 1].view(np.float16).astype(np.float64)}
 

@@ -9,7 +9,7 @@ page, GPU kernel optimisation section, n_rep item):
   and scored against the rotated codes):
       q_r = Pi q,  q_s = S q_r,
       s_t = n_t / sqrt(d) * ( <q_r, c[idx_t]> + gamma_t sqrt(pi/2)/d <q_s, sigma_t> )
-  compressed tokens, affine keys:   s_t = <q, m + a * q8_t> / sqrt(d)
+  compressed tokens, affine keys:   s_t = <q, m + a * q_t> / sqrt(d)
   recent-buffer tokens (exact fp16; TurboQuant vLLM guide section 5, benchmark page
   buffering strategy):             s_r = <q, k_r> / sqrt(d)
   p = softmax over all N_c + R scores;
@@ -55,7 +55,7 @@ def _scores_compressed(lay, q: np.ndarray, kd: dict, state: dict) -> np.ndarray:
         c = state["cb_k"][0].astype(np.float64)
         q_r = rotation_matrix(state["signs_k"]) @ q
         return kd["n"] / math.sqrt(d) * (c[kd["idx"]] @ q_r)
-    # affine 8-bit keys: k_hat = m + a * q8 per 32-block
+    # per-block affine keys: k_hat = m + a * q per 32-block
     k_hat = _affine_k_hat(kd, d)
     return k_hat @ q / math.sqrt(d)
 
@@ -63,7 +63,7 @@ def _scores_compressed(lay, q: np.ndarray, kd: dict, state: dict) -> np.ndarray:
 def _affine_k_hat(kd: dict, d: int) -> np.ndarray:
     a = np.repeat(kd["a"], 32, axis=-1)
     m = np.repeat(kd["m"], 32, axis=-1)
-    return m + a * kd["q8"]
+    return m + a * kd["q"]
 
 
 def _v_hat_group(lay, vd: dict) -> np.ndarray:

@@ -18,10 +18,10 @@ values keep a per-group minimum and maximum): each group of 32 channels gets an
 fp16 step a = (max - min)/(L-1) and offset m = min, and codes 0 .. L-1 -- the same
 quantiser as the per-block affine keys below, at 2 or 4 bits.
 
-Keys, per-block affine 8-bit and values, rotated Lloyd-Max 3-bit (vllm-metal
-TurboQuant guide, quantisation principle table): keys keep their own scale and
-offset per block with no rotation; values are rotated, then mapped to the
-8-centroid codebook.
+Keys, per-block affine 8-bit (and 5/4/2-bit, the guide's compression-ratio table) and
+values, rotated Lloyd-Max 3-bit (vllm-metal TurboQuant guide, quantisation principle
+table): keys keep their own scale and offset per block with no rotation; values are
+rotated, then mapped to the 8-centroid codebook.
 
 Readings where the pages are silent (each also listed in the design notes):
   * the vector is normalised before rotation; its norm n (and the residual norm
@@ -32,8 +32,8 @@ Readings where the pages are silent (each also listed in the design notes):
     bit = (z_j >= 0), z = S r, with z evaluated in float64 on the float64 residual;
   * group scale Delta = fp16(2 amax / (L-1)), idx = clamp(rne(v/Delta + (L-1)/2), 0, L-1)
     with the stored Delta; Delta = 0 gives idx = L-1, 0, L/2 for v > 0, v < 0, v = 0;
-  * affine scale a = fp16((max-min)/255), offset m = fp16(min), q = clamp(rne((k-m)/a), 0, 255);
-    a = 0 gives q = 0; min/max values alike with L - 1 = 3 or 15 in place of 255;
+  * affine scale a = fp16((max-min)/(2^b-1)), offset m = fp16(min), q = clamp(rne((k-m)/a), 0, 2^b-1)
+    for keys of b = 8, 5, 4, 2 bits; a = 0 gives q = 0; min/max values alike with L - 1 = 3 or 15;
   * a quotient lying exactly on a half-integer is an exact tie, decided by round-half-
     to-even and compared like any other element; only inexact values within BAND of a
     boundary are marked near.  Exact ties are common with fp16 inputs (a value that is
@@ -138,9 +138,12 @@ def _group_minmax(x: np.ndarray, top: int):
     return q.reshape(x.shape), a16, m16, near.reshape(x.shape)
 
 
-def encode_k_affine8(k: np.ndarray) -> dict:
-    q, a16, m16, near = _group_minmax(k, 255)
-    return {"q8": q, "a16": a16, "m16": m16, "near_idx": near}
+def encode_k_affine(k: np.ndarray, bits: int = 8) -> dict:
+    """Per-block affine keys (vllm-metal guide, quantisation principle and compression-ratio
+    table: q8_0, q5_0, q4_0 and the 2-bit uint2/int2 keys): per block of 32, a = fp16((max -
+    min)/(2^bits - 1)), m = fp16(min), q = clamp(rne((k - m)/a), 0, 2^bits - 1)."""
+    q, a16, m16, near = _group_minmax(k, (1 << bits) - 1)
+    return {"q": q, "a16": a16, "m16": m16, "near_idx": near}
 
 
 def encode_v_group_asym(v: np.ndarray, bits: int) -> dict:

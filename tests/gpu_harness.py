@@ -224,9 +224,9 @@ def compare_encode(wl, gpu: dict, ek: dict, ev: dict, rows=slice(None)) -> dict:
         st["k_idx_excluded_differ"] = int((diff & near).sum())
         st["k_aux_mismatch"] = int((g["k_aux"].view(np.uint32) != ek["k_aux"].view(np.uint32)).sum())
     else:
-        q8 = OL.unpack_codes(g["k_codes"], 8, d)
+        qa = OL.unpack_codes(g["k_codes"], wl.k_bits, d)
         near = ek["near_idx"]
-        diff = q8 != ek["enc"]["q8"]
+        diff = qa != ek["enc"]["q"]
         st["k_idx_mismatch"] = int((diff & ~near).sum())
         st["k_idx_excluded"] = int(near.sum())
         st["k_idx_excluded_differ"] = int((diff & near).sum())

@@ -224,6 +224,26 @@ def test_compression_ratios_against_printed_values():
     assert sum(L.bytes_per_token_head(64, "lm_qjl", 3, "group_sym", 2).values()) == 60
 
 
+def test_narrow_affine_key_ratios_against_printed_values():
+    """The guide's other printed rows: q5_0 / q4_0 / uint2 keys with q3_0 values come out of
+    the layout's byte accounting to the printed precision (3.37x, 3.76x, 4.92x).  The
+    int2 / q2_0 row (printed 5.82x) is 512 / 88 bytes; this layout stores 2-bit value codes
+    sixteen to a word (84 bytes, 6.10x) -- the printed figure equals 2-bit codes fifteen to a
+    word, the 30-bit payload of the ten-to-a-word 3-bit packing (recorded as a reading)."""
+    g = json.load(open(os.path.join(GOLDEN, "compression_ratios.json")))
+    rows = {(r["k_quant"], r["v_quant"]): r["ratio"] for r in g["ratios_vs_fp16"]["rows"]}
+    kbits = {"q8_0": 8, "q5_0": 5, "q4_0": 4, "uint2": 2, "int2": 2}
+    vbits = {"q3_0": 3, "q2_0": 2}
+    for (kq, vq), printed in rows.items():
+        ours = L.compression_ratio(128, "affine8", kbits[kq], "lm_rot", vbits[vq])
+        if (kq, vq) == ("int2", "q2_0"):
+            assert round(ours, 2) == 6.10
+            assert round(512 / (48 + 4 * -(-128 // 15) + 4), 2) == printed
+        else:
+            assert round(ours, 2) == printed, (kq, vq, ours, printed)
+    assert sum(L.bytes_per_token_head(128, "affine8", 5, "lm_rot", 3).values()) == 152
+
+
 # --------------------------------------------------------------------------- QJL estimator
 def test_qjl_sign_identity_and_unbiased_score():
     """E_S[sign(<s,r>) <s,q>] = sqrt(2/pi) <q,r>/|r| makes the full score unbiased."""
@@ -346,19 +366,52 @@ def test_group_sym_grid_and_ties_by_hand():
 
 def test_affine8_grid_by_hand():
     k = np.arange(32) * 8.0 / 16.0            # 0 .. 15.5 step 0.5 -> a = 15.5/255 (fp16), m = 0
-    e = E.encode_k_affine8(k[None])
+    e = E.encode_k_affine(k[None])
     a = float(e["a16"][0, 0])
     assert a == float(np.float16(15.5 / 255))
-    assert e["q8"][0, 0] == 0 and e["q8"][0, -1] == 255
+    assert e["q"][0, 0] == 0 and e["q"][0, -1] == 255
     k2 = np.full(32, 3.0)
-    e2 = E.encode_k_affine8(k2[None])
-    assert float(e2["a16"][0, 0]) == 0 and np.all(e2["q8"] == 0)
+    e2 = E.encode_k_affine(k2[None])
+    assert float(e2["a16"][0, 0]) == 0 and np.all(e2["q"] == 0)
     # values on the grid m + a*q reconstruct exactly
     k3 = np.float16(-1.0) + np.float16(2.0 ** -4) * np.arange(32).astype(np.float64)
     k3[-1] = -1.0 + 255 * 2.0 ** -4
-    e3 = E.encode_k_affine8(k3[None])
+    e3 = E.encode_k_affine(k3[None])
     assert float(e3["a16"][0, 0]) == 2.0 ** -4
-    assert np.array_equal(-1.0 + 2.0 ** -4 * e3["q8"][0], k3)
+    assert np.array_equal(-1.0 + 2.0 ** -4 * e3["q"][0], k3)
+
+
+@pytest.mark.parametrize("bits", [2, 4, 5])
+def test_affine_keys_narrow_widths_by_hand(bits):
+    """q5_0 / q4_0 / 2-bit affine keys (vllm-metal guide, compression-ratio table): the block
+    min goes to code 0 and the max to 2^b - 1, values on the grid m + a q reconstruct exactly,
+    exact half-way points go to the even code, a flat block has a = 0 and codes 0, and the
+    5-bit row packs into its two planes at the documented bit positions."""
+    top = (1 << bits) - 1
+    a, m = 2.0 ** -4, -0.5
+    q = np.arange(32) % (top + 1)
+    k = m + a * q.astype(np.float64)
+    k[0], k[1] = m, m + a * top
+    e = E.encode_k_affine(k[None], bits)
+    assert float(e["a16"][0, 0]) == a and float(e["m16"][0, 0]) == m
+    assert e["q"][0, 0] == 0 and e["q"][0, 1] == top
+    assert np.array_equal(m + a * e["q"][0], k) and not e["near_idx"].any()
+    w = k.copy()
+    w[2:2 + min(top, 30)] = m + a * (np.arange(min(top, 30)) + 0.5)
+    e2 = E.encode_k_affine(w[None], bits)
+    lo = np.arange(min(top, 30))
+    assert np.array_equal(e2["q"][0, 2:2 + len(lo)], np.where(lo % 2 == 0, lo, lo + 1))
+    e3 = E.encode_k_affine(np.full((1, 32), 0.7), bits)
+    assert float(e3["a16"][0, 0]) == 0 and np.all(e3["q"] == 0)
+    if bits == 5:
+        codes = np.zeros((1, 64), dtype=np.int64)
+        codes[0, 0], codes[0, 9], codes[0, 40], codes[0, 63] = 31, 17, 16, 5
+        w5 = L.pack_codes(codes, 5)
+        assert w5.shape == (1, 10)                      # 8 nibble words + 2 fifth-bit words
+        assert int(w5[0, 0]) == 0xF and int(w5[0, 1]) == 0x10 and int(w5[0, 5]) == 0x0
+        assert int(w5[0, 7]) == 0x50000000
+        assert int(w5[0, 8]) == (1 << 0) | (1 << 9) and int(w5[0, 9]) == 1 << 8
+        assert np.array_equal(L.unpack_codes(w5, 5, 64), codes)
 
 
 @pytest.mark.parametrize("bits", [2, 4])
@@ -448,6 +501,7 @@ def test_zero_residual_when_unit_vector_lands_on_centroids():
 # --------------------------------------------------------------------------- decode
 KINDS = [("lm_qjl", 3, "group_sym", 2), ("lm_qjl", 4, "group_sym", 4), ("lm_qjl", 2, "group_sym", 2),
          ("affine8", 8, "lm_rot", 3), ("affine8", 8, "lm_rot", 2),
+         ("affine8", 5, "lm_rot", 3), ("affine8", 4, "lm_rot", 3), ("affine8", 2, "lm_rot", 2),
          ("lm_mse", 3, "lm_rot", 3), ("lm_mse", 4, "group_sym", 4), ("lm_mse", 2, "lm_rot", 2),
          ("f16", 16, "lm_rot", 3), ("f16", 16, "group_sym", 2),
          ("lm_qjl", 2, "group_asym", 2), ("lm_qjl", 3, "group_asym", 4)]
