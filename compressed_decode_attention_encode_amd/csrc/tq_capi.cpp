@@ -29,7 +29,8 @@ int lm_words(int d, int bits) {
   return (d + per - 1) / per;
 }
 int k_code_words(const tq_layout& L) {
-  if (L.k_kind == TQ_K_AFFINE8) return L.head_dim / 4;
+  if (L.k_kind == TQ_K_AFFINE8)   // per-block affine: bytes (8), nibble + fifth-bit planes (5), 4/2-bit words
+    return L.k_bits == 8 ? L.head_dim / 4 : (L.k_bits == 5 ? L.head_dim / 8 + L.head_dim / 32 : L.head_dim * L.k_bits / 32);
   if (L.k_kind == TQ_K_F16) return L.head_dim / 2;
   return lm_words(L.head_dim, L.k_bits);
 }
@@ -78,7 +79,8 @@ int check_layout(const tq_layout* L) {
   if (L->k_kind == TQ_K_LM_QJL || L->k_kind == TQ_K_LM_MSE) {
     if (L->k_bits < 2 || L->k_bits > 4) return fail(TQ_ERR_UNSUPPORTED, "LM keys need k_bits 2..4, got %d", L->k_bits);
   } else if (L->k_kind == TQ_K_AFFINE8) {
-    if (L->k_bits != 8) return fail(TQ_ERR_UNSUPPORTED, "affine keys need k_bits 8, got %d", L->k_bits);
+    if (L->k_bits != 8 && L->k_bits != 5 && L->k_bits != 4 && L->k_bits != 2)
+      return fail(TQ_ERR_UNSUPPORTED, "affine keys need k_bits 8, 5, 4 or 2, got %d", L->k_bits);
   } else if (L->k_kind == TQ_K_F16) {
     if (L->k_bits != 16) return fail(TQ_ERR_UNSUPPORTED, "16-bit keys need k_bits 16, got %d", L->k_bits);
   } else {

@@ -230,6 +230,15 @@ MainKernel find_main(const tq_layout& L) {
     }
   }
   if (L.k_kind == TQ_K_AFFINE8 && L.k_bits == 8) { TQ_BY_D(find_main_aff8) }
+  if (L.k_kind == TQ_K_AFFINE8 && (d == 64 || d == 128)) {   // 5/4/2-bit affine keys
+    const bool d64 = d == 64;
+    switch (L.k_bits) {
+      case 5: return d64 ? find_main_aff5_d64(nrep, vk, vb) : find_main_aff5_d128(nrep, vk, vb);
+      case 4: return d64 ? find_main_aff4_d64(nrep, vk, vb) : find_main_aff4_d128(nrep, vk, vb);
+      case 2: return d64 ? find_main_aff2_d64(nrep, vk, vb) : find_main_aff2_d128(nrep, vk, vb);
+      default: return MainKernel{nullptr, nullptr};
+    }
+  }
   // 16-bit keys: d = 64 and 128; d = 256 only fp16-stored, on the matrix cores with 32-token tiles
   if (L.k_kind == TQ_K_F16 && L.k_bits == 16) {
     // fp16-stored keys are exact matrix-core operands; bf16 ones stay on the vector ALUs

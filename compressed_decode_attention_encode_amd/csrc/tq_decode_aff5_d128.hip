@@ -1,0 +1,36 @@
+// Compiled instantiations of the decode kernel: per-block affine 5-bit keys (vllm-metal guide,
+// compression-ratio table), head_dim 128, n_rep 1..8, rotated Lloyd-Max 2/3/4-bit values, all on
+// the matrix cores (the query rows beyond n_rep are zero operand columns).
+#include "tq_decode_mma.h"
+
+namespace tq {
+
+namespace {
+template <int VB>
+MainKernel pick(int nrep) {
+  constexpr int KK = TQ_K_AFFINE8, VK = TQ_V_LM_ROT;
+  switch (nrep) {
+    case 1: return mma_kernel_kv<128, 1, KK, 5, VK, VB>();
+    case 2: return mma_kernel_kv<128, 2, KK, 5, VK, VB>();
+    case 3: return mma_kernel_kv<128, 3, KK, 5, VK, VB>();
+    case 4: return mma_kernel_kv<128, 4, KK, 5, VK, VB>();
+    case 5: return mma_kernel_kv<128, 5, KK, 5, VK, VB>();
+    case 6: return mma_kernel_kv<128, 6, KK, 5, VK, VB>();
+    case 7: return mma_kernel_kv<128, 7, KK, 5, VK, VB>();
+    case 8: return mma_kernel_kv<128, 8, KK, 5, VK, VB>();
+    default: return MainKernel{nullptr, nullptr};
+  }
+}
+}  // namespace
+
+MainKernel find_main_aff5_d128(int nrep, int vk, int vb) {
+  if (vk != TQ_V_LM_ROT) return MainKernel{nullptr, nullptr};
+  switch (vb) {
+    case 2: return pick<2>(nrep);
+    case 3: return pick<3>(nrep);
+    case 4: return pick<4>(nrep);
+    default: return MainKernel{nullptr, nullptr};
+  }
+}
+
+}  // namespace tq

@@ -46,8 +46,10 @@ constexpr float kSqrtHalfPi = 1.2533141373155003f;   // sqrt(pi/2)
 
 template <int D, int NREP, int KK, int KB, int VK, int VB>
 struct DecodeGeom {
-  static constexpr int KPER = (KB == 3) ? 10 : (KK == TQ_K_AFFINE8 ? 4 : 32 / KB);
-  static constexpr int WK = (KK == TQ_K_AFFINE8) ? D / 4 : (D + KPER - 1) / KPER;
+  static constexpr int KPER = (KB == 3) ? 10 : (KK == TQ_K_AFFINE8 ? (KB == 8 ? 4 : 32 / KB) : 32 / KB);
+  // affine keys: bytes (8 bits), low-nibble plane + fifth-bit plane (5 bits), words of 4/2-bit codes
+  static constexpr int WK = (KK == TQ_K_AFFINE8) ? (KB == 8 ? D / 4 : (KB == 5 ? D / 8 + D / 32 : D * KB / 32))
+                                                 : (D + KPER - 1) / KPER;
   static constexpr int WS = (KK == TQ_K_LM_QJL) ? D / 32 : 0;
   static constexpr int WAK = (KK == TQ_K_AFFINE8) ? D / 32 : (KK == TQ_K_F16 ? 0 : 1);
   static constexpr int VPER = (VB == 3) ? 10 : 32 / VB;
@@ -1005,6 +1007,12 @@ MainKernel find_main_lm2_d128(int nrep, int vk, int vb);
 MainKernel find_main_lm3_d128(int nrep, int vk, int vb);
 MainKernel find_main_lm4_d128(int nrep, int vk, int vb);
 MainKernel find_main_aff8_d128(int nrep, int vk, int vb);
+MainKernel find_main_aff2_d64(int nrep, int vk, int vb);
+MainKernel find_main_aff4_d64(int nrep, int vk, int vb);
+MainKernel find_main_aff5_d64(int nrep, int vk, int vb);
+MainKernel find_main_aff2_d128(int nrep, int vk, int vb);
+MainKernel find_main_aff4_d128(int nrep, int vk, int vb);
+MainKernel find_main_aff5_d128(int nrep, int vk, int vb);
 MainKernel find_main_lm2_d256(int nrep, int vk, int vb);
 MainKernel find_main_lm3_d256(int nrep, int vk, int vb);
 MainKernel find_main_lm4_d256(int nrep, int vk, int vb);

@@ -575,8 +575,9 @@ decode_mma_kernel(const DecodeArgs A) {
         }
       }
     } else {
-      // affine keys: per 32-dimension block, sum_j (c_j - 128) q_j on the matrix cores, then
-      // a times it plus (m + 128 a) times the block's query sum
+      // affine keys: per 32-dimension block, sum_j (c_j - o) q_j on the matrix cores (o = 2^(KB-1),
+      // the codes' centre), then a times it plus (m + o a) times the block's query sum
+      constexpr float kAffOff = (float)(1 << (KB - 1));
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -592,15 +593,39 @@ decode_mma_kernel(const DecodeArgs A) {
         const mma_u4_t bq1 = mma_u4_t{r1.x, r1.y, r1.z, r1.w};
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-          const uint32_t* row = stk + (16 * mb + l16) * M::SK + 8 * kb + 2 * q4;
-          const uint32_t w0 = row[0], w1 = row[1];
-          // bytes c -> fp16 1024 + c (0x64 over the byte) -> c - 128, exact
-          const f16x2_t off = {(_Float16)-1152.f, (_Float16)-1152.f};
+          const uint32_t* krow = stk + (16 * mb + l16) * M::SK;
           mma_u4_t ac;
-          ac[0] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0x64646464u, w0, 0x04010400u)) + off);
-          ac[1] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0x64646464u, w0, 0x04030402u)) + off);
-          ac[2] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0x64646464u, w1, 0x04010400u)) + off);
-          ac[3] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0x64646464u, w1, 0x04030402u)) + off);
+          if constexpr (KB == 8) {
+            const uint32_t w0 = krow[8 * kb + 2 * q4], w1 = krow[8 * kb + 2 * q4 + 1];
+            // bytes c -> fp16 1024 + c (0x64 over the byte) -> c - 128, exact
+            const f16x2_t off = {(_Float16)-1152.f, (_Float16)-1152.f};
+            ac[0] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0x64646464u, w0, 0x04010400u)) + off);
+            ac[1] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0x64646464u, w0, 0x04030402u)) + off);
+            ac[2] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0x64646464u, w1, 0x04010400u)) + off);
+            ac[3] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0x64646464u, w1, 0x04030402u)) + off);
+          } else {
+            // 5/4/2-bit codes c of dimensions 32 kb + 8 q4 .. + 7 -> fp16 1024 + c -> c - 2^(KB-1), exact
+            constexpr float kOff = 1024.f + (float)(1 << (KB - 1));
+            const f16x2_t off = {(_Float16)-kOff, (_Float16)-kOff};
+            uint32_t c8[8];
+            if constexpr (KB == 2) {
+              const uint32_t w = krow[2 * kb + (q4 >> 1)] >> (16 * (q4 & 1));
+#pragma unroll
+              for (int i = 0; i < 8; ++i) c8[i] = (w >> (2 * i)) & 3u;
+            } else {
+              const uint32_t w = krow[4 * kb + q4];        // eight low nibbles
+#pragma unroll
+              for (int i = 0; i < 8; ++i) c8[i] = (w >> (4 * i)) & 15u;
+              if constexpr (KB == 5) {
+                const uint32_t hb = krow[D / 8 + kb] >> (8 * q4);   // their fifth bits
+#pragma unroll
+                for (int i = 0; i < 8; ++i) c8[i] |= ((hb >> i) & 1u) << 4;
+              }
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              ac[k] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, (0x6400u | c8[2 * k]) | ((0x6400u | c8[2 * k + 1]) << 16)) + off);
+          }
           mma_f4_t t = mma16(ac, bq0, mma_f4_t{0.f, 0.f, 0.f, 0.f});
           t = mma16(ac, bq1, t);
           const uint4 aw = *reinterpret_cast<const uint4*>(stak + kb * M::TS + 16 * mb + 4 * q4);
@@ -608,7 +633,7 @@ decode_mma_kernel(const DecodeArgs A) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const float a = f16_to_f32(am[r] & 0xFFFFu), m = f16_to_f32(am[r] >> 16);
-            p[mb][r] = fmaf(a, t[r], fmaf(fmaf(128.f, a, m), qsum[kb], p[mb][r]));
+            p[mb][r] = fmaf(a, t[r], fmaf(fmaf(kAffOff, a, m), qsum[kb], p[mb][r]));
           }
         }
       }

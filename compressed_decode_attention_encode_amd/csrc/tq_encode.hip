@@ -554,7 +554,7 @@ template <int D, int DT, int QB = 8>
 __global__ void __launch_bounds__(256)
 encode_affine8_kernel(const uint16_t* __restrict__ x, int T, int slices, int dst_offset, int cap,
                       uint32_t* __restrict__ codes_out, uint32_t* __restrict__ aux_out) {
-  static_assert(QB == 8 || QB == 4 || QB == 2, "8-bit keys, 2/4-bit values");
+  static_assert(QB == 8 || QB == 5 || QB == 4 || QB == 2, "8/5/4/2-bit keys, 2/4-bit values");
   constexpr int G = D / 32;
   constexpr int TOP = (1 << QB) - 1;
   const int parts = T * (D / 8);
@@ -610,13 +610,25 @@ encode_affine8_kernel(const uint16_t* __restrict__ x, int T, int slices, int dst
           qf = passes64((double)ve, fma(a, (double)bf - 0.5, m), (int)bf) ? bf : bf - 1.f;
           qf = fminf(fmaxf(qf, 0.f), (float)TOP);
         }
-        if constexpr (QB == 8) words[e >> 2] |= (uint32_t)qf << (8 * (e & 3));
-        else words[0] |= (uint32_t)qf << (QB * e);
+        if constexpr (QB == 8) {
+          words[e >> 2] |= (uint32_t)qf << (8 * (e & 3));
+        } else if constexpr (QB == 5) {
+          words[0] |= ((uint32_t)qf & 15u) << (4 * e);        // low nibble
+          words[1] |= ((uint32_t)qf >> 4) << (8 * sub + e);    // fifth bit, at the group's bit 8 sub + e
+        } else {
+          words[0] |= (uint32_t)qf << (QB * e);
+        }
       }
+      if constexpr (QB == 5) words[1] |= xor_lanes_u32<1>(words[1]), words[1] |= xor_lanes_u32<2>(words[1]);
       if (p < parts) {
         const size_t row = row_s + t;
         if constexpr (QB == 8) {
           *reinterpret_cast<uint2*>(codes_out + row * (D / 4) + 8 * g + 2 * sub) = make_uint2(words[0], words[1]);
+        } else if constexpr (QB == 5) {
+          // row: D/8 words of low nibbles, then D/32 words of fifth bits
+          constexpr int W5 = D / 8 + D / 32;
+          codes_out[row * W5 + g * 4 + sub] = words[0];
+          if (sub == 0) codes_out[row * W5 + D / 8 + g] = words[1];
         } else if constexpr (QB == 4) {
           codes_out[row * (D / 8) + g * 4 + sub] = words[0];                                  // 8 codes = one word
         } else {
@@ -722,11 +734,11 @@ hipError_t run_minmax_v(const tq_layout& Lay, const void* x, int batch, int T, i
   return hipGetLastError();
 }
 
-template <int D, int DT>
+template <int D, int DT, int QB>
 hipError_t run_affine(const tq_layout& Lay, const void* x, int batch, int T, int dst, const tq_cache& C,
                       hipStream_t st) {
   const int slices = batch * Lay.n_kv_heads;
-  hipLaunchKernelGGL((encode_affine8_kernel<D, DT>), group_grid(slices, T, D), dim3(256), 0, st,
+  hipLaunchKernelGGL((encode_affine8_kernel<D, DT, QB>), group_grid(slices, T, D), dim3(256), 0, st,
                      (const uint16_t*)x, T, slices, dst, C.capacity, (uint32_t*)C.k_codes, (uint32_t*)C.k_aux);
   return hipGetLastError();
 }
@@ -759,7 +771,8 @@ bool encode_k_compiled(const tq_layout& L) {
   const bool d_ok = L.head_dim == 64 || L.head_dim == 128 || L.head_dim == 256;
   const bool dt_ok = L.in_dtype == TQ_F16 || L.in_dtype == TQ_BF16;
   if (L.k_kind == TQ_K_LM_QJL || L.k_kind == TQ_K_LM_MSE) return d_ok && dt_ok && L.k_bits >= 2 && L.k_bits <= 4;
-  if (L.k_kind == TQ_K_AFFINE8) return d_ok && dt_ok && L.k_bits == 8;
+  if (L.k_kind == TQ_K_AFFINE8)
+    return d_ok && dt_ok && (L.k_bits == 8 || L.k_bits == 5 || L.k_bits == 4 || L.k_bits == 2);
   if (L.k_kind == TQ_K_F16) return d_ok && dt_ok && L.k_bits == 16;
   return false;
 }
@@ -791,7 +804,13 @@ hipError_t launch_encode_k(const tq_layout& L, const tq_state& S, const void* k,
         err = (run_lm<DD, BB, DTT, false>(L, S, k, batch, n_tokens, dst_offset, C, st, false));)))
   } else {
     TQ_D_SWITCH(L.head_dim, TQ_DT_SWITCH(L.in_dtype,
-        err = (run_affine<DD, DTT>(L, k, batch, n_tokens, dst_offset, C, st));))
+        switch (L.k_bits) {
+          case 8: err = (run_affine<DD, DTT, 8>(L, k, batch, n_tokens, dst_offset, C, st)); break;
+          case 5: err = (run_affine<DD, DTT, 5>(L, k, batch, n_tokens, dst_offset, C, st)); break;
+          case 4: err = (run_affine<DD, DTT, 4>(L, k, batch, n_tokens, dst_offset, C, st)); break;
+          case 2: err = (run_affine<DD, DTT, 2>(L, k, batch, n_tokens, dst_offset, C, st)); break;
+          default: break;
+        }))
   }
   return err;
 }

@@ -86,6 +86,15 @@ __global__ void __launch_bounds__(256) materialize_elem_kernel(const uint32_t* _
       v[e] = fmaf(a, (float)((w.x >> (8 * e)) & 0xFFu), m);
       v[4 + e] = fmaf(a, (float)((w.y >> (8 * e)) & 0xFFu), m);
     }
+  } else if constexpr (KIND == 4) {
+    // 5-bit affine keys: low nibbles (D/8 words), then the fifth bits (D/32 words)
+    constexpr int W5 = D / 8 + D / 32;
+    const uint32_t w = codes[row * W5 + o];
+    const uint32_t hb = codes[row * W5 + D / 8 + g] >> (8 * (o & 3));
+    const uint32_t am = aux[row * (D / 32) + g];
+    const float a = f16_to_f32(am & 0xFFFFu), m = f16_to_f32(am >> 16);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = fmaf(a, (float)(((w >> (4 * e)) & 15u) | (((hb >> e) & 1u) << 4)), m);
   } else if constexpr (KIND == 3) {
     constexpr int L = 1 << VB;
     constexpr int WR = D * VB / 32;
@@ -401,10 +410,22 @@ hipError_t launch_materialize_k(const tq_layout& L, const tq_state& S, const tq_
                                   : run_elem_d<2, TQ_F16, TQ_F16>(L.head_dim, codes, nullptr, slices, C.capacity, t0, n, o, st);
   }
   if (L.k_kind == TQ_K_AFFINE8) {
+    // m + a q per element: bytes (kind 0), nibble + fifth-bit planes (kind 4), 4/2-bit words (kind 3,
+    // the min/max value layout)
     const uint32_t* codes = static_cast<const uint32_t*>(C.k_codes);
     const uint32_t* aux = static_cast<const uint32_t*>(C.k_aux);
-    return (out_dtype == TQ_BF16) ? run_elem_d<0, 8, TQ_BF16>(L.head_dim, codes, aux, slices, C.capacity, t0, n, o, st)
-                                  : run_elem_d<0, 8, TQ_F16>(L.head_dim, codes, aux, slices, C.capacity, t0, n, o, st);
+    const bool bf = out_dtype == TQ_BF16;
+    switch (L.k_bits) {
+      case 8: return bf ? run_elem_d<0, 8, TQ_BF16>(L.head_dim, codes, aux, slices, C.capacity, t0, n, o, st)
+                        : run_elem_d<0, 8, TQ_F16>(L.head_dim, codes, aux, slices, C.capacity, t0, n, o, st);
+      case 5: return bf ? run_elem_d<4, 5, TQ_BF16>(L.head_dim, codes, aux, slices, C.capacity, t0, n, o, st)
+                        : run_elem_d<4, 5, TQ_F16>(L.head_dim, codes, aux, slices, C.capacity, t0, n, o, st);
+      case 4: return bf ? run_elem_d<3, 4, TQ_BF16>(L.head_dim, codes, aux, slices, C.capacity, t0, n, o, st)
+                        : run_elem_d<3, 4, TQ_F16>(L.head_dim, codes, aux, slices, C.capacity, t0, n, o, st);
+      case 2: return bf ? run_elem_d<3, 2, TQ_BF16>(L.head_dim, codes, aux, slices, C.capacity, t0, n, o, st)
+                        : run_elem_d<3, 2, TQ_F16>(L.head_dim, codes, aux, slices, C.capacity, t0, n, o, st);
+      default: return hipErrorInvalidValue;
+    }
   }
   const bool qjl = L.k_kind == TQ_K_LM_QJL;   // MSE-only keys: centroids and fp32 n alone
   LmArgs A{};

@@ -100,6 +100,10 @@ WORKLOADS = {
     "qwen32b_r1_h40x8_d128_b4_t32k": Workload(
         "qwen32b_r1_h40x8_d128_b4_t32k", 110, 4, 40, 8, 128, 32768, 128,
         "lm_qjl", 2, "group_asym", 2, "bf16", "f16"),
+    # the vllm-metal guide's low-memory row (q4_0 keys, q3_0 values) on the Qwen3-0.6B-like geometry
+    "qwen0p6b_q4k_h16x4_d128_b8_t64k": Workload(
+        "qwen0p6b_q4k_h16x4_d128_b8_t64k", 111, 8, 16, 4, 128, 65536, 0,
+        "affine8", 4, "lm_rot", 3, "f16", "f16"),
     "qwen7b_k8v4_h28x4_d128_b16_t32k": Workload(
         "qwen7b_k8v4_h28x4_d128_b16_t32k", 108, 16, 28, 4, 128, 32768, 128,
         "affine8", 8, "lm_rot", 4, "bf16", "f16", "studentt3x10", 4, flush_tokens=128),

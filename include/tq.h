@@ -66,8 +66,11 @@ typedef enum { TQ_F16 = 0, TQ_BF16 = 1 } tq_dtype;
  *   (Lloyd-Max, k_bits in {2,3,4}), r = y - c[idx], gamma = |r|, one QJL bit per
  *   dimension: bit_j = (z_j >= 0), z = S r (S the d x d Gaussian matrix).
  * TQ_K_AFFINE8 (vllm-metal guide, quantisation principle table: per-block affine,
- *   no rotation): per 32-block a = fp16((max-min)/255), m = fp16(min),
- *   q = clamp(rne((k - m)/a), 0, 255)  (q = 0 where a = 0). k_bits must be 8.      */
+ *   no rotation; its compression-ratio table: q8_0, q5_0, q4_0 and the 2-bit uint2/int2
+ *   key widths): per 32-block a = fp16((max-min)/(2^k_bits - 1)), m = fp16(min),
+ *   q = clamp(rne((k - m)/a), 0, 2^k_bits - 1)  (q = 0 where a = 0); k_bits 8, 5, 4 or 2.
+ *   Decode of the 5/4/2-bit widths is compiled for head_dim 64 and 128 with rotated
+ *   Lloyd-Max values (TQ_ERR_UNSUPPORTED otherwise).                                */
 typedef enum { TQ_K_LM_QJL = 0, TQ_K_AFFINE8 = 1, TQ_K_LM_MSE = 2, TQ_K_F16 = 3 } tq_kkind;
 
 /* Value encodings.
@@ -90,7 +93,7 @@ typedef struct {
   int32_t n_kv_heads;    /* Hkv; Hq % Hkv == 0; n_rep = Hq/Hkv in 1..8; q-head h reads
                             kv-head floor(h / n_rep)                                    */
   int32_t k_kind;        /* tq_kkind                                                    */
-  int32_t k_bits;        /* 2, 3, 4 (LM_QJL) or 8 (AFFINE8)                             */
+  int32_t k_bits;        /* 2, 3, 4 (LM_QJL / LM_MSE); 8, 5, 4, 2 (AFFINE8); 16 (F16)     */
   int32_t v_kind;        /* tq_vkind                                                    */
   int32_t v_bits;        /* 2, 4 (GROUP_SYM) or 2, 3, 4 (LM_ROT)                        */
   int32_t in_dtype;      /* tq_dtype of K/V passed to tq_encode and of q                */
@@ -123,7 +126,10 @@ typedef struct {
  *   k_codes  LM_QJL: uint32[W], b-bit code j in bits b*(j%P).. of word j/P, P = 16/10/8
  *                    codes per word for b = 2/3/4 (3-bit: bits 30..31 zero; MLX page:
  *                    ten 3-bit codes per uint32; vLLM guide: four 2-bit codes per byte)
- *            AFFINE8: uint8[d], byte j = code j
+ *            AFFINE8: k_bits 8: uint8[d], byte j = code j;  k_bits 4 / 2: packed like the
+ *                    LM codes (8 / 16 per word);  k_bits 5: uint32[d/8] low nibbles (code j's
+ *                    low 4 bits at bits 4 (j%8) of word j/8), then uint32[d/32] fifth bits
+ *                    (bit j%32 of word d/8 + j/32)
  *   k_signs  LM_QJL: uint32[d/32], bit j%32 of word j/32 = QJL bit j   (else unused)
  *   k_aux    LM_QJL: fp16[2] = (n, gamma);  AFFINE8: fp16[d/32][2] = (a, m) per block;
  *            LM_MSE: fp32 n  (LM_MSE codes are packed like LM_QJL codes)

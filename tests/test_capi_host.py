@@ -53,6 +53,7 @@ def test_rotation_state_matches_reference_generator(d):
 
 
 CONFIGS = [(64, "lm_qjl", 3, "group_sym", 2), (128, "lm_qjl", 4, "group_sym", 4), (128, "affine8", 8, "lm_rot", 3),
+           (128, "affine8", 5, "lm_rot", 3), (64, "affine8", 4, "lm_rot", 2), (128, "affine8", 2, "lm_rot", 2),
            (256, "lm_qjl", 4, "group_sym", 4), (128, "lm_qjl", 2, "lm_rot", 2), (128, "lm_qjl", 2, "group_asym", 2),
            (64, "lm_qjl", 3, "group_asym", 4)]
 
@@ -89,7 +90,8 @@ def _cache(batch=1, cap=256):
     (dict(head_dim=96), tq.TQ_ERR_UNSUPPORTED),
     (dict(n_q_heads=7), tq.TQ_ERR_UNSUPPORTED),
     (dict(k_bits=5), tq.TQ_ERR_UNSUPPORTED),
-    (dict(k_kind="affine8", k_bits=4), tq.TQ_ERR_UNSUPPORTED),
+    (dict(k_kind="affine8", k_bits=3), tq.TQ_ERR_UNSUPPORTED),
+    (dict(k_kind="affine8", k_bits=6), tq.TQ_ERR_UNSUPPORTED),
     (dict(v_bits=3), tq.TQ_ERR_UNSUPPORTED),
     (dict(v_kind="lm_rot", v_bits=5), tq.TQ_ERR_UNSUPPORTED),
     (dict(n_kv_heads=0), tq.TQ_ERR_INVALID),
@@ -265,3 +267,17 @@ def test_one_hip_runtime_in_process():
     # libtq must share torch's HIP runtime (device pointers and streams come from torch)
     loaded = tq._hip_runtimes_loaded()
     assert len(loaded) == 1, loaded
+
+
+def test_narrow_affine_key_decode_limits():
+    """5/4/2-bit affine keys decode with rotated values at head_dim 64/128; other combinations
+    fail loudly before any HIP call."""
+    ws = 1 << 30
+    for bad in (dict(head_dim=256, k_kind="affine8", k_bits=4, v_kind="lm_rot", v_bits=3),
+                dict(head_dim=128, k_kind="affine8", k_bits=5, v_kind="group_sym", v_bits=2)):
+        with pytest.raises(tq.TQError) as e:
+            tq.tq_decode_attn(_layout(**bad), _state(), FAKE, _cache(), 100, None, None, 0, 0, FAKE, FAKE, ws)
+        assert e.value.status == tq.TQ_ERR_UNSUPPORTED
+    sizes = tq.tq_cache_plane_bytes(_layout(head_dim=128, k_kind="affine8", k_bits=5, v_kind="lm_rot", v_bits=3), 1, 10)
+    assert sizes[0] == 4 * (128 // 8 + 128 // 32) * 10 * 2 and sizes[1] == 0   # 5 bits per code, 2 kv-heads
+

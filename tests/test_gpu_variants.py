@@ -1,7 +1,7 @@
 """GPU parity over the compiled variants the benchmark workloads do not reach.
 
 Every kernel family (2/3/4-bit Lloyd-Max + QJL keys, MSE-only Lloyd-Max keys, per-block
-affine keys, group-32 and rotated Lloyd-Max values, head_dim 64/128/256, n_rep 1..8, fp16/bf16 inputs) is
+affine keys at 8/5/4/2 bits, group-32 and rotated Lloyd-Max values, head_dim 64/128/256, n_rep 1..8, fp16/bf16 inputs) is
 encoded and decoded at a small, ragged size against the CPU oracle, and degenerate
 vectors (all zero, constant, a single non-zero element, signed zeros, subnormals) go
 through both sides.
@@ -62,6 +62,14 @@ VARIANTS = [
     (64, "lm_qjl", 3, "group_asym", 2, 2, 2, "f16", 200, 5),
     (128, "lm_qjl", 3, "group_asym", 4, 10, 2, "bf16", 260, 0),
     (128, "lm_qjl", 2, "group_asym", 2, 16, 2, "f16", 222, 64),
+    # 5/4/2-bit affine keys with rotated values (matrix cores at every n_rep)
+    (128, "affine8", 5, "lm_rot", 3, 16, 4, "f16", 300, 17),
+    (64, "affine8", 5, "lm_rot", 2, 2, 2, "bf16", 230, 0),
+    (128, "affine8", 4, "lm_rot", 3, 4, 2, "bf16", 260, 9),
+    (64, "affine8", 4, "lm_rot", 4, 14, 2, "f16", 222, 40),
+    (128, "affine8", 2, "lm_rot", 3, 8, 1, "f16", 333, 5),
+    (128, "affine8", 2, "lm_rot", 2, 6, 2, "bf16", 190, 64),
+    (64, "affine8", 2, "lm_rot", 2, 10, 2, "f16", 250, 0),
 ]
 
 
