@@ -105,11 +105,11 @@ __global__ void __launch_bounds__(256) decode_finish_kernel(const DecodeArgs A) 
   }
   __syncthreads();
   if constexpr (VK == TQ_V_LM_ROT) {
-    if (tid < D) {
+    for (int j = tid; j < D; j += 256) {
       float a = 0.f;
 #pragma unroll
-      for (int q = 0; q < SG; ++q) a += s_rot[q][tid];
-      s_rot[0][tid] = a;
+      for (int q = 0; q < SG; ++q) a += s_rot[q][j];
+      s_rot[0][j] = a;
     }
     __syncthreads();
     // Pi^T acc = diag(s) H acc / sqrt(d): butterflies in LDS
@@ -206,6 +206,7 @@ int device_cus() {
 MainKernel find_main(const tq_layout& L) {
   const int nrep = L.n_q_heads / L.n_kv_heads;
   const int d = L.head_dim, vk = L.v_kind, vb = L.v_bits;
+  if (d == 512) return find_main_d512(L);
 #define TQ_BY_D(name)                                                   \
   switch (d) {                                                          \
     case 64: return name##_d64(nrep, vk, vb);                           \
@@ -336,7 +337,7 @@ hipError_t run_decode_d(const tq_layout& L, const tq_state& S, const void* q, co
 }  // namespace
 
 bool decode_compiled(const tq_layout& L) {
-  if (!(L.head_dim == 64 || L.head_dim == 128 || L.head_dim == 256)) return false;
+  if (!(L.head_dim == 64 || L.head_dim == 128 || L.head_dim == 256 || L.head_dim == 512)) return false;
   if (L.n_kv_heads <= 0 || L.n_q_heads % L.n_kv_heads) return false;
   return find_main(L).launch != nullptr;
 }
@@ -349,6 +350,7 @@ hipError_t launch_decode(const tq_layout& L, const tq_state& S, const void* q, c
     case 64: return run_decode_d<64>(L, S, q, C, n_c, rk, rv, n_recent, rcap, out, ws, plan, st, mk, 1);
     case 128: return run_decode_d<128>(L, S, q, C, n_c, rk, rv, n_recent, rcap, out, ws, plan, st, mk, 1);
     case 256: return run_decode_d<256>(L, S, q, C, n_c, rk, rv, n_recent, rcap, out, ws, plan, st, mk, 1);
+    case 512: return run_decode_d<512>(L, S, q, C, n_c, rk, rv, n_recent, rcap, out, ws, plan, st, mk, 1);
     default: return hipErrorInvalidValue;
   }
 }

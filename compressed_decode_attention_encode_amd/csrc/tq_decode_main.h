@@ -1031,6 +1031,8 @@ MainKernel find_main_f16_d128(int nrep, int vk, int vb);
 // 16-bit keys in fp16 storage on the matrix cores (n_rep 3..8)
 MainKernel find_mma_f16_d64(int nrep, int vk, int vb);
 MainKernel find_mma_f16_d256(int nrep, int vk, int vb);
+// head_dim 512: every key / value kind on vector-ALU kernels, n_rep <= 8
+MainKernel find_main_d512(const tq_layout& L);
 // multi-query groups (LM + QJL keys, group values): n_rep heads x nq queries, vb value bits
 MainKernel find_multi_lm3_d64(int nrep, int nq, int vb);
 MainKernel find_multi_lm4_d64(int nrep, int nq, int vb);

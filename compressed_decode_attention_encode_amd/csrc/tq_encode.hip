@@ -751,6 +751,15 @@ hipError_t run_affine(const tq_layout& Lay, const void* x, int batch, int T, int
     case 256: { constexpr int DD = 256; __VA_ARGS__ } break;  \
     default: break;                                           \
   }
+// the same with head_dim 512 (the generic group / affine / copy kernels)
+#define TQ_D5_SWITCH(d, ...)                                  \
+  switch (d) {                                                \
+    case 64: { constexpr int DD = 64; __VA_ARGS__ } break;    \
+    case 128: { constexpr int DD = 128; __VA_ARGS__ } break;  \
+    case 256: { constexpr int DD = 256; __VA_ARGS__ } break;  \
+    case 512: { constexpr int DD = 512; __VA_ARGS__ } break;  \
+    default: break;                                           \
+  }
 #define TQ_DT_SWITCH(dt, ...)                                 \
   switch (dt) {                                               \
     case TQ_F16: { constexpr int DTT = TQ_F16; __VA_ARGS__ } break; \
@@ -768,7 +777,7 @@ hipError_t run_affine(const tq_layout& Lay, const void* x, int batch, int T, int
 }  // namespace
 
 bool encode_k_compiled(const tq_layout& L) {
-  const bool d_ok = L.head_dim == 64 || L.head_dim == 128 || L.head_dim == 256;
+  const bool d_ok = L.head_dim == 64 || L.head_dim == 128 || L.head_dim == 256 || L.head_dim == 512;
   const bool dt_ok = L.in_dtype == TQ_F16 || L.in_dtype == TQ_BF16;
   if (L.k_kind == TQ_K_LM_QJL || L.k_kind == TQ_K_LM_MSE) return d_ok && dt_ok && L.k_bits >= 2 && L.k_bits <= 4;
   if (L.k_kind == TQ_K_AFFINE8)
@@ -778,7 +787,7 @@ bool encode_k_compiled(const tq_layout& L) {
 }
 
 bool encode_v_compiled(const tq_layout& L) {
-  const bool d_ok = L.head_dim == 64 || L.head_dim == 128 || L.head_dim == 256;
+  const bool d_ok = L.head_dim == 64 || L.head_dim == 128 || L.head_dim == 256 || L.head_dim == 512;
   const bool dt_ok = L.in_dtype == TQ_F16 || L.in_dtype == TQ_BF16;
   if (L.v_kind == TQ_V_GROUP_SYM || L.v_kind == TQ_V_GROUP_ASYM) return d_ok && dt_ok && (L.v_bits == 2 || L.v_bits == 4);
   if (L.v_kind == TQ_V_LM_ROT) return d_ok && dt_ok && L.v_bits >= 2 && L.v_bits <= 4;
@@ -788,6 +797,8 @@ bool encode_v_compiled(const tq_layout& L) {
 hipError_t launch_encode_k(const tq_layout& L, const tq_state& S, const void* k, int batch, int n_tokens,
                            int dst_offset, const tq_cache& C, hipStream_t st) {
   hipError_t err = hipErrorInvalidValue;
+  if (L.head_dim == 512 && (L.k_kind == TQ_K_LM_QJL || L.k_kind == TQ_K_LM_MSE))
+    return launch_encode_lm512(L, S, k, batch, n_tokens, dst_offset, C, st, false);
   if (L.k_kind == TQ_K_LM_QJL) {
     TQ_D_SWITCH(L.head_dim, TQ_B_SWITCH(L.k_bits, TQ_DT_SWITCH(L.in_dtype,
         err = (run_lm<DD, BB, DTT, true>(L, S, k, batch, n_tokens, dst_offset, C, st, false));)))
@@ -803,7 +814,7 @@ hipError_t launch_encode_k(const tq_layout& L, const tq_state& S, const void* k,
     TQ_D_SWITCH(L.head_dim, TQ_B_SWITCH(L.k_bits, TQ_DT_SWITCH(L.in_dtype,
         err = (run_lm<DD, BB, DTT, false>(L, S, k, batch, n_tokens, dst_offset, C, st, false));)))
   } else {
-    TQ_D_SWITCH(L.head_dim, TQ_DT_SWITCH(L.in_dtype,
+    TQ_D5_SWITCH(L.head_dim, TQ_DT_SWITCH(L.in_dtype,
         switch (L.k_bits) {
           case 8: err = (run_affine<DD, DTT, 8>(L, k, batch, n_tokens, dst_offset, C, st)); break;
           case 5: err = (run_affine<DD, DTT, 5>(L, k, batch, n_tokens, dst_offset, C, st)); break;
@@ -818,12 +829,14 @@ hipError_t launch_encode_k(const tq_layout& L, const tq_state& S, const void* k,
 hipError_t launch_encode_v(const tq_layout& L, const tq_state& S, const void* v, int batch, int n_tokens,
                            int dst_offset, const tq_cache& C, hipStream_t st) {
   hipError_t err = hipErrorInvalidValue;
+  if (L.head_dim == 512 && L.v_kind == TQ_V_LM_ROT)
+    return launch_encode_lm512(L, S, v, batch, n_tokens, dst_offset, C, st, true);
   if (L.v_kind == TQ_V_GROUP_SYM) {
-    TQ_D_SWITCH(L.head_dim, TQ_DT_SWITCH(L.in_dtype,
+    TQ_D5_SWITCH(L.head_dim, TQ_DT_SWITCH(L.in_dtype,
         if (L.v_bits == 2) err = (run_group<DD, 2, DTT>(L, v, batch, n_tokens, dst_offset, C, st));
         else err = (run_group<DD, 4, DTT>(L, v, batch, n_tokens, dst_offset, C, st));))
   } else if (L.v_kind == TQ_V_GROUP_ASYM) {
-    TQ_D_SWITCH(L.head_dim, TQ_DT_SWITCH(L.in_dtype,
+    TQ_D5_SWITCH(L.head_dim, TQ_DT_SWITCH(L.in_dtype,
         if (L.v_bits == 2) err = (run_minmax_v<DD, 2, DTT>(L, v, batch, n_tokens, dst_offset, C, st));
         else err = (run_minmax_v<DD, 4, DTT>(L, v, batch, n_tokens, dst_offset, C, st));))
   } else {

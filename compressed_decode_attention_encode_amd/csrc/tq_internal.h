@@ -62,6 +62,14 @@ hipError_t launch_materialize_k(const tq_layout& L, const tq_state& S, const tq_
 hipError_t launch_materialize_v(const tq_layout& L, const tq_state& S, const tq_cache& C, int t0, int n_tokens,
                                 void* out, int out_dtype, hipStream_t st);
 
+// head_dim 512, rotated kinds (the other kinds use the generic templates).
+hipError_t launch_encode_lm512(const tq_layout& L, const tq_state& S, const void* x, int batch, int n_tokens,
+                               int dst_offset, const tq_cache& C, hipStream_t st, bool values);
+hipError_t launch_materialize_lm512(const uint32_t* codes, const uint32_t* signs, const uint32_t* aux,
+                                    const float* cent, const uint32_t* rsign, const uint16_t* S, int bits, bool qjl,
+                                    long slices, int n, int cap, int t0, uint16_t* out, int out_dtype,
+                                    hipStream_t st);
+
 // Whether a kernel instantiation exists for this layout.
 bool encode_k_compiled(const tq_layout& L);
 bool encode_v_compiled(const tq_layout& L);

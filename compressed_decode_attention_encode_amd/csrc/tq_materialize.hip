@@ -387,6 +387,7 @@ hipError_t run_elem_d(int d, const uint32_t* codes, const uint32_t* aux, int sli
     case 64: return run_elem<64, KIND, VB, OUT>(codes, aux, slices, cap, t0, n, out, st);
     case 128: return run_elem<128, KIND, VB, OUT>(codes, aux, slices, cap, t0, n, out, st);
     case 256: return run_elem<256, KIND, VB, OUT>(codes, aux, slices, cap, t0, n, out, st);
+    case 512: return run_elem<512, KIND, VB, OUT>(codes, aux, slices, cap, t0, n, out, st);
   }
   return hipErrorInvalidValue;
 }
@@ -394,7 +395,7 @@ hipError_t run_elem_d(int d, const uint32_t* codes, const uint32_t* aux, int sli
 }  // namespace
 
 bool materialize_compiled(const tq_layout& L) {
-  return L.head_dim == 64 || L.head_dim == 128 || L.head_dim == 256;
+  return L.head_dim == 64 || L.head_dim == 128 || L.head_dim == 256 || L.head_dim == 512;
 }
 
 hipError_t launch_materialize_k(const tq_layout& L, const tq_state& S, const tq_cache& C, int t0, int n,
@@ -428,6 +429,11 @@ hipError_t launch_materialize_k(const tq_layout& L, const tq_state& S, const tq_
     }
   }
   const bool qjl = L.k_kind == TQ_K_LM_QJL;   // MSE-only keys: centroids and fp32 n alone
+  if (L.head_dim == 512)
+    return launch_materialize_lm512(static_cast<const uint32_t*>(C.k_codes),
+                                    qjl ? static_cast<const uint32_t*>(C.k_signs) : nullptr,
+                                    static_cast<const uint32_t*>(C.k_aux), S.k_centroids, S.k_signs,
+                                    qjl ? S.qjl : nullptr, L.k_bits, qjl, slices, n, C.capacity, t0, o, out_dtype, st);
   LmArgs A{};
   A.codes = static_cast<const uint32_t*>(C.k_codes);
   A.signs = qjl ? static_cast<const uint32_t*>(C.k_signs) : nullptr;
@@ -465,6 +471,9 @@ hipError_t launch_materialize_v(const tq_layout& L, const tq_state& S, const tq_
     return (out_dtype == TQ_BF16) ? run_elem_d<1, 4, TQ_BF16>(L.head_dim, codes, aux, slices, C.capacity, t0, n, o, st)
                                   : run_elem_d<1, 4, TQ_F16>(L.head_dim, codes, aux, slices, C.capacity, t0, n, o, st);
   }
+  if (L.head_dim == 512)
+    return launch_materialize_lm512(codes, nullptr, aux, S.v_centroids, S.v_signs, nullptr, L.v_bits, false, slices, n,
+                                    C.capacity, t0, o, out_dtype, st);
   LmArgs A{};
   A.codes = codes;
   A.signs = nullptr;

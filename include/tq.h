@@ -56,7 +56,8 @@ typedef enum { TQ_F16 = 0, TQ_BF16 = 1 } tq_dtype;
 /* Key encodings.
  * TQ_K_F16     (MLX page, V-only mode: keys stay 16-bit, only the values are compressed):
  *   the key row is stored as given (layout->in_dtype bits); k_bits must be 16; decode
- *   is compiled for head_dim 64 and 128 (TQ_ERR_UNSUPPORTED for 256).
+ *   is compiled for head_dim 64, 128 and 512, and for 256 with fp16 keys
+ *   (TQ_ERR_UNSUPPORTED for bf16 keys at 256).
  * TQ_K_LM_MSE  (vLLM guide section 2 steps 1-2 only: the MSE-optimal codes without the
  *   QJL residual sketch; vLLM guide, MSE score kernel): n = |k| stored fp32, y = Pi k/n,
  *   idx_j = #{i : t_i < y_j} (k_bits in {2,3,4}); decoded key n Pi^T c[idx].  Its
@@ -70,7 +71,7 @@ typedef enum { TQ_F16 = 0, TQ_BF16 = 1 } tq_dtype;
  *   key widths): per 32-block a = fp16((max-min)/(2^k_bits - 1)), m = fp16(min),
  *   q = clamp(rne((k - m)/a), 0, 2^k_bits - 1)  (q = 0 where a = 0); k_bits 8, 5, 4 or 2.
  *   Decode of the 5/4/2-bit widths is compiled for head_dim 64 and 128 with rotated
- *   Lloyd-Max values (TQ_ERR_UNSUPPORTED otherwise).                                */
+ *   Lloyd-Max values, and for 512 with every value kind (TQ_ERR_UNSUPPORTED otherwise). */
 typedef enum { TQ_K_LM_QJL = 0, TQ_K_AFFINE8 = 1, TQ_K_LM_MSE = 2, TQ_K_F16 = 3 } tq_kkind;
 
 /* Value encodings.
@@ -88,7 +89,8 @@ typedef enum { TQ_K_LM_QJL = 0, TQ_K_AFFINE8 = 1, TQ_K_LM_MSE = 2, TQ_K_F16 = 3 
 typedef enum { TQ_V_GROUP_SYM = 0, TQ_V_LM_ROT = 1, TQ_V_GROUP_ASYM = 2 } tq_vkind;
 
 typedef struct {
-  int32_t head_dim;      /* d in {64, 128, 256}                                          */
+  int32_t head_dim;      /* d in {64, 128, 256, 512} (512: one-wave-per-token kernels,   *
+                          * every key / value kind, n_rep <= 8 in decode)               */
   int32_t n_q_heads;     /* Hq                                                          */
   int32_t n_kv_heads;    /* Hkv; Hq % Hkv == 0; n_rep = Hq/Hkv in 1..8; q-head h reads
                             kv-head floor(h / n_rep)                                    */
@@ -284,8 +286,8 @@ int tq_decode_attn_multi(const tq_layout* layout, const tq_state* state, const v
  *   out_dtype     TQ_F16 or TQ_BF16
  * The state fields the decode needs for a half are needed here too.  Errors:
  * TQ_ERR_INVALID for both outputs NULL, null/misaligned pointers or negative sizes;
- * TQ_ERR_CAPACITY if t0 + n_tokens > cache->capacity; TQ_ERR_UNSUPPORTED for head_dim
- * 512, an unknown out_dtype or batch * n_kv_heads * n_tokens * head_dim / 8 >= 2^31
+ * TQ_ERR_CAPACITY if t0 + n_tokens > cache->capacity; TQ_ERR_UNSUPPORTED for an
+ * unknown out_dtype or batch * n_kv_heads * n_tokens * head_dim / 8 >= 2^31
  * (split such a call); TQ_ERR_HIP.  n_tokens == 0 is a no-op.                       */
 int tq_materialize(const tq_layout* layout, const tq_state* state, const tq_cache* cache, int t0, int n_tokens,
                    void* out_k, void* out_v, int out_dtype, void* stream);

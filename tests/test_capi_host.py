@@ -123,10 +123,26 @@ def test_encode_rejects_bad_arguments():
         assert e.value.status == code, (over, e.value)
 
 
-def test_encode_unsupported_head_dim_512_is_loud():
+def test_encode_unsupported_head_dim_is_loud():
+    """head_dim 64 / 128 / 256 / 512 are the supported set; 1024 fails before any HIP call."""
     with pytest.raises(tq.TQError) as e:
-        tq.tq_encode(_layout(head_dim=512), _state(), FAKE, FAKE, 1, 16, 0, _cache())
+        tq.tq_encode(_layout(head_dim=1024), _state(), FAKE, FAKE, 1, 16, 0, _cache())
     assert e.value.status == tq.TQ_ERR_UNSUPPORTED
+
+
+def test_head_dim_512_decode_limits():
+    """head_dim 512 decodes every key / value kind up to n_rep 8; n_rep 9 fails loudly before any
+    HIP call, and the plane sizes follow the row layouts at d = 512."""
+    ws = 1 << 30
+    with pytest.raises(tq.TQError) as e:
+        tq.tq_decode_attn(_layout(head_dim=512, n_q_heads=18, n_kv_heads=2), _state(), FAKE, _cache(), 100,
+                          None, None, 0, 0, FAKE, FAKE, ws)
+    assert e.value.status == tq.TQ_ERR_UNSUPPORTED
+    sizes = tq.tq_cache_plane_bytes(_layout(head_dim=512, k_kind="lm_qjl", k_bits=3, v_kind="lm_rot", v_bits=3), 1, 10)
+    per = 10 * 2                                            # 10 tokens, 2 kv-heads
+    assert sizes == [4 * 52 * per, 4 * 16 * per, 4 * per, 4 * 52 * per, 4 * per]   # 52 words of ten 3-bit codes
+    sizes = tq.tq_cache_plane_bytes(_layout(head_dim=512, k_kind="affine8", k_bits=5, v_kind="group_sym", v_bits=4), 1, 10)
+    assert sizes == [4 * (64 + 16) * per, 0, 4 * 16 * per, 4 * 64 * per, 2 * 16 * per]
 
 
 def test_decode_rejects_bad_arguments():
@@ -215,7 +231,7 @@ def test_materialize_rejects_bad_arguments():
             tq.tq_materialize(L, a["state"], a["cache"], a["t0"], a["n"], a["ok"], a["ov"], a["dt"])
         assert e.value.status == code, (over, e.value)
     with pytest.raises(tq.TQError) as e:
-        tq.tq_materialize(_layout(head_dim=512), _state(), _cache(), 0, 16, FAKE, FAKE, tq.TQ_F16)
+        tq.tq_materialize(_layout(head_dim=1024), _state(), _cache(), 0, 16, FAKE, FAKE, tq.TQ_F16)
     assert e.value.status == tq.TQ_ERR_UNSUPPORTED
 
 

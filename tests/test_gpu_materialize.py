@@ -166,6 +166,13 @@ VARIANTS = [
     (64, "affine8", 5, "lm_rot", 4, 8, 2, "bf16"),
     (64, "affine8", 4, "lm_rot", 2, 4, 2, "bf16"),
     (128, "affine8", 2, "lm_rot", 2, 2, 2, "f16"),
+    # head_dim 512
+    (512, "lm_qjl", 3, "group_sym", 2, 4, 2, "f16"),
+    (512, "lm_qjl", 2, "lm_rot", 4, 2, 1, "bf16"),
+    (512, "lm_mse", 4, "lm_rot", 3, 2, 2, "f16"),
+    (512, "affine8", 5, "group_asym", 4, 4, 2, "bf16"),
+    (512, "affine8", 8, "group_sym", 4, 2, 1, "f16"),
+    (512, "f16", 16, "lm_rot", 2, 2, 2, "bf16"),
 ]
 
 

@@ -1,7 +1,7 @@
 """GPU parity over the compiled variants the benchmark workloads do not reach.
 
 Every kernel family (2/3/4-bit Lloyd-Max + QJL keys, MSE-only Lloyd-Max keys, per-block
-affine keys at 8/5/4/2 bits, group-32 and rotated Lloyd-Max values, head_dim 64/128/256, n_rep 1..8, fp16/bf16 inputs) is
+affine keys at 8/5/4/2 bits, group-32 and rotated Lloyd-Max values, head_dim 64/128/256/512, n_rep 1..8, fp16/bf16 inputs) is
 encoded and decoded at a small, ragged size against the CPU oracle, and degenerate
 vectors (all zero, constant, a single non-zero element, signed zeros, subnormals) go
 through both sides.
@@ -70,6 +70,18 @@ VARIANTS = [
     (128, "affine8", 2, "lm_rot", 3, 8, 1, "f16", 333, 5),
     (128, "affine8", 2, "lm_rot", 2, 6, 2, "bf16", 190, 64),
     (64, "affine8", 2, "lm_rot", 2, 10, 2, "f16", 250, 0),
+    # head_dim 512 (vector-ALU kernels: one wave per token), every key and value kind
+    (512, "lm_qjl", 3, "group_sym", 2, 8, 2, "f16", 200, 17),
+    (512, "lm_qjl", 2, "lm_rot", 3, 2, 2, "bf16", 150, 0),
+    (512, "lm_qjl", 4, "group_asym", 4, 16, 2, "f16", 1200, 5),     # several splits
+    (512, "lm_mse", 3, "lm_rot", 4, 4, 1, "bf16", 170, 9),
+    (512, "lm_mse", 2, "group_sym", 4, 2, 2, "f16", 100, 0),
+    (512, "affine8", 8, "lm_rot", 2, 6, 2, "f16", 130, 31),
+    (512, "affine8", 5, "group_asym", 2, 4, 2, "bf16", 120, 0),
+    (512, "affine8", 4, "group_sym", 2, 2, 1, "f16", 100, 3),
+    (512, "affine8", 2, "lm_rot", 3, 8, 2, "f16", 90, 0),
+    (512, "f16", 16, "lm_rot", 3, 4, 2, "bf16", 110, 7),
+    (512, "f16", 16, "group_sym", 4, 16, 2, "f16", 120, 0),
 ]
 
 
@@ -110,11 +122,16 @@ def _bits(dt, x):
     return int(W.to_storage(np.array([x], dtype=np.float32), dt)[0])
 
 
-@pytest.mark.parametrize("name", ["llama1b_h32x8_d64_t32k", "qwen0p6b_h16x4_d128_b8_t64k",
-                                  "qwen32b_h40x8_d128_b4_t128k"])
+DEGENERATE = ["llama1b_h32x8_d64_t32k", "qwen0p6b_h16x4_d128_b8_t64k", "qwen32b_h40x8_d128_b4_t128k",
+              (512, "lm_qjl", 3, "lm_rot", 3, 4, 2, "bf16", 200, 0),
+              (512, "lm_mse", 4, "group_sym", 2, 4, 2, "f16", 200, 0)]
+
+
+@pytest.mark.parametrize("name", DEGENERATE, ids=lambda v: v if isinstance(v, str) else make(v).name)
 def test_degenerate_vectors(name):
     """Zero, constant, one-hot, signed-zero and subnormal vectors through encode and decode."""
-    wl = dataclasses.replace(W.WORKLOADS[name].scaled(200, batch=1), n_recent=0)
+    wl = W.WORKLOADS[name] if isinstance(name, str) else make(name)
+    wl = dataclasses.replace(wl.scaled(200, batch=1), n_recent=0)
     s = H.Setup(wl)
     K, V = s.kv()
     dt, d = wl.in_dtype, wl.head_dim
@@ -144,3 +161,37 @@ def test_degenerate_vectors(name):
     err = H.rel_err(out, ref)
     H.log(f"  decode max rel err {err:.3e}")
     assert err <= H.ATTN_TOL
+
+
+EXTREME = [(64, "lm_qjl", 4, "lm_rot", 3, 4, 2, "bf16", 100, 0),
+           (128, "lm_qjl", 3, "lm_rot", 2, 4, 2, "bf16", 100, 0),
+           (256, "lm_mse", 3, "lm_rot", 4, 2, 2, "bf16", 100, 0),
+           (512, "lm_qjl", 3, "lm_rot", 3, 4, 2, "bf16", 100, 0),
+           (512, "lm_mse", 4, "lm_rot", 2, 2, 1, "bf16", 100, 0)]
+
+
+@pytest.mark.parametrize("v", EXTREME, ids=lambda v: make(v).name)
+def test_encode_extreme_bf16_magnitudes(v):
+    """bf16 tokens whose float32 square sum leaves float32's range (a one-hot 1e38, constant
+    rows of 3e38, 1e30 and +-1e-30, a random row with one 2e37 element) encode like the oracle's
+    float64 path: identical codes and signs, norms within the side values' tolerance (an fp16
+    norm of a QJL key overflows to inf on both sides; decoding such a key is outside the
+    format's range and is not checked)."""
+    wl = dataclasses.replace(make(v), n_recent=0)
+    s = H.Setup(wl)
+    K, V = s.kv()
+    d = wl.head_dim
+    for X in (K, V):
+        X[:, :, 0] = 0
+        X[:, :, 0, 5] = _bits("bf16", 1.0e38)
+        X[:, :, 1] = _bits("bf16", 3.0e38)
+        X[:, :, 2] = _bits("bf16", 1.0e30)
+        X[:, :, 3] = _bits("bf16", -1.0e-30)
+        X[:, :, 3, ::3] = _bits("bf16", 1.0e-30)
+        X[:, :, 4, d // 3] = _bits("bf16", 2.0e37)
+    n = wl.n_compressed
+    cache = s.gpu_encode(K[:, :, :n], V[:, :, :n], n, n)
+    gpu = H.download(cache, wl, K.shape[0], n)
+    _, ek, ev = s.oracle_encode(K[:, :, :n], V[:, :, :n])
+    st = H.compare_encode(wl, gpu, ek, ev)
+    H.log(f"[extreme] {wl.name}: {st}")
