@@ -240,7 +240,7 @@ MainKernel find_main(const tq_layout& L) {
       default: return MainKernel{nullptr, nullptr};
     }
   }
-  // 16-bit keys: d = 64 and 128; d = 256 only fp16-stored, on the matrix cores with 32-token tiles
+  // 16-bit keys: d = 64 and 128; d = 256 on the matrix cores with 32-token tiles (either storage)
   if (L.k_kind == TQ_K_F16 && L.k_bits == 16) {
     // fp16-stored keys are exact matrix-core operands; bf16 ones stay on the vector ALUs
     if (d == 64 && L.in_dtype == TQ_F16 && nrep >= 3) {
@@ -249,7 +249,7 @@ MainKernel find_main(const tq_layout& L) {
     }
     if (d == 64) return find_main_f16_d64(nrep, vk, vb);
     if (d == 128) return find_main_f16_d128(nrep, vk, vb);
-    if (d == 256 && L.in_dtype == TQ_F16) return find_mma_f16_d256(nrep, vk, vb);
+    if (d == 256) return find_mma_f16_d256(nrep, vk, vb);          // fp16 or bf16 storage
     return MainKernel{nullptr, nullptr};
   }
 #undef TQ_BY_D

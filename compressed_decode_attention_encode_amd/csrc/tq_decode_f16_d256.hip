@@ -1,7 +1,8 @@
-// Compiled instantiations of the decode kernel: 16-bit keys (V-only mode) in fp16 storage, head_dim
-// 256, n_rep 1..8, group-32 symmetric 2/4-bit values and rotated Lloyd-Max 2/3/4-bit values, on the
-// matrix cores with 32-token wave tiles (a 64-token tile of 512-byte key rows does not fit a group's
-// LDS share; bf16 keys at this head_dim are not compiled).
+// Compiled instantiations of the decode kernel: 16-bit keys (V-only mode), head_dim 256, n_rep
+// 1..8, group-32 symmetric 2/4-bit values and rotated Lloyd-Max 2/3/4-bit values, on the matrix
+// cores with 32-token wave tiles (a 64-token tile of 512-byte key rows does not fit a group's LDS
+// share); fp16 rows use the fp16 products, bf16 rows the bf16 ones (the storage type is the
+// layout's input type, chosen at run time).
 #include "tq_decode_mma.h"
 
 namespace tq {

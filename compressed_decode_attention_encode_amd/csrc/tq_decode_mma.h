@@ -61,6 +61,19 @@ __device__ __forceinline__ mma_f4_t mma16(mma_u4_t a, mma_u4_t b, mma_f4_t c) {
                                                 c, 0, 0, 0);
 }
 
+typedef __bf16 mma_b8_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ mma_f4_t mma16_bf(mma_u4_t a, mma_u4_t b, mma_f4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(mma_b8_t, a), __builtin_bit_cast(mma_b8_t, b),
+                                                 c, 0, 0, 0);
+}
+
+// float -> bf16 bits, round to nearest even (finite values)
+__device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
 // Operand scales: centroids x 8 (O(1) values, fp16 halves both normal); the query operands
 // carry 2^8 / 8 (codebook) and 2^8 (QJL) so that the sum is 2^8 times the log2-domain score.
 constexpr float kMmaCentScale = 8.f;
@@ -348,7 +361,26 @@ decode_mma_kernel(const DecodeArgs A) {
       smw[M::OFF_SGT + 4 * i + k] = (((i >> (2 * k)) & 1) ? 0u : 0x8000u) | (((i >> (2 * k + 1)) & 1) ? 0u : 0x80000000u);
   }
   prepare_queries<D, NREP, KK, KB, VK, VB, false, NQ>(A, b, g, sm);
-  {
+  // 16-bit keys at head_dim 256 come in either storage type: bf16 rows are bf16 matrix-core
+  // operands against a three-term bf16 split of the query (hi + mid + lo carries its 24 bits)
+  constexpr bool KBF = F16K && D == 256;
+  const bool kbf = KBF && A.q_bf16;
+  if (kbf) {
+    const float* qa = sm + M::G::OFF_QA;
+    uint16_t* bq = reinterpret_cast<uint16_t*>(smw + M::OFF_BQ);
+    constexpr int RS = M::NRB * 2 * M::QS;
+    for (int i = threadIdx.x; i < M::NRB * D; i += 256) {
+      const float a = (i < NREP * D) ? qa[i] * kMmaAffQScale : 0.f;
+      const uint32_t h = bf16_rne_bits(a);
+      const float r = a - __uint_as_float(h << 16);
+      const uint32_t m = bf16_rne_bits(r);
+      const uint32_t l = bf16_rne_bits(r - __uint_as_float(m << 16));
+      const int o = (i / D) * 2 * M::QS + i % D;
+      bq[o] = (uint16_t)h;
+      bq[RS + o] = (uint16_t)m;
+      bq[2 * RS + o] = (uint16_t)l;
+    }
+  } else {
     // fp16 query operands (hi, lo) from the prepared fp32 queries
     const float* qa = sm + M::G::OFF_QA;
     const float* qb = sm + M::G::OFF_QB;
@@ -413,8 +445,8 @@ decode_mma_kernel(const DecodeArgs A) {
     // p[mb][r]: head l16, token 16 mb + 4 q4 + r (log2-domain score, then its weight)
     float p[MB][4];
     if constexpr (F16K) {
-      // 16-bit keys (fp16 storage): the stored rows are the A operand as they are, against the
-      // hi/lo query operands (x16); every product exact
+      // 16-bit keys: the stored rows are the A operand as they are, against the hi/lo (fp16
+      // storage) or hi/mid/lo (bf16 storage) query operands (x16); every product exact
       mma_f4_t sacc[MB];
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) sacc[mb] = mma_f4_t{0.f, 0.f, 0.f, 0.f};
@@ -427,6 +459,19 @@ decode_mma_kernel(const DecodeArgs A) {
         const uint4 r1 = *reinterpret_cast<const uint4*>(src + RW);
         const mma_u4_t bq0 = mma_u4_t{r0.x, r0.y, r0.z, r0.w};
         const mma_u4_t bq1 = mma_u4_t{r1.x, r1.y, r1.z, r1.w};
+        if (KBF && kbf) {
+          const uint4 r2 = *reinterpret_cast<const uint4*>(src + 2 * RW);
+          const mma_u4_t bq2 = mma_u4_t{r2.x, r2.y, r2.z, r2.w};
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) {
+            const uint4 w = *reinterpret_cast<const uint4*>(stk + (16 * mb + l16) * M::SK + kw);
+            const mma_u4_t ak = mma_u4_t{w.x, w.y, w.z, w.w};
+            sacc[mb] = mma16_bf(ak, bq0, sacc[mb]);
+            sacc[mb] = mma16_bf(ak, bq1, sacc[mb]);
+            sacc[mb] = mma16_bf(ak, bq2, sacc[mb]);
+          }
+          continue;
+        }
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
           const uint4 w = *reinterpret_cast<const uint4*>(stk + (16 * mb + l16) * M::SK + kw);

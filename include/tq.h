@@ -56,8 +56,7 @@ typedef enum { TQ_F16 = 0, TQ_BF16 = 1 } tq_dtype;
 /* Key encodings.
  * TQ_K_F16     (MLX page, V-only mode: keys stay 16-bit, only the values are compressed):
  *   the key row is stored as given (layout->in_dtype bits); k_bits must be 16; decode
- *   is compiled for head_dim 64, 128 and 512, and for 256 with fp16 keys
- *   (TQ_ERR_UNSUPPORTED for bf16 keys at 256).
+ *   is compiled for head_dim 64, 128, 256 and 512, fp16 or bf16 storage.
  * TQ_K_LM_MSE  (vLLM guide section 2 steps 1-2 only: the MSE-optimal codes without the
  *   QJL residual sketch; vLLM guide, MSE score kernel): n = |k| stored fp32, y = Pi k/n,
  *   idx_j = #{i : t_i < y_j} (k_bits in {2,3,4}); decoded key n Pi^T c[idx].  Its

@@ -251,8 +251,8 @@ def test_mse_only_keys_arguments():
 
 
 def test_sixteen_bit_keys_arguments():
-    """16-bit keys (V-only mode): k_bits 16, no aux plane; decode compiled for d 64/128 and, with fp16
-    storage, 256."""
+    """16-bit keys (V-only mode): k_bits 16, no aux plane; decode compiled for d 64/128/256/512 in
+    either storage type, n_rep <= 8."""
     with pytest.raises(tq.TQError) as e:
         tq.tq_encode(_layout(k_kind="f16", k_bits=8), _state(), FAKE, None, 1, 16, 0, _cache())
     assert e.value.status == tq.TQ_ERR_UNSUPPORTED
@@ -261,8 +261,9 @@ def test_sixteen_bit_keys_arguments():
     assert sizes[:3] == [2 * 128 * 10 * L.n_kv_heads, 0, 0]
     ws = tq.tq_decode_workspace_bytes(L, 1, 100)
     cache = tq.tq_cache(FAKE, None, None, FAKE, FAKE, 1, 256)
-    with pytest.raises(tq.TQError) as e:          # d = 256 bf16-key decode is not compiled
-        tq.tq_decode_attn(_layout(head_dim=256, k_kind="f16", k_bits=16, v_kind="lm_rot", v_bits=3, in_dtype="bf16"),
+    with pytest.raises(tq.TQError) as e:          # n_rep 9 has no 16-bit-key decode at any head_dim
+        tq.tq_decode_attn(_layout(head_dim=256, n_q_heads=18, k_kind="f16", k_bits=16, v_kind="lm_rot", v_bits=3,
+                                  in_dtype="bf16"),
                           _state(), FAKE, cache, 100, None, None, 0, 0, FAKE, FAKE, 1 << 30)
     assert e.value.status == tq.TQ_ERR_UNSUPPORTED
     assert ws > 0

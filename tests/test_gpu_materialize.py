@@ -159,6 +159,7 @@ VARIANTS = [
     (256, "lm_mse", 2, "lm_rot", 4, 2, 1, "f16"),
     (128, "f16", 16, "lm_rot", 3, 4, 2, "bf16"),
     (256, "f16", 16, "group_sym", 2, 2, 2, "f16"),
+    (256, "f16", 16, "lm_rot", 4, 2, 2, "bf16"),
     (128, "lm_qjl", 2, "group_asym", 2, 4, 2, "f16"),
     (64, "lm_qjl", 3, "group_asym", 4, 4, 2, "bf16"),
     # 5/4/2-bit affine keys (the vllm-metal compression-ratio table's q5_0, q4_0, uint2/int2)

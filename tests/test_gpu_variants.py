@@ -57,6 +57,8 @@ VARIANTS = [
     (64, "f16", 16, "lm_rot", 4, 10, 2, "f16", 190, 0),
     (256, "f16", 16, "lm_rot", 3, 4, 2, "f16", 200, 17),        # d 256: fp16 keys, 32-token tiles
     (256, "f16", 16, "group_sym", 2, 2, 2, "f16", 150, 0),
+    (256, "f16", 16, "lm_rot", 3, 10, 2, "bf16", 210, 17),      # d 256 bf16 keys: bf16 products
+    (256, "f16", 16, "group_sym", 4, 2, 2, "bf16", 150, 0),
     # group-32 min/max values (matrix cores at every n_rep)
     (64, "lm_qjl", 2, "group_asym", 2, 4, 2, "f16", 300, 17),
     (64, "lm_qjl", 3, "group_asym", 2, 2, 2, "f16", 200, 5),
