@@ -63,6 +63,12 @@ __device__ __forceinline__ mma_f4_t mma16(mma_u4_t a, mma_u4_t b, mma_f4_t c) {
 
 typedef __bf16 mma_b8_t __attribute__((ext_vector_type(8)));
 
+// x of lane l + S within the lane's row of 16 (zero past the row's end)
+template <int S>
+__device__ __forceinline__ float row_shl(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x100 + S, 0xF, 0xF, true));
+}
+
 __device__ __forceinline__ mma_f4_t mma16_bf(mma_u4_t a, mma_u4_t b, mma_f4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(mma_b8_t, a), __builtin_bit_cast(mma_b8_t, b),
                                                  c, 0, 0, 0);
@@ -80,6 +86,20 @@ constexpr float kMmaCentScale = 8.f;
 constexpr float kMmaQScale = 256.f;
 constexpr float kMmaUnscale = 1.f / 256.f;
 constexpr float kMmaAffQScale = 16.f;        // affine keys: query operands carry 16
+
+// fp16 pair (fp16(a x), fp16(b y)) of float a, b and the fp16 x, y held in half `hf` of words
+// dx, dy: the mixed-precision multiply-add rounds each product to fp16 once
+__device__ __forceinline__ uint32_t mul_f32_f16_pair(float a, uint32_t dx, float b, uint32_t dy, int hf) {
+  uint32_t r;
+  if (hf == 0) {
+    asm("v_fma_mixlo_f16 %0, %1, %2, 0 op_sel_hi:[0,1,0]" : "=v"(r) : "v"(a), "v"(dx));
+    asm("v_fma_mixhi_f16 %0, %1, %2, 0 op_sel_hi:[0,1,0]" : "+v"(r) : "v"(b), "v"(dy));
+  } else {
+    asm("v_fma_mixlo_f16 %0, %1, %2, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]" : "=v"(r) : "v"(a), "v"(dx));
+    asm("v_fma_mixhi_f16 %0, %1, %2, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]" : "+v"(r) : "v"(b), "v"(dy));
+  }
+  return r;
+}
 
 // (a, b) -> fp16 hi pair and the pair of their fp16 remainders (a - hi_a, b - hi_b)
 __device__ __forceinline__ void split_f16x2(float a, float b, uint32_t& hi, uint32_t& lo) {
@@ -113,12 +133,16 @@ struct MmaGeom {
   static constexpr bool DIRECT = !AFF && !F16K && D >= 128;
   // one wave's staging area (words): key rows, sign rows, key aux (word-major [block][token]
   // for affine keys), value codes and value aux word-major
+  // group values (symmetric or min/max) in 64-token tiles: code rows kept row-major in LDS (a
+  // two-word pad per row) and read back transposed, scale rows row-major and dense
+  static constexpr bool TRV = VK != TQ_V_LM_ROT && TT == 64;
+  static constexpr int LSV = WV + 2;
   static constexpr int OFF_SK = 0;
   static constexpr int OFF_SS = OFF_SK + (DIRECT ? 0 : TT * SK);
   static constexpr int OFF_SAK = OFF_SS + (DIRECT ? 0 : TT * SS);
   static constexpr int OFF_SV = OFF_SAK + (DIRECT ? 0 : (AFF ? WAK * TS : TT));
-  static constexpr int OFF_SAV = OFF_SV + WV * TS;
-  static constexpr int STAGE = OFF_SAV + WAV * TS;
+  static constexpr int OFF_SAV = OFF_SV + (TRV ? TT * LSV : WV * TS);
+  static constexpr int STAGE = OFF_SAV + (TRV ? TT * WAV : WAV * TS);
   static_assert(OFF_SS % 4 == 0 && OFF_SAK % 4 == 0 && OFF_SV % 4 == 0 && OFF_SAV % 4 == 0 && STAGE % 4 == 0,
                 "16-byte LDS reads");
   // group LDS (words): qa, qb as prepare_queries leaves them, the fp16 query operands
@@ -133,13 +157,19 @@ struct MmaGeom {
   // different LDS banks
   static constexpr int QS = D / 2 + 4;         // words per query operand row
   static constexpr int OFF_PT = OFF_BQ + 4 * NRB * QS;
-  static constexpr int OFF_VT = OFF_PT + 2 * NPT;
+  // the lo words of a pair table sit PLO words after its hi words: a distance no paired LDS
+  // read encodes (> 255 words, not a multiple of 64), so each read lands in its operand register
+  static constexpr int plo(int n) { return n == 0 ? 0 : (n > 256 ? n : 256) + 1; }
+  static constexpr int PLO = plo(NPT), VLO = plo(NVT);
+  static constexpr int al4(int w) { return (w + 3) & ~3; }   // 16-byte alignment of the regions after
+  static constexpr int OFF_VT = al4(OFF_PT + (NPT ? PLO + NPT : 0));
   // 3-bit rotated values (ten codes per word): per 16-dimension block and column l16 of it, the
   // word offset of dimension 16 nb + l16 in the transposed staging and its bit, (TS w) | bit << 16
   static constexpr int NVW = (VK == TQ_V_LM_ROT && VB == 3) ? D : 0;
-  static constexpr int OFF_VW = OFF_VT + 2 * NVT;
-  static constexpr int OFF_SGT = OFF_VW + NVW;
-  static constexpr int OFF_ST = OFF_SGT + (QJL ? 4 * 256 : 0);
+  static constexpr int OFF_VW = al4(OFF_VT + (NVT ? VLO + NVT : 0));
+  static constexpr int OFF_SGT = al4(OFF_VW + NVW);
+  static constexpr int OFF_ST = al4(OFF_SGT + (QJL ? 4 * 256 : 0));
+  static_assert(OFF_BQ % 4 == 0 && OFF_SGT % 4 == 0 && OFF_ST % 4 == 0, "16-byte LDS reads of the operand, sign and staging regions");
   // the four staging areas also hold the waves' value sums for the merge
   static constexpr int STAGE_ALL = (4 * STAGE > 4 * NREP * D) ? 4 * STAGE : 4 * NREP * D;
   static constexpr int OFF_MRG = OFF_ST + STAGE_ALL;
@@ -269,6 +299,76 @@ struct DirectKeys {
 // only the softmax and the output rows grow.  Below, NREP counts rows.
 // TT: tokens per wave tile (64; 32 at head_dim 256, where a 64-token tile's staging and
 // registers would leave one wave per SIMD).
+// Group values (symmetric or min/max, 2 or 4 bits) of a 64-token tile.  Code and scale rows
+// arrive through 16-byte raw buffer loads over exactly the tile's rows (words past them read as
+// zero) and go to LDS row-major: code rows padded to LSV words, scale rows dense.  The value
+// product then reads the codes with the transposing LDS read (ds_read_b64_tr_b4): in each group
+// of 16 lanes, lane k points at an 8-byte chunk of one token row and lane n receives nibble n of
+// every chunk, i.e. one 4-bit code (or one pair of 2-bit codes) of 16 tokens.
+template <int D, int VB, bool ASYMV, int TT>
+struct GroupValueTile {
+  static constexpr int WV = D * VB / 32;          // code words per token
+  static constexpr int LSV = WV + 2;              // LDS row stride: 8-byte reads of 64 rows spread over the banks
+  static constexpr int WAV = ASYMV ? D / 32 : D / 64;
+  static constexpr int NVL = TT * WV / 256;       // 16-byte code loads per lane
+  static constexpr int NS = TT * WAV / 64;        // scale words per lane
+  static_assert(WV % 4 == 0 && NVL >= 1 && (NS == 1 || NS == 2 || NS == 4 || NS == 8), "tile geometry");
+  uint32_t c[NVL][4];
+  uint32_t sc[NS];
+
+  __device__ __forceinline__ void load(const uint32_t* vc_g, const uint32_t* va_g, int rows, int lane) {
+    const __amdgpu_buffer_rsrc_t rc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(vc_g), (short)0, 4 * rows * WV, kBufferRsrcWord3);
+#pragma unroll
+    for (int u = 0; u < NVL; ++u) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rc, 16 * (lane + 64 * u), 0, 0);
+      c[u][0] = v[0]; c[u][1] = v[1]; c[u][2] = v[2]; c[u][3] = v[3];
+    }
+    const __amdgpu_buffer_rsrc_t ra =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(va_g), (short)0, 4 * rows * WAV, kBufferRsrcWord3);
+    if constexpr (NS == 1) {
+      sc[0] = __builtin_amdgcn_raw_buffer_load_b32(ra, 4 * lane, 0, 0);
+    } else if constexpr (NS == 2) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b64(ra, 8 * lane, 0, 0);
+      sc[0] = v[0]; sc[1] = v[1];
+    } else {
+#pragma unroll
+      for (int u = 0; u < NS / 4; ++u) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(ra, 4 * NS * lane + 16 * u, 0, 0);
+        sc[4 * u] = v[0]; sc[4 * u + 1] = v[1]; sc[4 * u + 2] = v[2]; sc[4 * u + 3] = v[3];
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(uint32_t* __restrict__ codes, uint32_t* __restrict__ scales, int lane) const {
+#pragma unroll
+    for (int u = 0; u < NVL; ++u) {
+      const int q = 4 * (lane + 64 * u);          // first word of the chunk in the tile
+      uint32_t* d = codes + (q / WV) * LSV + q % WV;
+      *reinterpret_cast<uint2*>(d) = make_uint2(c[u][0], c[u][1]);
+      *reinterpret_cast<uint2*>(d + 2) = make_uint2(c[u][2], c[u][3]);
+    }
+    if constexpr (NS == 1) {
+      scales[lane] = sc[0];
+    } else if constexpr (NS == 2) {
+      *reinterpret_cast<uint2*>(scales + 2 * lane) = make_uint2(sc[0], sc[1]);
+    } else {
+#pragma unroll
+      for (int u = 0; u < NS / 4; ++u)
+        *reinterpret_cast<uint4*>(scales + NS * lane + 4 * u) = make_uint4(sc[4 * u], sc[4 * u + 1], sc[4 * u + 2], sc[4 * u + 3]);
+    }
+  }
+};
+
+typedef int mma_i2_t __attribute__((ext_vector_type(2)));
+
+// the transposing 8-byte LDS read (ds_read_b64_tr_b4) at word `w` of the LDS
+__device__ __forceinline__ uint2 lds_read_tr4(const uint32_t* w) {
+  const mma_i2_t v = __builtin_amdgcn_ds_read_tr4_b64_v2i32(
+      (__attribute__((address_space(3))) mma_i2_t*)((__attribute__((address_space(3))) uint32_t*)w));
+  return make_uint2((uint32_t)v[0], (uint32_t)v[1]);
+}
+
 template <int D, int NREP_KV, int KK, int KB, int VK, int VB, int NQ = 1, int TT = kTile>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((D == 64 && KK != TQ_K_F16) ? 3 : (D == 256 ? 1 : 2))))
 decode_mma_kernel(const DecodeArgs A) {
@@ -320,8 +420,10 @@ decode_mma_kernel(const DecodeArgs A) {
   RowLoader<M::WK, M::SK, TT, DWL> ld_k;
   RowLoader<M::WS, M::SS, TT, DWL> ld_s;
   RowLoader<M::WAK, AFF ? M::TS : 1, TT, DWL> ld_ak;
-  RowLoader<M::WV, M::TS, TT, DWL> ld_v;
-  RowLoader<M::WAV, M::TS, TT, DWL> ld_av;
+  RowLoader<M::TRV ? 0 : M::WV, M::TS, TT, DWL> ld_v;
+  RowLoader<M::TRV ? 0 : M::WAV, M::TS, TT, DWL> ld_av;
+  using GV = GroupValueTile<D, (M::TRV ? VB : 4), ASYM, 64>;
+  GV gv;
   using DK = DirectKeys<D, (M::DIRECT ? KB : 2), QJL, TT>;
   DK dkn;                                       // the next tile's keys (Lloyd-Max kinds)
   auto issue = [&](int t0) {
@@ -334,23 +436,28 @@ decode_mma_kernel(const DecodeArgs A) {
       ld_s.load(A.ks + row0 * M::WS, nv, lane);
       ld_ak.load(A.ka + row0 * M::WAK, nv, lane);
     }
-    ld_v.load(A.vc + row0 * M::WV, nv, lane);
-    ld_av.load(A.va + row0 * M::WAV, nv, lane);
+    if constexpr (M::TRV) {
+      gv.load(A.vc + row0 * M::WV, A.va + row0 * M::WAV, nv, lane);
+    } else {
+      ld_v.load(A.vc + row0 * M::WV, nv, lane);
+      ld_av.load(A.va + row0 * M::WAV, nv, lane);
+    }
   };
   if (tb + wave * TT < te) issue(tb + wave * TT);
 
-  // code-pair tables: entry pc = (code a = low bits, code b), words (hi pair, lo pair) of 8 c
+  // code-pair tables: entry pc = (code a = low bits, code b): the hi pair of 8 c at word pc, the
+  // lo pair at word PLO + pc
   for (int i = threadIdx.x; i < M::NPT; i += 256) {
     uint32_t hi, lo;
     split_f16x2(A.kcent[i & (LK - 1)] * kMmaCentScale, A.kcent[i >> KB] * kMmaCentScale, hi, lo);
-    smw[M::OFF_PT + 2 * i] = hi;
-    smw[M::OFF_PT + 2 * i + 1] = lo;
+    smw[M::OFF_PT + i] = hi;
+    smw[M::OFF_PT + M::PLO + i] = lo;
   }
   for (int i = threadIdx.x; i < M::NVT; i += 256) {
     uint32_t hi, lo;
     split_f16x2(A.vcent[i & (LV - 1)] * kMmaCentScale, A.vcent[i >> VB] * kMmaCentScale, hi, lo);
-    smw[M::OFF_VT + 2 * i] = hi;
-    smw[M::OFF_VT + 2 * i + 1] = lo;
+    smw[M::OFF_VT + i] = hi;
+    smw[M::OFF_VT + M::VLO + i] = lo;
   }
   for (int j = threadIdx.x; j < M::NVW; j += 256) smw[M::OFF_VW + j] = (j / 10) * M::TS | (3 * (j % 10)) << 16;
   // sign table: 8 stored bits (bit 1 <=> sigma = +1) -> xor masks of 4 fp16 pairs
@@ -405,6 +512,12 @@ decode_mma_kernel(const DecodeArgs A) {
   const uint32_t* ptab = smw + M::OFF_PT;
   const uint32_t* sgt = smw + M::OFF_SGT;
   const int hq = (l16 < NREP) ? l16 : NREP;    // operand column (head); the zero row beyond n_rep
+  // Lloyd-Max keys with n_rep <= 8: score columns 0..NREP-1 take the hi parts of the heads' query
+  // operands and columns NREP..2 NREP-1 their lo parts, folded onto the heads after the products,
+  // so every key operand meets both parts of the query in one product
+  constexpr bool FOLD = !AFF && !F16K && 2 * NREP <= 16;
+  constexpr int RWQ = M::NRB * M::QS;          // words per query operand region
+  const uint32_t* bqf = bqw + ((FOLD && l16 >= NREP && l16 < 2 * NREP) ? RWQ + (l16 - NREP) * M::QS : hq * M::QS);
   const uint32_t* vtab = smw + M::OFF_VT;
   // affine keys: per 32-dimension block, the sum of the lane's head's query operand
   float qsum[AFF ? NKB : 1];
@@ -413,6 +526,16 @@ decode_mma_kernel(const DecodeArgs A) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) qsum[kb] = (l16 < NREP) ? qb[l16 * NKB + kb] * kMmaAffQScale : 0.f;
   }
+
+  // group-value operands: lane l16 takes dimension 16 nb + l16, whose code sits in byte vbyte of
+  // each token's word at bit vsh of that byte; perm selector gathering that byte of two tokens
+  // into the low bytes of the two halves, mask of the code there, shift to bit MV
+  constexpr int MV = (VB == 2) ? 8 : 6;
+  const uint32_t vbyte = (VB == 2) ? (uint32_t)(l16 >> 2) : (uint32_t)((l16 & 7) >> 1);
+  const uint32_t vsh = (VB == 2) ? (uint32_t)(2 * (l16 & 3)) : (uint32_t)(4 * (l16 & 1));
+  const uint32_t vsel = vbyte | 0x0C00u | ((4u + vbyte) << 16) | 0x0C000000u;
+  const uint32_t vmask = (((1u << VB) - 1u) * 0x00010001u) << vsh;
+  const uint32_t vls = (uint32_t)MV - vsh;
 
   float m_run = -INFINITY, l_part = 0.f;        // head l16 (per lane: its tokens)
   float off[NG];                                // sum of P' per group, head l16
@@ -434,8 +557,12 @@ decode_mma_kernel(const DecodeArgs A) {
       if constexpr (AFF) ld_ak.store_transposed(st + M::OFF_SAK, lane);
       else ld_ak.store(st + M::OFF_SAK, lane);
     }
-    ld_v.store_transposed(st + M::OFF_SV, lane);
-    ld_av.store_transposed(st + M::OFF_SAV, lane);
+    if constexpr (M::TRV) {
+      gv.store(st + M::OFF_SV, st + M::OFF_SAV, lane);
+    } else {
+      ld_v.store_transposed(st + M::OFF_SV, lane);
+      ld_av.store_transposed(st + M::OFF_SAV, lane);
+    }
     if (t0 + 4 * TT < te) issue(t0 + 4 * TT);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -492,16 +619,24 @@ decode_mma_kernel(const DecodeArgs A) {
       for (int kb = 0; kb < NKB; ++kb) {
         const int kw = 16 * kb + 4 * q4;           // word offset of this lane's 8 dimensions
         mma_u4_t bq0, bq1, bq2, bq3;
-        {
-          constexpr int RW = M::NRB * M::QS;         // words per operand region
+        if constexpr (FOLD) {
+          // folded columns: hi or lo part by lane (region 0 / 1; the projected query in 2 / 3)
+          const uint32_t* src = bqf + kw;
+          const uint4 r0 = *reinterpret_cast<const uint4*>(src);
+          bq0 = mma_u4_t{r0.x, r0.y, r0.z, r0.w};
+          if constexpr (QJL) {
+            const uint4 r2 = *reinterpret_cast<const uint4*>(src + 2 * RWQ);
+            bq2 = mma_u4_t{r2.x, r2.y, r2.z, r2.w};
+          }
+        } else {
           const uint32_t* src = bqw + hq * M::QS + kw;
           const uint4 r0 = *reinterpret_cast<const uint4*>(src);
-          const uint4 r1 = *reinterpret_cast<const uint4*>(src + RW);
+          const uint4 r1 = *reinterpret_cast<const uint4*>(src + RWQ);
           bq0 = mma_u4_t{r0.x, r0.y, r0.z, r0.w};
           bq1 = mma_u4_t{r1.x, r1.y, r1.z, r1.w};
           if constexpr (QJL) {
-            const uint4 r2 = *reinterpret_cast<const uint4*>(src + 2 * RW);
-            const uint4 r3 = *reinterpret_cast<const uint4*>(src + 3 * RW);
+            const uint4 r2 = *reinterpret_cast<const uint4*>(src + 2 * RWQ);
+            const uint4 r3 = *reinterpret_cast<const uint4*>(src + 3 * RWQ);
             bq2 = mma_u4_t{r2.x, r2.y, r2.z, r2.w};
             bq3 = mma_u4_t{r3.x, r3.y, r3.z, r3.w};
           }
@@ -528,13 +663,12 @@ decode_mma_kernel(const DecodeArgs A) {
 #pragma unroll
           for (int pp = 0; pp < 4; ++pp) {
             const uint32_t pc = (y >> (2 * KB * pp)) & (M::NPT - 1);
-            const uint2 e = *reinterpret_cast<const uint2*>(ptab + 2 * pc);
-            ahi[pp] = e.x;
-            alo[pp] = e.y;
+            ahi[pp] = ptab[pc];
+            alo[pp] = ptab[M::PLO + pc];
           }
           sacc[mb] = mma16(ahi, bq0, sacc[mb]);
           sacc[mb] = mma16(alo, bq0, sacc[mb]);
-          sacc[mb] = mma16(ahi, bq1, sacc[mb]);
+          if constexpr (!FOLD) sacc[mb] = mma16(ahi, bq1, sacc[mb]);
           if constexpr (QJL) {
             const uint32_t sb = (sts[tok * M::SS + kb] >> (8 * q4)) & 0xFFu;
             const uint4 mk = *reinterpret_cast<const uint4*>(sgt + 4 * sb);
@@ -542,9 +676,15 @@ decode_mma_kernel(const DecodeArgs A) {
             const uint32_t g2 = __builtin_amdgcn_perm(aux, aux, 0x03020302u);   // (gamma, gamma)
             const mma_u4_t asg = mma_u4_t{g2 ^ mk.x, g2 ^ mk.y, g2 ^ mk.z, g2 ^ mk.w};
             sacc[mb] = mma16(asg, bq2, sacc[mb]);
-            sacc[mb] = mma16(asg, bq3, sacc[mb]);
+            if constexpr (!FOLD) sacc[mb] = mma16(asg, bq3, sacc[mb]);
           }
         }
+      }
+      if constexpr (FOLD) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sacc[mb][r] += row_shl<FOLD ? NREP : 1>(sacc[mb][r]);
       }
       // times n (fp16 with gamma for LM + QJL keys, fp32 for MSE-only keys) and the unscale
 #pragma unroll
@@ -568,16 +708,24 @@ decode_mma_kernel(const DecodeArgs A) {
       for (int kb = 0; kb < NKB; ++kb) {
         const int kw = q4 * (D / 8) + 4 * kb;     // word offset of this lane's 8 query dimensions
         mma_u4_t bq0, bq1, bq2, bq3;
-        {
-          constexpr int RW = M::NRB * M::QS;         // words per operand region
+        if constexpr (FOLD) {
+          // folded columns: hi or lo part by lane (region 0 / 1; the projected query in 2 / 3)
+          const uint32_t* src = bqf + kw;
+          const uint4 r0 = *reinterpret_cast<const uint4*>(src);
+          bq0 = mma_u4_t{r0.x, r0.y, r0.z, r0.w};
+          if constexpr (QJL) {
+            const uint4 r2 = *reinterpret_cast<const uint4*>(src + 2 * RWQ);
+            bq2 = mma_u4_t{r2.x, r2.y, r2.z, r2.w};
+          }
+        } else {
           const uint32_t* src = bqw + hq * M::QS + kw;
           const uint4 r0 = *reinterpret_cast<const uint4*>(src);
-          const uint4 r1 = *reinterpret_cast<const uint4*>(src + RW);
+          const uint4 r1 = *reinterpret_cast<const uint4*>(src + RWQ);
           bq0 = mma_u4_t{r0.x, r0.y, r0.z, r0.w};
           bq1 = mma_u4_t{r1.x, r1.y, r1.z, r1.w};
           if constexpr (QJL) {
-            const uint4 r2 = *reinterpret_cast<const uint4*>(src + 2 * RW);
-            const uint4 r3 = *reinterpret_cast<const uint4*>(src + 3 * RW);
+            const uint4 r2 = *reinterpret_cast<const uint4*>(src + 2 * RWQ);
+            const uint4 r3 = *reinterpret_cast<const uint4*>(src + 3 * RWQ);
             bq2 = mma_u4_t{r2.x, r2.y, r2.z, r2.w};
             bq3 = mma_u4_t{r3.x, r3.y, r3.z, r3.w};
           }
@@ -591,22 +739,27 @@ decode_mma_kernel(const DecodeArgs A) {
 #pragma unroll
           for (int pp = 0; pp < 4; ++pp) {
             const uint32_t pc = (y >> (2 * KB * pp)) & (M::NPT - 1);
-            const uint2 e = *reinterpret_cast<const uint2*>(ptab + 2 * pc);
-            ahi[pp] = e.x;
-            alo[pp] = e.y;
+            ahi[pp] = ptab[pc];
+            alo[pp] = ptab[M::PLO + pc];
           }
           sacc[mb] = mma16(ahi, bq0, sacc[mb]);
           sacc[mb] = mma16(alo, bq0, sacc[mb]);
-          sacc[mb] = mma16(ahi, bq1, sacc[mb]);
+          if constexpr (!FOLD) sacc[mb] = mma16(ahi, bq1, sacc[mb]);
           if constexpr (QJL) {
             const uint32_t sb = dk.sign_byte(mb, kb, q4);
             const uint4 mk = *reinterpret_cast<const uint4*>(sgt + 4 * sb);
             const uint32_t g2 = __builtin_amdgcn_perm(dk.ka[mb], dk.ka[mb], 0x03020302u);   // (gamma, gamma)
             const mma_u4_t asg = mma_u4_t{g2 ^ mk.x, g2 ^ mk.y, g2 ^ mk.z, g2 ^ mk.w};
             sacc[mb] = mma16(asg, bq2, sacc[mb]);
-            sacc[mb] = mma16(asg, bq3, sacc[mb]);
+            if constexpr (!FOLD) sacc[mb] = mma16(asg, bq3, sacc[mb]);
           }
         }
+      }
+      if constexpr (FOLD) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sacc[mb][r] += row_shl<FOLD ? NREP : 1>(sacc[mb][r]);
       }
       // times n (fp16 with gamma for LM + QJL keys, fp32 for MSE-only keys) and the unscale;
       // accumulator row r of this lane is token 16 mb + 4 q4 + r, whose aux word lane 4 q4 + r holds
@@ -717,13 +870,15 @@ decode_mma_kernel(const DecodeArgs A) {
     }
     l_part = fmaf(l_part, alpha, ps);
     m_run = mn;
-#pragma unroll
-    for (int k = 0; k < NG; ++k) off[k] *= alpha;
-    if constexpr (ASYM) {
-#pragma unroll
-      for (int k = 0; k < NG; ++k) moff[k] *= alpha;
-    }
+    // (no branch around the rescale: a join inside the tile loop makes the compiler wait for
+    // the next tile's loads there)
     {
+#pragma unroll
+      for (int k = 0; k < NG; ++k) off[k] *= alpha;
+      if constexpr (ASYM) {
+#pragma unroll
+        for (int k = 0; k < NG; ++k) moff[k] *= alpha;
+      }
       float al[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) al[r] = __shfl(alpha, 4 * q4 + r);
@@ -734,7 +889,79 @@ decode_mma_kernel(const DecodeArgs A) {
     }
 
     // ---- weighted values: two 32-token blocks ------------------------------------------
-    if constexpr (!ROT) {
+    if constexpr (M::TRV) {
+      // group values from the row-major tile.  Product j (tokens of blocks mb = 2j, 2j + 1): in
+      // lane group q4, k-slots (2m, 2m + 1) are tokens 32 j + 4 q4 + m and 32 j + 16 + 4 q4 + m,
+      // the two tokens of the lane's score rows p[2j][m], p[2j + 1][m].  The transposing read
+      // gives lane (n, q4) nibble n of token tau(q4, k) = 16 (k >> 2) + 4 q4 + (k & 3) in its
+      // nibble k: k = m and m + 4 of the low word for j = 0, of the high word for j = 1.
+      constexpr uint32_t kOne = 0x3C003C00u;       // fp16 pair (1, 1)
+      constexpr int MV = (VB == 2) ? 8 : 6;        // code c -> fp16 1 + c / 2^(10 - MV)
+      constexpr int WAVv = M::WAV;
+      const uint32_t* vrow = stv + (16 * (l16 >> 2) + 4 * q4 + (l16 & 3)) * M::LSV;   // token tau(q4, l16)
+#pragma unroll
+      for (int j = 0; j < TT / 32; ++j) {
+        // scale words of the lane's 8 tokens: rows 32 j + 4 q4 + m (blocks 2j) and + 16 (2j + 1)
+        uint32_t sw[2][4 * WAVv];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const uint32_t* src = stav + (32 * j + 16 * h2 + 4 * q4) * WAVv;
+#pragma unroll
+          for (int u = 0; u < WAVv; ++u) {
+            const uint4 v = *reinterpret_cast<const uint4*>(src + 4 * u);
+            sw[h2][4 * u] = v.x; sw[h2][4 * u + 1] = v.y; sw[h2][4 * u + 2] = v.z; sw[h2][4 * u + 3] = v.w;
+          }
+        }
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+          // P' = fp16(p Delta) (or fp16(p a) for min/max groups) of the lane's 8 tokens
+          const int w = ASYM ? gi : gi / 2, hf = ASYM ? 0 : gi % 2;
+          mma_u4_t apv;
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            apv[m] = mul_f32_f16_pair(p[2 * j][m], sw[0][m * WAVv + w], p[2 * j + 1][m], sw[1][m * WAVv + w], hf);
+            off[gi] = dot2_f16(apv[m], kOne, off[gi]);
+          }
+          if constexpr (ASYM) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+              moff[gi] = fmaf(p[2 * j][m], f16_to_f32(sw[0][m * WAVv + w] >> 16), moff[gi]);
+              moff[gi] = fmaf(p[2 * j + 1][m], f16_to_f32(sw[1][m * WAVv + w] >> 16), moff[gi]);
+            }
+          }
+          if constexpr (VB == 4) {
+            // the group's two 16-dimension blocks: lane n takes dimension 16 nb + n
+#pragma unroll
+            for (int nb = 2 * gi; nb < 2 * gi + 2; ++nb) {
+              const uint2 t = lds_read_tr4(vrow + 2 * nb);
+              const uint32_t x = j ? t.y : t.x;
+              mma_u4_t bv;
+#pragma unroll
+              for (int m = 0; m < 4; ++m) {
+                const uint32_t sh = (m < 2) ? (x << (MV - 4 * m)) : (x >> (4 * m - MV));
+                bv[m] = (sh & (0x000F000Fu << MV)) | kOne;
+              }
+              acc[nb] = mma16(apv, bv, acc[nb]);
+            }
+          } else {
+            // 2-bit codes: one read covers the group's 32 dimensions, lane n the pair 2n, 2n + 1
+            // (block 2 gi: dimension 32 gi + 2 n, block 2 gi + 1: 32 gi + 2 n + 1)
+            const uint2 t = lds_read_tr4(vrow + 2 * gi);
+            const uint32_t x = j ? t.y : t.x;
+            mma_u4_t be, bo;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+              const uint32_t xe = (4 * m <= MV) ? (x << (MV - 4 * m)) : (x >> (4 * m - MV));
+              const uint32_t xo = (4 * m + 2 <= MV) ? (x << (MV - 4 * m - 2)) : (x >> (4 * m + 2 - MV));
+              be[m] = (xe & (0x00030003u << MV)) | kOne;
+              bo[m] = (xo & (0x00030003u << MV)) | kOne;
+            }
+            acc[2 * gi] = mma16(apv, be, acc[2 * gi]);
+            acc[2 * gi + 1] = mma16(apv, bo, acc[2 * gi + 1]);
+          }
+        }
+      }
+    } else if constexpr (!ROT) {
       // group values: P' = fp16(p Delta) against the exact fp16 1 + c/2^m; min/max values
       // also sum p m per group in fp32 (their offset term)
       constexpr uint32_t kOne = 0x3C003C00u;       // fp16 pair (1, 1)
@@ -752,13 +979,12 @@ decode_mma_kernel(const DecodeArgs A) {
           const uint32_t dw[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
           mma_u4_t apv;
           {
-            float wt[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-              wt[i] = p[2 * kb2 + (i >> 2)][i & 3] * f16_to_f32((dw[i] >> (16 * hf)) & 0xFFFFu);
+            // P' = fp16(p Delta) in one mixed-precision product per token
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-              apv[k] = pack_f16x2(wt[2 * k], wt[2 * k + 1]);
+              const int i0 = 2 * k, i1 = 2 * k + 1;
+              apv[k] = mul_f32_f16_pair(p[2 * kb2 + (i0 >> 2)][i0 & 3], dw[i0], p[2 * kb2 + (i1 >> 2)][i1 & 3], dw[i1],
+                                        hf);
               off[gi] = dot2_f16(apv[k], kOne, off[gi]);
             }
             if constexpr (ASYM) {
@@ -770,23 +996,19 @@ decode_mma_kernel(const DecodeArgs A) {
 #pragma unroll
           for (int nb = 2 * gi; nb < 2 * gi + 2; ++nb) {
             uint32_t x[8];
-            int bit;
             {
               const uint32_t* src = (VB == 2) ? stv + nb * M::TS + tk : stv + (2 * nb + (l16 >> 3)) * M::TS + tk;
               const uint4 x0 = *reinterpret_cast<const uint4*>(src);
               const uint4 x1 = *reinterpret_cast<const uint4*>(src + 16);
               x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w; x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
-              bit = (VB == 2) ? 2 * l16 : 4 * (l16 & 7);
             }
-            // code c -> fp16 1 + c / 2^MV: the code dropped into the mantissa under 1.0's exponent
-            constexpr int MV = (VB == 2) ? 8 : 6;
+            // code c -> fp16 1 + c / 2^MV (the code dropped into the mantissa under 1.0's
+            // exponent): the byte holding dimension 16 nb + l16 of both tokens of a k-slot pair
+            // gathered into the two halves, the code masked in place and shifted up to bit MV
             mma_u4_t bv;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              const uint32_t c0 = __builtin_amdgcn_ubfe(x[2 * k], (uint32_t)bit, VB);
-              const uint32_t c1 = __builtin_amdgcn_ubfe(x[2 * k + 1], (uint32_t)bit, VB);
-              bv[k] = (c0 << MV) | (c1 << (16 + MV)) | kOne;
-            }
+            for (int k = 0; k < 4; ++k)
+              bv[k] = ((__builtin_amdgcn_perm(x[2 * k + 1], x[2 * k], vsel) & vmask) << vls) | kOne;
             acc[nb] = mma16(apv, bv, acc[nb]);
           }
         }
@@ -836,9 +1058,9 @@ decode_mma_kernel(const DecodeArgs A) {
           for (int k = 0; k < 4; ++k) {
             const uint32_t c0 = __builtin_amdgcn_ubfe(x[2 * k], (uint32_t)bit, VB);
             const uint32_t c1 = __builtin_amdgcn_ubfe(x[2 * k + 1], (uint32_t)bit, VB);
-            const uint2 e = *reinterpret_cast<const uint2*>(vtab + 2 * (c0 | (c1 << VB)));
-            bvh[k] = e.x;
-            bvl[k] = e.y;
+            const uint32_t vc = c0 | (c1 << VB);
+            bvh[k] = vtab[vc];
+            bvl[k] = vtab[M::VLO + vc];
           }
           acc[nb] = mma16(aph, bvh, acc[nb]);
           acc[nb] = mma16(apl, bvh, acc[nb]);
@@ -886,8 +1108,11 @@ decode_mma_kernel(const DecodeArgs A) {
     }
     if (h < NREP) {
 #pragma unroll
-      for (int nb = 0; nb < NNB; ++nb)
-        s_mrg_acc[wave][h * D + 16 * nb + l16] = ROT ? F * acc[nb][r] : fmaf(F, acc[nb][r], fmaf(-FO, o[nb / 2], mo[nb / 2]));
+      for (int nb = 0; nb < NNB; ++nb) {
+        // 2-bit group values from the transposing reads: block nb holds dimensions 32 (nb/2) + 2 l16 + nb%2
+        const int dim = (M::TRV && VB == 2) ? 32 * (nb >> 1) + 2 * l16 + (nb & 1) : 16 * nb + l16;
+        s_mrg_acc[wave][h * D + dim] = ROT ? F * acc[nb][r] : fmaf(F, acc[nb][r], fmaf(-FO, o[nb / 2], mo[nb / 2]));
+      }
     }
   }
   if (lane < NREP) {
