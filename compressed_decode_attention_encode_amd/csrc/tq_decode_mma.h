@@ -460,12 +460,12 @@ decode_mma_kernel(const DecodeArgs A) {
     smw[M::OFF_VT + M::VLO + i] = lo;
   }
   for (int j = threadIdx.x; j < M::NVW; j += 256) smw[M::OFF_VW + j] = (j / 10) * M::TS | (3 * (j % 10)) << 16;
-  // sign table: 8 stored bits (bit 1 <=> sigma = +1) -> xor masks of 4 fp16 pairs
+  // sign table: 8 stored bits (bit 1 <=> sigma = +1) -> 4 fp16 pairs of +-1
   if constexpr (QJL) {
     const int i = threadIdx.x;
 #pragma unroll
     for (int k = 0; k < 4; ++k)
-      smw[M::OFF_SGT + 4 * i + k] = (((i >> (2 * k)) & 1) ? 0u : 0x8000u) | (((i >> (2 * k + 1)) & 1) ? 0u : 0x80000000u);
+      smw[M::OFF_SGT + 4 * i + k] = 0x3C003C00u ^ ((((i >> (2 * k)) & 1) ? 0u : 0x8000u) | (((i >> (2 * k + 1)) & 1) ? 0u : 0x80000000u));
   }
   prepare_queries<D, NREP, KK, KB, VK, VB, false, NQ>(A, b, g, sm);
   // 16-bit keys at head_dim 256 come in either storage type: bf16 rows are bf16 matrix-core
@@ -612,9 +612,11 @@ decode_mma_kernel(const DecodeArgs A) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) p[mb][r] = sacc[mb][r] * (1.f / kMmaAffQScale);
     } else if constexpr (!AFF && !M::DIRECT) {
-      mma_f4_t sacc[MB];
+      mma_f4_t sacc[MB], sqj[QJL ? MB : 1];      // codebook term; QJL sign term (before gamma)
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) sacc[mb] = mma_f4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int mb = 0; mb < (QJL ? MB : 1); ++mb) sqj[mb] = mma_f4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         const int kw = 16 * kb + 4 * q4;           // word offset of this lane's 8 dimensions
@@ -670,13 +672,12 @@ decode_mma_kernel(const DecodeArgs A) {
           sacc[mb] = mma16(alo, bq0, sacc[mb]);
           if constexpr (!FOLD) sacc[mb] = mma16(ahi, bq1, sacc[mb]);
           if constexpr (QJL) {
+            // the sign bits as +-1 operands; gamma scales the token's sum afterwards
             const uint32_t sb = (sts[tok * M::SS + kb] >> (8 * q4)) & 0xFFu;
             const uint4 mk = *reinterpret_cast<const uint4*>(sgt + 4 * sb);
-            const uint32_t aux = stak[tok];
-            const uint32_t g2 = __builtin_amdgcn_perm(aux, aux, 0x03020302u);   // (gamma, gamma)
-            const mma_u4_t asg = mma_u4_t{g2 ^ mk.x, g2 ^ mk.y, g2 ^ mk.z, g2 ^ mk.w};
-            sacc[mb] = mma16(asg, bq2, sacc[mb]);
-            if constexpr (!FOLD) sacc[mb] = mma16(asg, bq3, sacc[mb]);
+            const mma_u4_t asg = mma_u4_t{mk.x, mk.y, mk.z, mk.w};
+            sqj[mb] = mma16(asg, bq2, sqj[mb]);
+            if constexpr (!FOLD) sqj[mb] = mma16(asg, bq3, sqj[mb]);
           }
         }
       }
@@ -684,7 +685,10 @@ decode_mma_kernel(const DecodeArgs A) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) sacc[mb][r] += row_shl<FOLD ? NREP : 1>(sacc[mb][r]);
+          for (int r = 0; r < 4; ++r) {
+            sacc[mb][r] += row_shl<FOLD ? NREP : 1>(sacc[mb][r]);
+            if constexpr (QJL) sqj[mb][r] += row_shl<FOLD ? NREP : 1>(sqj[mb][r]);
+          }
       }
       // times n (fp16 with gamma for LM + QJL keys, fp32 for MSE-only keys) and the unscale
 #pragma unroll
@@ -694,13 +698,16 @@ decode_mma_kernel(const DecodeArgs A) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float n = QJL ? f16_to_f32(nn[r] & 0xFFFFu) : __uint_as_float(nn[r]);
-          p[mb][r] = sacc[mb][r] * (n * kMmaUnscale);
+          const float sc = QJL ? fmaf(f16_to_f32(nn[r] >> 16), sqj[QJL ? mb : 0][r], sacc[mb][r]) : sacc[mb][r];
+          p[mb][r] = sc * (n * kMmaUnscale);
         }
       }
     } else if constexpr (!AFF) {
-      mma_f4_t sacc[MB];
+      mma_f4_t sacc[MB], sqj[QJL ? MB : 1];      // codebook term; QJL sign term (before gamma)
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) sacc[mb] = mma_f4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int mb = 0; mb < (QJL ? MB : 1); ++mb) sqj[mb] = mma_f4_t{0.f, 0.f, 0.f, 0.f};
       uint32_t al[MB][DK::SAL];                  // 3-bit codes: each block's aligned stream
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) dk.align3(mb, q4, al[mb]);
@@ -746,12 +753,12 @@ decode_mma_kernel(const DecodeArgs A) {
           sacc[mb] = mma16(alo, bq0, sacc[mb]);
           if constexpr (!FOLD) sacc[mb] = mma16(ahi, bq1, sacc[mb]);
           if constexpr (QJL) {
+            // the sign bits as +-1 operands; gamma scales the token's sum afterwards
             const uint32_t sb = dk.sign_byte(mb, kb, q4);
             const uint4 mk = *reinterpret_cast<const uint4*>(sgt + 4 * sb);
-            const uint32_t g2 = __builtin_amdgcn_perm(dk.ka[mb], dk.ka[mb], 0x03020302u);   // (gamma, gamma)
-            const mma_u4_t asg = mma_u4_t{g2 ^ mk.x, g2 ^ mk.y, g2 ^ mk.z, g2 ^ mk.w};
-            sacc[mb] = mma16(asg, bq2, sacc[mb]);
-            if constexpr (!FOLD) sacc[mb] = mma16(asg, bq3, sacc[mb]);
+            const mma_u4_t asg = mma_u4_t{mk.x, mk.y, mk.z, mk.w};
+            sqj[mb] = mma16(asg, bq2, sqj[mb]);
+            if constexpr (!FOLD) sqj[mb] = mma16(asg, bq3, sqj[mb]);
           }
         }
       }
@@ -759,7 +766,10 @@ decode_mma_kernel(const DecodeArgs A) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) sacc[mb][r] += row_shl<FOLD ? NREP : 1>(sacc[mb][r]);
+          for (int r = 0; r < 4; ++r) {
+            sacc[mb][r] += row_shl<FOLD ? NREP : 1>(sacc[mb][r]);
+            if constexpr (QJL) sqj[mb][r] += row_shl<FOLD ? NREP : 1>(sqj[mb][r]);
+          }
       }
       // times n (fp16 with gamma for LM + QJL keys, fp32 for MSE-only keys) and the unscale;
       // accumulator row r of this lane is token 16 mb + 4 q4 + r, whose aux word lane 4 q4 + r holds
@@ -769,7 +779,8 @@ decode_mma_kernel(const DecodeArgs A) {
         for (int r = 0; r < 4; ++r) {
           const uint32_t nn = (uint32_t)__shfl((int)dk.ka[mb], 4 * q4 + r);
           const float n = QJL ? f16_to_f32(nn & 0xFFFFu) : __uint_as_float(nn);
-          p[mb][r] = sacc[mb][r] * (n * kMmaUnscale);
+          const float sc = QJL ? fmaf(f16_to_f32(nn >> 16), sqj[QJL ? mb : 0][r], sacc[mb][r]) : sacc[mb][r];
+          p[mb][r] = sc * (n * kMmaUnscale);
         }
       }
     } else {
@@ -840,7 +851,7 @@ decode_mma_kernel(const DecodeArgs A) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) p[mb][r] *= 1.f / kMmaAffQScale;
     }
-    if (nv < TT) {      // the last tile of a split: tokens past its end score -inf
+    if (__builtin_amdgcn_readfirstlane(nv) < TT) {      // the last tile of a split: tokens past its end score -inf
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -899,6 +910,9 @@ decode_mma_kernel(const DecodeArgs A) {
       constexpr int MV = (VB == 2) ? 8 : 6;        // code c -> fp16 1 + c / 2^(10 - MV)
       constexpr int WAVv = M::WAV;
       const uint32_t* vrow = stv + (16 * (l16 >> 2) + 4 * q4 + (l16 & 3)) * M::LSV;   // token tau(q4, l16)
+      // the constants in registers (one mask and the pair (1, 1)) turn mask-and-or into one instruction
+      uint32_t vone = kOne, vmask4 = 0x000F000Fu << MV, vmask2 = 0x00030003u << MV;
+      asm volatile("" : "+v"(vone), "+s"(vmask4), "+s"(vmask2));
 #pragma unroll
       for (int j = 0; j < TT / 32; ++j) {
         // scale words of the lane's 8 tokens: rows 32 j + 4 q4 + m (blocks 2j) and + 16 (2j + 1)
@@ -939,7 +953,7 @@ decode_mma_kernel(const DecodeArgs A) {
 #pragma unroll
               for (int m = 0; m < 4; ++m) {
                 const uint32_t sh = (m < 2) ? (x << (MV - 4 * m)) : (x >> (4 * m - MV));
-                bv[m] = (sh & (0x000F000Fu << MV)) | kOne;
+                bv[m] = (sh & vmask4) | vone;
               }
               acc[nb] = mma16(apv, bv, acc[nb]);
             }
@@ -953,8 +967,8 @@ decode_mma_kernel(const DecodeArgs A) {
             for (int m = 0; m < 4; ++m) {
               const uint32_t xe = (4 * m <= MV) ? (x << (MV - 4 * m)) : (x >> (4 * m - MV));
               const uint32_t xo = (4 * m + 2 <= MV) ? (x << (MV - 4 * m - 2)) : (x >> (4 * m + 2 - MV));
-              be[m] = (xe & (0x00030003u << MV)) | kOne;
-              bo[m] = (xo & (0x00030003u << MV)) | kOne;
+              be[m] = (xe & vmask2) | vone;
+              bo[m] = (xo & vmask2) | vone;
             }
             acc[2 * gi] = mma16(apv, be, acc[2 * gi]);
             acc[2 * gi + 1] = mma16(apv, bo, acc[2 * gi + 1]);
