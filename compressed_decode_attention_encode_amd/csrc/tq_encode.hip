@@ -39,31 +39,67 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 // QJL = false: rotated values or MSE-only keys (codes + fp32 n).
 // ---------------------------------------------------------------------------------
 
-// Keys work on y, thresholds and centroids scaled by 2^12 (exact): the residual then
-// enters the fp16 split as |r| 2^12 < 8192, where the low half of nearly every coordinate
-// stays a normal fp16 number; decisions are unchanged, the projection's sign needs no
-// rescaling and gamma = sqrt(sum r'^2) 2^-12.
-constexpr float kKeyScale = 4096.f;
+// Decisions work on y, thresholds and centroids scaled by the table's cell unit U = 2^e
+// (exact), at least 2^6 for keys: the residual then enters the fp16 split as |r| U, where
+// its low half stays a normal fp16 number for all but the smallest residuals (those keep an
+// absolute error below 2^-25 / U); decisions are unchanged, the projection's sign needs no
+// rescaling and gamma = sqrt(sum r'^2) / U.
+constexpr int kKeyTabMinExp = 6;
 
-// Number of positive thresholds p_0 < p_1 < ... below |y| (binary search over the L/2
-// magnitude cells of the symmetric codebook).
-template <int KB>
-__device__ __forceinline__ uint32_t magnitude_cell(float ay, const float (&p)[(1 << KB) / 2 - 1]) {
-  if constexpr (KB == 2) {
-    return ay > p[0] ? 1u : 0u;
-  } else if constexpr (KB == 3) {
-    const uint32_t c1 = ay > p[1] ? 1u : 0u;
-    const uint32_t c2 = ay > (c1 ? p[2] : p[0]) ? 1u : 0u;
-    return 2u * c1 + c2;
-  } else {
-    // selects written as bit masks, so that the search stays branch-free
-    auto pick = [](uint32_t m, float a, float b) { return __uint_as_float((__float_as_uint(a) & m) | (__float_as_uint(b) & ~m)); };
-    const uint32_t m1 = ay > p[3] ? ~0u : 0u;
-    const uint32_t m2 = ay > pick(m1, p[5], p[1]) ? ~0u : 0u;
-    const float t3 = pick(m2, pick(m1, p[6], p[2]), pick(m1, p[4], p[0]));
-    const uint32_t c3 = ay > t3 ? 1u : 0u;
-    return (m1 & 4u) | (m2 & 2u) | c3;
+// floor(x) as int32 in one instruction (x already clamped to the int range).
+__device__ __forceinline__ int floor_i32(float x) {
+  int r;
+  asm("v_cvt_flr_i32_f32 %0, %1" : "=v"(r) : "v"(x));
+  return r;
+}
+// Cell table of the Lloyd-Max decision.  Measure y in units of 2^-e of the unit
+// coordinate, with e the smallest exponent from e_min on at which the scaled thresholds
+// fall into different unit cells [j, j + 1) (so each cell holds at most one of them).  The
+// entry of cell j then gives that threshold (+inf if the cell has none), the index
+// #{i : t_i < j} of the cell's lower end and the centroids on both sides of the threshold:
+// idx(y) = #{i : t_i < y} = entry.base + (y > entry.t) for every y in the cell, with one
+// table read and one comparison instead of a search.  Scaling by 2^e is exact, so decisions
+// and residuals are those of the unscaled arithmetic.  Codebooks whose thresholds crowd
+// closer than 2^-kTabMaxExp (or are not ascending) return -1: the kernel then still builds
+// the table at 2^kTabMaxExp (every read stays inside it) but decides each block again by
+// counting the thresholds below y.
+constexpr int kTabMaxExp = 7;
+constexpr int kTabEntries = 2 * (1 << kTabMaxExp) + 2;   // cells j = -(U + 1) .. U, U = 2^e
+struct __attribute__((aligned(16))) TabEntry {
+  float t;         // threshold inside the cell, or +inf
+  uint32_t base;   // #{i : t_i < j}
+  float c_lo, c_hi;
+};
+
+template <int L>
+__device__ int table_exponent(const float* __restrict__ thr, int e_min) {
+  for (int e = e_min; e <= kTabMaxExp; ++e) {
+    const float u = (float)(1 << e);
+    bool ok = true;
+    float prev = floorf(thr[0] * u);
+    for (int i = 1; i < L - 1; ++i) {
+      const float f = floorf(thr[i] * u);
+      ok = ok && f > prev;           // false for NaN as well
+      prev = f;
+    }
+    if (ok) return e;
   }
+  return -1;
+}
+
+// Entry of cell j = e - (U + 1) for U = 2^te (thresholds and centroids scaled by U).
+template <int L>
+__device__ TabEntry table_entry(const float* __restrict__ thr, const float* __restrict__ cent, int e, int te) {
+  const float u = (float)(1 << te);
+  const float j = (float)(e - ((1 << te) + 1));
+  uint32_t base = 0u;
+  float t_in = __builtin_huge_valf();
+  for (int i = 0; i < L - 1; ++i) {
+    const float t = thr[i] * u;
+    if (t < j) ++base;
+    else if (t < j + 1.f) t_in = t;
+  }
+  return {t_in, base, cent[base] * u, cent[base + 1 < (uint32_t)L ? base + 1 : base] * u};
 }
 
 // Row of H_32 (or of S within a 32-row block) fed to matrix row m: the accumulator of
@@ -131,11 +167,11 @@ encode_lm_kernel(const uint16_t* __restrict__ x, int T, int mb_per_slice, int n_
   constexpr int CW = (16 * KB + 31) / 32;          // words of a lane's 16-code chunk
   constexpr int SP = D + 8;                        // LDS row stride of S (halves)
   constexpr bool kPrefetch = D <= 128 || QJL;       // next block's inputs held in registers
-  constexpr float kPre = QJL ? kKeyScale : 1.f;
   static_assert(NB >= 2 && NB <= 8, "head_dim 64..256");
 
   __shared__ uint4 s_h[NB * 2 * kWave];            // rotation A operands, per (block, k-half, lane)
   __shared__ float s_cent[16];
+  __shared__ TabEntry s_tab[kTabEntries];
   __shared__ __attribute__((aligned(16))) uint16_t s_S[QJL ? D * SP : 8];
 
   const int tid = threadIdx.x;
@@ -165,19 +201,27 @@ encode_lm_kernel(const uint16_t* __restrict__ x, int T, int mb_per_slice, int n_
     }
     s_h[e] = make_uint4(w[0], w[1], w[2], w[3]);
   }
-  if (tid < L) s_cent[tid] = cent[tid] * kPre;
+  // decision units: U = 2^te per unit coordinate
+  const int te0 = table_exponent<L>(thr, QJL ? kKeyTabMinExp : 0);
+  const bool crowded = te0 < 0;                    // uniform over the launch
+  const int te = crowded ? kTabMaxExp : te0;
+  const int U = 1 << te;
+  const float uf = (float)U, inv_uf = 1.f / (float)U;   // exact
+  for (int e = tid; e < 2 * U + 2; e += kWave * NW) s_tab[e] = table_entry<L>(thr, cent, e, te);
+  if (tid < L) s_cent[tid] = cent[tid] * uf;
   if constexpr (QJL) {
     for (int e = tid; e < D * D / 8; e += kWave * NW) {
       const int r = e / (D / 8), c8 = e % (D / 8);
       *reinterpret_cast<uint4*>(&s_S[r * SP + 8 * c8]) = reinterpret_cast<const uint4*>(S)[e];
     }
   }
-  // symmetric codebook: t[L/2-1] = 0 and t[L/2-1+i] = -t[L/2-1-i]; only the positive
-  // thresholds are compared, against |y|
-  float thp[L / 2 - 1];
-#pragma unroll
-  for (int i = 0; i < L / 2 - 1; ++i) thp[i] = thr[L / 2 + i] * kPre;
   __syncthreads();
+  const TabEntry* tab0 = s_tab + (U + 1);          // entry of cell j at tab0[j]
+  const float lo_cell = (float)(-(U + 1)), hi_cell = (float)U;
+  // -1 kept opaque so that r - (float)hi stays a multiply-add with an fp16 operand
+  // (v_fma_mix_f32) instead of a conversion and a subtraction
+  float neg_one = -1.f;
+  asm volatile("" : "+v"(neg_one));
 
   // this lane's S row offset (QJL A operands): row rot_row(col) of each 32-row block,
   // columns 16 h + 8 j of each 32-feature block
@@ -308,22 +352,42 @@ encode_lm_kernel(const uint16_t* __restrict__ x, int T, int mb_per_slice, int n_
       const HalfPair p = half_pair(__float_as_uint(ss32));
       const float ns = sqrtf(__uint_as_float(p.lo) + __uint_as_float(p.hi));   // norm of the (rescaled) input
       n = ns * inv_s;
-      scale = (ns > 0.f) ? kPre / (sqrtf((float)D) * ns) : 0.f;
+      scale = (ns > 0.f) ? uf / (sqrtf((float)D) * ns) : 0.f;
     } else {
       const uint64_t u = (uint64_t)__double_as_longlong(ss64);
       const HalfPair plo = half_pair((uint32_t)u), phi = half_pair((uint32_t)(u >> 32));
       const double n64 = sqrt(__longlong_as_double((long long)(((uint64_t)phi.lo << 32) | plo.lo)) +
                               __longlong_as_double((long long)(((uint64_t)phi.hi << 32) | plo.hi)));
       n = (float)n64;
-      scale = (n64 > 0.0) ? (float)(1.0 / (sqrt((double)D) * n64 / (double)inv_s)) : 0.f;
+      scale = (n64 > 0.0) ? (float)((double)uf / (sqrt((double)D) * n64 / (double)inv_s)) : 0.f;
     }
 
     // ---- Lloyd-Max decision, packed codes, residual --------------------------------
     uint32_t cw[NB][CW];
     uint32_t rh[QJL ? NB : 1][8], rl[QJL ? NB : 1][8];
     float gg = 0.f;
+    // block b's codes (and residual halves), with g accumulated over its coordinates: by
+    // the cell table, or (COUNT) by counting the thresholds below y.  idx = #{i : t_i < y};
+    // the float32 y differs from the exact one by ~1e-7, so a decision can change only next
+    // to a threshold
+    auto decide = [&](const int b, float g, auto count_tag) -> float {
+      constexpr bool COUNT = decltype(count_tag)::value;
+      // table path: entries are read kAhead coordinates ahead of their use (a ring in
+      // registers), so the LDS latency hides behind the work on earlier coordinates
+      using Ent = std::conditional_t<QJL, TabEntry, float2>;   // values need (t, base) only
+      constexpr int kAhead = 4;
+      float ysv[16];
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
+      for (int i = 0; i < 16; ++i) ysv[i] = y[b][i] * scale;
+      auto fetch = [&](int i) -> Ent {
+        // |ys| <= U up to rounding, so the clamp only guards non-finite inputs
+        return *reinterpret_cast<const Ent*>(tab0 + floor_i32(__builtin_amdgcn_fmed3f(ysv[i], lo_cell, hi_cell)));
+      };
+      Ent ring[kAhead];
+      if constexpr (!COUNT) {
+#pragma unroll
+        for (int i = 0; i < kAhead; ++i) ring[i] = fetch(i);
+      }
 #pragma unroll
       for (int i = 0; i < CW; ++i) cw[b][i] = 0u;
 #pragma unroll
@@ -331,29 +395,55 @@ encode_lm_kernel(const uint16_t* __restrict__ x, int T, int mb_per_slice, int n_
         float rr[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          // idx = #{i : t_i < y} = L/2 + cnt for y > 0 and L/2 - 1 - cnt otherwise, with cnt
-          // the number of positive thresholds below |y| (L/2 + cnt = cnt ^ L/2 and
-          // L/2 - 1 - cnt = cnt ^ (L/2 - 1) for cnt < L/2); the float32 y differs from the
-          // exact one by ~1e-7, so a decision can change only next to a threshold
-          const float ys = y[b][r + u] * scale;
-          const uint32_t cnt = magnitude_cell<KB>(fabsf(ys), thp);
-          const uint32_t idx = cnt ^ ((ys > 0.f) ? (uint32_t)(L / 2) : (uint32_t)(L / 2 - 1));
-          const int bit = KB * (r + u);
+          const int i = r + u;
+          const float ys = ysv[i];
+          uint32_t idx;
+          float c = 0.f;                             // centroid (keys: for the residual)
+          if constexpr (COUNT) {
+            // against the unscaled thresholds (uniform loads; ys / U is exact)
+            const float yu = ys * inv_uf;
+            idx = 0u;
+#pragma unroll
+            for (int k = 0; k < L - 1; ++k) idx += (thr[k] < yu) ? 1u : 0u;
+            if constexpr (QJL) c = s_cent[idx];
+          } else {
+            const Ent e = ring[i % kAhead];
+            if (i + kAhead < 16) ring[i % kAhead] = fetch(i + kAhead);
+            // idx (and c) taken while the comparison is live (else every mask waits for the
+            // packing); the volatile statement also keeps the reads in this order
+            if constexpr (QJL) {
+              const bool up = ys > e.t;
+              idx = e.base + (up ? 1u : 0u);
+              c = up ? e.c_hi : e.c_lo;
+              asm volatile("" : "+v"(idx), "+v"(c));
+            } else {
+              idx = __float_as_uint(e.y) + ((ys > e.x) ? 1u : 0u);
+              asm volatile("" : "+v"(idx));
+            }
+          }
+          const int bit = KB * i;
           cw[b][bit >> 5] |= idx << (bit & 31);
           if ((bit & 31) + KB > 32) cw[b][(bit >> 5) + 1] |= idx >> (32 - (bit & 31));
           if constexpr (QJL) {
-            rr[u] = ys - s_cent[idx];
-            gg = fmaf(rr[u], rr[u], gg);
+            rr[u] = ys - c;
+            g = fmaf(rr[u], rr[u], g);
           }
         }
         if constexpr (QJL) {
-          // hi = fp16(r) and lo = fp16(r - hi), both rounded toward zero
+          // hi = fp16(r) and lo = fp16(r - hi), both rounded toward zero (r - hi is exact in
+          // float32: one mixed-precision multiply-add per coordinate)
           const auto hi = __builtin_amdgcn_cvt_pkrtz(rr[0], rr[1]);
-          const auto lo = __builtin_amdgcn_cvt_pkrtz(rr[0] - (float)hi[0], rr[1] - (float)hi[1]);
+          const auto lo = __builtin_amdgcn_cvt_pkrtz(fmaf((float)hi[0], neg_one, rr[0]), fmaf((float)hi[1], neg_one, rr[1]));
           rh[b][r / 2] = __builtin_bit_cast(uint32_t, hi);
           rl[b][r / 2] = __builtin_bit_cast(uint32_t, lo);
         }
       }
+      return g;
+    };
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      if (crowded) gg = decide(b, gg, std::true_type{});
+      else gg = decide(b, gg, std::false_type{});
       __builtin_amdgcn_sched_barrier(0);     // block b's rotated values die here
     }
 
@@ -394,7 +484,7 @@ encode_lm_kernel(const uint16_t* __restrict__ x, int T, int mb_per_slice, int n_
 
     if constexpr (QJL) {
       const HalfPair p = half_pair(__float_as_uint(gg));
-      const float g = sqrtf(__uint_as_float(p.lo) + __uint_as_float(p.hi)) * (1.f / kKeyScale);
+      const float g = sqrtf(__uint_as_float(p.lo) + __uint_as_float(p.hi)) * inv_uf;
       if (valid && h == 0) {
         const uint32_t nb16 = __builtin_bit_cast(uint16_t, (_Float16)n);
         const uint32_t gb16 = __builtin_bit_cast(uint16_t, (_Float16)g);
@@ -415,9 +505,10 @@ encode_lm_kernel(const uint16_t* __restrict__ x, int T, int mb_per_slice, int n_
           }
         }
         // register r holds output 32 nb + 16 h + r; stored bit = (z >= 0), from the sign bit
+        // (shifted in from the top register down: bit r = sign of z[r])
         uint32_t neg = 0u;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) neg |= (__float_as_uint(z[r]) >> 31) << r;
+        for (int r = 15; r >= 0; --r) neg = __builtin_amdgcn_alignbit(neg, __float_as_uint(z[r]), 31);
         const HalfPair p2 = half_pair(~neg & 0xFFFFu);
         if (valid && h == (nb & 1)) signs_out[row * NB + nb] = p2.lo | (p2.hi << 16);
         __builtin_amdgcn_sched_barrier(0);   // one output block's operands live at a time

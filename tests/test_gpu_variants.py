@@ -197,3 +197,70 @@ def test_encode_extreme_bf16_magnitudes(v):
     _, ek, ev = s.oracle_encode(K[:, :, :n], V[:, :, :n])
     st = H.compare_encode(wl, gpu, ek, ev)
     H.log(f"[extreme] {wl.name}: {st}")
+
+
+def _set_codebook(s, role, c, t):
+    """Give both sides the same (float32) codebook for `role` ("k" or "v")."""
+    import torch
+    tq = s.tq
+    s.dstate.tensors[f"{role}_centroids"] = torch.from_numpy(np.ascontiguousarray(c, np.float32)).cuda()
+    s.dstate.tensors[f"{role}_thresholds"] = torch.from_numpy(np.ascontiguousarray(t, np.float32)).cuda()
+    s.dstate.struct = tq.tq_state(*[(s.dstate.tensors[n].data_ptr() if n in s.dstate.tensors else None)
+                                    for n, _ in tq.tq_state._fields_])
+    s.ostate[f"cb_{role}"] = (np.asarray(c, np.float32), np.asarray(t, np.float32))
+
+
+def _crowded(c, t):
+    """Two thresholds 0.003 apart (closer than the encoder's finest decision cell, 2^-7 of
+    the unit coordinate): the encoder decides by counting the thresholds below y."""
+    t = t.copy()
+    m = len(t) // 2
+    t[m + 1] = t[m] + np.float32(0.003)
+    return c, t
+
+
+def _shifted(c, t):
+    """Every centroid and threshold moved by +0.01: no longer symmetric about 0."""
+    return c + np.float32(0.01), t + np.float32(0.01)
+
+
+# (variant, codebook transform, roles)
+CODEBOOKS = [((128, "lm_qjl", 4, "group_sym", 2, 12, 2, "bf16", 150, 0), _crowded, "k"),
+             ((64, "lm_qjl", 2, "group_sym", 2, 4, 2, "f16", 150, 0), _crowded, "k"),
+             ((256, "lm_qjl", 3, "group_sym", 2, 2, 2, "f16", 120, 0), _crowded, "k"),
+             ((64, "lm_mse", 3, "lm_rot", 3, 4, 2, "f16", 150, 0), _crowded, "kv"),
+             ((256, "lm_mse", 4, "lm_rot", 2, 10, 2, "f16", 120, 0), _crowded, "v"),
+             ((128, "lm_mse", 4, "lm_rot", 4, 8, 1, "f16", 150, 0), _shifted, "kv"),
+             ((128, "lm_qjl", 3, "group_asym", 4, 10, 2, "bf16", 150, 0), _shifted, "k"),
+             ((512, "lm_qjl", 2, "lm_rot", 3, 2, 2, "bf16", 100, 0), _shifted, "kv")]
+
+
+@pytest.mark.parametrize("case", CODEBOOKS, ids=lambda c: f"{make(c[0]).name}-{c[1].__name__.strip('_')}")
+def test_custom_codebooks(case):
+    """Ascending codebooks other than the Lloyd-Max ones (crowded thresholds, or shifted off
+    symmetry) give the oracle's indices idx = #{i : t_i < y}, signs and side values, and the
+    decode of the oracle's planes matches."""
+    v, transform, roles = case
+    wl = dataclasses.replace(make(v), n_recent=0)
+    s = H.Setup(wl)
+    for role in roles:
+        kind = wl.k_kind if role == "k" else wl.v_kind
+        if kind not in ("lm_qjl", "lm_mse", "lm_rot"):
+            continue
+        c, t = s.ostate[f"cb_{role}"]
+        _set_codebook(s, role, *transform(c, t))
+    K, V = s.kv()
+    n = wl.n_compressed
+    cache = s.gpu_encode(K[:, :, :n], V[:, :, :n], n, n)
+    gpu = H.download(cache, wl, K.shape[0], n)
+    planes, ek, ev = s.oracle_encode(K[:, :, :n], V[:, :, :n])
+    st = H.compare_encode(wl, gpu, ek, ev)
+    H.log(f"[codebook] {wl.name} {transform.__name__}: {st}")
+    Q = W.q_bits(wl)
+    c2 = s.tq.alloc_cache(s.layout, K.shape[0], n)
+    H.upload_planes(c2, planes)
+    out = s.gpu_decode(c2, Q, n)
+    ref = s.oracle_decode(planes, Q, n)
+    err = H.rel_err(out, ref)
+    H.log(f"  decode max rel err {err:.3e}")
+    assert err <= H.ATTN_TOL
