@@ -46,7 +46,7 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 // rescaling and gamma = sqrt(sum r'^2) / U.
 constexpr int kKeyTabMinExp = 6;
 
-// floor(x) as int32 in one instruction (x already clamped to the int range).
+// floor(x) as int32 in one instruction (NaN gives 0, values outside the int range saturate).
 __device__ __forceinline__ int floor_i32(float x) {
   int r;
   asm("v_cvt_flr_i32_f32 %0, %1" : "=v"(r) : "v"(x));
@@ -217,7 +217,6 @@ encode_lm_kernel(const uint16_t* __restrict__ x, int T, int mb_per_slice, int n_
   }
   __syncthreads();
   const TabEntry* tab0 = s_tab + (U + 1);          // entry of cell j at tab0[j]
-  const float lo_cell = (float)(-(U + 1)), hi_cell = (float)U;
   // -1 kept opaque so that r - (float)hi stays a multiply-add with an fp16 operand
   // (v_fma_mix_f32) instead of a conversion and a subtraction
   float neg_one = -1.f;
@@ -380,8 +379,13 @@ encode_lm_kernel(const uint16_t* __restrict__ x, int T, int mb_per_slice, int n_
 #pragma unroll
       for (int i = 0; i < 16; ++i) ysv[i] = y[b][i] * scale;
       auto fetch = [&](int i) -> Ent {
-        // |ys| <= U up to rounding, so the clamp only guards non-finite inputs
-        return *reinterpret_cast<const Ent*>(tab0 + floor_i32(__builtin_amdgcn_fmed3f(ysv[i], lo_cell, hi_cell)));
+        // |ys| <= U (1 + 1e-6): y is the unnormalised rotation of x (|y| <= sqrt(d) |x|) and
+        // scale = U / (sqrt(d) |x|), so floor(ys) lies in [-(U + 1), U] and no clamp is
+        // needed.  ys is NaN only when the input norm is not finite (scale 0): the
+        // conversion then gives 0, or a saturated value whose offset wraps to cell 0 / -1
+        // (16 x 2^31 = 0 and 16 (2^31 - 1) = -16 modulo 2^32), so every read stays inside
+        // the table.
+        return *reinterpret_cast<const Ent*>(tab0 + floor_i32(ysv[i]));
       };
       Ent ring[kAhead];
       if constexpr (!COUNT) {
