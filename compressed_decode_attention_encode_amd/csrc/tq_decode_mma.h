@@ -41,11 +41,11 @@
 // P'' = p n (hi/lo fp16) against the centroid values (hi/lo, through a value code-pair table);
 // their sum stays in the rotated domain for the merge kernel's single inverse butterfly.
 //
-// Codes become operands through LDS tables: one 8-byte entry (hi pair, lo pair) per pair of
-// codes (2 KB for 4-bit codes), and one 16-byte xor-mask entry per 8 sign bits.  Tiles are
-// staged as in the vector-ALU kernel (coalesced 16-byte loads, next tile in flight), value
-// codes and scales transposed (word-major) so that 4 consecutive tokens of one word are one
-// 16-byte LDS read.
+// Codes become operands through LDS tables: a (hi pair, lo pair) entry per pair of 2/3-bit
+// codes; for 4-bit codes read straight into registers a (hi, lo) word per single code, paired
+// with a query operand that holds every value twice; and a 16-byte entry of four fp16 +-1
+// pairs per 8 sign bits.  The next tile's loads are in flight through the current tile; group
+// value codes are staged row-major and read back with the transposing LDS read.
 #pragma once
 
 #include "tq_decode_main.h"
@@ -168,7 +168,14 @@ struct MmaGeom {
   static constexpr int NVW = (VK == TQ_V_LM_ROT && VB == 3) ? D : 0;
   static constexpr int OFF_VW = al4(OFF_VT + (NVT ? VLO + NVT : 0));
   static constexpr int OFF_SGT = al4(OFF_VW + NVW);
-  static constexpr int OFF_ST = al4(OFF_SGT + (QJL ? 4 * 256 : 0));
+  // 4-bit Lloyd-Max keys from registers with folded query columns: the score operand word is
+  // (hi, lo) of ONE code, from a 16-entry table (its reads never collide in the LDS banks, where
+  // the 256-entry pair table's did), against a query operand holding every value twice, so one
+  // product sums c_hi q + c_lo q over 16 dimensions; rows of the doubled operand are D + 4 words
+  static constexpr bool ILV = DIRECT && KB == 4 && 2 * NREP <= 16;
+  static constexpr int QSD = D + 4;
+  static constexpr int OFF_BQD = al4(OFF_SGT + (QJL ? 4 * 256 : 0));
+  static constexpr int OFF_ST = al4(OFF_BQD + (ILV ? 2 * NRB * QSD : 0));
   static_assert(OFF_BQ % 4 == 0 && OFF_SGT % 4 == 0 && OFF_ST % 4 == 0, "16-byte LDS reads of the operand, sign and staging regions");
   // the four staging areas also hold the waves' value sums for the merge
   static constexpr int STAGE_ALL = (4 * STAGE > 4 * NREP * D) ? 4 * STAGE : 4 * NREP * D;
@@ -447,11 +454,20 @@ decode_mma_kernel(const DecodeArgs A) {
 
   // code-pair tables: entry pc = (code a = low bits, code b): the hi pair of 8 c at word pc, the
   // lo pair at word PLO + pc
-  for (int i = threadIdx.x; i < M::NPT; i += 256) {
-    uint32_t hi, lo;
-    split_f16x2(A.kcent[i & (LK - 1)] * kMmaCentScale, A.kcent[i >> KB] * kMmaCentScale, hi, lo);
-    smw[M::OFF_PT + i] = hi;
-    smw[M::OFF_PT + M::PLO + i] = lo;
+  if constexpr (M::ILV) {
+    // single-code table: word c = (hi, lo) fp16 halves of 8 c[c]
+    for (int i = threadIdx.x; i < 16; i += 256) {
+      uint32_t hi, lo;
+      split_f16x2(A.kcent[i] * kMmaCentScale, A.kcent[i] * kMmaCentScale, hi, lo);
+      smw[M::OFF_PT + i] = (hi & 0xFFFFu) | (lo << 16);
+    }
+  } else {
+    for (int i = threadIdx.x; i < M::NPT; i += 256) {
+      uint32_t hi, lo;
+      split_f16x2(A.kcent[i & (LK - 1)] * kMmaCentScale, A.kcent[i >> KB] * kMmaCentScale, hi, lo);
+      smw[M::OFF_PT + i] = hi;
+      smw[M::OFF_PT + M::PLO + i] = lo;
+    }
   }
   for (int i = threadIdx.x; i < M::NVT; i += 256) {
     uint32_t hi, lo;
@@ -504,6 +520,13 @@ decode_mma_kernel(const DecodeArgs A) {
       bq[RS + o] = (_Float16)(a - (float)ah);
       bq[2 * RS + o] = sh;
       bq[3 * RS + o] = (_Float16)(s - (float)sh);
+      if constexpr (M::ILV) {
+        // the same hi / lo halves, each value twice: rows [NRB][QSD] words, hi region then lo
+        const uint32_t hb = __builtin_bit_cast(uint16_t, ah), lb = __builtin_bit_cast(uint16_t, (_Float16)(a - (float)ah));
+        const int od = (i / D) * M::QSD + i % D;
+        smw[M::OFF_BQD + od] = hb | (hb << 16);
+        smw[M::OFF_BQD + M::NRB * M::QSD + od] = lb | (lb << 16);
+      }
     }
   }
   __syncthreads();
@@ -742,16 +765,35 @@ decode_mma_kernel(const DecodeArgs A) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
           const uint32_t y = dk.codes(mb, kb, al[mb]);   // the lane's 8 codes, KB bits each
-          mma_u4_t ahi, alo;
+          if constexpr (M::ILV) {
+            // two products of 16 dimensions: lane q4 takes dimensions q4 D/4 + 8 kb + 4 m .. + 3
+            // (m = 0, 1; the codes' order above), k slots 2 i, 2 i + 1 = (hi, lo) of one code
+            // against that dimension's query value twice
+            const uint32_t* bqd = smw + M::OFF_BQD +
+                ((l16 >= NREP && l16 < 2 * NREP) ? M::NRB * M::QSD + (l16 - NREP) * M::QSD : hq * M::QSD) + q4 * (D / 4) + 8 * kb;
+            const uint4 d0 = *reinterpret_cast<const uint4*>(bqd), d1 = *reinterpret_cast<const uint4*>(bqd + 4);
+            // byte k of y << 2 (y >> 2), masked to 0x3C: 4 x code 2k (2k + 1), the entry's offset
+            const uint32_t yy = (y << 2) & 0x3C3C3C3Cu, yo = (y >> 2) & 0x3C3C3C3Cu;
+            const char* tb = reinterpret_cast<const char*>(ptab);
+            auto T = [&](uint32_t w, int k) {
+              return *reinterpret_cast<const uint32_t*>(tb + __builtin_amdgcn_perm(0u, w, 0x0C0C0C00u | (uint32_t)k));
+            };
+            const mma_u4_t a0 = mma_u4_t{T(yy, 0), T(yo, 0), T(yy, 1), T(yo, 1)};
+            const mma_u4_t a1 = mma_u4_t{T(yy, 2), T(yo, 2), T(yy, 3), T(yo, 3)};
+            sacc[mb] = mma16(a0, mma_u4_t{d0.x, d0.y, d0.z, d0.w}, sacc[mb]);
+            sacc[mb] = mma16(a1, mma_u4_t{d1.x, d1.y, d1.z, d1.w}, sacc[mb]);
+          } else {
+            mma_u4_t ahi, alo;
 #pragma unroll
-          for (int pp = 0; pp < 4; ++pp) {
-            const uint32_t pc = (y >> (2 * KB * pp)) & (M::NPT - 1);
-            ahi[pp] = ptab[pc];
-            alo[pp] = ptab[M::PLO + pc];
+            for (int pp = 0; pp < 4; ++pp) {
+              const uint32_t pc = (y >> (2 * KB * pp)) & (M::NPT - 1);
+              ahi[pp] = ptab[pc];
+              alo[pp] = ptab[M::PLO + pc];
+            }
+            sacc[mb] = mma16(ahi, bq0, sacc[mb]);
+            sacc[mb] = mma16(alo, bq0, sacc[mb]);
+            if constexpr (!FOLD) sacc[mb] = mma16(ahi, bq1, sacc[mb]);
           }
-          sacc[mb] = mma16(ahi, bq0, sacc[mb]);
-          sacc[mb] = mma16(alo, bq0, sacc[mb]);
-          if constexpr (!FOLD) sacc[mb] = mma16(ahi, bq1, sacc[mb]);
           if constexpr (QJL) {
             // the sign bits as +-1 operands; gamma scales the token's sum afterwards
             const uint32_t sb = dk.sign_byte(mb, kb, q4);

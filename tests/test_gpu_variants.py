@@ -37,6 +37,7 @@ VARIANTS = [
     (128, "lm_qjl", 4, "group_sym", 2, 12, 2, "bf16", 333, 5),
     (256, "lm_qjl", 3, "group_sym", 2, 2, 2, "f16", 150, 31),
     (256, "lm_qjl", 2, "group_sym", 4, 8, 1, "f16", 190, 0),
+    (256, "lm_qjl", 4, "group_sym", 4, 10, 2, "bf16", 150, 9),      # 4-bit single-code operands
     (64, "affine8", 8, "lm_rot", 2, 8, 2, "f16", 280, 0),
     (64, "affine8", 8, "lm_rot", 4, 2, 2, "bf16", 200, 20),
     (128, "affine8", 8, "lm_rot", 2, 14, 2, "f16", 222, 100),
@@ -46,6 +47,7 @@ VARIANTS = [
     (64, "lm_mse", 2, "group_sym", 2, 16, 2, "bf16", 260, 0),
     (128, "lm_mse", 4, "lm_rot", 4, 8, 1, "f16", 333, 64),
     (128, "lm_mse", 3, "group_sym", 4, 6, 2, "bf16", 222, 5),
+    (128, "lm_mse", 4, "group_sym", 2, 10, 2, "f16", 200, 5),      # 4-bit single-code operands
     (256, "lm_mse", 4, "lm_rot", 2, 10, 2, "f16", 190, 31),
     (256, "lm_mse", 2, "group_sym", 2, 3, 3, "f16", 150, 0),
     # 16-bit keys (V-only mode)
