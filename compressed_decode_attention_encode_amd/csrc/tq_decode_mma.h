@@ -738,6 +738,14 @@ decode_mma_kernel(const DecodeArgs A) {
       for (int kb = 0; kb < NKB; ++kb) {
         const int kw = q4 * (D / 8) + 4 * kb;     // word offset of this lane's 8 query dimensions
         mma_u4_t bq0, bq1, bq2, bq3;
+        mma_u4_t bqd0, bqd1;                       // doubled query operands (4-bit single-code path)
+        if constexpr (M::ILV) {
+          const uint32_t* bqd = smw + M::OFF_BQD +
+              ((l16 >= NREP && l16 < 2 * NREP) ? M::NRB * M::QSD + (l16 - NREP) * M::QSD : hq * M::QSD) + 2 * kw;
+          const uint4 d0 = *reinterpret_cast<const uint4*>(bqd), d1 = *reinterpret_cast<const uint4*>(bqd + 4);
+          bqd0 = mma_u4_t{d0.x, d0.y, d0.z, d0.w};
+          bqd1 = mma_u4_t{d1.x, d1.y, d1.z, d1.w};
+        }
         if constexpr (FOLD) {
           // folded columns: hi or lo part by lane (region 0 / 1; the projected query in 2 / 3)
           const uint32_t* src = bqf + kw;
@@ -768,10 +776,7 @@ decode_mma_kernel(const DecodeArgs A) {
           if constexpr (M::ILV) {
             // two products of 16 dimensions: lane q4 takes dimensions q4 D/4 + 8 kb + 4 m .. + 3
             // (m = 0, 1; the codes' order above), k slots 2 i, 2 i + 1 = (hi, lo) of one code
-            // against that dimension's query value twice
-            const uint32_t* bqd = smw + M::OFF_BQD +
-                ((l16 >= NREP && l16 < 2 * NREP) ? M::NRB * M::QSD + (l16 - NREP) * M::QSD : hq * M::QSD) + q4 * (D / 4) + 8 * kb;
-            const uint4 d0 = *reinterpret_cast<const uint4*>(bqd), d1 = *reinterpret_cast<const uint4*>(bqd + 4);
+            // against that dimension's query value twice (bqd0 / bqd1, read once per kb)
             // byte k of y << 2 (y >> 2), masked to 0x3C: 4 x code 2k (2k + 1), the entry's offset
             const uint32_t yy = (y << 2) & 0x3C3C3C3Cu, yo = (y >> 2) & 0x3C3C3C3Cu;
             const char* tb = reinterpret_cast<const char*>(ptab);
@@ -780,8 +785,8 @@ decode_mma_kernel(const DecodeArgs A) {
             };
             const mma_u4_t a0 = mma_u4_t{T(yy, 0), T(yo, 0), T(yy, 1), T(yo, 1)};
             const mma_u4_t a1 = mma_u4_t{T(yy, 2), T(yo, 2), T(yy, 3), T(yo, 3)};
-            sacc[mb] = mma16(a0, mma_u4_t{d0.x, d0.y, d0.z, d0.w}, sacc[mb]);
-            sacc[mb] = mma16(a1, mma_u4_t{d1.x, d1.y, d1.z, d1.w}, sacc[mb]);
+            sacc[mb] = mma16(a0, bqd0, sacc[mb]);
+            sacc[mb] = mma16(a1, bqd1, sacc[mb]);
           } else {
             mma_u4_t ahi, alo;
 #pragma unroll
