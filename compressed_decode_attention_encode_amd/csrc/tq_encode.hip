@@ -42,7 +42,7 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 // Decisions work on y, thresholds and centroids scaled by the table's cell unit U = 2^e
 // (exact), at least 2^6 for keys: the residual then enters the fp16 split as |r| U, where
 // its low half stays a normal fp16 number for all but the smallest residuals (those keep an
-// absolute error below 2^-25 / U); decisions are unchanged, the projection's sign needs no
+// absolute error below 2^-24 / U); decisions are unchanged, the projection's sign needs no
 // rescaling and gamma = sqrt(sum r'^2) / U.
 constexpr int kKeyTabMinExp = 6;
 
