@@ -560,7 +560,13 @@ decode_mma_kernel(const DecodeArgs A) {
   const uint32_t vmask = (((1u << VB) - 1u) * 0x00010001u) << vsh;
   const uint32_t vls = (uint32_t)MV - vsh;
 
-  float m_run = -INFINITY, l_part = 0.f;        // head l16 (per lane: its tokens)
+  // scale of the score products to the log2 domain: affine and 16-bit keys carry the query
+  // operands' 16, Lloyd-Max keys the 2^8 of the centroid and query operand scales
+  constexpr float PS = (AFF || F16K) ? 1.f / kMmaAffQScale : kMmaUnscale;
+  // zero kept opaque so that n (fp16) times the score stays one mixed-precision multiply-add
+  float zero_v = 0.f;
+  asm volatile("" : "+v"(zero_v));
+  float m_run = -INFINITY, l_part = 0.f;        // head l16 (per lane: its tokens; product scale)
   float off[NG];                                // sum of P' per group, head l16
   float moff[ASYM ? NG : 1];                    // min/max values: sum of p m per group, head l16
   mma_f4_t acc[NNB];                            // head 4 q4 + r, dimension 16 nb + l16
@@ -633,7 +639,7 @@ decode_mma_kernel(const DecodeArgs A) {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) p[mb][r] = sacc[mb][r] * (1.f / kMmaAffQScale);
+        for (int r = 0; r < 4; ++r) p[mb][r] = sacc[mb][r];
     } else if constexpr (!AFF && !M::DIRECT) {
       mma_f4_t sacc[MB], sqj[QJL ? MB : 1];      // codebook term; QJL sign term (before gamma)
 #pragma unroll
@@ -713,16 +719,16 @@ decode_mma_kernel(const DecodeArgs A) {
             if constexpr (QJL) sqj[mb][r] += row_shl<FOLD ? NREP : 1>(sqj[mb][r]);
           }
       }
-      // times n (fp16 with gamma for LM + QJL keys, fp32 for MSE-only keys) and the unscale
+      // times n (fp16 with gamma for LM + QJL keys, fp32 for MSE-only keys; the unscale PS is
+      // applied in the softmax)
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         const uint4 nw = *reinterpret_cast<const uint4*>(stak + 16 * mb + 4 * q4);
         const uint32_t nn[4] = {nw.x, nw.y, nw.z, nw.w};
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float n = QJL ? f16_to_f32(nn[r] & 0xFFFFu) : __uint_as_float(nn[r]);
           const float sc = QJL ? fmaf(f16_to_f32(nn[r] >> 16), sqj[QJL ? mb : 0][r], sacc[mb][r]) : sacc[mb][r];
-          p[mb][r] = sc * (n * kMmaUnscale);
+          p[mb][r] = QJL ? fmaf(f16_to_f32(nn[r] & 0xFFFFu), sc, zero_v) : sc * __uint_as_float(nn[r]);
         }
       }
     } else if constexpr (!AFF) {
@@ -818,16 +824,16 @@ decode_mma_kernel(const DecodeArgs A) {
             if constexpr (QJL) sqj[mb][r] += row_shl<FOLD ? NREP : 1>(sqj[mb][r]);
           }
       }
-      // times n (fp16 with gamma for LM + QJL keys, fp32 for MSE-only keys) and the unscale;
-      // accumulator row r of this lane is token 16 mb + 4 q4 + r, whose aux word lane 4 q4 + r holds
+      // times n (fp16 with gamma for LM + QJL keys, fp32 for MSE-only keys; the unscale PS is
+      // applied in the softmax); accumulator row r of this lane is token 16 mb + 4 q4 + r, whose
+      // aux word lane 4 q4 + r holds
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const uint32_t nn = (uint32_t)__shfl((int)dk.ka[mb], 4 * q4 + r);
-          const float n = QJL ? f16_to_f32(nn & 0xFFFFu) : __uint_as_float(nn);
           const float sc = QJL ? fmaf(f16_to_f32(nn >> 16), sqj[QJL ? mb : 0][r], sacc[mb][r]) : sacc[mb][r];
-          p[mb][r] = sc * (n * kMmaUnscale);
+          p[mb][r] = QJL ? fmaf(f16_to_f32(nn & 0xFFFFu), sc, zero_v) : sc * __uint_as_float(nn);
         }
       }
     } else {
@@ -893,10 +899,6 @@ decode_mma_kernel(const DecodeArgs A) {
           }
         }
       }
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) p[mb][r] *= 1.f / kMmaAffQScale;
     }
     if (__builtin_amdgcn_readfirstlane(nv) < TT) {      // the last tile of a split: tokens past its end score -inf
 #pragma unroll
@@ -914,15 +916,18 @@ decode_mma_kernel(const DecodeArgs A) {
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float mn = fmaxf(m_run, mx);
-    // v_exp_f32 directly: arguments are <= 0, results in [0, 1] (a result below 2^-126 is
-    // flushed to zero, far below the fp32 sums it joins)
-    const float alpha = (mn == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - mn);
+    // scores and the running maximum are held in the products' scale: the log2-domain value is
+    // PS times them (a power of two, so exp2(PS p - PS mn) is exactly exp2 of the unscaled
+    // difference).  v_exp_f32 directly: arguments are <= 0, results in [0, 1] (a result below
+    // 2^-126 is flushed to zero, far below the fp32 sums it joins)
+    const float alpha = (mn == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f((m_run - mn) * PS);
+    const float nms = -mn * PS;
     float ps = 0.f;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        p[mb][r] = __builtin_amdgcn_exp2f(p[mb][r] - mn);
+        p[mb][r] = __builtin_amdgcn_exp2f(fmaf(p[mb][r], PS, nms));
         ps += p[mb][r];
       }
     }
@@ -1177,7 +1182,7 @@ decode_mma_kernel(const DecodeArgs A) {
     }
   }
   if (lane < NREP) {
-    s_mrg_m[wave * NREP + lane] = m_run;
+    s_mrg_m[wave * NREP + lane] = m_run * PS;   // log2 domain
     s_mrg_l[wave * NREP + lane] = l_part;
   }
   __syncthreads();
