@@ -92,6 +92,9 @@ struct DecodeGeom {
 // paths join, which serialises the prefetch behind the tile in flight).
 // Fourth word of a raw buffer resource on CDNA (gfx9 family): 32-bit data format, no swizzle.
 constexpr int kBufferRsrcWord3 = 0x00020000;
+// cache policy of the packed-cache tile loads: non-temporal (each tile is read once per decode
+// step, so it is streamed rather than kept in the caches)
+constexpr int kTileLoadPolicy = 2;
 
 template <int W, int LS, int TR = kTile, bool DW = false>
 struct RowLoader {
@@ -111,7 +114,7 @@ struct RowLoader {
       const __amdgpu_buffer_rsrc_t rs =
           __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(g), (short)0, 4 * nvalid, kBufferRsrcWord3);
 #pragma unroll
-      for (int i = 0; i < NR; ++i) r[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * (i * kWave + lane), 0, 0);
+      for (int i = 0; i < NR; ++i) r[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * (i * kWave + lane), 0, kTileLoadPolicy);
       return;
     }
     const int nvalid = rows * W;

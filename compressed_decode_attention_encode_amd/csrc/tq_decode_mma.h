@@ -174,7 +174,7 @@ struct MmaGeom {
   // product sums c_hi q + c_lo q over 16 dimensions; rows of the doubled operand are D + 4 words
   static constexpr bool ILV = DIRECT && KB == 4 && 2 * NREP <= 16;
   static constexpr int QSD = D + 4;
-  static constexpr int OFF_BQD = al4(OFF_SGT + (QJL ? 4 * 256 : 0));
+  static constexpr int OFF_BQD = al4(OFF_SGT + (QJL ? 2 * 16 : 0));
   static constexpr int OFF_ST = al4(OFF_BQD + (ILV ? 2 * NRB * QSD : 0));
   static_assert(OFF_BQ % 4 == 0 && OFF_SGT % 4 == 0 && OFF_ST % 4 == 0, "16-byte LDS reads of the operand, sign and staging regions");
   // the four staging areas also hold the waves' value sums for the merge
@@ -231,26 +231,26 @@ struct DirectKeys {
       if constexpr (KB != 3 && KWL % 4 == 0) {
 #pragma unroll
         for (int i = 0; i < KWL; i += 4) {
-          const auto v = __builtin_amdgcn_raw_buffer_load_b128(rc, cb + 4 * i, 0, 0);
+          const auto v = __builtin_amdgcn_raw_buffer_load_b128(rc, cb + 4 * i, 0, kTileLoadPolicy);
           kc[mb][i] = v[0]; kc[mb][i + 1] = v[1]; kc[mb][i + 2] = v[2]; kc[mb][i + 3] = v[3];
         }
       } else if constexpr (KB != 3 && KWL == 2) {
-        const auto v = __builtin_amdgcn_raw_buffer_load_b64(rc, cb, 0, 0);
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(rc, cb, 0, kTileLoadPolicy);
         kc[mb][0] = v[0]; kc[mb][1] = v[1];
       } else {
 #pragma unroll
-        for (int i = 0; i < KWL; ++i) kc[mb][i] = __builtin_amdgcn_raw_buffer_load_b32(rc, cb + 4 * i, 0, 0);
+        for (int i = 0; i < KWL; ++i) kc[mb][i] = __builtin_amdgcn_raw_buffer_load_b32(rc, cb + 4 * i, 0, kTileLoadPolicy);
       }
-      ka[mb] = __builtin_amdgcn_raw_buffer_load_b32(ra, 4 * tok, 0, 0);
+      ka[mb] = __builtin_amdgcn_raw_buffer_load_b32(ra, 4 * tok, 0, kTileLoadPolicy);
       if constexpr (QJL) {
         const __amdgpu_buffer_rsrc_t rs =
             __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(ks_g), (short)0, 4 * rows * WS, kBufferRsrcWord3);
         const int sw0 = (DPL * q4) / 32;
         if constexpr (SWL == 2) {
-          const auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, 4 * (tok * WS + sw0), 0, 0);
+          const auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, 4 * (tok * WS + sw0), 0, kTileLoadPolicy);
           ks[mb][0] = v[0]; ks[mb][1] = v[1];
         } else {
-          ks[mb][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * (tok * WS + sw0), 0, 0);
+          ks[mb][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * (tok * WS + sw0), 0, kTileLoadPolicy);
         }
       }
     }
@@ -328,20 +328,20 @@ struct GroupValueTile {
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(vc_g), (short)0, 4 * rows * WV, kBufferRsrcWord3);
 #pragma unroll
     for (int u = 0; u < NVL; ++u) {
-      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rc, 16 * (lane + 64 * u), 0, 0);
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rc, 16 * (lane + 64 * u), 0, kTileLoadPolicy);
       c[u][0] = v[0]; c[u][1] = v[1]; c[u][2] = v[2]; c[u][3] = v[3];
     }
     const __amdgpu_buffer_rsrc_t ra =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(va_g), (short)0, 4 * rows * WAV, kBufferRsrcWord3);
     if constexpr (NS == 1) {
-      sc[0] = __builtin_amdgcn_raw_buffer_load_b32(ra, 4 * lane, 0, 0);
+      sc[0] = __builtin_amdgcn_raw_buffer_load_b32(ra, 4 * lane, 0, kTileLoadPolicy);
     } else if constexpr (NS == 2) {
-      const auto v = __builtin_amdgcn_raw_buffer_load_b64(ra, 8 * lane, 0, 0);
+      const auto v = __builtin_amdgcn_raw_buffer_load_b64(ra, 8 * lane, 0, kTileLoadPolicy);
       sc[0] = v[0]; sc[1] = v[1];
     } else {
 #pragma unroll
       for (int u = 0; u < NS / 4; ++u) {
-        const auto v = __builtin_amdgcn_raw_buffer_load_b128(ra, 4 * NS * lane + 16 * u, 0, 0);
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(ra, 4 * NS * lane + 16 * u, 0, kTileLoadPolicy);
         sc[4 * u] = v[0]; sc[4 * u + 1] = v[1]; sc[4 * u + 2] = v[2]; sc[4 * u + 3] = v[3];
       }
     }
@@ -368,6 +368,22 @@ struct GroupValueTile {
 };
 
 typedef int mma_i2_t __attribute__((ext_vector_type(2)));
+
+// the 8 QJL sign bits of one k-block as the score operand's four fp16 pairs of +-1: two reads
+// of the 16-entry table of 4-bit patterns (entry n: words 2 n, 2 n + 1)
+__device__ __forceinline__ mma_u4_t sign_operand(const uint32_t* sgt, uint32_t sb) {
+  const uint2 lo = *reinterpret_cast<const uint2*>(sgt + 2 * (sb & 15u));
+  const uint2 hi = *reinterpret_cast<const uint2*>(sgt + 2 * ((sb >> 4) & 15u));
+  return mma_u4_t{lo.x, lo.y, hi.x, hi.y};
+}
+// the same from byte offsets into the table: byte k of `ol` (`oh`) is 8 x the low (high) nibble
+// of sign byte k, so one byte-select gives each read's address
+__device__ __forceinline__ mma_u4_t sign_operand_at(const uint32_t* sgt, uint32_t ol, uint32_t oh, int k) {
+  const char* t = reinterpret_cast<const char*>(sgt);
+  const uint2 lo = *reinterpret_cast<const uint2*>(t + __builtin_amdgcn_perm(0u, ol, 0x0C0C0C00u | (uint32_t)k));
+  const uint2 hi = *reinterpret_cast<const uint2*>(t + __builtin_amdgcn_perm(0u, oh, 0x0C0C0C00u | (uint32_t)k));
+  return mma_u4_t{lo.x, lo.y, hi.x, hi.y};
+}
 
 // the transposing 8-byte LDS read (ds_read_b64_tr_b4) at word `w` of the LDS
 __device__ __forceinline__ uint2 lds_read_tr4(const uint32_t* w) {
@@ -476,12 +492,13 @@ decode_mma_kernel(const DecodeArgs A) {
     smw[M::OFF_VT + M::VLO + i] = lo;
   }
   for (int j = threadIdx.x; j < M::NVW; j += 256) smw[M::OFF_VW + j] = (j / 10) * M::TS | (3 * (j % 10)) << 16;
-  // sign table: 8 stored bits (bit 1 <=> sigma = +1) -> 4 fp16 pairs of +-1
+  // sign table: 4 stored bits (bit 1 <=> sigma = +1) -> 2 fp16 pairs of +-1; sixteen 8-byte
+  // entries fill the 32 LDS banks once, so no two lanes' reads of it collide
   if constexpr (QJL) {
-    const int i = threadIdx.x;
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      smw[M::OFF_SGT + 4 * i + k] = 0x3C003C00u ^ ((((i >> (2 * k)) & 1) ? 0u : 0x8000u) | (((i >> (2 * k + 1)) & 1) ? 0u : 0x80000000u));
+    if (threadIdx.x < 32) {
+      const int i = threadIdx.x >> 1, k = threadIdx.x & 1;
+      smw[M::OFF_SGT + threadIdx.x] = 0x3C003C00u ^ ((((i >> (2 * k)) & 1) ? 0u : 0x8000u) | (((i >> (2 * k + 1)) & 1) ? 0u : 0x80000000u));
+    }
   }
   prepare_queries<D, NREP, KK, KB, VK, VB, false, NQ>(A, b, g, sm);
   // 16-bit keys at head_dim 256 come in either storage type: bf16 rows are bf16 matrix-core
@@ -702,9 +719,7 @@ decode_mma_kernel(const DecodeArgs A) {
           if constexpr (!FOLD) sacc[mb] = mma16(ahi, bq1, sacc[mb]);
           if constexpr (QJL) {
             // the sign bits as +-1 operands; gamma scales the token's sum afterwards
-            const uint32_t sb = (sts[tok * M::SS + kb] >> (8 * q4)) & 0xFFu;
-            const uint4 mk = *reinterpret_cast<const uint4*>(sgt + 4 * sb);
-            const mma_u4_t asg = mma_u4_t{mk.x, mk.y, mk.z, mk.w};
+            const mma_u4_t asg = sign_operand(sgt, (sts[tok * M::SS + kb] >> (8 * q4)) & 0xFFu);
             sqj[mb] = mma16(asg, bq2, sqj[mb]);
             if constexpr (!FOLD) sqj[mb] = mma16(asg, bq3, sqj[mb]);
           }
@@ -740,6 +755,17 @@ decode_mma_kernel(const DecodeArgs A) {
       uint32_t al[MB][DK::SAL];                  // 3-bit codes: each block's aligned stream
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) dk.align3(mb, q4, al[mb]);
+      // QJL sign words as sign-table byte offsets: byte k of sol (soh) = 8 x nibble 0 (1) of byte k
+      uint32_t sol[QJL ? MB : 1][DK::SWL], soh[QJL ? MB : 1][DK::SWL];
+      if constexpr (QJL) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int w = 0; w < DK::SWL; ++w) {
+            sol[mb][w] = (dk.ks[mb][w] << 3) & 0x78787878u;
+            soh[mb][w] = (dk.ks[mb][w] >> 1) & 0x78787878u;
+          }
+      }
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         const int kw = q4 * (D / 8) + 4 * kb;     // word offset of this lane's 8 query dimensions
@@ -807,9 +833,8 @@ decode_mma_kernel(const DecodeArgs A) {
           }
           if constexpr (QJL) {
             // the sign bits as +-1 operands; gamma scales the token's sum afterwards
-            const uint32_t sb = dk.sign_byte(mb, kb, q4);
-            const uint4 mk = *reinterpret_cast<const uint4*>(sgt + 4 * sb);
-            const mma_u4_t asg = mma_u4_t{mk.x, mk.y, mk.z, mk.w};
+            static_assert(DK::DPL >= 32, "a lane's sign bits of a k-block are one byte of its words");
+            const mma_u4_t asg = sign_operand_at(sgt, sol[mb][kb >> 2], soh[mb][kb >> 2], kb & 3);
             sqj[mb] = mma16(asg, bq2, sqj[mb]);
             if constexpr (!FOLD) sqj[mb] = mma16(asg, bq3, sqj[mb]);
           }
