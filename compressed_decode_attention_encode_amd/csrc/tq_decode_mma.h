@@ -766,6 +766,55 @@ decode_mma_kernel(const DecodeArgs A) {
             soh[mb][w] = (dk.ks[mb][w] >> 1) & 0x78787878u;
           }
       }
+      if constexpr (M::ILV) {
+        // 4-bit codes, single-code operands (below): the table reads of step s + 1 (one k-block
+        // of one 16-token block) are issued before the products of step s wait for theirs, so
+        // the LDS latency of each step hides behind the previous step's products
+        constexpr int NSTEP = NKB * MB;
+        const char* tb = reinterpret_cast<const char*>(ptab);
+        const uint32_t* bqd_row = smw + M::OFF_BQD +
+            ((l16 >= NREP && l16 < 2 * NREP) ? M::NRB * M::QSD + (l16 - NREP) * M::QSD : hq * M::QSD) + 2 * q4 * (D / 8);
+        struct Step { mma_u4_t a0, a1, sg; };
+        auto operands = [&](int st) {
+          const int kb = st / MB, mb = st % MB;
+          const uint32_t y = dk.codes(mb, kb, al[mb]);
+          const uint32_t yy = (y << 2) & 0x3C3C3C3Cu, yo = (y >> 2) & 0x3C3C3C3Cu;
+          auto T = [&](uint32_t w, int k) {
+            return *reinterpret_cast<const uint32_t*>(tb + __builtin_amdgcn_perm(0u, w, 0x0C0C0C00u | (uint32_t)k));
+          };
+          Step o;
+          o.a0 = mma_u4_t{T(yy, 0), T(yo, 0), T(yy, 1), T(yo, 1)};
+          o.a1 = mma_u4_t{T(yy, 2), T(yo, 2), T(yy, 3), T(yo, 3)};
+          if constexpr (QJL) o.sg = sign_operand_at(sgt, sol[mb][kb >> 2], soh[mb][kb >> 2], kb & 3);
+          else o.sg = mma_u4_t{0u, 0u, 0u, 0u};
+          return o;
+        };
+        Step cur = operands(0);
+        mma_u4_t bqd0, bqd1, bq2;
+#pragma unroll
+        for (int st = 0; st < NSTEP; ++st) {
+          const int kb = st / MB, mb = st % MB;
+          if (mb == 0) {
+            const uint4 d0 = *reinterpret_cast<const uint4*>(bqd_row + 8 * kb);
+            const uint4 d1 = *reinterpret_cast<const uint4*>(bqd_row + 8 * kb + 4);
+            bqd0 = mma_u4_t{d0.x, d0.y, d0.z, d0.w};
+            bqd1 = mma_u4_t{d1.x, d1.y, d1.z, d1.w};
+            if constexpr (QJL) {
+              const uint4 r2 = *reinterpret_cast<const uint4*>(bqf + q4 * (D / 8) + 4 * kb + 2 * RWQ);
+              bq2 = mma_u4_t{r2.x, r2.y, r2.z, r2.w};
+            }
+          }
+          Step nxt = cur;
+          if (st + 1 < NSTEP) nxt = operands(st + 1);
+          // the products of step st from here on (a volatile statement keeps the reads above it)
+          asm volatile("" : "+v"(cur.a0), "+v"(cur.a1));
+          if constexpr (QJL) asm volatile("" : "+v"(cur.sg));
+          sacc[mb] = mma16(cur.a0, bqd0, sacc[mb]);
+          sacc[mb] = mma16(cur.a1, bqd1, sacc[mb]);
+          if constexpr (QJL) sqj[mb] = mma16(cur.sg, bq2, sqj[mb]);
+          cur = nxt;
+        }
+      } else
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         const int kw = q4 * (D / 8) + 4 * kb;     // word offset of this lane's 8 query dimensions
