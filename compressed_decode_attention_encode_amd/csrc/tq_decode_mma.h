@@ -767,9 +767,12 @@ decode_mma_kernel(const DecodeArgs A) {
           }
       }
       if constexpr (M::ILV) {
-        // 4-bit codes, single-code operands (below): the table reads of step s + 1 (one k-block
-        // of one 16-token block) are issued before the products of step s wait for theirs, so
-        // the LDS latency of each step hides behind the previous step's products
+        // 4-bit codes, single-code operands: per step (one k-block of one 16-token block) two
+        // products of 16 dimensions; lane q4 takes dimensions q4 D/4 + 8 kb + 4 m .. + 3 (m = 0,
+        // 1), k slots 2 i, 2 i + 1 = (hi, lo) of one code against that dimension's query value
+        // twice (bqd0 / bqd1, read once per k-block).  The table reads of step s + 1 are issued
+        // before the products of step s wait for theirs, so the LDS latency of each step hides
+        // behind the previous step's products
         constexpr int NSTEP = NKB * MB;
         const char* tb = reinterpret_cast<const char*>(ptab);
         const uint32_t* bqd_row = smw + M::OFF_BQD +
@@ -778,6 +781,7 @@ decode_mma_kernel(const DecodeArgs A) {
         auto operands = [&](int st) {
           const int kb = st / MB, mb = st % MB;
           const uint32_t y = dk.codes(mb, kb, al[mb]);
+          // byte k of y << 2 (y >> 2), masked to 0x3C: 4 x code 2k (2k + 1), the entry's offset
           const uint32_t yy = (y << 2) & 0x3C3C3C3Cu, yo = (y >> 2) & 0x3C3C3C3Cu;
           auto T = [&](uint32_t w, int k) {
             return *reinterpret_cast<const uint32_t*>(tb + __builtin_amdgcn_perm(0u, w, 0x0C0C0C00u | (uint32_t)k));
@@ -817,16 +821,9 @@ decode_mma_kernel(const DecodeArgs A) {
       } else
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
+        // 2/3-bit codes (and 4-bit codes with n_rep > 8): code-pair operands
         const int kw = q4 * (D / 8) + 4 * kb;     // word offset of this lane's 8 query dimensions
         mma_u4_t bq0, bq1, bq2, bq3;
-        mma_u4_t bqd0, bqd1;                       // doubled query operands (4-bit single-code path)
-        if constexpr (M::ILV) {
-          const uint32_t* bqd = smw + M::OFF_BQD +
-              ((l16 >= NREP && l16 < 2 * NREP) ? M::NRB * M::QSD + (l16 - NREP) * M::QSD : hq * M::QSD) + 2 * kw;
-          const uint4 d0 = *reinterpret_cast<const uint4*>(bqd), d1 = *reinterpret_cast<const uint4*>(bqd + 4);
-          bqd0 = mma_u4_t{d0.x, d0.y, d0.z, d0.w};
-          bqd1 = mma_u4_t{d1.x, d1.y, d1.z, d1.w};
-        }
         if constexpr (FOLD) {
           // folded columns: hi or lo part by lane (region 0 / 1; the projected query in 2 / 3)
           const uint32_t* src = bqf + kw;
@@ -854,32 +851,16 @@ decode_mma_kernel(const DecodeArgs A) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
           const uint32_t y = dk.codes(mb, kb, al[mb]);   // the lane's 8 codes, KB bits each
-          if constexpr (M::ILV) {
-            // two products of 16 dimensions: lane q4 takes dimensions q4 D/4 + 8 kb + 4 m .. + 3
-            // (m = 0, 1; the codes' order above), k slots 2 i, 2 i + 1 = (hi, lo) of one code
-            // against that dimension's query value twice (bqd0 / bqd1, read once per kb)
-            // byte k of y << 2 (y >> 2), masked to 0x3C: 4 x code 2k (2k + 1), the entry's offset
-            const uint32_t yy = (y << 2) & 0x3C3C3C3Cu, yo = (y >> 2) & 0x3C3C3C3Cu;
-            const char* tb = reinterpret_cast<const char*>(ptab);
-            auto T = [&](uint32_t w, int k) {
-              return *reinterpret_cast<const uint32_t*>(tb + __builtin_amdgcn_perm(0u, w, 0x0C0C0C00u | (uint32_t)k));
-            };
-            const mma_u4_t a0 = mma_u4_t{T(yy, 0), T(yo, 0), T(yy, 1), T(yo, 1)};
-            const mma_u4_t a1 = mma_u4_t{T(yy, 2), T(yo, 2), T(yy, 3), T(yo, 3)};
-            sacc[mb] = mma16(a0, bqd0, sacc[mb]);
-            sacc[mb] = mma16(a1, bqd1, sacc[mb]);
-          } else {
-            mma_u4_t ahi, alo;
+          mma_u4_t ahi, alo;
 #pragma unroll
-            for (int pp = 0; pp < 4; ++pp) {
-              const uint32_t pc = (y >> (2 * KB * pp)) & (M::NPT - 1);
-              ahi[pp] = ptab[pc];
-              alo[pp] = ptab[M::PLO + pc];
-            }
-            sacc[mb] = mma16(ahi, bq0, sacc[mb]);
-            sacc[mb] = mma16(alo, bq0, sacc[mb]);
-            if constexpr (!FOLD) sacc[mb] = mma16(ahi, bq1, sacc[mb]);
+          for (int pp = 0; pp < 4; ++pp) {
+            const uint32_t pc = (y >> (2 * KB * pp)) & (M::NPT - 1);
+            ahi[pp] = ptab[pc];
+            alo[pp] = ptab[M::PLO + pc];
           }
+          sacc[mb] = mma16(ahi, bq0, sacc[mb]);
+          sacc[mb] = mma16(alo, bq0, sacc[mb]);
+          if constexpr (!FOLD) sacc[mb] = mma16(ahi, bq1, sacc[mb]);
           if constexpr (QJL) {
             // the sign bits as +-1 operands; gamma scales the token's sum afterwards
             static_assert(DK::DPL >= 32, "a lane's sign bits of a k-block are one byte of its words");
